@@ -1,0 +1,253 @@
+/*
+ * kvc_oracle.c -- plain CPU oracle for attention over a per-layer KV cache.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark load this library.  It shares no
+ * source, header, table or build flag with the HIP library; the two meet only
+ * at the byte level, on inputs made by the seeded generators.
+ *
+ * Everything here is the plain definition written out: loops in the obvious
+ * order, every product and sum in double precision, no blocking, no fusion,
+ * no reordering beyond what the definition states.  Keys are visited in
+ * ascending position, so two calls that see the same keys give bit-identical
+ * results.
+ *
+ * Pages followed (cited by address and section title):
+ *   [KV-1] gitcode.csdn.net/69e62cef0a2f6a37c5a11c4f.html  (miniONNXRuntime GPT-2)
+ *          sections "KV Cache 原理", "Decode Shape 示例"
+ *   [KV-2] openai-hub.com/news/2435 "GPT-2缓存实测：千倍计算只快6倍"
+ *          sections "一个很容易漏掉的错误", "GPT-2缓存要占多少显存"
+ *   [KV-4] jennyma11.github.io/infra/ch07-01.html "7.1 自回归生成过程"
+ *          section "Decode 阶段", code listing 1-2
+ *
+ * Layout (the pages' [batch, heads, sequence, head_dim] per layer, stacked
+ * over layers): cache K and V are each [L, B, Hkv, Tmax, D], row-major,
+ * contiguous.  New rows and queries are [n_layers, B, H, N, D].
+ *
+ * Element types: 0 = IEEE fp32, 1 = bfloat16 (the high 16 bits of an fp32).
+ * Inputs are decoded exactly into double; results are returned in double and
+ * any rounding to an output type is left to the caller.
+ *
+ * Parity pins for every function live in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_E_ARG (-1)
+#define ORACLE_E_CAPACITY (-4)
+
+static size_t elem_size(int dtype) { return dtype == 1 ? 2u : 4u; }
+
+/* Exact decode of one stored element into double. */
+static double load_elem(const void *base, size_t index, int dtype) {
+  if (dtype == 1) {
+    uint16_t hi;
+    memcpy(&hi, (const char *)base + index * 2u, 2u);
+    uint32_t bits = (uint32_t)hi << 16;
+    float f;
+    memcpy(&f, &bits, 4u);
+    return (double)f;
+  }
+  float f;
+  memcpy(&f, (const char *)base + index * 4u, 4u);
+  return (double)f;
+}
+
+/* Flat element index of cache[l][b][h][t][0]. */
+static size_t cache_row(int l, int b, int h, int t, int B, int Hkv, int Tmax,
+                        int D) {
+  return ((((size_t)l * B + b) * Hkv + h) * (size_t)Tmax + (size_t)t) *
+         (size_t)D;
+}
+
+/* Flat element index of x[l][b][h][i][0] for an [n_layers, B, H, N, D] array. */
+static size_t step_row(int l, int b, int h, int i, int B, int H, int N,
+                       int D) {
+  return ((((size_t)l * B + b) * H + h) * (size_t)N + (size_t)i) * (size_t)D;
+}
+
+/*
+ * Bytes held by one model's cache: 2 (K and V) x layers x KV heads x head dim
+ * x tokens x batch x bytes per element.  [KV-2] "GPT-2缓存要占多少显存", the
+ * cache-size formula.
+ */
+uint64_t oracle_cache_bytes(int64_t layers, int64_t batch, int64_t kv_heads,
+                            int64_t tokens, int64_t head_dim,
+                            int64_t elem_bytes) {
+  return (uint64_t)(2 * layers * kv_heads * head_dim * tokens * batch *
+                    elem_bytes);
+}
+
+/*
+ * Write the N new K/V rows of layers [layer0, layer0+n_layers) at sequence
+ * positions [P_b, P_b+N) of each batch entry b, where P_b = hist_len[b].
+ * Nothing else in the cache changes.  The rows are copied byte for byte.
+ *
+ * [KV-1] "KV Cache 原理" (new K/V are appended to the cache for the next
+ * round) and "Decode Shape 示例" (the append is along the sequence axis,
+ * [1,H,T,D] + [1,H,1,D] -> [1,H,T+1,D]); [KV-2] "一个很容易漏掉的错误"
+ * (prefill fills the cache, each decode step concatenates the new rows on the
+ * sequence dimension before attention).  A preallocated cache replaces the
+ * concatenation by a write into slots P_b..P_b+N-1, which leaves the same
+ * bytes at the same positions.
+ *
+ * Returns ORACLE_E_CAPACITY and writes nothing if any P_b + N > Tmax.
+ */
+int oracle_append(void *k_cache, void *v_cache, int L, int B, int Hkv,
+                  int Tmax, int D, int dtype, int layer0, int n_layers,
+                  const void *k_new, const void *v_new, int N,
+                  const int32_t *hist_len) {
+  if (L < 0 || B < 0 || Hkv < 0 || Tmax < 0 || D < 0 || N < 0 ||
+      layer0 < 0 || n_layers < 0 || layer0 + n_layers > L)
+    return ORACLE_E_ARG;
+  for (int b = 0; b < B; ++b) {
+    if (hist_len[b] < 0) return ORACLE_E_ARG;
+    if ((int64_t)hist_len[b] + N > Tmax) return ORACLE_E_CAPACITY;
+  }
+  const size_t es = elem_size(dtype);
+  for (int l = 0; l < n_layers; ++l)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < Hkv; ++h)
+        for (int i = 0; i < N; ++i) {
+          size_t dst = cache_row(layer0 + l, b, h, hist_len[b] + i, B, Hkv,
+                                 Tmax, D);
+          size_t src = step_row(l, b, h, i, B, Hkv, N, D);
+          memcpy((char *)k_cache + dst * es, (const char *)k_new + src * es,
+                 (size_t)D * es);
+          memcpy((char *)v_cache + dst * es, (const char *)v_new + src * es,
+                 (size_t)D * es);
+        }
+  return ORACLE_OK;
+}
+
+/*
+ * Attention of N new query rows against the cache, after their K/V rows have
+ * been appended.  For layer l, batch b, query head hq and new row i:
+ *
+ *   n      = P_b + i + 1            visible keys, positions 0 .. P_b+i
+ *   hkv    = floor(hq / (Hq/Hkv))   KV head shared by a contiguous group
+ *   s_j    = scale * sum_d q[d] * K[hkv][j][d]            (j < n)
+ *   m      = max_j s_j
+ *   w_j    = exp(s_j - m)
+ *   out[d] = (sum_j w_j * V[hkv][j][d]) / (sum_j w_j)
+ *
+ * [KV-4] "Decode 阶段", listing 1-2: scores are q times the transposed key
+ * cache divided by sqrt(D), then softmax, then times the value cache.
+ * [KV-2] "一个很容易漏掉的错误": with P cached tokens and N new ones, new row
+ * i may attend to P+i+1 keys (causal mask offset by the history length).
+ * [KV-2] "GPT-2缓存要占多少显存" and listing 1-2's H_q / H_kv: several query
+ * heads share fewer KV heads.  The pages do not fix which ones; the reading
+ * taken is contiguous groups (query heads g*G .. g*G+G-1 share KV head g,
+ * G = Hq/Hkv).  Subtracting m leaves the softmax unchanged and keeps exp finite.
+ *
+ * q is [n_layers, B, Hq, N, D] in `dtype`; out is [n_layers, B, Hq, N, D]
+ * double.  Returns ORACLE_E_ARG on bad shapes, ORACLE_E_CAPACITY if any
+ * P_b + N > Tmax; out is then untouched.
+ */
+int oracle_attention(const void *q, const void *k_cache, const void *v_cache,
+                     int L, int B, int Hkv, int Tmax, int D, int dtype,
+                     int layer0, int n_layers, int Hq, int N,
+                     const int32_t *hist_len, double scale, double *out) {
+  if (L < 0 || B < 0 || Hkv <= 0 || Tmax < 0 || D <= 0 || N < 0 ||
+      Hq <= 0 || Hq % Hkv != 0 || layer0 < 0 || n_layers < 0 ||
+      layer0 + n_layers > L)
+    return ORACLE_E_ARG;
+  for (int b = 0; b < B; ++b) {
+    if (hist_len[b] < 0) return ORACLE_E_ARG;
+    if ((int64_t)hist_len[b] + N > Tmax) return ORACLE_E_CAPACITY;
+  }
+  const int group = Hq / Hkv;
+  const long units = (long)n_layers * B * Hq;
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+  for (long u = 0; u < units; ++u) {
+    const int hq = (int)(u % Hq);
+    const int b = (int)((u / Hq) % B);
+    const int l = (int)(u / ((long)Hq * B));
+    const int hkv = hq / group;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Tmax > 0 ? Tmax : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+      free(s);
+      free(acc);
+      failed = 1;
+      continue;
+    }
+    for (int i = 0; i < N; ++i) {
+      const int n = hist_len[b] + i + 1;
+      const size_t qrow = step_row(l, b, hq, i, B, Hq, N, D);
+      for (int j = 0; j < n; ++j) {
+        const size_t krow = cache_row(layer0 + l, b, hkv, j, B, Hkv, Tmax, D);
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+          dot += load_elem(q, qrow + d, dtype) *
+                 load_elem(k_cache, krow + d, dtype);
+        s[j] = scale * dot;
+      }
+      double m = -INFINITY;
+      for (int j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
+      double denom = 0.0;
+      for (int d = 0; d < D; ++d) acc[d] = 0.0;
+      for (int j = 0; j < n; ++j) {
+        const double w = exp(s[j] - m);
+        const size_t vrow = cache_row(layer0 + l, b, hkv, j, B, Hkv, Tmax, D);
+        denom += w;
+        for (int d = 0; d < D; ++d) acc[d] += w * load_elem(v_cache, vrow + d, dtype);
+      }
+      for (int d = 0; d < D; ++d) out[qrow + d] = acc[d] / denom;
+    }
+    free(s);
+    free(acc);
+  }
+  return failed ? ORACLE_E_ARG : ORACLE_OK;
+}
+
+/*
+ * Prefill of a whole prompt of S tokens into an empty cache: the prompt's K/V
+ * rows go to positions [0, S) and every prompt row attends causally to
+ * itself and the rows before it.  This is exactly append with P_b = 0 and
+ * N = S followed by attention with the same P_b and N.
+ * [KV-1] "KV Cache 原理" (the first round runs the whole prompt and yields
+ * each layer's K/V); [KV-4] "Prefill 阶段" (all prompt positions in parallel
+ * under a causal mask, K/V written into the cache).
+ */
+int oracle_prefill(void *k_cache, void *v_cache, int L, int B, int Hkv,
+                   int Tmax, int D, int dtype, int layer0, int n_layers,
+                   const void *q, const void *k, const void *v, int Hq, int S,
+                   double scale, double *out) {
+  if (B < 0) return ORACLE_E_ARG;
+  int32_t *zeros = (int32_t *)calloc((size_t)(B > 0 ? B : 1), sizeof(int32_t));
+  if (!zeros) return ORACLE_E_ARG;
+  int rc = oracle_append(k_cache, v_cache, L, B, Hkv, Tmax, D, dtype, layer0,
+                         n_layers, k, v, S, zeros);
+  if (rc == ORACLE_OK)
+    rc = oracle_attention(q, k_cache, v_cache, L, B, Hkv, Tmax, D, dtype,
+                          layer0, n_layers, Hq, S, zeros, scale, out);
+  free(zeros);
+  return rc;
+}
+
+/* Thread control for the timed CPU baseline (independent (l, b, hq) units). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

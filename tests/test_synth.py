@@ -1,0 +1,44 @@
+"""Seeded input generators: bf16 rounding against torch, determinism, and the
+shapes and length draws of the five workloads."""
+import numpy as np
+import torch
+
+from transformer_kv_cache_amd import synth
+
+
+def test_bf16_rne_matches_torch_all_high_halves():
+    """Every high half with low halves covering exact values, ties, near-ties
+    and the largest low half; NaN inputs only need to stay NaN."""
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
+    bits = (hi[:, None] | lows[None, :]).reshape(-1)
+    x = bits.view(np.float32)
+    ours = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.isnan(synth.bf16_bits_to_f32(ours[nan])).all()
+
+
+def test_bf16_widening_is_exact():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = synth.bf16_bits_to_f32(b)
+    back = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    fin = ~np.isnan(f)
+    assert np.array_equal(f[fin].view(np.uint32), back[fin].view(np.uint32))
+
+
+def test_generators_are_deterministic_and_shaped():
+    a = synth.single_layer_generation(seed=3)
+    b = synth.single_layer_generation(seed=3)
+    assert np.array_equal(a.prefill[0], b.prefill[0])
+    assert a.k_cache.shape == (1, 1, 12, 32, 64) and synth.is_canary(a.k_cache).all()
+    assert a.prefill[0].shape == (1, 1, 12, 16, 64) and len(a.steps) == 4
+    c = synth.make_workload("x", seed=0, dtype="bf16", L=2, B=3, Hq=4, Hkv=2, D=8,
+                            Tmax=16, draw_lengths=(1, 16), step_lens=(1,))
+    assert ((c.hist >= 0) & (c.hist <= 15)).all()
+    for bb in range(3):
+        p = int(c.hist[bb])
+        assert not synth.is_canary(c.k_cache[:, bb, :, :p]).any()
+        assert synth.is_canary(c.k_cache[:, bb, :, p:]).all()
+    assert c.steps[0][0].shape == (2, 3, 4, 1, 8) and c.steps[0][1].shape == (2, 3, 2, 1, 8)

@@ -1,0 +1,193 @@
+"""Seeded synthetic inputs for the KV-cache attention workloads.
+
+This module is shared by the tests, the smoke check and the benchmark, and
+feeds both the HIP path and the CPU oracle with the same bytes.  It holds no
+attention arithmetic: only random draws, bf16 rounding of the draws, canary
+fills and the layout of the draws into cache-shaped arrays.
+
+Recipe:
+  * ``numpy.random.default_rng(seed)`` (PCG64), ``standard_normal(shape,
+    dtype=float32)``: N(0,1) fp32 samples, as GPT-2-Small-shaped activations
+    would be after their projections (the pages use trained weights, which are
+    not available; N(0,1) stands in for them).
+  * Draw order inside one call: lengths first (if any), then history K, history
+    V, then for each phase (prefill, then each decode step) q, k, v as whole
+    ``[n_layers, B, H, N, D]`` tensors.
+  * bf16 tensors are the fp32 draws rounded once to nearest-even.
+  * Cache slots that hold no token carry a NaN canary bit pattern, so a kernel
+    that reads past a sequence's length, or writes where it should not, shows
+    up bit-exactly.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F32_CANARY = np.uint32(0x7FC0CA7A)  # quiet NaN with a payload
+BF16_CANARY = np.uint16(0x7FCA)  # quiet NaN
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bfloat16 by round-to-nearest-even; returns uint16 bits.
+    NaN inputs map to the quiet NaN 0x7FC0."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bits to fp32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def as_dtype(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 draws stored as 'f32' (float32) or 'bf16' (uint16 bits)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x_f32, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x_f32)
+    raise ValueError(dtype)
+
+
+def to_float(x: np.ndarray) -> np.ndarray:
+    """Stored array (float32 or bf16 bits) to float64 values."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def canary_cache(shape, dtype: str) -> np.ndarray:
+    """A cache-shaped array filled entirely with the canary pattern."""
+    if dtype == "f32":
+        return np.full(shape, F32_CANARY, dtype=np.uint32).view(np.float32)
+    if dtype == "bf16":
+        return np.full(shape, BF16_CANARY, dtype=np.uint16)
+    raise ValueError(dtype)
+
+
+def is_canary(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.float32:
+        return x.view(np.uint32) == F32_CANARY
+    return x == BF16_CANARY
+
+
+def elem_bytes(dtype: str) -> int:
+    return {"f32": 4, "bf16": 2}[dtype]
+
+
+@dataclass
+class Workload:
+    """One seeded workload: cache geometry, history, and phases.
+
+    ``k_cache``/``v_cache`` are ``[L,B,Hkv,Tmax,D]`` with history rows
+    [0, hist[b]) filled and the rest canary.  ``prefill`` is None or
+    ``(q, k, v)`` of ``[L,B,H,S,D]``; ``steps`` is a list of ``(q, k, v)`` of
+    ``[L,B,H,N,D]`` decode inputs applied in order after the prefill.
+    """
+    name: str
+    dtype: str
+    L: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    Tmax: int
+    hist: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    prefill: tuple | None = None
+    steps: list = field(default_factory=list)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def make_workload(name, *, seed, dtype, L, B, Hq, Hkv, D, Tmax, hist=None,
+                  prefill_len=0, step_lens=(), draw_lengths=None) -> Workload:
+    """General generator.  ``hist`` gives each sequence's history length (rows
+    drawn N(0,1) into the cache); ``draw_lengths=(lo, hi)`` instead draws the
+    number of keys each sequence sees after one appended row,
+    L_b ~ U[lo, hi], so that hist = L_b - 1."""
+    rng = np.random.default_rng(seed)
+    if draw_lengths is not None:
+        lo, hi = draw_lengths
+        seen = rng.integers(lo, hi + 1, size=B)
+        hist = (seen - 1).astype(np.int32)
+    elif hist is None:
+        hist = np.zeros(B, dtype=np.int32)
+    hist = np.asarray(hist, dtype=np.int32).copy()
+    if hist.shape != (B,):
+        hist = np.full(B, int(hist.reshape(-1)[0]), dtype=np.int32)
+    shape = (L, B, Hkv, Tmax, D)
+    kc = canary_cache(shape, dtype)
+    vc = canary_cache(shape, dtype)
+    pmax = int(hist.max()) if B else 0
+    if pmax > 0:
+        kh = as_dtype(_normal(rng, (L, B, Hkv, pmax, D)), dtype)
+        vh = as_dtype(_normal(rng, (L, B, Hkv, pmax, D)), dtype)
+        for b in range(B):
+            p = int(hist[b])
+            kc[:, b, :, :p, :] = kh[:, b, :, :p, :]
+            vc[:, b, :, :p, :] = vh[:, b, :, :p, :]
+    pre = None
+    if prefill_len:
+        pre = tuple(as_dtype(_normal(rng, (L, B, H, prefill_len, D)), dtype)
+                    for H in (Hq, Hkv, Hkv))
+    steps = []
+    for n in step_lens:
+        steps.append(tuple(as_dtype(_normal(rng, (L, B, H, n, D)), dtype)
+                           for H in (Hq, Hkv, Hkv)))
+    return Workload(name, dtype, L, B, Hq, Hkv, D, Tmax, hist, kc, vc, pre, steps)
+
+
+# ---- the five workloads, GPT-2 Small shaped (12 layers, 12 heads, D = 64) ----
+
+def single_layer_generation(seed=0) -> Workload:
+    """One attention layer, fp32, B=1, H=12, D=64, Tmax=32: a 16-token prompt
+    prefill, then four single-token decode steps."""
+    return make_workload("single_layer_generation", seed=seed, dtype="f32", L=1, B=1,
+                         Hq=12, Hkv=12, D=64, Tmax=32, prefill_len=16,
+                         step_lens=(1, 1, 1, 1))
+
+
+def decode_12layer(P, seed=0, dtype="f32") -> Workload:
+    """All 12 layers, B=1, H=12, D=64, Tmax=1024: history P, one new token."""
+    return make_workload(f"decode_12layer_P{P}", seed=seed, dtype=dtype, L=12, B=1,
+                         Hq=12, Hkv=12, D=64, Tmax=1024, hist=[P], step_lens=(1,))
+
+
+def chunked_decode(P=1000, N=8, seed=0) -> Workload:
+    """12 layers, fp32, B=1, H=12, D=64: history P plus N rows in one call."""
+    return make_workload(f"chunked_decode_P{P}_N{N}", seed=seed, dtype="f32", L=12, B=1,
+                         Hq=12, Hkv=12, D=64, Tmax=1024, hist=[P], step_lens=(N,))
+
+
+def causal_prefill(S, dtype, seed=0, L=12) -> Workload:
+    """Causal prefill, B=1, H=12, D=64, prompt S, into an empty Tmax=1024 cache."""
+    return make_workload(f"prefill_S{S}_{dtype}", seed=seed, dtype=dtype, L=L, B=1,
+                         Hq=12, Hkv=12, D=64, Tmax=1024, prefill_len=S)
+
+
+def batched_decode(seed=0, gqa=False, B=8, L=12) -> Workload:
+    """bf16 cache, B sequences whose visible-key counts are U[1, 1024],
+    Tmax=1024; MHA (H=12, D=64) or GQA (32 query heads, 8 KV heads, D=128)."""
+    if gqa:
+        return make_workload("batched_decode_gqa", seed=seed, dtype="bf16", L=L, B=B,
+                             Hq=32, Hkv=8, D=128, Tmax=1024, draw_lengths=(1, 1024),
+                             step_lens=(1,))
+    return make_workload("batched_decode_mha", seed=seed, dtype="bf16", L=L, B=B,
+                         Hq=12, Hkv=12, D=64, Tmax=1024, draw_lengths=(1, 1024),
+                         step_lens=(1,))
