@@ -1,0 +1,184 @@
+/*
+ * kvcache.h -- C ABI of libkvcache.so: attention over a per-layer KV cache on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * Three operations make up the hot path of autoregressive GPT-2-style
+ * generation with a KV cache:
+ *
+ *   kvc_append        write the new K/V rows of a step into the cache
+ *   kvc_attn_decode   N >= 1 new query rows against the P+N cached keys
+ *   kvc_attn_prefill  causal self-attention over a whole prompt, which also
+ *                     writes the prompt's K/V into the cache
+ *
+ * Pages defining the operations (cited by address and section title):
+ *   [KV-1] gitcode.csdn.net/69e62cef0a2f6a37c5a11c4f.html
+ *          "KV Cache 原理", "Prefill/Decode 双图", "Decode Shape 示例"
+ *   [KV-2] openai-hub.com/news/2435 "GPT-2缓存实测：千倍计算只快6倍"
+ *          "正确性先于性能", "一个很容易漏掉的错误", "GPT-2缓存要占多少显存"
+ *   [KV-4] jennyma11.github.io/infra/ch07-01.html "7.1 自回归生成过程"
+ *          "Prefill 阶段", "Decode 阶段" (listing 1-2)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory.  Every tensor argument is a DEVICE pointer to contiguous,
+ *    row-major memory owned by the caller (for example a torch tensor on
+ *    the GPU), 16-byte aligned.  hist_len is a HOST pointer.  The library
+ *    allocates no memory and keeps no pointer after a call returns.
+ *  - Streams.  `stream` is a hipStream_t passed as void* (NULL = the legacy
+ *    default stream).  All work is enqueued on it; no call synchronises the
+ *    host with the device.
+ *  - Cache.  One K and one V tensor per model, each [L, B, Hkv, Tmax, D]:
+ *    layer l's slice is the pages' per-layer [batch, heads, sequence,
+ *    head_dim] tensor, with the sequence axis preallocated to Tmax rows
+ *    ([KV-1] "Decode Shape 示例"; [KV-2] "一个很容易漏掉的错误").
+ *  - Step tensors.  Queries, new K/V rows and outputs of a call that covers
+ *    layers [layer0, layer0 + n_layers) are [n_layers, B, H, N, D] with
+ *    H = Hq for queries and outputs and H = Hkv for new K/V rows.  All of
+ *    them share the cache's element type.
+ *  - Element types.  KVC_F32 (IEEE binary32) or KVC_BF16 (bfloat16: the high
+ *    16 bits of a binary32).  Arithmetic is fp32 in both cases; bf16 outputs
+ *    are rounded to nearest-even.
+ *  - Positions.  hist_len[b] = P_b is the number of tokens of sequence b
+ *    already in the cache.  Calls read it and never change it; after a step
+ *    the caller adds N.
+ *  - Head dims.  D is 64 or 128.  Hq must be a multiple of Hkv; query head
+ *    hq uses KV head hq / (Hq / Hkv) (contiguous groups: GQA / MQA, [KV-2]
+ *    "GPT-2缓存要占多少显存"; Hq == Hkv is plain multi-head attention).
+ *  - Errors.  Every argument is checked before anything is enqueued.  On a
+ *    non-zero status nothing has been enqueued, no memory has been written,
+ *    and kvc_last_error() describes the problem.  KVC_E_HIP reports a failed
+ *    kernel launch; work enqueued before it by the same call may have run.
+ *    No exception crosses the ABI and there is no CPU fallback.
+ *  - Empty work.  N = 0, S = 0, B = 0 or n_layers = 0 are valid no-ops.
+ *  - Concurrency.  Calls on different streams may run concurrently unless
+ *    they write the same cache rows or share a decode workspace.
+ */
+#ifndef KVCACHE_H
+#define KVCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_NULL = -1,        /* a required pointer is NULL */
+  KVC_E_SHAPE = -2,       /* a size is negative, inconsistent or out of range */
+  KVC_E_DTYPE = -3,       /* unknown element type */
+  KVC_E_CAPACITY = -4,    /* hist_len[b] + N (or S) exceeds Tmax */
+  KVC_E_WORKSPACE = -5,   /* decode workspace missing or too small */
+  KVC_E_UNSUPPORTED = -6, /* a valid shape this build has no kernel for */
+  KVC_E_HIP = -7          /* the HIP runtime refused a launch */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* A caller-owned cache: k and v are device pointers to [L,B,Hkv,Tmax,D]. */
+typedef struct {
+  void *k;
+  void *v;
+  int32_t L, B, Hkv, Tmax, D;
+  int32_t dtype; /* kvc_dtype */
+} kvc_cache;
+
+/*
+ * Bytes of one model's cache (K and V together):
+ *   2 x L x Hkv x D x Tmax x B x element size.
+ * [KV-2] "GPT-2缓存要占多少显存", the cache-size formula; for GPT-2 Small in
+ * fp32 (L = 12, Hkv = 12, D = 64, B = 1) this is 73,728 bytes per token.
+ * Returns 0 for negative sizes or an unknown dtype.
+ */
+uint64_t kvc_cache_bytes(int64_t L, int64_t B, int64_t Hkv, int64_t Tmax,
+                         int64_t D, int32_t dtype);
+
+/*
+ * kv_append: for layers l in [layer0, layer0+n_layers), every b < B, every
+ * KV head h and i < N, copy row k_new[l-layer0][b][h][i][:] to
+ * cache.k[l][b][h][hist_len[b] + i][:], and the same for v.  Nothing else in
+ * the cache changes; the copy is bit-exact.
+ * [KV-1] "KV Cache 原理" (each round's new K/V join the cache) and
+ * "Decode Shape 示例" (the join is along the sequence axis); [KV-4] "Decode
+ * 阶段" (a real implementation writes into slots in place rather than
+ * concatenating).
+ *   k_new, v_new : device, [n_layers, B, Hkv, N, D], cache dtype
+ *   hist_len     : host int32[B]; requires hist_len[b] + N <= Tmax
+ *                  (KVC_E_CAPACITY otherwise, nothing written)
+ */
+kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                      const void *k_new, const void *v_new, int32_t N,
+                      const int32_t *hist_len, void *stream);
+
+/*
+ * Workspace bytes kvc_attn_decode needs for this geometry: partial softmax
+ * states of the split-K passes plus one int32 ticket per (layer, sequence,
+ * KV head, row tile).  It depends only on the cache geometry, n_layers, Hq
+ * and N, never on the lengths, so one workspace serves every step.  Returns
+ * 0 on invalid sizes.
+ */
+size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers,
+                                  int32_t Hq, int32_t N);
+
+/*
+ * attn_decode: for layers l in [layer0, layer0+n_layers), sequences b, query
+ * heads hq and new rows i < N, with P = hist_len[b], G = Hq / Hkv and
+ * h = hq / G:
+ *   s_j   = scale * <q[l][b][hq][i], K[l][b][h][j]>   for j = 0 .. P + i
+ *   o[l][b][hq][i] = sum_j softmax(s)_j * V[l][b][h][j]
+ * i.e. the causal mask is offset by the history length and new row i sees
+ * P + i + 1 keys ([KV-2] "一个很容易漏掉的错误"; the score, softmax and
+ * weighted sum are [KV-4] "Decode 阶段", listing 1-2, with scale = 1/sqrt(D)
+ * there).  The K/V rows of the N new tokens must already be in the cache at
+ * positions [P, P+N) (call kvc_append first with the same hist_len).
+ *   q, o       : device, [n_layers, B, Hq, N, D], cache dtype
+ *   scale      : finite score scale, normally 1/sqrt(D)
+ *   workspace  : device, >= kvc_decode_workspace_bytes(...) bytes, 256-byte
+ *                aligned.  ZERO-FILL IT BEFORE ITS FIRST USE WITH A GIVEN
+ *                GEOMETRY (cache geometry, n_layers, Hq, N).  Every call
+ *                leaves its tickets at zero again, so a workspace zeroed once
+ *                serves every later call of that geometry.  Its layout
+ *                depends on the geometry: before using it with another one,
+ *                zero it again.  Two calls in flight at the same time must
+ *                not share a workspace.
+ */
+kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0,
+                           int32_t n_layers, const void *q, int32_t Hq,
+                           int32_t N, const int32_t *hist_len, float scale,
+                           void *o, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * attn_prefill: causal self-attention over an S-token prompt that starts an
+ * empty cache.  Writes k[..][i] and v[..][i] to cache rows [0, S) of every
+ * sequence (as kvc_append with hist_len = 0 and N = S would) and computes,
+ * for every prompt row i,
+ *   o[l][b][hq][i] = sum_{j <= i} softmax_j(scale * <q_i, k_j>) * v_j
+ * with the contiguous GQA grouping above.  Equal to kvc_append +
+ * kvc_attn_decode with P = 0 and N = S, computed with matrix-core tiles.
+ * [KV-1] "KV Cache 原理" (the first round runs the whole prompt and yields
+ * each layer's K/V) and "Prefill/Decode 双图"; [KV-4] "Prefill 阶段" (all
+ * prompt positions in parallel under a causal mask).
+ *   q, o : device, [n_layers, B, Hq, S, D];  k, v : device, [n_layers, B,
+ *   Hkv, S, D]; all in the cache dtype.  Requires S <= Tmax.  Prior cache
+ *   contents at rows >= S are left unchanged.
+ */
+kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0,
+                            int32_t n_layers, const void *q, const void *k,
+                            const void *v, int32_t Hq, int32_t S, float scale,
+                            void *o, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *kvc_last_error(void);
+
+/* KVC_ABI_VERSION of the loaded library. */
+int32_t kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCACHE_H */

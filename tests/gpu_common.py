@@ -1,0 +1,84 @@
+"""Helpers shared by the GPU parity tests: moving seeded numpy inputs to the
+device and back, and running one workload through the HIP path and through
+the oracle on the same bytes."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from transformer_kv_cache_amd import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}  # max abs error against the oracle
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def torch_dtype(dtype: str):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def run_gpu(w: synth.Workload):
+    """Prefill (if any) then every decode step through libkvcache.so.
+    Returns (outputs as numpy in the workload dtype, final K, final V)."""
+    from transformer_kv_cache_amd import kvcache as K
+    kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
+    cache = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, torch_dtype(w.dtype), k=kc, v=vc)
+    hist = w.hist.copy()
+    outs = []
+    if w.prefill is not None:
+        q, k, v = (to_dev(a) for a in w.prefill)
+        outs.append(K.attn_prefill(cache, q, k, v, scale=w.scale))
+        hist[:] = w.prefill[0].shape[3]
+    for (q, k, v) in w.steps:
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        K.append(cache, kd, vd, hist)
+        outs.append(K.attn_decode(cache, qd, hist, scale=w.scale))
+        hist += q.shape[3]
+    torch.cuda.synchronize()
+    return [to_host(o) for o in outs], to_host(cache.k), to_host(cache.v)
+
+
+def run_oracle(w: synth.Workload):
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    hist = w.hist.copy()
+    outs = []
+    if w.prefill is not None:
+        outs.append(oracle.prefill(kc, vc, *w.prefill, w.scale))
+        hist[:] = w.prefill[0].shape[3]
+    for (q, k, v) in w.steps:
+        oracle.append(kc, vc, k, v, hist)
+        outs.append(oracle.attention(q, kc, vc, hist, w.scale))
+        hist += q.shape[3]
+    return outs, kc, vc
+
+
+def assert_matches(w: synth.Workload, gpu, ref, tol=None):
+    """Outputs within the dtype tolerance, cache bytes identical (canary
+    slots included)."""
+    tol = TOL[w.dtype] if tol is None else tol
+    g_outs, g_k, g_v = gpu
+    r_outs, r_k, r_v = ref
+    assert len(g_outs) == len(r_outs)
+    for n, (g, r) in enumerate(zip(g_outs, r_outs)):
+        gf = synth.to_float(g)
+        assert np.isfinite(gf).all(), f"{w.name} phase {n}: non-finite output"
+        err = float(np.max(np.abs(gf - r))) if r.size else 0.0
+        assert err <= tol, f"{w.name} phase {n}: max abs error {err:.3e} > {tol:.1e}"
+    assert np.array_equal(bits(g_k), bits(r_k)), f"{w.name}: K cache bytes differ"
+    assert np.array_equal(bits(g_v), bits(r_v)), f"{w.name}: V cache bytes differ"

@@ -1,0 +1,192 @@
+"""The C ABI without a GPU: libkvcache.so loads, exports every entry point
+include/kvcache.h declares, and rejects every invalid argument before it
+enqueues anything (so these calls never reach the HIP runtime).  Pointers
+passed here are host addresses that a valid call would hand to kernels; the
+library must refuse each call before it could use them."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle_pins import GOLDEN
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvcache.h")
+
+kvcache = pytest.importorskip("transformer_kv_cache_amd.kvcache")
+K = kvcache
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_CAPACITY, E_WORKSPACE, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return K.library()
+    except K.KVCacheLibraryMissing:
+        from transformer_kv_cache_amd import build
+        build.build(verbose=False)
+        return K.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w ]+?[\s*])(kvc_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kvc_append", "kvc_attn_decode", "kvc_attn_prefill", "kvc_cache_bytes",
+            "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kvc_abi_version() == 1
+
+
+def test_cache_bytes_against_the_page_table(lib):
+    """kvc_cache_bytes against the sizes printed on the openai-hub page."""
+    unit = {"B": 1, "KiB": 1024, "MiB": 1024 * 1024}
+    for line in open(os.path.join(GOLDEN, "cache_sizes.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        L, B, H, D, T, e, val, u, digits = line.split()
+        dtype = 0 if int(e) == 4 else 1
+        got = lib.kvc_cache_bytes(int(L), int(B), int(H), int(T), int(D), dtype)
+        assert round(got / unit[u], int(digits)) == float(val), line
+    assert lib.kvc_cache_bytes(-1, 1, 1, 1, 64, 0) == 0
+    assert lib.kvc_cache_bytes(1, 1, 1, 1, 64, 9) == 0
+
+
+class Host:
+    """Host buffers standing in for device pointers in calls that must fail."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def ptr(self, nbytes=4096, offset=0):
+        a = np.zeros(nbytes + 512, np.uint8)
+        self.bufs.append(a)
+        base = a.ctypes.data
+        return ctypes.c_void_p(base + (-base) % 256 + offset)
+
+
+def desc(h, L=2, B=2, Hkv=2, Tmax=16, D=64, dtype=0):
+    return K.CacheDesc(h.ptr().value, h.ptr().value, L, B, Hkv, Tmax, D, dtype)
+
+
+def hist(*v):
+    a = (ctypes.c_int32 * max(len(v), 1))(*v)
+    return a
+
+
+def err(lib):
+    return lib.kvc_last_error().decode()
+
+
+def test_append_error_paths(lib):
+    h = Host()
+    d = desc(h)
+    p = h.ptr()
+    s = None
+    assert lib.kvc_append(None, 0, 1, p, p, 1, hist(0, 0), s) == E_NULL
+    assert "NULL" in err(lib)
+    assert lib.kvc_append(ctypes.byref(desc(h, dtype=5)), 0, 1, p, p, 1, hist(0, 0), s) == E_DTYPE
+    assert lib.kvc_append(ctypes.byref(desc(h, D=96)), 0, 1, p, p, 1, hist(0, 0), s) == E_UNSUPPORTED
+    assert lib.kvc_append(ctypes.byref(desc(h, Hkv=0)), 0, 1, p, p, 1, hist(0, 0), s) == E_SHAPE
+    assert lib.kvc_append(ctypes.byref(d), 1, 2, p, p, 1, hist(0, 0), s) == E_SHAPE
+    assert lib.kvc_append(ctypes.byref(d), -1, 1, p, p, 1, hist(0, 0), s) == E_SHAPE
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, p, p, -1, hist(0, 0), s) == E_SHAPE
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, p, p, 1, hist(0, -3), s) == E_SHAPE
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, p, p, 2, hist(0, 15), s) == E_CAPACITY
+    assert "Tmax" in err(lib)
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, p, p, 1, None, s) == E_NULL
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, None, p, 1, hist(0, 0), s) == E_NULL
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, h.ptr(offset=4), p, 1, hist(0, 0), s) == E_SHAPE
+    nul = K.CacheDesc(None, None, 2, 2, 2, 16, 64, 0)
+    assert lib.kvc_append(ctypes.byref(nul), 0, 1, p, p, 1, hist(0, 0), s) == E_NULL
+
+
+def test_empty_calls_are_noops(lib):
+    """N = 0, n_layers = 0, B = 0 and S = 0 are valid and enqueue nothing
+    (the empty prompt)."""
+    h = Host()
+    d = desc(h)
+    assert lib.kvc_append(ctypes.byref(d), 0, 1, None, None, 0, hist(3, 4), None) == OK
+    assert err(lib) == ""
+    assert lib.kvc_append(ctypes.byref(d), 0, 0, None, None, 1, hist(3, 4), None) == OK
+    assert lib.kvc_attn_decode(ctypes.byref(d), 0, 1, None, 4, 0, hist(3, 4), 0.125, None, None, 0,
+                               None) == OK
+    assert lib.kvc_attn_prefill(ctypes.byref(d), 0, 1, None, None, None, 2, 0, 0.125, None,
+                                None) == OK
+    d0 = desc(h, B=0)
+    assert lib.kvc_attn_decode(ctypes.byref(d0), 0, 1, None, 2, 1, None, 0.125, None, None, 0,
+                               None) == OK
+
+
+def test_decode_error_paths(lib):
+    h = Host()
+    d = desc(h)
+    q, o = h.ptr(), h.ptr()
+    need = lib.kvc_decode_workspace_bytes(ctypes.byref(d), 2, 4, 3)
+    assert need > 0 and need % 256 == 0
+    ws = h.ptr(need)
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=q, Hq=4, N=3, hist=hist(2, 5),
+                 scale=0.125, o=o, ws=ws, wsb=need, s=None)
+        a.update(kw)
+        return lib.kvc_attn_decode(a["c"], a["layer0"], a["n_layers"], a["q"], a["Hq"], a["N"],
+                                   a["hist"], a["scale"], a["o"], a["ws"], a["wsb"], a["s"])
+
+    assert call(Hq=3) == E_SHAPE
+    assert call(Hq=0) == E_SHAPE
+    assert call(N=-2) == E_SHAPE
+    assert call(scale=float("nan")) == E_SHAPE
+    assert call(scale=float("inf")) == E_SHAPE
+    assert call(hist=hist(2, 14)) == E_CAPACITY
+    assert call(hist=None) == E_NULL
+    assert call(q=None) == E_NULL
+    assert call(o=None) == E_NULL
+    assert call(ws=None) == E_WORKSPACE
+    assert call(wsb=need - 1) == E_WORKSPACE
+    assert "needs" in err(lib)
+    assert call(ws=h.ptr(need + 64, offset=16)) == E_WORKSPACE
+    assert call(q=h.ptr(offset=8)) == E_SHAPE
+    assert call(layer0=1) == E_SHAPE
+    assert call(c=None) == E_NULL
+
+
+def test_prefill_error_paths(lib):
+    h = Host()
+    d = desc(h)
+    p = h.ptr()
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=p, k=p, v=p, Hq=2, S=8, scale=0.125,
+                 o=p, s=None)
+        a.update(kw)
+        return lib.kvc_attn_prefill(a["c"], a["layer0"], a["n_layers"], a["q"], a["k"], a["v"],
+                                    a["Hq"], a["S"], a["scale"], a["o"], a["s"])
+
+    assert call(S=17) == E_CAPACITY
+    assert call(S=-1) == E_SHAPE
+    assert call(Hq=3) == E_SHAPE
+    assert call(k=None) == E_NULL
+    assert call(o=None) == E_NULL
+    assert call(scale=float("nan")) == E_SHAPE
+    assert call(v=h.ptr(offset=2)) == E_SHAPE
+    assert call(c=ctypes.byref(desc(h, D=32))) == E_UNSUPPORTED
+
+
+def test_workspace_size_is_length_independent(lib):
+    """The workspace depends on geometry only; it grows with Tmax, rows and
+    layers, and invalid geometry gives 0."""
+    h = Host()
+    small = lib.kvc_decode_workspace_bytes(ctypes.byref(desc(h, Tmax=64)), 2, 2, 1)
+    big = lib.kvc_decode_workspace_bytes(ctypes.byref(desc(h, Tmax=1024)), 2, 2, 1)
+    assert 0 < small < big
+    assert lib.kvc_decode_workspace_bytes(ctypes.byref(desc(h)), 2, 3, 1) == 0
+    assert lib.kvc_decode_workspace_bytes(None, 2, 2, 1) == 0

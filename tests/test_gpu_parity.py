@@ -1,0 +1,217 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by
+element on the same seeded inputs: cache bytes bit-exact (NaN canaries in
+unused slots included), outputs within 1e-4 (fp32) or 2e-2 (bf16) max abs
+error.  Covers the five GPT-2-Small workloads at full size plus ragged and
+degenerate shapes."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_kv_cache_amd import synth
+from gpu_common import TOL, assert_matches, bits, run_gpu, run_oracle, to_dev, to_host, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_kv_cache_amd import kvcache as K
+    K.library()  # fail loudly if the HIP library is missing
+    return K
+
+
+def check(w):
+    print(f"[parity] {w.name} dtype={w.dtype} L={w.L} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+          f"Tmax={w.Tmax} hist={w.hist.tolist()[:8]}", flush=True)
+    assert_matches(w, run_gpu(w), run_oracle(w))
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_single_layer_generation(seed):
+    """Prompt of 16 then four single-token steps, one layer, Tmax=32."""
+    w = synth.single_layer_generation(seed)
+    gpu = run_gpu(w)
+    assert_matches(w, gpu, run_oracle(w))
+    k = gpu[1]
+    assert not synth.is_canary(k[:, :, :, :20]).any() and synth.is_canary(k[:, :, :, 20:]).all()
+
+
+@pytest.mark.parametrize("P", [128, 512, 1000, 1023])
+def test_decode_12layer(P):
+    check(synth.decode_12layer(P, seed=P))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_chunked_decode(seed):
+    check(synth.chunked_decode(1000, 8, seed=seed))
+
+
+@pytest.mark.parametrize("S", [256, 1024])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_causal_prefill(S, dtype):
+    check(synth.causal_prefill(S, dtype, seed=S + (dtype == "bf16")))
+
+
+@pytest.mark.parametrize("gqa", [False, True])
+def test_batched_decode(gqa):
+    check(synth.batched_decode(seed=5, gqa=gqa))
+
+
+# ------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("S", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_ragged(S, dtype):
+    check(synth.make_workload(f"prefill_ragged_S{S}", seed=S, dtype=dtype, L=2, B=2, Hq=3,
+                              Hkv=3, D=64, Tmax=256, prefill_len=S))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_gqa_and_d128(dtype, D):
+    check(synth.make_workload(f"prefill_gqa_D{D}", seed=D, dtype=dtype, L=1, B=2, Hq=8, Hkv=2,
+                              D=D, Tmax=200, prefill_len=150, step_lens=(1, 3)))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 9, 17])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_rows_and_groups(N, G, dtype):
+    """Every row-tile size (G*N rows per KV head, tiles of up to 8), several
+    sequences with different histories including an empty one, and a Tmax
+    that is not a multiple of the split size."""
+    Tmax = 300
+    hist = [0, 37, Tmax - N, 150]
+    check(synth.make_workload(f"decode_N{N}_G{G}", seed=N * 10 + G, dtype=dtype, L=2, B=4,
+                              Hq=2 * G, Hkv=2, D=64, Tmax=Tmax, hist=hist, step_lens=(N,)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_d128(dtype):
+    check(synth.make_workload("decode_d128", seed=11, dtype=dtype, L=2, B=3, Hq=8, Hkv=2, D=128,
+                              Tmax=520, hist=[519, 0, 260], step_lens=(1,)))
+
+
+def test_batch_wider_than_one_launch():
+    """B = 70 sequences: the host splits the launch over batch slices."""
+    rng = np.random.default_rng(3)
+    hist = rng.integers(0, 60, size=70)
+    check(synth.make_workload("decode_B70", seed=3, dtype="f32", L=1, B=70, Hq=2, Hkv=1, D=64,
+                              Tmax=64, hist=hist, step_lens=(2,)))
+
+
+def test_layer_subset():
+    """layer0 > 0: only the named layers' slices are written and read."""
+    from transformer_kv_cache_amd import kvcache as K
+    w = synth.make_workload("layer_subset", seed=9, dtype="f32", L=4, B=2, Hq=4, Hkv=2, D=64,
+                            Tmax=64, hist=[10, 20], step_lens=(3,))
+    q, k, v = (np.ascontiguousarray(a[:2]) for a in w.steps[0])
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    oracle.append(kc, vc, k, v, w.hist, layer0=1)
+    ref = oracle.attention(q, kc, vc, w.hist, w.scale, layer0=1)
+    cache = K.KVCache(4, 2, 2, 64, 64, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    K.append(cache, to_dev(k), to_dev(v), w.hist, layer0=1)
+    out = to_host(K.attn_decode(cache, to_dev(q), w.hist, layer0=1))
+    assert np.max(np.abs(out - ref)) <= TOL["f32"]
+    assert np.array_equal(bits(to_host(cache.k)), bits(kc))
+    assert np.array_equal(bits(to_host(cache.v)), bits(vc))
+
+
+# ------------------------------------------------------------- invariants
+
+def test_cached_decode_equals_recompute():
+    """Prefill of P+N rows, last N outputs, against prefill of P then
+    append + decode of N, on the GPU (within tolerance: different kernels)."""
+    from transformer_kv_cache_amd import kvcache as K
+    P, N, L, H, D, T = 300, 8, 2, 4, 64, 512
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((L, 1, H, P + N, D), dtype=np.float32) for _ in range(3))
+    c1 = K.KVCache(L, 1, H, T, D, torch.float32, k=to_dev(synth.canary_cache((L, 1, H, T, D), "f32")),
+                   v=to_dev(synth.canary_cache((L, 1, H, T, D), "f32")))
+    full = to_host(K.attn_prefill(c1, to_dev(q), to_dev(k), to_dev(v)))
+    c2 = K.KVCache(L, 1, H, T, D, torch.float32, k=to_dev(synth.canary_cache((L, 1, H, T, D), "f32")),
+                   v=to_dev(synth.canary_cache((L, 1, H, T, D), "f32")))
+    head = [to_dev(np.ascontiguousarray(a[:, :, :, :P])) for a in (q, k, v)]
+    tail = [to_dev(np.ascontiguousarray(a[:, :, :, P:])) for a in (q, k, v)]
+    K.attn_prefill(c2, *head)
+    K.append(c2, tail[1], tail[2], [P])
+    inc = to_host(K.attn_decode(c2, tail[0], [P]))
+    assert np.max(np.abs(full[:, :, :, P:] - inc)) <= TOL["f32"]
+    assert np.array_equal(bits(to_host(c1.k)), bits(to_host(c2.k)))
+
+
+def test_permutation_property_on_gpu():
+    """Jointly permuting every cached (K_j, V_j) pair leaves single-row decode
+    unchanged and changes chunked decode."""
+    from transformer_kv_cache_amd import kvcache as K
+    P, L, H, D = 200, 1, 2, 64
+    rng = np.random.default_rng(22)
+    for N, same in ((1, True), (8, False)):
+        T = P + N
+        w = synth.make_workload("perm", seed=N, dtype="f32", L=L, B=1, Hq=H, Hkv=H, D=D, Tmax=T,
+                                hist=[P], step_lens=(N,))
+        q, k, v = w.steps[0]
+        cache = K.KVCache(L, 1, H, T, D, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+        K.append(cache, to_dev(k), to_dev(v), [P])
+        ref = to_host(K.attn_decode(cache, to_dev(q), [P]))
+        perm = torch.from_numpy(rng.permutation(T)).cuda()
+        pc = K.KVCache(L, 1, H, T, D, torch.float32, k=cache.k[:, :, :, perm].contiguous(),
+                       v=cache.v[:, :, :, perm].contiguous())
+        got = to_host(K.attn_decode(pc, to_dev(q), [P]))
+        diff = float(np.max(np.abs(got - ref)))
+        assert (diff <= TOL["f32"]) if same else (diff > 1e-2), (N, diff)
+
+
+def test_repeated_calls_reuse_workspace_bitwise():
+    """The split-K tickets return to zero after each call: repeated calls on
+    one workspace give bit-identical outputs."""
+    from transformer_kv_cache_amd import kvcache as K
+    w = synth.decode_12layer(1000, seed=4)
+    q, k, v = w.steps[0]
+    cache = K.KVCache(12, 1, 12, 1024, 64, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    K.append(cache, to_dev(k), to_dev(v), w.hist)
+    ws = K.new_decode_workspace(cache, 12, 12, 1)
+    qd = to_dev(q)
+    outs = [to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)) for _ in range(5)]
+    for o in outs[1:]:
+        assert np.array_equal(bits(o), bits(outs[0]))
+    # the ticket region closes the workspace: 12 layers x 1 sequence x 12 KV
+    # heads x 1 row tile int32s, rounded up to 256 bytes = 768 bytes
+    assert int(torch.count_nonzero(ws[-768:]).item()) == 0
+
+
+def test_capacity_error_leaves_cache_untouched():
+    from transformer_kv_cache_amd import kvcache as K
+    w = synth.decode_12layer(1023, seed=1)
+    cache = K.KVCache(12, 1, 12, 1024, 64, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    before = to_host(cache.k)
+    kn = torch.zeros((12, 1, 12, 2, 64), device="cuda")
+    with pytest.raises(K.KVCacheError) as e:
+        K.append(cache, kn, kn, [1023])
+    assert e.value.status == -4
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(to_host(cache.k)), bits(before))
+
+
+def test_cache_allocation_matches_formula():
+    """torch.cuda.memory_allocated grows by exactly the formula's bytes."""
+    import gc
+    from transformer_kv_cache_amd import kvcache as K
+    gc.collect()
+    gc.disable()  # no collection of earlier tests' tensors between the readings
+    try:
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        cache = K.KVCache(12, 1, 12, 1024, 64, torch.float32)
+        grown = torch.cuda.memory_allocated() - before
+    finally:
+        gc.enable()
+    assert cache.nbytes == 75_497_472 == grown
+    del cache

@@ -1,0 +1,254 @@
+// kvc_api.hip -- the C ABI of libkvcache.so (declared in include/kvcache.h):
+// argument validation, launch geometry and the kernel launches.  Every check
+// runs before the first enqueue, so a rejected call leaves device memory
+// untouched and never touches the HIP runtime.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+int prefill_query_tile();
+}
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kvc_status fail(kvc_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvc_status ok() {
+  g_last_error[0] = '\0';
+  return KVC_OK;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == KVC_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by every entry point: the cache descriptor and layer range.
+kvc_status check_cache(const kvc_cache *c, int32_t layer0, int32_t n_layers, const char *fn) {
+  if (!c) return fail(KVC_E_NULL, "%s: cache descriptor is NULL", fn);
+  if (c->dtype != KVC_F32 && c->dtype != KVC_BF16)
+    return fail(KVC_E_DTYPE, "%s: unknown dtype %d", fn, (int)c->dtype);
+  if (c->L < 0 || c->B < 0 || c->Hkv <= 0 || c->Tmax < 0 || c->D <= 0)
+    return fail(KVC_E_SHAPE, "%s: bad cache geometry L=%d B=%d Hkv=%d Tmax=%d D=%d", fn, c->L, c->B,
+                c->Hkv, c->Tmax, c->D);
+  if (c->D != 64 && c->D != 128)
+    return fail(KVC_E_UNSUPPORTED, "%s: head dim D=%d (supported: 64, 128)", fn, c->D);
+  if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > c->L)
+    return fail(KVC_E_SHAPE, "%s: layers [%d, %d+%d) outside [0, %d)", fn, layer0, layer0, n_layers,
+                c->L);
+  return KVC_OK;
+}
+
+kvc_status check_cache_pointers(const kvc_cache *c, const char *fn) {
+  if (!c->k || !c->v) return fail(KVC_E_NULL, "%s: cache k or v pointer is NULL", fn);
+  if (!aligned16(c->k) || !aligned16(c->v))
+    return fail(KVC_E_SHAPE, "%s: cache pointers must be 16-byte aligned", fn);
+  return KVC_OK;
+}
+
+kvc_status check_hist(const kvc_cache *c, const int32_t *hist_len, int32_t N, const char *fn) {
+  if (c->B > 0 && !hist_len) return fail(KVC_E_NULL, "%s: hist_len is NULL", fn);
+  for (int b = 0; b < c->B; ++b) {
+    if (hist_len[b] < 0) return fail(KVC_E_SHAPE, "%s: hist_len[%d] = %d < 0", fn, b, hist_len[b]);
+    if ((int64_t)hist_len[b] + N > c->Tmax)
+      return fail(KVC_E_CAPACITY, "%s: hist_len[%d] + N = %d + %d exceeds Tmax = %d", fn, b,
+                  hist_len[b], N, c->Tmax);
+  }
+  return KVC_OK;
+}
+
+kvc_status hip_status(hipError_t e, const char *fn) {
+  if (e != hipSuccess) return fail(KVC_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+struct DecodeGeometry {
+  int rows, row_tile, row_tiles, split_keys, max_splits;
+  size_t ws_o_bytes, ws_ml_bytes, ticket_bytes, total;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq, int32_t N) {
+  DecodeGeometry g{};
+  const int G = Hq / c->Hkv;
+  g.rows = G * N;
+  g.row_tile = kvc::decode_row_tile(g.rows);
+  g.row_tiles = (g.rows + g.row_tile - 1) / g.row_tile;
+  g.split_keys = kvc::decode_split_keys(c->dtype, c->D);
+  g.max_splits = (c->Tmax + g.split_keys - 1) / g.split_keys;
+  if (g.max_splits < 1) g.max_splits = 1;
+  const size_t qrows = (size_t)n_layers * c->B * Hq * N;
+  g.ws_o_bytes = round_up(qrows * g.max_splits * c->D * sizeof(float), 256);
+  g.ws_ml_bytes = round_up(qrows * g.max_splits * 2 * sizeof(float), 256);
+  g.ticket_bytes = round_up((size_t)n_layers * c->B * c->Hkv * g.row_tiles * sizeof(int32_t), 256);
+  g.total = g.ws_o_bytes + g.ws_ml_bytes + g.ticket_bytes;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char *kvc_last_error(void) { return g_last_error; }
+
+uint64_t kvc_cache_bytes(int64_t L, int64_t B, int64_t Hkv, int64_t Tmax, int64_t D, int32_t dtype) {
+  if (L < 0 || B < 0 || Hkv < 0 || Tmax < 0 || D < 0) return 0;
+  if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
+  return (uint64_t)2 * L * Hkv * D * Tmax * B * elem_bytes(dtype);
+}
+
+kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *k_new,
+                      const void *v_new, int32_t N, const int32_t *hist_len, void *stream) {
+  static const char *fn = "kvc_append";
+  kvc_status st = check_cache(cache, layer0, n_layers, fn);
+  if (st != KVC_OK) return st;
+  if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
+  if ((st = check_hist(cache, hist_len, N, fn)) != KVC_OK) return st;
+  if (N == 0 || n_layers == 0 || cache->B == 0) return ok();
+  if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
+  if (!k_new || !v_new) return fail(KVC_E_NULL, "%s: k_new or v_new is NULL", fn);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(KVC_E_SHAPE, "%s: k_new / v_new must be 16-byte aligned", fn);
+
+  kvc::AppendArgs a{};
+  a.k_cache = (char *)cache->k;
+  a.v_cache = (char *)cache->v;
+  a.k_new = (const char *)k_new;
+  a.v_new = (const char *)v_new;
+  a.B = cache->B;
+  a.Hkv = cache->Hkv;
+  a.Tmax = cache->Tmax;
+  a.layer0 = layer0;
+  a.n_layers = n_layers;
+  a.N = N;
+  a.row_vec16 = cache->D * elem_bytes(cache->dtype) / 16;
+  for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
+    a.b0 = b0;
+    a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
+    for (int i = 0; i < a.nb; ++i) a.hist[i] = hist_len[b0 + i];
+    hipError_t e = kvc::launch_append(a, cache->dtype, cache->D, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
+}
+
+size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers, int32_t Hq, int32_t N) {
+  if (!cache || cache->Hkv <= 0 || cache->B < 0 || cache->Tmax < 0 || n_layers < 0 || Hq <= 0 ||
+      N < 0 || Hq % cache->Hkv != 0 || (cache->D != 64 && cache->D != 128) ||
+      (cache->dtype != KVC_F32 && cache->dtype != KVC_BF16))
+    return 0;
+  return decode_geometry(cache, n_layers, Hq, N).total;
+}
+
+kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
+                           int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  static const char *fn = "kvc_attn_decode";
+  kvc_status st = check_cache(cache, layer0, n_layers, fn);
+  if (st != KVC_OK) return st;
+  if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
+  if (Hq <= 0 || Hq % cache->Hkv != 0)
+    return fail(KVC_E_SHAPE, "%s: Hq = %d is not a positive multiple of Hkv = %d", fn, Hq, cache->Hkv);
+  if (!std::isfinite(scale)) return fail(KVC_E_SHAPE, "%s: scale is not finite", fn);
+  if ((st = check_hist(cache, hist_len, N, fn)) != KVC_OK) return st;
+  if (N == 0 || n_layers == 0 || cache->B == 0) return ok();
+  if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
+  if (!q || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
+  if (!aligned16(q) || !aligned16(o)) return fail(KVC_E_SHAPE, "%s: q / o must be 16-byte aligned", fn);
+  const DecodeGeometry g = decode_geometry(cache, n_layers, Hq, N);
+  if (!workspace) return fail(KVC_E_WORKSPACE, "%s: workspace is NULL", fn);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(KVC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  if (workspace_bytes < g.total)
+    return fail(KVC_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, g.total);
+
+  kvc::DecodeArgs a{};
+  a.k_cache = (const char *)cache->k;
+  a.v_cache = (const char *)cache->v;
+  a.q = (const char *)q;
+  a.o = (char *)o;
+  a.ws_o = (float *)workspace;
+  a.ws_ml = (float *)((char *)workspace + g.ws_o_bytes);
+  a.tickets = (int32_t *)((char *)workspace + g.ws_o_bytes + g.ws_ml_bytes);
+  a.B = cache->B;
+  a.Hkv = cache->Hkv;
+  a.Hq = Hq;
+  a.Tmax = cache->Tmax;
+  a.N = N;
+  a.layer0 = layer0;
+  a.n_layers = n_layers;
+  a.group = Hq / cache->Hkv;
+  a.rows = g.rows;
+  a.row_tiles = g.row_tiles;
+  a.max_splits = g.max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
+    a.b0 = b0;
+    a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
+    int max_keys = 0;
+    for (int i = 0; i < a.nb; ++i) {
+      a.hist[i] = hist_len[b0 + i];
+      if (hist_len[b0 + i] + N > max_keys) max_keys = hist_len[b0 + i] + N;
+    }
+    const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
+    hipError_t e = kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
+}
+
+kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
+                            const void *k, const void *v, int32_t Hq, int32_t S, float scale, void *o,
+                            void *stream) {
+  static const char *fn = "kvc_attn_prefill";
+  kvc_status st = check_cache(cache, layer0, n_layers, fn);
+  if (st != KVC_OK) return st;
+  if (S < 0) return fail(KVC_E_SHAPE, "%s: S = %d < 0", fn, S);
+  if (Hq <= 0 || Hq % cache->Hkv != 0)
+    return fail(KVC_E_SHAPE, "%s: Hq = %d is not a positive multiple of Hkv = %d", fn, Hq, cache->Hkv);
+  if (!std::isfinite(scale)) return fail(KVC_E_SHAPE, "%s: scale is not finite", fn);
+  if (S > cache->Tmax)
+    return fail(KVC_E_CAPACITY, "%s: S = %d exceeds Tmax = %d", fn, S, cache->Tmax);
+  if (S == 0 || n_layers == 0 || cache->B == 0) return ok();
+  if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
+  if (!q || !k || !v || !o) return fail(KVC_E_NULL, "%s: q, k, v or o is NULL", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
+  if ((int64_t)n_layers * cache->B * Hq > 2147483647LL)
+    return fail(KVC_E_UNSUPPORTED, "%s: too many heads for one launch", fn);
+
+  kvc::PrefillArgs a{};
+  a.k_cache = (char *)cache->k;
+  a.v_cache = (char *)cache->v;
+  a.q = (const char *)q;
+  a.k = (const char *)k;
+  a.v = (const char *)v;
+  a.o = (char *)o;
+  a.B = cache->B;
+  a.Hkv = cache->Hkv;
+  a.Hq = Hq;
+  a.Tmax = cache->Tmax;
+  a.S = S;
+  a.layer0 = layer0;
+  a.n_layers = n_layers;
+  a.group = Hq / cache->Hkv;
+  a.q_tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(kvc::launch_prefill(a, cache->dtype, cache->D, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,318 @@
+// kvc_decode.hip -- split-K ("flash-decode") attention of N new query rows
+// against the KV cache.
+//
+// What it computes ([KV-4] jennyma11.github.io/infra/ch07-01.html, "Decode
+// 阶段", listing 1-2; [KV-2] openai-hub.com/news/2435, "一个很容易漏掉的错误"):
+// for each (layer, sequence b, query head, new row i) the softmax of
+// scale * q . K_j over keys j = 0 .. P_b + i, applied to V.  Decode reads every
+// cached K/V byte once and does ~1 flop per byte, so it is bound by HBM
+// bandwidth ([KV-2] "千倍计算量为何只换来6倍速度").
+//
+// Work split.  A workgroup (256 lanes, 4 waves) owns one (layer, sequence,
+// KV head, tile of RT query rows, split of SPLIT consecutive keys).  The RT
+// rows are the G*N query rows (GQA group x new rows) that read the same KV
+// head, so each K/V byte is fetched once for all of them.  Inside the
+// workgroup:
+//   * a key row of D elements is LPR = D*elem/16 lanes wide; each lane loads
+//     one 16-byte vector of it (global_load_dwordx4).  Consecutive lane groups
+//     take consecutive rows, so one wave-wide load covers 64*16 contiguous
+//     bytes.  Every K and V load of the split is issued before any arithmetic
+//     so the whole split is in flight at once.
+//   * the dot product is a per-lane partial over its 16 bytes followed by a
+//     butterfly across the LPR lanes of the row with DPP lane permutes
+//     (quad_perm, row_half_mirror, row_mirror); no LDS traffic.
+//   * each row group keeps a private softmax state (max, sum, partial P.V)
+//     over its keys; the states are merged across the wave with cross-lane
+//     exchanges and across the 4 waves through LDS, rescaling by exp2 of
+//     the max difference (log2(e) is folded into the scale).
+// Combine.  With more than one split, each workgroup writes its (max, sum,
+// P.V) state to the workspace, releases it with a device-scope fence and
+// takes a ticket; the workgroup that draws the last ticket of its (layer,
+// sequence, KV head, row tile) merges all splits and writes the output, then
+// resets the ticket to zero.  One launch per call.
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPR lanes that hold one key row; every lane gets the total.
+// Lane groups are aligned blocks of LPR lanes.  After the two quad steps a
+// quad is uniform, so mirroring inside 8 (then 16) lanes pairs uniform blocks.
+template <int LPR>
+__device__ __forceinline__ float row_allreduce(float x) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  if (LPR >= 16) x += dpp_mov<kDppRowMirror>(x);
+  if (LPR >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a softmax state with max m when merged under a common max M.
+__device__ __forceinline__ float rescale(float m, float M) {
+  return m == kNegInf ? 0.f : fast_exp2(m - M);
+}
+
+template <int DT, int D, int RT, int KPL>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
+  constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
+  constexpr int NRG = 256 / LPR;                 // key rows per wave-group load
+  constexpr int SPLIT = NRG * KPL;               // keys per workgroup
+  static_assert(LPR * EV == D, "row layout");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = tid / LPR;
+  const int c = tid % LPR;
+
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int rt = blockIdx.z;
+  const int hkv = unit % a.Hkv;
+  const int bb = (unit / a.Hkv) % a.nb;
+  const int l = unit / (a.Hkv * a.nb);
+  const int b = a.b0 + bb;
+  const int P = a.hist[bb];
+  const int nkeys = P + a.N;
+  const int nsplit = (nkeys + SPLIT - 1) / SPLIT;
+  if (split >= nsplit) return;
+
+  const int key0 = split * SPLIT;
+  const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
+  const u32x4 *kc = reinterpret_cast<const u32x4 *>(a.k_cache) + crow0 * LPR + c;
+  const u32x4 *vc = reinterpret_cast<const u32x4 *>(a.v_cache) + crow0 * LPR + c;
+
+  // 1. Issue every K and V load of this split.
+  u32x4 kw[KPL], vw[KPL];
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    const int key = key0 + kk * NRG + rg;
+    kw[kk] = u32x4{0u, 0u, 0u, 0u};
+    vw[kk] = u32x4{0u, 0u, 0u, 0u};
+    if (key < nkeys) {
+      kw[kk] = __builtin_nontemporal_load(kc + (size_t)key * LPR);
+      vw[kk] = __builtin_nontemporal_load(vc + (size_t)key * LPR);
+    }
+  }
+
+  // 2. Query fragments of the tile's rows (row rr = g*N + i of this KV head).
+  const long long qrow0 = (((long long)l * a.B + b) * a.Hq + (long long)hkv * a.group) * a.N;
+  const int rr0 = rt * RT;
+  float qf[RT][EV];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    if (rr0 + r < a.rows) {
+      const u32x4 w = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + rr0 + r) * LPR + c];
+      unpack16<DT>(w, qf[r]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EV; ++e) qf[r][e] = 0.f;
+    }
+  }
+
+  // 3. Scores in the log2 domain, masked keys at -inf.
+  float s[RT][KPL];
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    float kf[EV];
+    unpack16<DT>(kw[kk], kf);
+    const int key = key0 + kk * NRG + rg;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) dot = fmaf(qf[r][e], kf[e], dot);
+      dot = row_allreduce<LPR>(dot);
+      const int i = (rr0 + r) % a.N;
+      const bool visible = (key < nkeys) && (key <= P + i) && (rr0 + r < a.rows);
+      s[r][kk] = visible ? dot * a.scale_log2 : kNegInf;
+    }
+  }
+
+  // 4. Per-row-group softmax state over its KPL keys.
+  float m[RT], lsum[RT], acc[RT][EV];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float mx = s[r][0];
+#pragma unroll
+    for (int kk = 1; kk < KPL; ++kk) mx = fmaxf(mx, s[r][kk]);
+    m[r] = mx;
+    lsum[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[r][e] = 0.f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    float vf[EV];
+    unpack16<DT>(vw[kk], vf);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const float p = (m[r] == kNegInf) ? 0.f : fast_exp2(s[r][kk] - m[r]);
+      lsum[r] += p;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[r][e] = fmaf(p, vf[e], acc[r][e]);
+    }
+  }
+
+  // 5. Merge the row groups of this wave (lanes with the same c).
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float M = m[r];
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float f = rescale(m[r], M);
+    lsum[r] *= f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[r][e] *= f;
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      lsum[r] += __shfl_xor(lsum[r], off);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[r][e] += __shfl_xor(acc[r][e], off);
+    }
+    m[r] = M;
+  }
+
+  // 6. Merge the four waves through LDS.
+  __shared__ float sh_o[4][RT][D];
+  __shared__ float sh_m[4][RT];
+  __shared__ float sh_l[4][RT];
+  if (lane < LPR) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+      for (int e = 0; e < EV; ++e) sh_o[wave][r][c * EV + e] = acc[r][e];
+      if (c == 0) {
+        sh_m[wave][r] = m[r];
+        sh_l[wave][r] = lsum[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int t = tid; t < RT * D; t += 256) {
+    const int r = t / D;
+    const int d = t % D;
+    if (rr0 + r >= a.rows) continue;
+    float M = sh_m[0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh_m[w][r]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = rescale(sh_m[w][r], M);
+      o = fmaf(f, sh_o[w][r][d], o);
+      L = fmaf(f, sh_l[w][r], L);
+    }
+    const long long row = qrow0 + rr0 + r;
+    if (nsplit == 1) {
+      const float val = o / L;
+      store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
+    } else {
+      const size_t ws = (size_t)row * a.max_splits + split;
+      a.ws_o[ws * D + d] = o;
+      if (d == 0) {
+        a.ws_ml[ws * 2] = M;
+        a.ws_ml[ws * 2 + 1] = L;
+      }
+    }
+  }
+  if (nsplit == 1) return;
+
+  // 7. Ticket: the last split of this (layer, sequence, KV head, row tile)
+  //    merges every split.
+  __shared__ int sh_last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int *ticket = a.tickets + (((long long)l * a.B + b) * a.Hkv + hkv) * a.row_tiles + rt;
+    const int old = atomicAdd(ticket, 1);
+    sh_last = (old == nsplit - 1);
+    if (sh_last) atomicExch(ticket, 0);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  __threadfence();
+
+  for (int t = tid; t < RT * D; t += 256) {
+    const int r = t / D;
+    const int d = t % D;
+    if (rr0 + r >= a.rows) continue;
+    const long long row = qrow0 + rr0 + r;
+    const size_t ws0 = (size_t)row * a.max_splits;
+    float M = kNegInf;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, __builtin_nontemporal_load(&a.ws_ml[(ws0 + sp) * 2]));
+    float o = 0.f, L = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float f = rescale(__builtin_nontemporal_load(&a.ws_ml[(ws0 + sp) * 2]), M);
+      o = fmaf(f, __builtin_nontemporal_load(&a.ws_o[(ws0 + sp) * D + d]), o);
+      L = fmaf(f, __builtin_nontemporal_load(&a.ws_ml[(ws0 + sp) * 2 + 1]), L);
+    }
+    const float val = o / L;
+    store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
+  }
+}
+
+constexpr int kKeysPerLane = 4;
+
+template <int DT, int D, int RT>
+hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
+  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.nb * a.Hkv), (unsigned)a.row_tiles);
+  hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_rt(const DecodeArgs &a, int rt, int splits, hipStream_t s) {
+  switch (rt) {
+    case 1: return launch_one<DT, D, 1>(a, splits, s);
+    case 2: return launch_one<DT, D, 2>(a, splits, s);
+    case 4: return launch_one<DT, D, 4>(a, splits, s);
+    default: return launch_one<DT, D, 8>(a, splits, s);
+  }
+}
+
+}  // namespace
+
+int decode_row_tile(int rows) {
+  if (rows <= 1) return 1;
+  if (rows <= 2) return 2;
+  if (rows <= 4) return 4;
+  return 8;
+}
+
+int decode_split_keys(int dtype, int D) {
+  const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;
+  return (256 / lpr) * kKeysPerLane;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile, int splits,
+                         hipStream_t s) {
+  if (dtype == KVC_F32) {
+    if (D == 64) return launch_rt<KVC_F32, 64>(a, row_tile, splits, s);
+    return launch_rt<KVC_F32, 128>(a, row_tile, splits, s);
+  }
+  if (D == 64) return launch_rt<KVC_BF16, 64>(a, row_tile, splits, s);
+  return launch_rt<KVC_BF16, 128>(a, row_tile, splits, s);
+}
+
+}  // namespace kvc

@@ -1,0 +1,120 @@
+// kvc_internal.h -- shared definitions of the HIP kernels and their host
+// launchers inside libkvcache.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvcache.h"
+
+namespace kvc {
+
+// Sequences carried per launch in the kernel-argument block.  Larger batches
+// are split into several launches over batch slices.
+constexpr int kMaxBatchPerLaunch = 64;
+
+// 16-byte vector moved by one lane per global load or store.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Dtype;
+template <> struct Dtype<KVC_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPer16B = 4;  // elements per 16-byte vector
+};
+template <> struct Dtype<KVC_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPer16B = 8;
+};
+
+// Widen a 16-byte vector into fp32 values (bf16 widening is exact).
+template <int DT>
+__device__ __forceinline__ void unpack16(const u32x4 &w, float *out);
+template <>
+__device__ __forceinline__ void unpack16<KVC_F32>(const u32x4 &w, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+}
+template <>
+__device__ __forceinline__ void unpack16<KVC_BF16>(const u32x4 &w, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Store n consecutive fp32 values as the output element type.
+template <int DT>
+__device__ __forceinline__ void store_elems(void *base, size_t index, const float *v, int n);
+template <>
+__device__ __forceinline__ void store_elems<KVC_F32>(void *base, size_t index, const float *v, int n) {
+  float *p = reinterpret_cast<float *>(base) + index;
+  for (int i = 0; i < n; ++i) p[i] = v[i];
+}
+template <>
+__device__ __forceinline__ void store_elems<KVC_BF16>(void *base, size_t index, const float *v, int n) {
+  uint16_t *p = reinterpret_cast<uint16_t *>(base) + index;
+  for (int i = 0; i < n; ++i) p[i] = (uint16_t)f32_to_bf16_rne(v[i]);
+}
+
+// ---- launch descriptors (passed by value as kernel arguments) -------------
+
+struct AppendArgs {
+  char *k_cache, *v_cache;
+  const char *k_new, *v_new;
+  int32_t B, Hkv, Tmax;
+  int32_t layer0, n_layers, N;
+  int32_t b0, nb;       // batch slice [b0, b0+nb) of this launch
+  int32_t row_vec16;    // 16-byte vectors per row (D * elem / 16)
+  int32_t hist[kMaxBatchPerLaunch];
+};
+
+struct DecodeArgs {
+  const char *k_cache, *v_cache;
+  const char *q;
+  char *o;
+  float *ws_o;       // [rows][max_splits][D] unnormalised partial outputs
+  float *ws_ml;      // [rows][max_splits][2] partial (max, sum), log2 domain
+  int32_t *tickets;  // [n_layers][B][Hkv][row_tiles]
+  int32_t B, Hkv, Hq, Tmax, N;
+  int32_t layer0, n_layers;
+  int32_t group;       // Hq / Hkv
+  int32_t rows;        // G * N query rows per (layer, sequence, KV head)
+  int32_t row_tiles;   // ceil(rows / row tile)
+  int32_t max_splits;  // workspace stride in splits
+  int32_t b0, nb;
+  float scale_log2;    // scale * log2(e)
+  int32_t hist[kMaxBatchPerLaunch];
+};
+
+struct PrefillArgs {
+  char *k_cache, *v_cache;
+  const char *q, *k, *v;
+  char *o;
+  int32_t B, Hkv, Hq, Tmax, S;
+  int32_t layer0, n_layers;
+  int32_t group;
+  int32_t q_tiles;
+  float scale_log2;
+};
+
+// Host launchers (one translation unit each).  They assume validated
+// arguments and return the launch status.
+hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile,
+                         int splits, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s);
+
+// Geometry shared by kvc_decode_workspace_bytes and the decode launcher.
+int decode_row_tile(int rows);
+int decode_split_keys(int dtype, int D);
+
+}  // namespace kvc

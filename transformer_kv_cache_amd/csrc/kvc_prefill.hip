@@ -1,0 +1,304 @@
+// kvc_prefill.hip -- causal self-attention over a whole prompt on the matrix
+// cores, writing the prompt's K/V rows into the cache on the way.
+//
+// What it computes ([KV-4] jennyma11.github.io/infra/ch07-01.html, "Prefill
+// 阶段"; [KV-1] gitcode.csdn.net/69e62cef0a2f6a37c5a11c4f.html, "KV Cache
+// 原理"): every prompt row i attends to rows 0..i; the K/V of all S rows land
+// in cache rows [0, S).  Unlike decode this is a dense contraction (two
+// S x S x D products per head), so it runs on MFMA.
+//
+// Tiling.  A workgroup of 4 waves owns one (layer, sequence, query head) and a
+// tile of BM = 128 query rows (32 per wave); it walks key tiles of BN = 64
+// rows up to the diagonal, staging each K/V tile in LDS once for all four
+// waves.  Per wave and key tile:
+//   S^T = K_tile . Q^T   (keys x queries; 32x32 MFMA blocks, Q held in
+//                          registers for the whole kernel)
+//   online softmax per query: each lane owns one query column, so the running
+//   max / sum need a single exchange between the two half-waves
+//   O^T += V^T . P^T     (P^T is taken straight from the S^T accumulators)
+// Computing the transposed products keeps the softmax probabilities in the
+// registers that feed the second MFMA: the key order inside each 16-key MFMA
+// step is permuted to match the accumulator layout, and the V tile is stored
+// to LDS in that permuted order (bf16) so each operand fetch is one 16-byte
+// LDS read.
+//   bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV product,
+//         fp32 accumulation.
+//   fp32: v_mfma_f32_32x32x2_f32, everything in fp32 (no reduced precision).
+// Tiles above the diagonal are never loaded; a wave skips key tiles that lie
+// entirely above its own 32 rows.  Grid order puts the longest (last) query
+// tiles of every head first, and with a head count that is a multiple of 8
+// all tiles of one head land on the same XCD and share its L2.
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+constexpr int BN = 64;   // keys per tile
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position of key k (0..15) of a 16-key group in the permuted V^T rows: bits
+// 2 and 3 swapped, so a half-wave's eight probabilities of one MFMA step
+// ({0-3, 8-11} for the low half, {4-7, 12-15} for the high half) are
+// contiguous.
+__device__ __forceinline__ int perm16(int k) {
+  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+template <int DT, int D> struct Smem;
+template <int D> struct Smem<KVC_BF16, D> {
+  static constexpr int kKStride = D + 8;    // bf16 elements per K row (16-B multiple)
+  static constexpr int kVtStride = BN + 8;  // bf16 elements per V^T row
+  uint16_t k[BN * kKStride];
+  uint16_t vt[D * kVtStride];
+};
+template <int D> struct Smem<KVC_F32, D> {
+  static constexpr int kKStride = D + 4;
+  static constexpr int kVStride = D;
+  float k[BN * kKStride];
+  float v[BN * kVStride];
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  constexpr int EB = Dtype<DT>::kBytes;
+  constexpr int EV = Dtype<DT>::kPer16B;
+  constexpr int LPR = D * EB / 16;             // 16-byte vectors per row
+  constexpr int TILE_VECS = BN * LPR;          // 16-byte vectors per K (or V) tile
+  constexpr int VPT = TILE_VECS / 256;         // per thread
+  constexpr int DB = D / 32;                   // 32-wide d blocks of O^T
+  constexpr int KB = BN / 32;                  // 32-key blocks of S^T
+  static_assert(TILE_VECS % 256 == 0, "tile load split");
+  __shared__ Smem<DT, D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;     // half-wave
+  const int col = lane & 31;   // MFMA column / row within a 32 block
+
+  const int head = blockIdx.x;  // (l, b, hq)
+  const int qt = a.q_tiles - 1 - (int)blockIdx.y;
+  const int hq = head % a.Hq;
+  const int b = (head / a.Hq) % a.B;
+  const int l = head / (a.Hq * a.B);
+  const int hkv = hq / a.group;
+  const bool writer = (hq % a.group) == 0;
+  const int S = a.S;
+  const int q0 = qt * BM;
+  const int qrow = q0 + wave * 32 + col;  // this lane's query row
+  const int wave_last = q0 + wave * 32 + 31;
+
+  const size_t step_head = ((size_t)l * a.B + b);
+  const char *qbase = a.q + ((step_head * a.Hq + hq) * (size_t)S) * D * EB;
+  const char *kbase = a.k + ((step_head * a.Hkv + hkv) * (size_t)S) * D * EB;
+  const char *vbase = a.v + ((step_head * a.Hkv + hkv) * (size_t)S) * D * EB;
+  char *kcache = a.k_cache + (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax * D * EB;
+  char *vcache = a.v_cache + (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax * D * EB;
+
+  // Q fragments, resident for the whole kernel.
+  //   bf16: qv[ds] = Q[qrow][16 ds + 8 h .. +7]        (B operand of 32x32x16)
+  //   fp32: qv[j]  = Q[qrow][8 j + 4 h .. +3]           (4 B operands of 32x32x2)
+  constexpr int QV = (DT == KVC_BF16) ? D / 16 : D / 8;
+  u32x4 qv[QV];
+#pragma unroll
+  for (int j = 0; j < QV; ++j) {
+    qv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (qrow < S) {
+      const int d0 = (DT == KVC_BF16) ? 16 * j + 8 * h : 8 * j + 4 * h;
+      qv[j] = *reinterpret_cast<const u32x4 *>(qbase + ((size_t)qrow * D + d0) * EB);
+    }
+  }
+
+  f32x16 acc_o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_o[db] = f32x16{};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+
+  const int kv_end = (q0 + BM < S) ? q0 + BM : S;  // keys this tile needs
+  const int n_kt = (kv_end + BN - 1) / BN;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int key0 = kt * BN;
+    const bool store_cache = writer && key0 >= q0;  // this tile's rows are ours to write
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int it = 0; it < VPT; ++it) {
+      const int vec = tid + 256 * it;
+      const int row = vec / LPR;
+      const int c = vec % LPR;
+      const int key = key0 + row;
+      u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
+      if (key < S) {
+        kw = *reinterpret_cast<const u32x4 *>(kbase + ((size_t)key * D + c * EV) * EB);
+        vw = *reinterpret_cast<const u32x4 *>(vbase + ((size_t)key * D + c * EV) * EB);
+        if (store_cache) {
+          *reinterpret_cast<u32x4 *>(kcache + ((size_t)key * D + c * EV) * EB) = kw;
+          *reinterpret_cast<u32x4 *>(vcache + ((size_t)key * D + c * EV) * EB) = vw;
+        }
+      }
+      if constexpr (DT == KVC_BF16) {
+        *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kw;
+        const int pos = (row & ~15) | perm16(row & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sm.vt[(c * EV + 2 * j) * Smem<DT, D>::kVtStride + pos] = (uint16_t)(vw[j] & 0xFFFFu);
+          sm.vt[(c * EV + 2 * j + 1) * Smem<DT, D>::kVtStride + pos] = (uint16_t)(vw[j] >> 16);
+        }
+      } else {
+        *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kw;
+        *reinterpret_cast<u32x4 *>(&sm.v[row * Smem<DT, D>::kVStride + c * EV]) = vw;
+      }
+    }
+    __syncthreads();
+    if (key0 > wave_last) continue;  // whole tile above this wave's rows
+
+    // S^T blocks: acc_s[kb][i] = score of key key0 + 32 kb + 8 (i/4) + 4 h + i%4
+    // for query qrow.
+    f32x16 acc_s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      acc_s[kb] = f32x16{};
+      const int krow = 32 * kb + col;
+      if constexpr (DT == KVC_BF16) {
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+          const u32x4 kf =
+              *reinterpret_cast<const u32x4 *>(&sm.k[krow * Smem<DT, D>::kKStride + 16 * ds + 8 * h]);
+          acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qv[ds]), acc_s[kb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) {
+          const f32x4 kf =
+              *reinterpret_cast<const f32x4 *>(&sm.k[krow * Smem<DT, D>::kKStride + 8 * j + 4 * h]);
+          const f32x4 qf = __builtin_bit_cast(f32x4, qv[j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[r], qf[r], acc_s[kb], 0, 0, 0);
+        }
+      }
+    }
+
+    // Scale, causal mask, online softmax for this lane's query.
+    const bool need_mask = (key0 + BN - 1 > q0 + wave * 32) || (key0 + BN > S);
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = acc_s[kb][i] * a.scale_log2;
+        if (need_mask) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key > qrow || key >= S) s = kNegInf;
+        }
+        acc_s[kb][i] = s;
+        mt = fmaxf(mt, s);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(acc_s[kb][i] - m_new);
+        acc_s[kb][i] = p;
+        psum += p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (DT == KVC_BF16) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 pw;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pw[j] = pack_bf16x2(acc_s[kb][8 * t + 2 * j], acc_s[kb][8 * t + 2 * j + 1]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x4 vf = *reinterpret_cast<const u32x4 *>(
+                &sm.vt[(32 * db + col) * Smem<DT, D>::kVtStride + 32 * kb + 16 * t + 8 * h]);
+            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pw), acc_o[db], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const int vrow = 32 * kb + 8 * (s >> 2) + 4 * h + (s & 3);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const float vf = sm.v[vrow * Smem<DT, D>::kVStride + 32 * db + col];
+            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, acc_s[kb][s], acc_o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // Normalise and write O[qrow][d] for d = 32 db + 8 g + 4 h + 0..3.
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow >= S) return;
+  const float inv = 1.f / l_tot;
+  char *orow = a.o + ((step_head * a.Hq + hq) * (size_t)S + qrow) * D * EB;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * h;
+      const float o0 = acc_o[db][4 * g] * inv, o1 = acc_o[db][4 * g + 1] * inv;
+      const float o2 = acc_o[db][4 * g + 2] * inv, o3 = acc_o[db][4 * g + 3] * inv;
+      if constexpr (DT == KVC_BF16) {
+        *reinterpret_cast<u32x2 *>(orow + d0 * EB) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      } else {
+        *reinterpret_cast<f32x4 *>(orow + d0 * EB) = f32x4{o0, o1, o2, o3};
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n_layers * a.B * a.Hq), (unsigned)a.q_tiles);
+  if (dtype == KVC_F32) {
+    if (D == 64)
+      hipLaunchKernelGGL((prefill_kernel<KVC_F32, 64>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<KVC_F32, 128>), grid, dim3(256), 0, s, a);
+  } else {
+    if (D == 64)
+      hipLaunchKernelGGL((prefill_kernel<KVC_BF16, 64>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<KVC_BF16, 128>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+int prefill_query_tile() { return BM; }
+
+}  // namespace kvc

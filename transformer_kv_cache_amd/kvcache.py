@@ -1,0 +1,237 @@
+"""Thin Python binding of libkvcache.so (C ABI in include/kvcache.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape
+and contiguity, and their device pointers, sizes and the current HIP stream
+are handed to the library.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library has not been built the first
+call raises ``KVCacheLibraryMissing``.
+
+Layouts (row-major, contiguous):
+  cache K, V        [L, B, Hkv, Tmax, D]
+  q, o              [n_layers, B, Hq, N, D]
+  k_new, v_new      [n_layers, B, Hkv, N, D]
+  hist_len          host int32[B] (list, numpy array or CPU tensor)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvcache.so")
+
+KVC_F32, KVC_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
+_STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
+           -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
+
+
+class KVCacheLibraryMissing(ImportError):
+    pass
+
+
+class KVCacheError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of ``kvc_cache``."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("L", ctypes.c_int32), ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("Tmax", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load libkvcache.so (once) and declare its signatures."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise KVCacheLibraryMissing(
+            f"{p} is not built; run `python -m transformer_kv_cache_amd.build`")
+    with _lib_lock:
+        lib = ctypes.CDLL(p)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cp = ctypes.POINTER(CacheDesc)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.kvc_abi_version.argtypes, lib.kvc_abi_version.restype = [], i32
+        lib.kvc_last_error.argtypes, lib.kvc_last_error.restype = [], ctypes.c_char_p
+        lib.kvc_cache_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+        lib.kvc_cache_bytes.restype = ctypes.c_uint64
+        lib.kvc_append.argtypes = [cp, i32, i32, vp, vp, i32, ip, vp]
+        lib.kvc_append.restype = i32
+        lib.kvc_decode_workspace_bytes.argtypes = [cp, i32, i32, i32]
+        lib.kvc_decode_workspace_bytes.restype = sz
+        lib.kvc_attn_decode.argtypes = [cp, i32, i32, vp, i32, i32, ip, ctypes.c_float, vp, vp, sz, vp]
+        lib.kvc_attn_decode.restype = i32
+        lib.kvc_attn_prefill.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
+        lib.kvc_attn_prefill.restype = i32
+        if path is None:
+            _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KVCacheError(status, library().kvc_last_error().decode())
+
+
+def cache_bytes(L, B, Hkv, Tmax, D, dtype=torch.float32) -> int:
+    """2 x L x Hkv x D x Tmax x B x element size (the cache-size formula)."""
+    return int(library().kvc_cache_bytes(L, B, Hkv, Tmax, D, _DTYPE_CODE[dtype]))
+
+
+class KVCache:
+    """A preallocated per-model cache: ``k`` and ``v`` are [L,B,Hkv,Tmax,D]
+    torch tensors on one GPU.  Pass existing tensors or let it allocate."""
+
+    def __init__(self, L, B, Hkv, Tmax, D, dtype=torch.float32, device="cuda", k=None, v=None):
+        if dtype not in _DTYPE_CODE:
+            raise TypeError(f"unsupported cache dtype {dtype}")
+        shape = (L, B, Hkv, Tmax, D)
+        self.k = k if k is not None else torch.empty(shape, dtype=dtype, device=device)
+        self.v = v if v is not None else torch.empty(shape, dtype=dtype, device=device)
+        for t in (self.k, self.v):
+            if tuple(t.shape) != shape or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("cache tensors must be contiguous CUDA tensors of shape "
+                                 f"{shape} and dtype {dtype}")
+        self.L, self.B, self.Hkv, self.Tmax, self.D, self.dtype = L, B, Hkv, Tmax, D, dtype
+
+    @property
+    def device(self):
+        return self.k.device
+
+    def desc(self) -> CacheDesc:
+        return CacheDesc(self.k.data_ptr(), self.v.data_ptr(), self.L, self.B, self.Hkv,
+                         self.Tmax, self.D, _DTYPE_CODE[self.dtype])
+
+    @property
+    def nbytes(self) -> int:
+        return cache_bytes(self.L, self.B, self.Hkv, self.Tmax, self.D, self.dtype)
+
+
+def _hist(hist_len, B):
+    h = np.ascontiguousarray(
+        hist_len.cpu().numpy() if isinstance(hist_len, torch.Tensor) else hist_len, dtype=np.int32)
+    if h.shape != (B,):
+        raise ValueError(f"hist_len must have shape ({B},), got {h.shape}")
+    return h, h.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(name, t, cache, shape):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != cache.device:
+        raise ValueError(f"{name} must be a CUDA tensor on {cache.device}")
+    if t.dtype != cache.dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, cache has {cache.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def append(cache: KVCache, k_new, v_new, hist_len, layer0: int = 0, stream=None) -> None:
+    """Write k_new/v_new ([n_layers,B,Hkv,N,D]) into cache rows
+    [hist_len[b], hist_len[b]+N) of layers layer0 .. layer0+n_layers-1."""
+    n_layers, _, _, N, _ = k_new.shape
+    shape = (n_layers, cache.B, cache.Hkv, N, cache.D)
+    _check_tensor("k_new", k_new, cache, shape)
+    _check_tensor("v_new", v_new, cache, shape)
+    _, hp = _hist(hist_len, cache.B)
+    d = cache.desc()
+    _check(library().kvc_append(ctypes.byref(d), layer0, n_layers, k_new.data_ptr(),
+                                v_new.data_ptr(), N, hp, _stream(cache.device, stream)))
+
+
+def decode_workspace_bytes(cache: KVCache, n_layers: int, Hq: int, N: int) -> int:
+    d = cache.desc()
+    return int(library().kvc_decode_workspace_bytes(ctypes.byref(d), n_layers, Hq, N))
+
+
+def new_decode_workspace(cache: KVCache, n_layers: int, Hq: int, N: int) -> torch.Tensor:
+    """A zero-filled workspace for kvc_attn_decode with this geometry.  Every
+    decode call leaves its tickets at zero again, so it serves any number of
+    calls of the same (cache geometry, n_layers, Hq, N)."""
+    n = max(decode_workspace_bytes(cache, n_layers, Hq, N), 256)
+    ws = torch.zeros(n + 256, dtype=torch.uint8, device=cache.device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+_ws_cache: dict = {}
+
+
+def _default_workspace(cache, n_layers, Hq, N, stream):
+    """One workspace per (device, stream, geometry): a workspace must not
+    change geometry, since its ticket region would then overlap bytes that
+    held another geometry's partial states."""
+    key = (cache.device, int(_stream(cache.device, stream).value or 0), cache.L, cache.B,
+           cache.Hkv, cache.Tmax, cache.D, cache.dtype, n_layers, Hq, N)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = new_decode_workspace(cache, n_layers, Hq, N)
+        _ws_cache[key] = ws
+    return ws
+
+
+def attn_decode(cache: KVCache, q, hist_len, scale: float | None = None, out=None,
+                layer0: int = 0, workspace=None, stream=None):
+    """Attention of q ([n_layers,B,Hq,N,D]) against the cache; new row i of
+    sequence b sees keys 0 .. hist_len[b]+i.  The N new K/V rows must already
+    be appended.  Returns ``out`` (allocated if None)."""
+    n_layers, _, Hq, N, _ = q.shape
+    shape = (n_layers, cache.B, Hq, N, cache.D)
+    _check_tensor("q", q, cache, shape)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, cache.B)
+    if workspace is None:
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream)
+    if workspace.device != cache.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the cache's device")
+    d = cache.desc()
+    _check(library().kvc_attn_decode(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), Hq, N, hp, float(scale), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(cache.device, stream)))
+    return out
+
+
+def attn_prefill(cache: KVCache, q, k, v, scale: float | None = None, out=None,
+                 layer0: int = 0, stream=None):
+    """Causal attention over an S-token prompt (q [n_layers,B,Hq,S,D], k/v
+    [n_layers,B,Hkv,S,D]); also writes k/v into cache rows [0, S)."""
+    n_layers, _, Hq, S, _ = q.shape
+    _check_tensor("q", q, cache, (n_layers, cache.B, Hq, S, cache.D))
+    _check_tensor("k", k, cache, (n_layers, cache.B, cache.Hkv, S, cache.D))
+    _check_tensor("v", v, cache, (n_layers, cache.B, cache.Hkv, S, cache.D))
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    d = cache.desc()
+    _check(library().kvc_attn_prefill(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), k.data_ptr(), v.data_ptr(), Hq, S,
+        float(scale), out.data_ptr(), _stream(cache.device, stream)))
+    return out
