@@ -1,0 +1,385 @@
+"""Benchmark of the KV-cache attention hot path on one MI355X.
+
+One step = the whole decode hot path for GPT-2 Small at context 1024: append
+of the new token's K/V rows into all 12 layers' caches, then attention of the
+new query rows against the 1024 cached keys (split-K partials + combine in one
+launch).  Inputs: fp32, B=1, 12 layers x 12 heads, D=64, history P=1023,
+N(0,1) from a fixed seed.
+
+Timing: steps are captured in a HIP graph (torch.cuda.CUDAGraph) and replayed;
+HIP events on the capture/replay stream bracket exactly --steps steps.  Eight
+cache replicas (604 MB in total, more than twice the 256 MB Infinity Cache)
+rotate step by step, so every step streams its K/V from HBM rather than from
+a cache level.  The oracle (CPU, double precision) is timed beside it on a
+bounded sample of the same steps, and the timed outputs are checked against it.
+
+Prints ONE JSON line.  Extra entries: per-kernel times, the per-layer and
+eager launch modes, the decode sweep over history lengths, chunked and batched
+decode, and the prefill TFLOP/s with its matrix-core fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix-core peaks
+METRIC = "decode attention µs/step + achieved HBM GB/s at T=1024; prefill TFLOP/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")
+DECODE_SOURCES = [os.path.join(ROOT, "transformer_kv_cache_amd", "csrc", f)
+                  for f in ("kvc_decode.hip", "kvc_internal.h")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def elem_bytes(dtype):
+    return 4 if dtype == "f32" else 2
+
+
+def decode_bytes(w, N):
+    """Algorithmic bytes of one decode call: every visible K and V row once,
+    q read and o written once."""
+    e = elem_bytes(w.dtype)
+    kv = 2 * w.L * w.Hkv * w.D * e * int(np.sum(w.hist + N))
+    qo = 2 * w.L * w.B * w.Hq * N * w.D * e
+    return kv + qo
+
+
+def append_bytes(w, N):
+    """Algorithmic bytes of one append: new K/V rows read once, written once."""
+    return 2 * 2 * w.L * w.B * w.Hkv * N * w.D * elem_bytes(w.dtype)
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 PMC summary,
+    if it was measured on the current decode kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("decode_source_sha256") != decode_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class GraphTimer:
+    """Capture `fn(r)` for r in a rotation into HIP graphs and time exactly
+    `count` calls with events on the replay stream."""
+
+    def __init__(self, torch, fn, rotate):
+        self.torch = torch
+        self.rotate = rotate
+        self.fn = fn
+        self.graphs = {}
+
+    def _graph(self, n):
+        if n not in self.graphs:
+            torch = self.torch
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for r in range(n):
+                        self.fn(r)
+            torch.cuda.current_stream().wait_stream(s)
+            self.graphs[n] = g
+        return self.graphs[n]
+
+    def time(self, count, warm=2):
+        torch = self.torch
+        full, rem = divmod(count, self.rotate)
+        g_full = self._graph(self.rotate)
+        g_rem = self._graph(rem) if rem else None
+        for _ in range(warm):
+            g_full.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) * 1e3 / count  # microseconds per call
+
+
+def replicate(torch, arr_dev, n):
+    return [arr_dev] + [arr_dev.clone() for _ in range(n - 1)]
+
+
+def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=False):
+    """Time the decode step (append + attention) of workload `w` (one step
+    of N rows).  Returns a dict of timings and the device state of replica 0."""
+    from gpu_common import to_dev, torch_dtype
+    q_np, k_np, v_np = w.steps[0]
+    N = q_np.shape[3]
+    base_k, base_v = to_dev(w.k_cache), to_dev(w.v_cache)
+    dt = torch_dtype(w.dtype)
+    caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=kk, v=vv)
+              for kk, vv in zip(replicate(torch, base_k, rotate), replicate(torch, base_v, rotate))]
+    qs = replicate(torch, to_dev(q_np), rotate)
+    kns = replicate(torch, to_dev(k_np), rotate)
+    vns = replicate(torch, to_dev(v_np), rotate)
+    outs = [torch.empty_like(qs[0]) for _ in range(rotate)]
+    wss = [K.new_decode_workspace(caches[0], w.L, w.Hq, N) for _ in range(rotate)]
+    hist = w.hist.copy()
+
+    def step(r):
+        K.append(caches[r], kns[r], vns[r], hist)
+        K.attn_decode(caches[r], qs[r], hist, scale=w.scale, out=outs[r], workspace=wss[r])
+
+    def decode_only(r):
+        K.attn_decode(caches[r], qs[r], hist, scale=w.scale, out=outs[r], workspace=wss[r])
+
+    def append_only(r):
+        K.append(caches[r], kns[r], vns[r], hist)
+
+    for i in range(warmup):
+        step(i % rotate)
+    torch.cuda.synchronize()
+    res = {}
+    res["step_us"] = GraphTimer(torch, step, rotate).time(steps)
+    res["decode_kernel_us"] = GraphTimer(torch, decode_only, rotate).time(steps)
+    res["append_kernel_us"] = GraphTimer(torch, append_only, rotate).time(steps)
+    res["decode_bytes"] = decode_bytes(w, N)
+    res["append_bytes"] = append_bytes(w, N)
+    res["step_bytes"] = res["decode_bytes"] + res["append_bytes"]
+    res["step_gbs"] = res["step_bytes"] / res["step_us"] / 1e3
+    res["decode_gbs"] = res["decode_bytes"] / res["decode_kernel_us"] / 1e3
+    if eager:
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            step(i % rotate)
+        end.record()
+        torch.cuda.synchronize()
+        res["eager_step_us"] = start.elapsed_time(end) * 1e3 / steps
+    if per_layer:
+        ws1 = [K.new_decode_workspace(caches[0], 1, w.Hq, N) for _ in range(rotate)]
+
+        def step_per_layer(r):
+            for l in range(w.L):
+                K.append(caches[r], kns[r][l:l + 1], vns[r][l:l + 1], hist, layer0=l)
+                K.attn_decode(caches[r], qs[r][l:l + 1], hist, scale=w.scale,
+                              out=outs[r][l:l + 1], layer0=l, workspace=ws1[r])
+
+        for i in range(warmup):
+            step_per_layer(i % rotate)
+        res["perlayer_step_us"] = GraphTimer(torch, step_per_layer, rotate).time(steps)
+    torch.cuda.synchronize()
+    res["_out0"] = outs[0]
+    return res
+
+
+def bench_prefill(torch, K, S, dtype, reps, rotate=4):
+    from gpu_common import to_dev, torch_dtype
+    from transformer_kv_cache_amd import synth
+    w = synth.causal_prefill(S, dtype, seed=7)
+    dt = torch_dtype(dtype)
+    q0, k0, v0 = (to_dev(a) for a in w.prefill)
+    qs, ks, vs = (replicate(torch, t, rotate) for t in (q0, k0, v0))
+    caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt) for _ in range(rotate)]
+    outs = [torch.empty_like(q0) for _ in range(rotate)]
+
+    def call(r):
+        K.attn_prefill(caches[r], qs[r], ks[r], vs[r], scale=w.scale, out=outs[r])
+
+    for r in range(rotate):
+        call(r)
+    us = GraphTimer(torch, call, rotate).time(reps)
+    flops = 4 * w.D * w.L * w.Hq * S * (S + 1) // 2
+    tflops = flops / us / 1e6
+    e = elem_bytes(dtype)
+    hbm_bytes = 6 * w.L * w.Hq * S * w.D * e  # q, k, v read; o and the K/V cache rows written
+    return {"S": S, "dtype": dtype, "us": us, "tflops": tflops,
+            "mfma_frac": tflops / MFMA_PEAK_TFLOPS[dtype],
+            "hbm_gbs": hbm_bytes / us / 1e3, "algorithmic_flops": flops}
+
+
+def cpu_baseline(w, target_s, max_steps=100000):
+    """The oracle, as it stands, on a bounded sample of the headline step:
+    append + attention for all 12 layers, repeated until ~target_s seconds."""
+    import oracle
+    q, k, v = w.steps[0]
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        threads = min(threads, int(omp))
+    oracle.set_threads(threads)
+    out = None
+    n = 0
+    t0 = time.perf_counter()
+    while n < max_steps:
+        oracle.append(kc, vc, k, v, w.hist)
+        out = oracle.attention(q, kc, vc, w.hist, w.scale)
+        n += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"seconds": dt, "steps": n, "threads": oracle.max_threads(), "us_per_step": dt / n * 1e6,
+            "out": out}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=8, help="cache replicas cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="length of the oracle's timed CPU sample")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the sweep, chunked/batched decode and prefill extras")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (used to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 4}), flush=True)
+        return
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from transformer_kv_cache_amd import kvcache as K, synth
+    from gpu_common import to_host
+
+    if not os.path.exists(K.LIB_PATH):
+        from transformer_kv_cache_amd import build
+        build.build(verbose=False)
+    K.library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    log("headline: 12-layer fp32 decode at T=1024")
+    w = synth.decode_12layer(1023, seed=0)
+    head = bench_decode(torch, K, w, args.steps, args.warmup, args.rotate, per_layer=True,
+                        eager=True)
+    out0 = to_host(head.pop("_out0"))
+
+    log("cpu baseline (oracle)")
+    cpu = cpu_baseline(w, args.cpu_seconds)
+    max_err = float(np.max(np.abs(out0.astype(np.float64) - cpu["out"])))
+    if not max_err <= 1e-4:
+        raise SystemExit(f"timed outputs differ from the oracle: max abs error {max_err}")
+    step_bytes = head["step_bytes"]
+
+    extras = {}
+    if not args.headline_only:
+        sweep = {}
+        for P in (128, 512, 1000):
+            log(f"sweep P={P}")
+            r = bench_decode(torch, K, synth.decode_12layer(P, seed=P), args.steps, args.warmup,
+                             args.rotate)
+            r.pop("_out0")
+            sweep[f"P{P}"] = {k: round(v, 3) for k, v in r.items()}
+        sweep["P1023"] = {k: round(v, 3) for k, v in head.items()}
+        extras["decode_sweep_fp32_12layer"] = sweep
+        log("chunked decode P=1000 N=8")
+        r = bench_decode(torch, K, synth.chunked_decode(1000, 8, seed=1), args.steps, args.warmup,
+                         args.rotate)
+        r.pop("_out0")
+        extras["chunked_decode_P1000_N8"] = {k: round(v, 3) for k, v in r.items()}
+        for gqa in (False, True):
+            name = "batched_decode_bf16_" + ("gqa32q8kv_D128" if gqa else "mha12_D64")
+            log(name)
+            wb = synth.batched_decode(seed=3, gqa=gqa)
+            r = bench_decode(torch, K, wb, args.steps, args.warmup, 4)
+            r.pop("_out0")
+            r = {k: round(v, 3) for k, v in r.items()}
+            r["lengths"] = (wb.hist + 1).tolist()
+            extras[name] = r
+        pre = []
+        for dtype in ("f32", "bf16"):
+            for S in (256, 1024):
+                log(f"prefill S={S} {dtype}")
+                pre.append({k: (round(v, 4) if isinstance(v, float) else v)
+                            for k, v in bench_prefill(torch, K, S, dtype, 40).items()})
+        extras["prefill_12layer"] = pre
+
+    dec_us = head["decode_kernel_us"]
+    achieved = head["decode_bytes"] / dec_us / 1e3
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(step_bytes / head["step_us"] / 1e3, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic N(0,1), numpy PCG64 seed 0",
+        "config": {"workload": "GPT-2 Small KV-cache decode step, 12 layers, fp32, B=1, H=12, "
+                               "D=64, Tmax=1024, history 1023 + 1 new token (T=1024)",
+                   "layers": 12, "batch": 1, "heads": 12, "head_dim": 64, "context": 1024,
+                   "step": "append + split-K decode, one HIP graph node each per step",
+                   "rotating_cache_replicas": args.rotate},
+        "decode_us_per_step": round(head["step_us"], 3),
+        "step_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel<f32,D64,RT1>",
+                     "kernel_us": round(dec_us, 3), "algorithmic_bytes": head["decode_bytes"]},
+        "cpu_baseline": {"value": round(step_bytes / cpu["us_per_step"] / 1e3, 3), "unit": "GB/s",
+                         "cores": cpu["threads"], "kind": "oracle",
+                         "sample": f"{cpu['steps']} full decode steps (append + attention, all 12 "
+                                   f"layers) of the same workload, {cpu['seconds']:.1f} s",
+                         "us_per_step": round(cpu["us_per_step"], 1)},
+        "parity_max_abs_err": max_err,
+        "modes": {"graph_fused12_step_us": round(head["step_us"], 3),
+                  "graph_perlayer_step_us": round(head["perlayer_step_us"], 3),
+                  "eager_fused12_step_us": round(head["eager_step_us"], 3),
+                  "append_kernel_us": round(head["append_kernel_us"], 3)},
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

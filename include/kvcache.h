@@ -114,11 +114,11 @@ kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
                       const int32_t *hist_len, void *stream);
 
 /*
- * Workspace bytes kvc_attn_decode needs for this geometry: partial softmax
- * states of the split-K passes plus one int32 ticket per (layer, sequence,
- * KV head, row tile).  It depends only on the cache geometry, n_layers, Hq
- * and N, never on the lengths, so one workspace serves every step.  Returns
- * 0 on invalid sizes.
+ * Workspace bytes kvc_attn_decode needs for this geometry: the partial
+ * softmax states (max, sum and unnormalised output row) of the split-K
+ * passes.  It depends only on the cache geometry, n_layers, Hq and N, never
+ * on the lengths, so one workspace serves every step.  Returns 0 on invalid
+ * sizes.
  */
 size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers,
                                   int32_t Hq, int32_t N);
@@ -137,13 +137,11 @@ size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers,
  *   q, o       : device, [n_layers, B, Hq, N, D], cache dtype
  *   scale      : finite score scale, normally 1/sqrt(D)
  *   workspace  : device, >= kvc_decode_workspace_bytes(...) bytes, 256-byte
- *                aligned.  ZERO-FILL IT BEFORE ITS FIRST USE WITH A GIVEN
- *                GEOMETRY (cache geometry, n_layers, Hq, N).  Every call
- *                leaves its tickets at zero again, so a workspace zeroed once
- *                serves every later call of that geometry.  Its layout
- *                depends on the geometry: before using it with another one,
- *                zero it again.  Two calls in flight at the same time must
- *                not share a workspace.
+ *                aligned, caller-owned scratch.  Its contents need no
+ *                initialisation and are meaningless after the call; calls
+ *                enqueued one after another on a stream may share one.  Two
+ *                calls in flight at the same time must not share a
+ *                workspace.
  */
 kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0,
                            int32_t n_layers, const void *q, int32_t Hq,

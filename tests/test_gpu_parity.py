@@ -170,8 +170,8 @@ def test_permutation_property_on_gpu():
 
 
 def test_repeated_calls_reuse_workspace_bitwise():
-    """The split-K tickets return to zero after each call: repeated calls on
-    one workspace give bit-identical outputs."""
+    """Repeated calls on one workspace, including after a call of another
+    geometry scribbled over it, give bit-identical outputs."""
     from transformer_kv_cache_amd import kvcache as K
     w = synth.decode_12layer(1000, seed=4)
     q, k, v = w.steps[0]
@@ -179,12 +179,11 @@ def test_repeated_calls_reuse_workspace_bitwise():
     K.append(cache, to_dev(k), to_dev(v), w.hist)
     ws = K.new_decode_workspace(cache, 12, 12, 1)
     qd = to_dev(q)
-    outs = [to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)) for _ in range(5)]
+    outs = [to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)) for _ in range(3)]
+    ws.fill_(0xFF)  # NaN bit patterns everywhere in the scratch
+    outs += [to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)) for _ in range(2)]
     for o in outs[1:]:
         assert np.array_equal(bits(o), bits(outs[0]))
-    # the ticket region closes the workspace: 12 layers x 1 sequence x 12 KV
-    # heads x 1 row tile int32s, rounded up to 256 bytes = 768 bytes
-    assert int(torch.count_nonzero(ws[-768:]).item()) == 0
 
 
 def test_capacity_error_leaves_cache_untouched():

@@ -75,7 +75,7 @@ kvc_status hip_status(hipError_t e, const char *fn) {
 
 struct DecodeGeometry {
   int rows, row_tile, row_tiles, split_keys, max_splits;
-  size_t ws_o_bytes, ws_ml_bytes, ticket_bytes, total;
+  size_t ws_o_bytes, ws_ml_bytes, total;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -92,8 +92,7 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
   const size_t qrows = (size_t)n_layers * c->B * Hq * N;
   g.ws_o_bytes = round_up(qrows * g.max_splits * c->D * sizeof(float), 256);
   g.ws_ml_bytes = round_up(qrows * g.max_splits * 2 * sizeof(float), 256);
-  g.ticket_bytes = round_up((size_t)n_layers * c->B * c->Hkv * g.row_tiles * sizeof(int32_t), 256);
-  g.total = g.ws_o_bytes + g.ws_ml_bytes + g.ticket_bytes;
+  g.total = g.ws_o_bytes + g.ws_ml_bytes;
   return g;
 }
 
@@ -183,7 +182,6 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_lay
   a.o = (char *)o;
   a.ws_o = (float *)workspace;
   a.ws_ml = (float *)((char *)workspace + g.ws_o_bytes);
-  a.tickets = (int32_t *)((char *)workspace + g.ws_o_bytes + g.ws_ml_bytes);
   a.B = cache->B;
   a.Hkv = cache->Hkv;
   a.Hq = Hq;

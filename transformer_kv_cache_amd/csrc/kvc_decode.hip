@@ -26,10 +26,13 @@
 //     exchanges and across the 4 waves through LDS, rescaling by exp2 of
 //     the max difference (log2(e) is folded into the scale).
 // Combine.  With more than one split, each workgroup writes its (max, sum,
-// P.V) state to the workspace, releases it with a device-scope fence and
-// takes a ticket; the workgroup that draws the last ticket of its (layer,
-// sequence, KV head, row tile) merges all splits and writes the output, then
-// resets the ticket to zero.  One launch per call.
+// P.V) state to the workspace and a second, small kernel merges the splits of
+// every query row (rescaling by exp2 of the max difference) and writes the
+// output; with a single split the workgroup writes the output itself.  The
+// merge is a separate launch rather than a last-workgroup ticket because a
+// device-scope release/acquire on gfx950 writes back and invalidates the
+// whole L2 of the workgroup's XCD, which costs far more than one extra
+// launch.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -101,33 +104,33 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const u32x4 *kc = reinterpret_cast<const u32x4 *>(a.k_cache) + crow0 * LPR + c;
   const u32x4 *vc = reinterpret_cast<const u32x4 *>(a.v_cache) + crow0 * LPR + c;
 
-  // 1. Issue every K and V load of this split.
+  // 1. Issue the query loads and every K and V load of this split up front.
+  //    Key indices past the sequence are clamped to its last row (always
+  //    valid) so that no load sits behind a branch; their scores are masked.
+  const long long qrow0 = (((long long)l * a.B + b) * a.Hq + (long long)hkv * a.group) * a.N;
+  const int rr0 = rt * RT;
+  u32x4 qw[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int rr = (rr0 + r < a.rows) ? rr0 + r : a.rows - 1;
+    qw[r] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + rr) * LPR + c];
+  }
   u32x4 kw[KPL], vw[KPL];
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {
     const int key = key0 + kk * NRG + rg;
-    kw[kk] = u32x4{0u, 0u, 0u, 0u};
-    vw[kk] = u32x4{0u, 0u, 0u, 0u};
-    if (key < nkeys) {
-      kw[kk] = __builtin_nontemporal_load(kc + (size_t)key * LPR);
-      vw[kk] = __builtin_nontemporal_load(vc + (size_t)key * LPR);
-    }
+    const int kidx = key < nkeys ? key : nkeys - 1;
+    kw[kk] = __builtin_nontemporal_load(kc + (size_t)kidx * LPR);
+    vw[kk] = __builtin_nontemporal_load(vc + (size_t)kidx * LPR);
   }
+  // Keep the scheduler from interleaving arithmetic (and its waits) into the
+  // load burst: all loads of the split are in flight before the first wait.
+  __builtin_amdgcn_sched_barrier(0);
 
   // 2. Query fragments of the tile's rows (row rr = g*N + i of this KV head).
-  const long long qrow0 = (((long long)l * a.B + b) * a.Hq + (long long)hkv * a.group) * a.N;
-  const int rr0 = rt * RT;
   float qf[RT][EV];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    if (rr0 + r < a.rows) {
-      const u32x4 w = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + rr0 + r) * LPR + c];
-      unpack16<DT>(w, qf[r]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EV; ++e) qf[r][e] = 0.f;
-    }
-  }
+  for (int r = 0; r < RT; ++r) unpack16<DT>(qw[r], qf[r]);
 
   // 3. Scores in the log2 domain, masked keys at -inf.
   float s[RT][KPL];
@@ -236,48 +239,51 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (nsplit == 1) return;
-
-  // 7. Ticket: the last split of this (layer, sequence, KV head, row tile)
-  //    merges every split.
-  __shared__ int sh_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int *ticket = a.tickets + (((long long)l * a.B + b) * a.Hkv + hkv) * a.row_tiles + rt;
-    const int old = atomicAdd(ticket, 1);
-    sh_last = (old == nsplit - 1);
-    if (sh_last) atomicExch(ticket, 0);
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-
-  for (int t = tid; t < RT * D; t += 256) {
-    const int r = t / D;
-    const int d = t % D;
-    if (rr0 + r >= a.rows) continue;
-    const long long row = qrow0 + rr0 + r;
-    const size_t ws0 = (size_t)row * a.max_splits;
-    float M = kNegInf;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, __builtin_nontemporal_load(&a.ws_ml[(ws0 + sp) * 2]));
-    float o = 0.f, L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float f = rescale(__builtin_nontemporal_load(&a.ws_ml[(ws0 + sp) * 2]), M);
-      o = fmaf(f, __builtin_nontemporal_load(&a.ws_o[(ws0 + sp) * D + d]), o);
-      L = fmaf(f, __builtin_nontemporal_load(&a.ws_ml[(ws0 + sp) * 2 + 1]), L);
-    }
-    const float val = o / L;
-    store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
-  }
 }
 
-constexpr int kKeysPerLane = 4;
+// Merge of the split-K states of every query row whose sequence needed more
+// than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
+// per row, one output element per lane.
+template <int DT, int D, int SPLIT>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  constexpr int RPW = 256 / D;  // rows per workgroup
+  const int d = threadIdx.x % D;
+  const long long t = (long long)blockIdx.x * RPW + threadIdx.x / D;  // (l, bb, hq, i)
+  const long long rows_here = (long long)a.n_layers * a.nb * a.Hq * a.N;
+  if (t >= rows_here) return;
+  const int i = (int)(t % a.N);
+  const int hq = (int)((t / a.N) % a.Hq);
+  const int bb = (int)((t / ((long long)a.N * a.Hq)) % a.nb);
+  const int l = (int)(t / ((long long)a.N * a.Hq * a.nb));
+  const int b = a.b0 + bb;
+  const int nsplit = (a.hist[bb] + a.N + SPLIT - 1) / SPLIT;
+  if (nsplit <= 1) return;  // written by the split kernel
+  const long long row = (((long long)l * a.B + b) * a.Hq + hq) * a.N + i;
+  const size_t ws0 = (size_t)row * a.max_splits;
+  float M = kNegInf;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, a.ws_ml[(ws0 + sp) * 2]);
+  float o = 0.f, L = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float f = rescale(a.ws_ml[(ws0 + sp) * 2], M);
+    o = fmaf(f, a.ws_o[(ws0 + sp) * D + d], o);
+    L = fmaf(f, a.ws_ml[(ws0 + sp) * 2 + 1], L);
+  }
+  const float val = o / L;
+  store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
+}
+
+constexpr int kKeysPerLane = 8;
 
 template <int DT, int D, int RT>
 hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.nb * a.Hkv), (unsigned)a.row_tiles);
   hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane>), grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits <= 1) return e;
+  constexpr int SPLIT = (256 / (D * Dtype<DT>::kBytes / 16)) * kKeysPerLane;
+  const long long rows = (long long)a.n_layers * a.nb * a.Hq * a.N;
+  const long long blocks = (rows + 256 / D - 1) / (256 / D);
+  hipLaunchKernelGGL((combine_kernel<DT, D, SPLIT>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -83,7 +83,6 @@ struct DecodeArgs {
   char *o;
   float *ws_o;       // [rows][max_splits][D] unnormalised partial outputs
   float *ws_ml;      // [rows][max_splits][2] partial (max, sum), log2 domain
-  int32_t *tickets;  // [n_layers][B][Hkv][row_tiles]
   int32_t B, Hkv, Hq, Tmax, N;
   int32_t layer0, n_layers;
   int32_t group;       // Hq / Hkv

@@ -166,11 +166,10 @@ def decode_workspace_bytes(cache: KVCache, n_layers: int, Hq: int, N: int) -> in
 
 
 def new_decode_workspace(cache: KVCache, n_layers: int, Hq: int, N: int) -> torch.Tensor:
-    """A zero-filled workspace for kvc_attn_decode with this geometry.  Every
-    decode call leaves its tickets at zero again, so it serves any number of
-    calls of the same (cache geometry, n_layers, Hq, N)."""
+    """A 256-byte aligned workspace for kvc_attn_decode with this geometry
+    (scratch: no initialisation needed)."""
     n = max(decode_workspace_bytes(cache, n_layers, Hq, N), 256)
-    ws = torch.zeros(n + 256, dtype=torch.uint8, device=cache.device)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=cache.device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]
 
@@ -179,13 +178,12 @@ _ws_cache: dict = {}
 
 
 def _default_workspace(cache, n_layers, Hq, N, stream):
-    """One workspace per (device, stream, geometry): a workspace must not
-    change geometry, since its ticket region would then overlap bytes that
-    held another geometry's partial states."""
-    key = (cache.device, int(_stream(cache.device, stream).value or 0), cache.L, cache.B,
-           cache.Hkv, cache.Tmax, cache.D, cache.dtype, n_layers, Hq, N)
+    """One growing scratch workspace per (device, stream): calls on one
+    stream run one after another, so they can share it."""
+    need = decode_workspace_bytes(cache, n_layers, Hq, N)
+    key = (cache.device, int(_stream(cache.device, stream).value or 0))
     ws = _ws_cache.get(key)
-    if ws is None:
+    if ws is None or ws.numel() < need:
         ws = new_decode_workspace(cache, n_layers, Hq, N)
         _ws_cache[key] = ws
     return ws
