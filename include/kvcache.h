@@ -150,6 +150,28 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0,
                            void *stream);
 
 /*
+ * One whole decode step in one call: kvc_append of k_new / v_new at
+ * positions [hist_len[b], hist_len[b] + N) followed by kvc_attn_decode with
+ * the same hist_len, with identical results (cache bytes bit for bit,
+ * outputs as kvc_attn_decode computes them).  The new rows are read once,
+ * straight from k_new / v_new, and written into their slots by the attention
+ * kernel itself, so the step needs no separate append launch.  This is the
+ * decode graph's "one token + cache in, output + updated cache out" ([KV-1]
+ * "Prefill/Decode 双图"; [KV-2] "一个很容易漏掉的错误": append on the sequence
+ * axis, then attend with the offset mask).
+ *   q, o         : device, [n_layers, B, Hq, N, D]
+ *   k_new, v_new : device, [n_layers, B, Hkv, N, D]
+ *   other arguments, errors and workspace rules as kvc_attn_decode; on
+ *   KVC_E_CAPACITY nothing is written.
+ */
+kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0,
+                           int32_t n_layers, const void *q, const void *k_new,
+                           const void *v_new, int32_t Hq, int32_t N,
+                           const int32_t *hist_len, float scale, void *o,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
  * attn_prefill: causal self-attention over an S-token prompt that starts an
  * empty cache.  Writes k[..][i] and v[..][i] to cache rows [0, S) of every
  * sequence (as kvc_append with hist_len = 0 and N = S would) and computes,

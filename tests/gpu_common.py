@@ -33,8 +33,9 @@ def bits(a: np.ndarray) -> np.ndarray:
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-def run_gpu(w: synth.Workload):
-    """Prefill (if any) then every decode step through libkvcache.so.
+def run_gpu(w: synth.Workload, fused: bool = False):
+    """Prefill (if any) then every decode step through libkvcache.so, as
+    kvc_append + kvc_attn_decode, or as one kvc_decode_step if `fused`.
     Returns (outputs as numpy in the workload dtype, final K, final V)."""
     from transformer_kv_cache_amd import kvcache as K
     kc, vc = to_dev(w.k_cache), to_dev(w.v_cache)
@@ -47,8 +48,11 @@ def run_gpu(w: synth.Workload):
         hist[:] = w.prefill[0].shape[3]
     for (q, k, v) in w.steps:
         qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-        K.append(cache, kd, vd, hist)
-        outs.append(K.attn_decode(cache, qd, hist, scale=w.scale))
+        if fused:
+            outs.append(K.decode_step(cache, qd, kd, vd, hist, scale=w.scale))
+        else:
+            K.append(cache, kd, vd, hist)
+            outs.append(K.attn_decode(cache, qd, hist, scale=w.scale))
         hist += q.shape[3]
     torch.cuda.synchronize()
     return [to_host(o) for o in outs], to_host(cache.k), to_host(cache.v)

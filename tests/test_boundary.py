@@ -38,8 +38,9 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"kvc_append", "kvc_attn_decode", "kvc_attn_prefill", "kvc_cache_bytes",
-            "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
+    assert {"kvc_append", "kvc_attn_decode", "kvc_decode_step", "kvc_attn_prefill",
+            "kvc_cache_bytes", "kvc_decode_workspace_bytes", "kvc_last_error",
+            "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.kvc_abi_version() == 1
@@ -157,6 +158,30 @@ def test_decode_error_paths(lib):
     assert call(q=h.ptr(offset=8)) == E_SHAPE
     assert call(layer0=1) == E_SHAPE
     assert call(c=None) == E_NULL
+
+
+def test_decode_step_error_paths(lib):
+    h = Host()
+    d = desc(h)
+    q, o, kn = h.ptr(), h.ptr(), h.ptr()
+    need = lib.kvc_decode_workspace_bytes(ctypes.byref(d), 2, 4, 3)
+    ws = h.ptr(need)
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=q, k=kn, v=kn, Hq=4, N=3,
+                 hist=hist(2, 5), scale=0.125, o=o, ws=ws, wsb=need, s=None)
+        a.update(kw)
+        return lib.kvc_decode_step(a["c"], a["layer0"], a["n_layers"], a["q"], a["k"], a["v"],
+                                   a["Hq"], a["N"], a["hist"], a["scale"], a["o"], a["ws"],
+                                   a["wsb"], a["s"])
+
+    assert call(k=None) == E_NULL
+    assert call(v=None) == E_NULL
+    assert call(k=h.ptr(offset=4)) == E_SHAPE
+    assert call(hist=hist(2, 14)) == E_CAPACITY
+    assert call(Hq=5) == E_SHAPE
+    assert call(wsb=need - 256) == E_WORKSPACE
+    assert call(N=0, q=None, k=None, v=None, o=None, ws=None) == OK
 
 
 def test_prefill_error_paths(lib):

@@ -25,10 +25,10 @@ def gpu():
     return K
 
 
-def check(w):
+def check(w, fused=False):
     print(f"[parity] {w.name} dtype={w.dtype} L={w.L} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
-          f"Tmax={w.Tmax} hist={w.hist.tolist()[:8]}", flush=True)
-    assert_matches(w, run_gpu(w), run_oracle(w))
+          f"Tmax={w.Tmax} hist={w.hist.tolist()[:8]} fused={fused}", flush=True)
+    assert_matches(w, run_gpu(w, fused), run_oracle(w))
 
 
 # ---------------------------------------------------------------- workloads
@@ -122,6 +122,50 @@ def test_layer_subset():
     assert np.max(np.abs(out - ref)) <= TOL["f32"]
     assert np.array_equal(bits(to_host(cache.k)), bits(kc))
     assert np.array_equal(bits(to_host(cache.v)), bits(vc))
+
+
+# ------------------------------------------ fused step (append inside decode)
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fused_single_layer_generation(seed):
+    check(synth.single_layer_generation(seed), fused=True)
+
+
+@pytest.mark.parametrize("P", [0, 127, 128, 1000, 1023])
+def test_fused_decode_12layer(P):
+    check(synth.decode_12layer(P, seed=P + 7), fused=True)
+
+
+def test_fused_chunked_decode():
+    check(synth.chunked_decode(1000, 8, seed=3), fused=True)
+
+
+@pytest.mark.parametrize("gqa", [False, True])
+def test_fused_batched_decode(gqa):
+    check(synth.batched_decode(seed=6, gqa=gqa), fused=True)
+
+
+@pytest.mark.parametrize("N", [1, 3, 8, 9, 17])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_rows_and_groups(N, G, dtype):
+    """New rows that straddle a split boundary, several row tiles (only tile 0
+    writes the new rows), empty and full histories."""
+    Tmax = 300
+    hist = [0, 128 - N // 2, Tmax - N, 255]
+    check(synth.make_workload(f"fused_N{N}_G{G}", seed=N * 10 + G + 1, dtype=dtype, L=2, B=4,
+                              Hq=2 * G, Hkv=2, D=64, Tmax=Tmax, hist=hist, step_lens=(N,)),
+          fused=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_d128_and_wide_batch(dtype):
+    check(synth.make_workload("fused_d128", seed=12, dtype=dtype, L=2, B=3, Hq=8, Hkv=2, D=128,
+                              Tmax=520, hist=[518, 0, 260], step_lens=(2,)), fused=True)
+    rng = np.random.default_rng(4)
+    check(synth.make_workload("fused_B70", seed=4, dtype=dtype, L=1, B=70, Hq=2, Hkv=1, D=64,
+                              Tmax=96, hist=rng.integers(0, 90, size=70), step_lens=(3, 1)),
+          fused=True)
 
 
 # ------------------------------------------------------------- invariants

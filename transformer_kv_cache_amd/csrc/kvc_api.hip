@@ -153,10 +153,15 @@ size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers, int3
   return decode_geometry(cache, n_layers, Hq, N).total;
 }
 
-kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
-                           int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
-                           void *workspace, size_t workspace_bytes, void *stream) {
-  static const char *fn = "kvc_attn_decode";
+}  // extern "C"
+
+namespace {
+
+// Shared by kvc_attn_decode and kvc_decode_step (k_new / v_new non-NULL).
+kvc_status decode_impl(const char *fn, const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                       const void *q, const void *k_new, const void *v_new, bool fused,
+                       int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
+                       void *workspace, size_t workspace_bytes, void *stream) {
   kvc_status st = check_cache(cache, layer0, n_layers, fn);
   if (st != KVC_OK) return st;
   if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
@@ -168,6 +173,11 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_lay
   if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
   if (!q || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
   if (!aligned16(q) || !aligned16(o)) return fail(KVC_E_SHAPE, "%s: q / o must be 16-byte aligned", fn);
+  if (fused) {
+    if (!k_new || !v_new) return fail(KVC_E_NULL, "%s: k_new or v_new is NULL", fn);
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(KVC_E_SHAPE, "%s: k_new / v_new must be 16-byte aligned", fn);
+  }
   const DecodeGeometry g = decode_geometry(cache, n_layers, Hq, N);
   if (!workspace) return fail(KVC_E_WORKSPACE, "%s: workspace is NULL", fn);
   if (((uintptr_t)workspace & 255u) != 0)
@@ -176,8 +186,10 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_lay
     return fail(KVC_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, g.total);
 
   kvc::DecodeArgs a{};
-  a.k_cache = (const char *)cache->k;
-  a.v_cache = (const char *)cache->v;
+  a.k_cache = (char *)cache->k;
+  a.v_cache = (char *)cache->v;
+  a.k_new = (const char *)k_new;
+  a.v_new = (const char *)v_new;
   a.q = (const char *)q;
   a.o = (char *)o;
   a.ws_o = (float *)workspace;
@@ -203,10 +215,30 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_lay
       if (hist_len[b0 + i] + N > max_keys) max_keys = hist_len[b0 + i] + N;
     }
     const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
-    hipError_t e = kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, (hipStream_t)stream);
+    hipError_t e = kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, fused,
+                                      (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
+                           int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl("kvc_attn_decode", cache, layer0, n_layers, q, nullptr, nullptr, false, Hq, N,
+                     hist_len, scale, o, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
+                           const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+                           const int32_t *hist_len, float scale, void *o, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return decode_impl("kvc_decode_step", cache, layer0, n_layers, q, k_new, v_new, true, Hq, N,
+                     hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
 kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,

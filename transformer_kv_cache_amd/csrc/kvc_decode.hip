@@ -25,14 +25,19 @@
 //     over its keys; the states are merged across the wave with cross-lane
 //     exchanges and across the 4 waves through LDS, rescaling by exp2 of
 //     the max difference (log2(e) is folded into the scale).
+// Fused step.  kvc_decode_step also performs the append: keys at positions
+// [P, P+N) are read straight from the new K/V rows instead of the cache, and
+// the workgroups of row tile 0 that hold them write them to their cache slots.
+// No workgroup reads those slots during the call, so the write is race-free,
+// and the step needs no separate append launch.
 // Combine.  With more than one split, each workgroup writes its (max, sum,
 // P.V) state to the workspace and a second, small kernel merges the splits of
 // every query row (rescaling by exp2 of the max difference) and writes the
 // output; with a single split the workgroup writes the output itself.  The
-// merge is a separate launch rather than a last-workgroup ticket because a
-// device-scope release/acquire on gfx950 writes back and invalidates the
-// whole L2 of the workgroup's XCD, which costs far more than one extra
-// launch.
+// merge is a separate launch rather than a last-workgroup ticket: the ticket
+// needs a device-scope release fence in every workgroup, which on gfx950 is an
+// L2 write-back (buffer_wbl2), and that measured about ten times slower than
+// the extra launch.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -68,12 +73,25 @@ __device__ __forceinline__ float row_allreduce(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// K/V rows are read exactly once per call: non-temporal loads keep them from
+// displacing reusable lines in the caches.
+#ifndef KVC_DECODE_NONTEMPORAL
+#define KVC_DECODE_NONTEMPORAL 1
+#endif
+__device__ __forceinline__ u32x4 stream_load(const u32x4 *p) {
+#if KVC_DECODE_NONTEMPORAL
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 // Weight of a softmax state with max m when merged under a common max M.
 __device__ __forceinline__ float rescale(float m, float M) {
   return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
-template <int DT, int D, int RT, int KPL>
+template <int DT, int D, int RT, int KPL, bool FUSED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
   constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
@@ -103,6 +121,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
   const u32x4 *kc = reinterpret_cast<const u32x4 *>(a.k_cache) + crow0 * LPR + c;
   const u32x4 *vc = reinterpret_cast<const u32x4 *>(a.v_cache) + crow0 * LPR + c;
+  const size_t nrow0 = (((size_t)l * a.B + b) * a.Hkv + hkv) * (size_t)a.N * LPR + c;
+  const u32x4 *kn = FUSED ? reinterpret_cast<const u32x4 *>(a.k_new) + nrow0 : nullptr;
+  const u32x4 *vn = FUSED ? reinterpret_cast<const u32x4 *>(a.v_new) + nrow0 : nullptr;
 
   // 1. Issue the query loads and every K and V load of this split up front.
   //    Key indices past the sequence are clamped to its last row (always
@@ -120,8 +141,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   for (int kk = 0; kk < KPL; ++kk) {
     const int key = key0 + kk * NRG + rg;
     const int kidx = key < nkeys ? key : nkeys - 1;
-    kw[kk] = __builtin_nontemporal_load(kc + (size_t)kidx * LPR);
-    vw[kk] = __builtin_nontemporal_load(vc + (size_t)kidx * LPR);
+    const bool fresh = FUSED && kidx >= P;  // a new row: read it from k_new / v_new
+    const size_t nidx = (size_t)(fresh ? kidx - P : 0);
+    kw[kk] = stream_load(fresh ? kn + nidx * LPR : kc + (size_t)kidx * LPR);
+    vw[kk] = stream_load(fresh ? vn + nidx * LPR : vc + (size_t)kidx * LPR);
   }
   // Keep the scheduler from interleaving arithmetic (and its waits) into the
   // load burst: all loads of the split are in flight before the first wait.
@@ -195,6 +218,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     m[r] = M;
   }
 
+  // Fused step: row tile 0 writes the new rows it holds into their slots.
+  if constexpr (FUSED) {
+    if (rt == 0) {
+      u32x4 *kd = reinterpret_cast<u32x4 *>(a.k_cache) + crow0 * LPR + c;
+      u32x4 *vd = reinterpret_cast<u32x4 *>(a.v_cache) + crow0 * LPR + c;
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int key = key0 + kk * NRG + rg;
+        if (key >= P && key < nkeys) {
+          kd[(size_t)key * LPR] = kw[kk];
+          vd[(size_t)key * LPR] = vw[kk];
+        }
+      }
+    }
+  }
+
   // 6. Merge the four waves through LDS.
   __shared__ float sh_o[4][RT][D];
   __shared__ float sh_m[4][RT];
@@ -243,6 +282,50 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 // Merge of the split-K states of every query row whose sequence needed more
 // than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
+// per row, one output element per lane.  Splits are read in chunks of 8 with
+// every load of a chunk issued before any is used (indices clamped, extra
+// splits masked), merged online across chunks.
+// Merge of one query row's split states, element d of the output row.
+// Splits are read in chunks of 16 with every load of a chunk issued before any
+// is used (indices clamped, extra splits masked), merged online across chunks.
+template <int DT, int D>
+__device__ __forceinline__ void combine_row(const DecodeArgs &a, long long row, int nsplit, int d) {
+  constexpr int CH = 16;
+  const size_t ws0 = (size_t)row * a.max_splits;
+  float M = kNegInf, o = 0.f, L = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += CH) {
+    float mv[CH], lv[CH], ov[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int sp = (s0 + j < nsplit) ? s0 + j : nsplit - 1;
+      mv[j] = a.ws_ml[(ws0 + sp) * 2];
+      lv[j] = a.ws_ml[(ws0 + sp) * 2 + 1];
+      ov[j] = a.ws_o[(ws0 + sp) * D + d];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float Mc = M;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (s0 + j >= nsplit) mv[j] = kNegInf;
+      Mc = fmaxf(Mc, mv[j]);
+    }
+    const float fr = rescale(M, Mc);
+    o *= fr;
+    L *= fr;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float f = rescale(mv[j], Mc);
+      o = fmaf(f, ov[j], o);
+      L = fmaf(f, lv[j], L);
+    }
+    M = Mc;
+  }
+  const float val = o / L;
+  store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
+}
+
+// Merge of the split-K states of every query row whose sequence needed more
+// than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
 // per row, one output element per lane.
 template <int DT, int D, int SPLIT>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
@@ -258,26 +341,24 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = a.b0 + bb;
   const int nsplit = (a.hist[bb] + a.N + SPLIT - 1) / SPLIT;
   if (nsplit <= 1) return;  // written by the split kernel
-  const long long row = (((long long)l * a.B + b) * a.Hq + hq) * a.N + i;
-  const size_t ws0 = (size_t)row * a.max_splits;
-  float M = kNegInf;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, a.ws_ml[(ws0 + sp) * 2]);
-  float o = 0.f, L = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float f = rescale(a.ws_ml[(ws0 + sp) * 2], M);
-    o = fmaf(f, a.ws_o[(ws0 + sp) * D + d], o);
-    L = fmaf(f, a.ws_ml[(ws0 + sp) * 2 + 1], L);
-  }
-  const float val = o / L;
-  store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
+  combine_row<DT, D>(a, (((long long)l * a.B + b) * a.Hq + hq) * a.N + i, nsplit, d);
 }
 
-constexpr int kKeysPerLane = 8;
+// Keys each lane group loads per split: a split covers 256 / LPR * this many
+// keys (64 for fp32 D=64).  Build-time tuning constant; 4 measured best
+// across the fp32, bf16 and GQA decode workloads.
+#ifndef KVC_DECODE_KEYS_PER_LANE
+#define KVC_DECODE_KEYS_PER_LANE 4
+#endif
+constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
 
 template <int DT, int D, int RT>
-hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
+hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.nb * a.Hkv), (unsigned)a.row_tiles);
-  hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane>), grid, dim3(256), 0, s, a);
+  if (fused)
+    hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
   constexpr int SPLIT = (256 / (D * Dtype<DT>::kBytes / 16)) * kKeysPerLane;
@@ -288,12 +369,12 @@ hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
 }
 
 template <int DT, int D>
-hipError_t launch_rt(const DecodeArgs &a, int rt, int splits, hipStream_t s) {
+hipError_t launch_rt(const DecodeArgs &a, int rt, int splits, bool fused, hipStream_t s) {
   switch (rt) {
-    case 1: return launch_one<DT, D, 1>(a, splits, s);
-    case 2: return launch_one<DT, D, 2>(a, splits, s);
-    case 4: return launch_one<DT, D, 4>(a, splits, s);
-    default: return launch_one<DT, D, 8>(a, splits, s);
+    case 1: return launch_one<DT, D, 1>(a, splits, fused, s);
+    case 2: return launch_one<DT, D, 2>(a, splits, fused, s);
+    case 4: return launch_one<DT, D, 4>(a, splits, fused, s);
+    default: return launch_one<DT, D, 8>(a, splits, fused, s);
   }
 }
 
@@ -312,13 +393,13 @@ int decode_split_keys(int dtype, int D) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile, int splits,
-                         hipStream_t s) {
+                         bool fused_append, hipStream_t s) {
   if (dtype == KVC_F32) {
-    if (D == 64) return launch_rt<KVC_F32, 64>(a, row_tile, splits, s);
-    return launch_rt<KVC_F32, 128>(a, row_tile, splits, s);
+    if (D == 64) return launch_rt<KVC_F32, 64>(a, row_tile, splits, fused_append, s);
+    return launch_rt<KVC_F32, 128>(a, row_tile, splits, fused_append, s);
   }
-  if (D == 64) return launch_rt<KVC_BF16, 64>(a, row_tile, splits, s);
-  return launch_rt<KVC_BF16, 128>(a, row_tile, splits, s);
+  if (D == 64) return launch_rt<KVC_BF16, 64>(a, row_tile, splits, fused_append, s);
+  return launch_rt<KVC_BF16, 128>(a, row_tile, splits, fused_append, s);
 }
 
 }  // namespace kvc

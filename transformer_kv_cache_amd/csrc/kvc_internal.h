@@ -78,7 +78,8 @@ struct AppendArgs {
 };
 
 struct DecodeArgs {
-  const char *k_cache, *v_cache;
+  char *k_cache, *v_cache;    // written only by the fused step (new rows)
+  const char *k_new, *v_new;  // fused step: the N new rows, [n_layers,B,Hkv,N,D]
   const char *q;
   char *o;
   float *ws_o;       // [rows][max_splits][D] unnormalised partial outputs
@@ -109,7 +110,7 @@ struct PrefillArgs {
 // arguments and return the launch status.
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile,
-                         int splits, hipStream_t s);
+                         int splits, bool fused_append, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s);
 
 // Geometry shared by kvc_decode_workspace_bytes and the decode launcher.

@@ -76,6 +76,9 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_workspace_bytes.restype = sz
         lib.kvc_attn_decode.argtypes = [cp, i32, i32, vp, i32, i32, ip, ctypes.c_float, vp, vp, sz, vp]
         lib.kvc_attn_decode.restype = i32
+        lib.kvc_decode_step.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ip, ctypes.c_float, vp,
+                                        vp, sz, vp]
+        lib.kvc_decode_step.restype = i32
         lib.kvc_attn_prefill.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
         lib.kvc_attn_prefill.restype = i32
         if path is None:
@@ -212,6 +215,35 @@ def attn_decode(cache: KVCache, q, hist_len, scale: float | None = None, out=Non
         ctypes.byref(d), layer0, n_layers, q.data_ptr(), Hq, N, hp, float(scale), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream(cache.device, stream)))
+    return out
+
+
+def decode_step(cache: KVCache, q, k_new, v_new, hist_len, scale: float | None = None,
+                out=None, layer0: int = 0, workspace=None, stream=None):
+    """append + attn_decode in one launch: writes k_new/v_new into rows
+    [hist_len[b], hist_len[b]+N) and returns the attention of q over keys
+    0 .. hist_len[b]+i.  Same results as the two separate calls."""
+    n_layers, _, Hq, N, _ = q.shape
+    shape = (n_layers, cache.B, Hq, N, cache.D)
+    _check_tensor("q", q, cache, shape)
+    kshape = (n_layers, cache.B, cache.Hkv, N, cache.D)
+    _check_tensor("k_new", k_new, cache, kshape)
+    _check_tensor("v_new", v_new, cache, kshape)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, cache.B)
+    if workspace is None:
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream)
+    if workspace.device != cache.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the cache's device")
+    d = cache.desc()
+    _check(library().kvc_decode_step(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), Hq, N,
+        hp, float(scale), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(cache.device, stream)))
     return out
 
 
