@@ -105,14 +105,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int rg = tid / LPR;
   const int c = tid % LPR;
 
+  // Grid: x = split, y = (layer, KV head, row tile), z = sequence in the
+  // batch slice.  The sequence comes straight from blockIdx.z so its length
+  // can be fetched while the other indices are still being computed.
   const int split = blockIdx.x;
-  const int unit = blockIdx.y;
-  const int rt = blockIdx.z;
-  const int hkv = unit % a.Hkv;
-  const int bb = (unit / a.Hkv) % a.nb;
-  const int l = unit / (a.Hkv * a.nb);
-  const int b = a.b0 + bb;
+  const int bb = blockIdx.z;
   const int P = a.hist[bb];
+  const int rt = blockIdx.y % a.row_tiles;
+  const int lh = blockIdx.y / a.row_tiles;
+  const int hkv = lh % a.Hkv;
+  const int l = lh / a.Hkv;
+  const int b = a.b0 + bb;
   const int nkeys = P + a.N;
   const int nsplit = (nkeys + SPLIT - 1) / SPLIT;
   if (split >= nsplit) return;
@@ -354,7 +357,7 @@ constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
 
 template <int DT, int D, int RT>
 hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
-  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.nb * a.Hkv), (unsigned)a.row_tiles);
+  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv * a.row_tiles), (unsigned)a.nb);
   if (fused)
     hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
   else
