@@ -53,8 +53,13 @@ __device__ __forceinline__ int perm16(int k) {
   return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (low half = lo), round to nearest even, in
+// one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 template <int DT, int D> struct Smem;
@@ -131,39 +136,59 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int kv_end = (q0 + BM < S) ? q0 + BM : S;  // keys this tile needs
   const int n_kt = (kv_end + BN - 1) / BN;
 
+  // Tile staging.  Each thread moves VPT 16-byte vectors of K and of V per
+  // tile, as pairs of adjacent keys (rows 2p and 2p+1) at the same column c,
+  // so that the bf16 V^T store can write both keys of a column as one dword.
+  // Tile kt+1 is loaded into registers while tile kt is computed.  Key
+  // indices past the prompt are clamped to its last row (always valid): their
+  // scores are masked, so no load needs a branch.
+  auto tile_row = [&](int it) { return 2 * (tid / LPR + (it >> 1) * (256 / LPR)) + (it & 1); };
+  const int c = tid % LPR;
+  u32x4 kreg[VPT], vreg[VPT];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < VPT; ++it) {
+      const int key = kt * BN + tile_row(it);
+      const size_t off = ((size_t)(key < S ? key : S - 1) * D + c * EV) * EB;
+      kreg[it] = *reinterpret_cast<const u32x4 *>(kbase + off);
+      vreg[it] = *reinterpret_cast<const u32x4 *>(vbase + off);
+    }
+  };
+  load_tile(0);
+
   for (int kt = 0; kt < n_kt; ++kt) {
     const int key0 = kt * BN;
     const bool store_cache = writer && key0 >= q0;  // this tile's rows are ours to write
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int it = 0; it < VPT; ++it) {
-      const int vec = tid + 256 * it;
-      const int row = vec / LPR;
-      const int c = vec % LPR;
+      const int row = tile_row(it);
       const int key = key0 + row;
-      u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
-      if (key < S) {
-        kw = *reinterpret_cast<const u32x4 *>(kbase + ((size_t)key * D + c * EV) * EB);
-        vw = *reinterpret_cast<const u32x4 *>(vbase + ((size_t)key * D + c * EV) * EB);
-        if (store_cache) {
-          *reinterpret_cast<u32x4 *>(kcache + ((size_t)key * D + c * EV) * EB) = kw;
-          *reinterpret_cast<u32x4 *>(vcache + ((size_t)key * D + c * EV) * EB) = vw;
-        }
+      if (store_cache && key < S) {
+        const size_t off = ((size_t)key * D + c * EV) * EB;
+        *reinterpret_cast<u32x4 *>(kcache + off) = kreg[it];
+        *reinterpret_cast<u32x4 *>(vcache + off) = vreg[it];
       }
+      *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kreg[it];
       if constexpr (DT == KVC_BF16) {
-        *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kw;
-        const int pos = (row & ~15) | perm16(row & 15);
+        if (it & 1) {
+          // rows row-1 (even) and row: perm16 keeps bits 0-1, so they stay adjacent
+          const int pos = ((row - 1) & ~15) | perm16((row - 1) & 15);
+          const u32x4 lo = vreg[it - 1], hi = vreg[it];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sm.vt[(c * EV + 2 * j) * Smem<DT, D>::kVtStride + pos] = (uint16_t)(vw[j] & 0xFFFFu);
-          sm.vt[(c * EV + 2 * j + 1) * Smem<DT, D>::kVtStride + pos] = (uint16_t)(vw[j] >> 16);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t e0 = (lo[j] & 0xFFFFu) | (hi[j] << 16);          // element 2j
+            const uint32_t e1 = (lo[j] >> 16) | (hi[j] & 0xFFFF0000u);      // element 2j+1
+            *reinterpret_cast<uint32_t *>(&sm.vt[(c * EV + 2 * j) * Smem<DT, D>::kVtStride + pos]) = e0;
+            *reinterpret_cast<uint32_t *>(&sm.vt[(c * EV + 2 * j + 1) * Smem<DT, D>::kVtStride + pos]) = e1;
+          }
         }
       } else {
-        *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kw;
-        *reinterpret_cast<u32x4 *>(&sm.v[row * Smem<DT, D>::kVStride + c * EV]) = vw;
+        *reinterpret_cast<u32x4 *>(&sm.v[row * Smem<DT, D>::kVStride + c * EV]) = vreg[it];
       }
     }
     __syncthreads();
+    if (kt + 1 < n_kt) load_tile(kt + 1);
     if (key0 > wave_last) continue;  // whole tile above this wave's rows
 
     // S^T blocks: acc_s[kb][i] = score of key key0 + 32 kb + 8 (i/4) + 4 h + i%4
@@ -194,25 +219,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // Scale, causal mask, online softmax for this lane's query.
+    // Scale, causal mask, online softmax for this lane's query.  Key
+    // key0 + 32 kb + 8 (i/4) + 4 h + i%4 is visible iff it is <= qrow and < S,
+    // i.e. iff the compile-time offset 32 kb + 8 (i/4) + i%4 is <= lim.
     const bool need_mask = (key0 + BN - 1 > q0 + wave * 32) || (key0 + BN > S);
+    const int lim = (qrow < S - 1 ? qrow : S - 1) - key0 - 4 * h;
     float mt = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float s = acc_s[kb][i] * a.scale_log2;
-        if (need_mask) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= S) s = kNegInf;
-        }
+        if (need_mask && 32 * kb + 8 * (i >> 2) + (i & 3) > lim) s = kNegInf;
         acc_s[kb][i] = s;
         mt = fmaxf(mt, s);
       }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
+    // Lazy rescale: the running max only moves when this tile raises it by
+    // more than 8 (log2 domain), so probabilities stay <= 2^8 and the output
+    // rescale is skipped whenever no lane of the wave needs it.  Subtracting
+    // any constant leaves the softmax unchanged.
+    const bool grow = mt > m_run + 8.f;  // also true on the first tile
+    const float m_new = grow ? mt : m_run;
+    if (__any(grow)) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+    }
+    m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -223,10 +259,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         psum += p;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+    l_run += psum;
 
     // O^T += V^T . P^T
 #pragma unroll
