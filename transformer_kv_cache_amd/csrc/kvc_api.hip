@@ -74,6 +74,7 @@ kvc_status hip_status(hipError_t e, const char *fn) {
 }
 
 struct DecodeGeometry {
+  bool mfma;  // several query rows per KV head: matrix-core kernel
   int rows, row_tile, row_tiles, split_keys, max_splits;
   size_t ws_o_bytes, ws_ml_bytes, total;
 };
@@ -84,9 +85,11 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
   DecodeGeometry g{};
   const int G = Hq / c->Hkv;
   g.rows = G * N;
-  g.row_tile = kvc::decode_row_tile(g.rows);
+  g.mfma = g.rows > 1;
+  g.row_tile = g.mfma ? kvc::kMfmaRowTile : kvc::decode_row_tile(g.rows);
   g.row_tiles = (g.rows + g.row_tile - 1) / g.row_tile;
-  g.split_keys = kvc::decode_split_keys(c->dtype, c->D);
+  g.split_keys = g.mfma ? kvc::decode_mfma_split_keys(c->dtype, c->D)
+                        : kvc::decode_split_keys(c->dtype, c->D);
   g.max_splits = (c->Tmax + g.split_keys - 1) / g.split_keys;
   if (g.max_splits < 1) g.max_splits = 1;
   const size_t qrows = (size_t)n_layers * c->B * Hq * N;
@@ -205,6 +208,7 @@ kvc_status decode_impl(const char *fn, const kvc_cache *cache, int32_t layer0, i
   a.rows = g.rows;
   a.row_tiles = g.row_tiles;
   a.max_splits = g.max_splits;
+  a.split_keys = g.split_keys;
   a.scale_log2 = scale * 1.4426950408889634f;
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
@@ -215,8 +219,12 @@ kvc_status decode_impl(const char *fn, const kvc_cache *cache, int32_t layer0, i
       if (hist_len[b0 + i] + N > max_keys) max_keys = hist_len[b0 + i] + N;
     }
     const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
-    hipError_t e = kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, fused,
-                                      (hipStream_t)stream);
+    hipError_t e = g.mfma ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused,
+                                                     (hipStream_t)stream)
+                          : kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, fused,
+                                               (hipStream_t)stream);
+    if (e == hipSuccess && splits > 1)
+      e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();

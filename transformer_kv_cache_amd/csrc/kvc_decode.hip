@@ -330,7 +330,7 @@ __device__ __forceinline__ void combine_row(const DecodeArgs &a, long long row, 
 // Merge of the split-K states of every query row whose sequence needed more
 // than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
 // per row, one output element per lane.
-template <int DT, int D, int SPLIT>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int RPW = 256 / D;  // rows per workgroup
   const int d = threadIdx.x % D;
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int bb = (int)((t / ((long long)a.N * a.Hq)) % a.nb);
   const int l = (int)(t / ((long long)a.N * a.Hq * a.nb));
   const int b = a.b0 + bb;
-  const int nsplit = (a.hist[bb] + a.N + SPLIT - 1) / SPLIT;
+  const int nsplit = (a.hist[bb] + a.N + a.split_keys - 1) / a.split_keys;
   if (nsplit <= 1) return;  // written by the split kernel
   combine_row<DT, D>(a, (((long long)l * a.B + b) * a.Hq + hq) * a.N + i, nsplit, d);
 }
@@ -362,12 +362,6 @@ hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s
     hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits <= 1) return e;
-  constexpr int SPLIT = (256 / (D * Dtype<DT>::kBytes / 16)) * kKeysPerLane;
-  const long long rows = (long long)a.n_layers * a.nb * a.Hq * a.N;
-  const long long blocks = (rows + 256 / D - 1) / (256 / D);
-  hipLaunchKernelGGL((combine_kernel<DT, D, SPLIT>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -393,6 +387,20 @@ int decode_row_tile(int rows) {
 int decode_split_keys(int dtype, int D) {
   const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;
   return (256 / lpr) * kKeysPerLane;
+}
+
+hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) {
+  const long long rows = (long long)a.n_layers * a.nb * a.Hq * a.N;
+  const long long blocks = (rows + 256 / D - 1) / (256 / D);
+  const dim3 grid((unsigned)blocks);
+  if (dtype == KVC_F32) {
+    if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_F32, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<KVC_F32, 128>), grid, dim3(256), 0, s, a);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_BF16, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<KVC_BF16, 128>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile, int splits,

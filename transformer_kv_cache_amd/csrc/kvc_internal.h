@@ -90,6 +90,7 @@ struct DecodeArgs {
   int32_t rows;        // G * N query rows per (layer, sequence, KV head)
   int32_t row_tiles;   // ceil(rows / row tile)
   int32_t max_splits;  // workspace stride in splits
+  int32_t split_keys;  // keys per split of the launched kernel
   int32_t b0, nb;
   float scale_log2;    // scale * log2(e)
   int32_t hist[kMaxBatchPerLaunch];
@@ -111,10 +112,17 @@ struct PrefillArgs {
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile,
                          int splits, bool fused_append, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
+                              bool fused_append, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s);
 
-// Geometry shared by kvc_decode_workspace_bytes and the decode launcher.
+// Geometry shared by kvc_decode_workspace_bytes and the decode launchers.
+// One query row per KV head runs on the vector kernel; more rows (GQA groups,
+// chunked decode) run on the matrix-core kernel in tiles of 16 rows.
 int decode_row_tile(int rows);
 int decode_split_keys(int dtype, int D);
+int decode_mfma_split_keys(int dtype, int D);
+constexpr int kMfmaRowTile = 16;
 
 }  // namespace kvc
