@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix-core peaks
 METRIC = "decode attention µs/step + achieved HBM GB/s at T=1024; prefill TFLOP/s"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")  # split kernel
 DECODE_SOURCES = [os.path.join(ROOT, "transformer_kv_cache_amd", "csrc", f)
                   for f in ("kvc_decode.hip", "kvc_internal.h")]
 
@@ -49,18 +49,29 @@ def elem_bytes(dtype):
     return 4 if dtype == "f32" else 2
 
 
+def kv_read_bytes(w, N):
+    """Every visible K and V row read once."""
+    return 2 * w.L * w.Hkv * w.D * elem_bytes(w.dtype) * int(np.sum(w.hist + N))
+
+
+def q_bytes(w, N):
+    """One of q (read) or o (written)."""
+    return w.L * w.B * w.Hq * N * w.D * elem_bytes(w.dtype)
+
+
+def new_rows_bytes(w, N):
+    """The N new K and V rows, once."""
+    return 2 * w.L * w.B * w.Hkv * N * w.D * elem_bytes(w.dtype)
+
+
 def decode_bytes(w, N):
-    """Algorithmic bytes of one decode call: every visible K and V row once,
-    q read and o written once."""
-    e = elem_bytes(w.dtype)
-    kv = 2 * w.L * w.Hkv * w.D * e * int(np.sum(w.hist + N))
-    qo = 2 * w.L * w.B * w.Hq * N * w.D * e
-    return kv + qo
+    """Algorithmic bytes of one attn_decode call: K/V once, q and o once."""
+    return kv_read_bytes(w, N) + 2 * q_bytes(w, N)
 
 
 def append_bytes(w, N):
     """Algorithmic bytes of one append: new K/V rows read once, written once."""
-    return 2 * 2 * w.L * w.B * w.Hkv * N * w.D * elem_bytes(w.dtype)
+    return 2 * new_rows_bytes(w, N)
 
 
 def decode_source_hash():
@@ -166,6 +177,13 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     def decode_only(r):
         K.attn_decode(caches[r], qs[r], hist, scale=w.scale, out=outs[r], workspace=wss[r])
 
+    def split_only(r):
+        K.decode_split(caches[r], qs[r], hist, kns[r], vns[r], scale=w.scale, out=outs[r],
+                       workspace=wss[r])
+
+    def combine_only(r):
+        K.decode_combine(caches[r], outs[r], hist, w.L, w.Hq, N, workspace=wss[r])
+
     def append_only(r):
         K.append(caches[r], kns[r], vns[r], hist)
 
@@ -174,11 +192,17 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     torch.cuda.synchronize()
     res = {}
     res["step_us"] = GraphTimer(torch, step, rotate).time(steps)
+    res["split_us"] = GraphTimer(torch, split_only, rotate).time(steps)
+    res["combine_us"] = GraphTimer(torch, combine_only, rotate).time(steps)
     res["two_call_step_us"] = GraphTimer(torch, step_two_calls, rotate).time(steps)
     res["attn_decode_us"] = GraphTimer(torch, decode_only, rotate).time(steps)
     res["append_us"] = GraphTimer(torch, append_only, rotate).time(steps)
     # the fused step reads the new rows from k_new/v_new and writes them once
-    res["step_bytes"] = decode_bytes(w, N) + append_bytes(w, N) // 2
+    res["step_bytes"] = decode_bytes(w, N) + new_rows_bytes(w, N)
+    # split kernel alone: K/V (history from the cache, new rows from k_new/v_new)
+    # and q read, new rows written; outputs of multi-split rows come later
+    res["split_bytes"] = kv_read_bytes(w, N) + q_bytes(w, N) + new_rows_bytes(w, N)
+    res["split_gbs"] = res["split_bytes"] / res["split_us"] / 1e3
     res["step_gbs"] = res["step_bytes"] / res["step_us"] / 1e3
     res["attn_decode_bytes"] = decode_bytes(w, N)
     res["attn_decode_gbs"] = res["attn_decode_bytes"] / res["attn_decode_us"] / 1e3
@@ -366,12 +390,15 @@ def main():
                    "rotating_cache_replicas": args.rotate},
         "decode_us_per_step": round(step_us, 3),
         "step_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(step_bytes / step_us / 1e3, 1),
+        "roofline": {"bound": "hbm", "achieved": round(head["split_gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4),
+                     "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode step: decode_kernel<f32,D64,RT1,fused> + combine_kernel",
-                     "launch_us": round(step_us, 3), "algorithmic_bytes": step_bytes},
+                     "kernel": "decode_kernel<f32,D64,RT1,fused> (split-K pass, kvc_decode_split)",
+                     "launch_us": round(head["split_us"], 3),
+                     "algorithmic_bytes": head["split_bytes"],
+                     "combine_kernel_us": round(head["combine_us"], 3),
+                     "step_frac": round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": {"value": round(step_bytes / cpu["us_per_step"] / 1e3, 3), "unit": "GB/s",
                          "cores": cpu["threads"], "kind": "oracle",
                          "sample": f"{cpu['steps']} full decode steps (append + attention, all 12 "

@@ -172,6 +172,37 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0,
                            void *stream);
 
 /*
+ * The two phases of kvc_attn_decode / kvc_decode_step as separate calls, for
+ * callers that want to place other work between them (or time them apart).
+ *
+ * kvc_decode_split runs the split-K pass: with k_new and v_new both NULL it
+ * is the first phase of kvc_attn_decode (rows [P, P+N) already appended);
+ * with both given it is the first phase of kvc_decode_step and also writes
+ * the new rows into their slots.  Query rows of sequences whose P + N keys
+ * fit one split get their output in `o` at once; the others get their
+ * per-split softmax states (max, sum, unnormalised output) in `workspace`.
+ * kvc_decode_combine then merges those states and writes the remaining
+ * outputs: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
+ * M = max_s m_s (the rescaling that makes split softmax states additive;
+ * the result is the same softmax-weighted sum [KV-4] "Decode 阶段" defines).
+ * Call it on the same stream with the same cache, layer range, Hq, N,
+ * hist_len, o and workspace, before anything else uses the workspace.
+ * Arguments, errors and workspace rules as kvc_attn_decode / kvc_decode_step;
+ * passing only one of k_new / v_new is KVC_E_NULL.
+ */
+kvc_status kvc_decode_split(const kvc_cache *cache, int32_t layer0,
+                            int32_t n_layers, const void *q, const void *k_new,
+                            const void *v_new, int32_t Hq, int32_t N,
+                            const int32_t *hist_len, float scale, void *o,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+kvc_status kvc_decode_combine(const kvc_cache *cache, int32_t layer0,
+                              int32_t n_layers, int32_t Hq, int32_t N,
+                              const int32_t *hist_len, void *o,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * attn_prefill: causal self-attention over an S-token prompt that starts an
  * empty cache.  Writes k[..][i] and v[..][i] to cache rows [0, S) of every
  * sequence (as kvc_append with hist_len = 0 and N = S would) and computes,

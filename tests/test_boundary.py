@@ -38,9 +38,9 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"kvc_append", "kvc_attn_decode", "kvc_decode_step", "kvc_attn_prefill",
-            "kvc_cache_bytes", "kvc_decode_workspace_bytes", "kvc_last_error",
-            "kvc_abi_version"} <= set(names)
+    assert {"kvc_append", "kvc_attn_decode", "kvc_decode_step", "kvc_decode_split",
+            "kvc_decode_combine", "kvc_attn_prefill", "kvc_cache_bytes",
+            "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.kvc_abi_version() == 1
@@ -182,6 +182,26 @@ def test_decode_step_error_paths(lib):
     assert call(Hq=5) == E_SHAPE
     assert call(wsb=need - 256) == E_WORKSPACE
     assert call(N=0, q=None, k=None, v=None, o=None, ws=None) == OK
+
+
+def test_split_and_combine_error_paths(lib):
+    h = Host()
+    d = desc(h)
+    q, o, kn = h.ptr(), h.ptr(), h.ptr()
+    need = lib.kvc_decode_workspace_bytes(ctypes.byref(d), 2, 4, 3)
+    ws = h.ptr(need)
+    split = lib.kvc_decode_split
+    assert split(ctypes.byref(d), 0, 2, q, kn, None, 4, 3, hist(2, 5), 0.125, o, ws, need, None) == E_NULL
+    assert split(ctypes.byref(d), 0, 2, q, None, kn, 4, 3, hist(2, 5), 0.125, o, ws, need, None) == E_NULL
+    assert split(ctypes.byref(d), 0, 2, None, None, None, 4, 3, hist(2, 5), 0.125, o, ws, need, None) == E_NULL
+    assert split(ctypes.byref(d), 0, 2, q, None, None, 4, 3, hist(2, 14), 0.125, o, ws, need, None) == E_CAPACITY
+    assert split(ctypes.byref(d), 0, 2, q, None, None, 4, 3, hist(2, 5), 0.125, o, ws, 0, None) == E_WORKSPACE
+    comb = lib.kvc_decode_combine
+    assert comb(ctypes.byref(d), 0, 2, 4, 3, hist(2, 5), None, ws, need, None) == E_NULL
+    assert comb(ctypes.byref(d), 0, 2, 4, 3, hist(2, 5), o, None, need, None) == E_WORKSPACE
+    assert comb(ctypes.byref(d), 0, 2, 3, 3, hist(2, 5), o, ws, need, None) == E_SHAPE
+    assert comb(ctypes.byref(d), 0, 2, 4, 3, hist(2, 15), o, ws, need, None) == E_CAPACITY
+    assert comb(ctypes.byref(d), 0, 2, 4, 0, hist(2, 5), None, None, 0, None) == OK
 
 
 def test_prefill_error_paths(lib):

@@ -213,6 +213,37 @@ def test_permutation_property_on_gpu():
         assert (diff <= TOL["f32"]) if same else (diff > 1e-2), (N, diff)
 
 
+@pytest.mark.parametrize("case", ["mha_fp32", "gqa_bf16", "chunked"])
+def test_split_then_combine_equals_one_call(case):
+    """kvc_decode_split + kvc_decode_combine give the same bytes as the one
+    call (kvc_decode_step / kvc_attn_decode) and match the oracle."""
+    from transformer_kv_cache_amd import kvcache as K
+    w = {"mha_fp32": lambda: synth.decode_12layer(1000, seed=31),
+         "gqa_bf16": lambda: synth.batched_decode(seed=32, gqa=True),
+         "chunked": lambda: synth.chunked_decode(1000, 8, seed=33)}[case]()
+    q, k, v = w.steps[0]
+    ref_out = run_oracle(w)[0][0]
+    dt = torch_dtype(w.dtype)
+    outs = {}
+    for mode in ("one_call", "two_phases", "two_phases_unfused"):
+        cache = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        if mode == "one_call":
+            o = K.decode_step(cache, qd, kd, vd, w.hist)
+        elif mode == "two_phases":
+            o = K.decode_split(cache, qd, w.hist, kd, vd)
+            K.decode_combine(cache, o, w.hist, w.L, w.Hq, q.shape[3])
+        else:
+            K.append(cache, kd, vd, w.hist)
+            o = K.decode_split(cache, qd, w.hist)
+            K.decode_combine(cache, o, w.hist, w.L, w.Hq, q.shape[3])
+        outs[mode] = (to_host(o), to_host(cache.k))
+    for mode in ("two_phases", "two_phases_unfused"):
+        assert np.array_equal(bits(outs[mode][0]), bits(outs["one_call"][0])), mode
+        assert np.array_equal(bits(outs[mode][1]), bits(outs["one_call"][1])), mode
+    assert np.max(np.abs(synth.to_float(outs["one_call"][0]) - ref_out)) <= TOL[w.dtype]
+
+
 def test_repeated_calls_reuse_workspace_bitwise():
     """Repeated calls on one workspace, including after a call of another
     geometry scribbled over it, give bit-identical outputs."""

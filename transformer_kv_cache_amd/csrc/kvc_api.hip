@@ -160,11 +160,14 @@ size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers, int3
 
 namespace {
 
-// Shared by kvc_attn_decode and kvc_decode_step (k_new / v_new non-NULL).
-kvc_status decode_impl(const char *fn, const kvc_cache *cache, int32_t layer0, int32_t n_layers,
-                       const void *q, const void *k_new, const void *v_new, bool fused,
-                       int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
-                       void *workspace, size_t workspace_bytes, void *stream) {
+enum Phases { kSplit = 1, kCombine = 2, kBoth = 3 };
+
+// Shared by kvc_attn_decode, kvc_decode_step (fused: k_new / v_new given),
+// kvc_decode_split and kvc_decode_combine.
+kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32_t layer0,
+                       int32_t n_layers, const void *q, const void *k_new, const void *v_new,
+                       bool fused, int32_t Hq, int32_t N, const int32_t *hist_len, float scale,
+                       void *o, void *workspace, size_t workspace_bytes, void *stream) {
   kvc_status st = check_cache(cache, layer0, n_layers, fn);
   if (st != KVC_OK) return st;
   if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
@@ -174,8 +177,9 @@ kvc_status decode_impl(const char *fn, const kvc_cache *cache, int32_t layer0, i
   if ((st = check_hist(cache, hist_len, N, fn)) != KVC_OK) return st;
   if (N == 0 || n_layers == 0 || cache->B == 0) return ok();
   if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
-  if (!q || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
-  if (!aligned16(q) || !aligned16(o)) return fail(KVC_E_SHAPE, "%s: q / o must be 16-byte aligned", fn);
+  if (((phases & kSplit) && !q) || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
+  if (((phases & kSplit) && !aligned16(q)) || !aligned16(o))
+    return fail(KVC_E_SHAPE, "%s: q / o must be 16-byte aligned", fn);
   if (fused) {
     if (!k_new || !v_new) return fail(KVC_E_NULL, "%s: k_new or v_new is NULL", fn);
     if (!aligned16(k_new) || !aligned16(v_new))
@@ -219,11 +223,13 @@ kvc_status decode_impl(const char *fn, const kvc_cache *cache, int32_t layer0, i
       if (hist_len[b0 + i] + N > max_keys) max_keys = hist_len[b0 + i] + N;
     }
     const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
-    hipError_t e = g.mfma ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused,
-                                                     (hipStream_t)stream)
-                          : kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, fused,
-                                               (hipStream_t)stream);
-    if (e == hipSuccess && splits > 1)
+    hipError_t e = hipSuccess;
+    if (phases & kSplit)
+      e = g.mfma ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused,
+                                           (hipStream_t)stream)
+                 : kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, fused,
+                                      (hipStream_t)stream);
+    if (e == hipSuccess && (phases & kCombine) && splits > 1)
       e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
@@ -237,16 +243,34 @@ extern "C" {
 kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
                            int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_impl("kvc_attn_decode", cache, layer0, n_layers, q, nullptr, nullptr, false, Hq, N,
-                     hist_len, scale, o, workspace, workspace_bytes, stream);
+  return decode_impl("kvc_attn_decode", kBoth, cache, layer0, n_layers, q, nullptr, nullptr, false,
+                     Hq, N, hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
 kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
                            const void *k_new, const void *v_new, int32_t Hq, int32_t N,
                            const int32_t *hist_len, float scale, void *o, void *workspace,
                            size_t workspace_bytes, void *stream) {
-  return decode_impl("kvc_decode_step", cache, layer0, n_layers, q, k_new, v_new, true, Hq, N,
-                     hist_len, scale, o, workspace, workspace_bytes, stream);
+  return decode_impl("kvc_decode_step", kBoth, cache, layer0, n_layers, q, k_new, v_new, true, Hq,
+                     N, hist_len, scale, o, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_decode_split(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
+                            const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+                            const int32_t *hist_len, float scale, void *o, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(KVC_E_NULL, "kvc_decode_split: k_new and v_new must both be given or both NULL");
+  return decode_impl("kvc_decode_split", kSplit, cache, layer0, n_layers, q, k_new, v_new,
+                     k_new != nullptr, Hq, N, hist_len, scale, o, workspace, workspace_bytes,
+                     stream);
+}
+
+kvc_status kvc_decode_combine(const kvc_cache *cache, int32_t layer0, int32_t n_layers, int32_t Hq,
+                              int32_t N, const int32_t *hist_len, void *o, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  return decode_impl("kvc_decode_combine", kCombine, cache, layer0, n_layers, nullptr, nullptr,
+                     nullptr, false, Hq, N, hist_len, 1.0f, o, workspace, workspace_bytes, stream);
 }
 
 kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,

@@ -8,11 +8,12 @@
 // cached K/V byte once and does ~1 flop per byte, so it is bound by HBM
 // bandwidth ([KV-2] "千倍计算量为何只换来6倍速度").
 //
-// Work split.  A workgroup (256 lanes, 4 waves) owns one (layer, sequence,
-// KV head, tile of RT query rows, split of SPLIT consecutive keys).  The RT
-// rows are the G*N query rows (GQA group x new rows) that read the same KV
-// head, so each K/V byte is fetched once for all of them.  Inside the
-// workgroup:
+// Work split.  This vector kernel serves the case of one query row per KV
+// head (plain multi-head single-token decode); several rows per KV head (GQA
+// groups, chunked decode) go to the matrix-core kernel in kvc_decode_mfma.hip.
+// A workgroup (256 lanes, 4 waves) owns one (layer, sequence, KV head, split
+// of SPLIT consecutive keys); the code is written for a tile of RT rows but
+// instantiated with RT = 1.  Inside the workgroup:
 //   * a key row of D elements is LPR = D*elem/16 lanes wide; each lane loads
 //     one 16-byte vector of it (global_load_dwordx4).  Consecutive lane groups
 //     take consecutive rows, so one wave-wide load covers 64*16 contiguous
@@ -365,24 +366,16 @@ hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s
   return hipGetLastError();
 }
 
+// Several query rows per KV head run on the matrix-core kernel, so the vector
+// kernel is instantiated for one row per workgroup only.
 template <int DT, int D>
-hipError_t launch_rt(const DecodeArgs &a, int rt, int splits, bool fused, hipStream_t s) {
-  switch (rt) {
-    case 1: return launch_one<DT, D, 1>(a, splits, fused, s);
-    case 2: return launch_one<DT, D, 2>(a, splits, fused, s);
-    case 4: return launch_one<DT, D, 4>(a, splits, fused, s);
-    default: return launch_one<DT, D, 8>(a, splits, fused, s);
-  }
+hipError_t launch_rt(const DecodeArgs &a, int /*rt*/, int splits, bool fused, hipStream_t s) {
+  return launch_one<DT, D, 1>(a, splits, fused, s);
 }
 
 }  // namespace
 
-int decode_row_tile(int rows) {
-  if (rows <= 1) return 1;
-  if (rows <= 2) return 2;
-  if (rows <= 4) return 4;
-  return 8;
-}
+int decode_row_tile(int /*rows*/) { return 1; }
 
 int decode_split_keys(int dtype, int D) {
   const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;

@@ -79,6 +79,11 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_step.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ip, ctypes.c_float, vp,
                                         vp, sz, vp]
         lib.kvc_decode_step.restype = i32
+        lib.kvc_decode_split.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ip, ctypes.c_float, vp,
+                                         vp, sz, vp]
+        lib.kvc_decode_split.restype = i32
+        lib.kvc_decode_combine.argtypes = [cp, i32, i32, i32, i32, ip, vp, vp, sz, vp]
+        lib.kvc_decode_combine.restype = i32
         lib.kvc_attn_prefill.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
         lib.kvc_attn_prefill.restype = i32
         if path is None:
@@ -243,6 +248,50 @@ def decode_step(cache: KVCache, q, k_new, v_new, hist_len, scale: float | None =
     _check(library().kvc_decode_step(
         ctypes.byref(d), layer0, n_layers, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), Hq, N,
         hp, float(scale), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(cache.device, stream)))
+    return out
+
+
+def decode_split(cache: KVCache, q, hist_len, k_new=None, v_new=None, scale: float | None = None,
+                 out=None, layer0: int = 0, workspace=None, stream=None):
+    """First phase of attn_decode (k_new/v_new None) or decode_step (both
+    given): outputs of single-split sequences, split states for the rest."""
+    n_layers, _, Hq, N, _ = q.shape
+    shape = (n_layers, cache.B, Hq, N, cache.D)
+    _check_tensor("q", q, cache, shape)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new or neither")
+    if k_new is not None:
+        kshape = (n_layers, cache.B, cache.Hkv, N, cache.D)
+        _check_tensor("k_new", k_new, cache, kshape)
+        _check_tensor("v_new", v_new, cache, kshape)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, cache.B)
+    if workspace is None:
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream)
+    d = cache.desc()
+    _check(library().kvc_decode_split(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(),
+        None if k_new is None else k_new.data_ptr(), None if v_new is None else v_new.data_ptr(),
+        Hq, N, hp, float(scale), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(cache.device, stream)))
+    return out
+
+
+def decode_combine(cache: KVCache, out, hist_len, n_layers: int, Hq: int, N: int,
+                   layer0: int = 0, workspace=None, stream=None):
+    """Second phase: merge the split states left by decode_split into `out`."""
+    _check_tensor("out", out, cache, (n_layers, cache.B, Hq, N, cache.D))
+    _, hp = _hist(hist_len, cache.B)
+    if workspace is None:
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream)
+    d = cache.desc()
+    _check(library().kvc_decode_combine(
+        ctypes.byref(d), layer0, n_layers, Hq, N, hp, out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(cache.device, stream)))
     return out
 
