@@ -112,17 +112,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   const int bb = blockIdx.z;
   const int P = a.hist[bb];
-  const int rt = blockIdx.y % a.row_tiles;
-  const int lh = blockIdx.y / a.row_tiles;
+  const int rt = (RT == 1) ? 0 : (int)blockIdx.y % a.row_tiles;
+  const int lh = (RT == 1) ? (int)blockIdx.y : (int)blockIdx.y / a.row_tiles;
   const int hkv = lh % a.Hkv;
   const int l = lh / a.Hkv;
   const int b = a.b0 + bb;
   const int nkeys = P + a.N;
   const int nsplit = (nkeys + SPLIT - 1) / SPLIT;
   if (split >= nsplit) return;
+  const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
+  const long long qrow0 = (((long long)l * a.B + b) * a.Hq + (long long)hkv * a.group) * a.N;
 
   const int key0 = split * SPLIT;
-  const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
   const u32x4 *kc = reinterpret_cast<const u32x4 *>(a.k_cache) + crow0 * LPR + c;
   const u32x4 *vc = reinterpret_cast<const u32x4 *>(a.v_cache) + crow0 * LPR + c;
   const size_t nrow0 = (((size_t)l * a.B + b) * a.Hkv + hkv) * (size_t)a.N * LPR + c;
@@ -132,7 +133,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // 1. Issue the query loads and every K and V load of this split up front.
   //    Key indices past the sequence are clamped to its last row (always
   //    valid) so that no load sits behind a branch; their scores are masked.
-  const long long qrow0 = (((long long)l * a.B + b) * a.Hq + (long long)hkv * a.group) * a.N;
   const int rr0 = rt * RT;
   u32x4 qw[RT];
 #pragma unroll
