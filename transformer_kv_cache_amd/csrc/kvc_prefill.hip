@@ -53,6 +53,7 @@ __device__ __forceinline__ int perm16(int k) {
   return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -66,18 +67,24 @@ template <int DT, int D> struct Smem;
 template <int D> struct Smem<KVC_BF16, D> {
   static constexpr int kKStride = D + 8;    // bf16 elements per K row (16-B multiple)
   static constexpr int kVtStride = BN + 8;  // bf16 elements per V^T row
-  uint16_t k[BN * kKStride];
-  uint16_t vt[D * kVtStride];
+  // V^T row d starts at element vt_row(d): rows are kVtStride apart, plus 32
+  // bytes after every 16 rows.  Without that gap the staging writes, which put
+  // one key pair of eight rows 8 apart into the same LDS bank (8 rows span a
+  // multiple of 32 dwords), serialise eight ways; with it they are at most
+  // two-way, and the 16-byte operand reads stay conflict-free.
+  static __device__ __forceinline__ int vt_row(int d) { return d * kVtStride + (d >> 4) * 16; }
+  alignas(16) uint16_t k[BN * kKStride];
+  alignas(16) uint16_t vt[D * kVtStride + (D / 16) * 16];
 };
 template <int D> struct Smem<KVC_F32, D> {
   static constexpr int kKStride = D + 4;
   static constexpr int kVStride = D;
-  float k[BN * kKStride];
-  float v[BN * kVStride];
+  alignas(16) float k[BN * kKStride];
+  alignas(16) float v[BN * kVStride];
 };
 
 template <int DT, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   constexpr int EB = Dtype<DT>::kBytes;
   constexpr int EV = Dtype<DT>::kPer16B;
   constexpr int LPR = D * EB / 16;             // 16-byte vectors per row
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int h = lane >> 5;     // half-wave
   const int col = lane & 31;   // MFMA column / row within a 32 block
 
@@ -156,7 +163,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   };
   load_tile(0);
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // Stage tile kt in LDS (and in the cache when it is ours to write), then
+  // start loading tile kt + 1.
+  auto stage = [&](int kt) {
     const int key0 = kt * BN;
     const bool store_cache = writer && key0 >= q0;  // this tile's rows are ours to write
     __syncthreads();  // the previous tile's LDS reads are done
@@ -179,8 +188,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
           for (int j = 0; j < 4; ++j) {
             const uint32_t e0 = (lo[j] & 0xFFFFu) | (hi[j] << 16);          // element 2j
             const uint32_t e1 = (lo[j] >> 16) | (hi[j] & 0xFFFF0000u);      // element 2j+1
-            *reinterpret_cast<uint32_t *>(&sm.vt[(c * EV + 2 * j) * Smem<DT, D>::kVtStride + pos]) = e0;
-            *reinterpret_cast<uint32_t *>(&sm.vt[(c * EV + 2 * j + 1) * Smem<DT, D>::kVtStride + pos]) = e1;
+            *reinterpret_cast<uint32_t *>(&sm.vt[Smem<DT, D>::vt_row(c * EV + 2 * j) + pos]) = e0;
+            *reinterpret_cast<uint32_t *>(&sm.vt[Smem<DT, D>::vt_row(c * EV + 2 * j + 1) + pos]) = e1;
           }
         }
       } else {
@@ -189,29 +198,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
     if (kt + 1 < n_kt) load_tile(kt + 1);
-    if (key0 > wave_last) continue;  // whole tile above this wave's rows
+  };
 
+  auto compute = [&](int kt) {
+    const int key0 = kt * BN;
     // S^T blocks: acc_s[kb][i] = score of key key0 + 32 kb + 8 (i/4) + 4 h + i%4
     // for query qrow.
+    // The KB accumulator chains are interleaved so that consecutive MFMAs are
+    // independent.
     f32x16 acc_s[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      acc_s[kb] = f32x16{};
-      const int krow = 32 * kb + col;
-      if constexpr (DT == KVC_BF16) {
+    for (int kb = 0; kb < KB; ++kb) acc_s[kb] = f32x16{};
+    if constexpr (DT == KVC_BF16) {
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) {
-          const u32x4 kf =
-              *reinterpret_cast<const u32x4 *>(&sm.k[krow * Smem<DT, D>::kKStride + 16 * ds + 8 * h]);
+      for (int ds = 0; ds < D / 16; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 kf = *reinterpret_cast<const u32x4 *>(
+              &sm.k[(32 * kb + col) * Smem<DT, D>::kKStride + 16 * ds + 8 * h]);
           acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qv[ds]), acc_s[kb], 0, 0, 0);
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < D / 8; ++j) {
-          const f32x4 kf =
-              *reinterpret_cast<const f32x4 *>(&sm.k[krow * Smem<DT, D>::kKStride + 8 * j + 4 * h]);
-          const f32x4 qf = __builtin_bit_cast(f32x4, qv[j]);
+      for (int j = 0; j < D / 8; ++j) {
+        const f32x4 qf = __builtin_bit_cast(f32x4, qv[j]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const f32x4 kf = *reinterpret_cast<const f32x4 *>(
+              &sm.k[(32 * kb + col) * Smem<DT, D>::kKStride + 8 * j + 4 * h]);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[r], qf[r], acc_s[kb], 0, 0, 0);
@@ -219,23 +235,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // Scale, causal mask, online softmax for this lane's query.  Key
-    // key0 + 32 kb + 8 (i/4) + 4 h + i%4 is visible iff it is <= qrow and < S,
-    // i.e. iff the compile-time offset 32 kb + 8 (i/4) + i%4 is <= lim.
-    const bool need_mask = (key0 + BN - 1 > q0 + wave * 32) || (key0 + BN > S);
-    const int lim = (qrow < S - 1 ? qrow : S - 1) - key0 - 4 * h;
+    // Causal mask, only on tiles that reach past the wave's first row or the
+    // prompt's end (a wave-uniform branch).  Key key0 + 32 kb + 8 (i/4) + 4 h
+    // + i%4 is visible iff it is <= qrow and < S, i.e. iff the compile-time
+    // offset 32 kb + 8 (i/4) + i%4 is <= lim.
+    if ((key0 + BN - 1 > q0 + wave * 32) || (key0 + BN > S)) {
+      const int lim = (qrow < S - 1 ? qrow : S - 1) - key0 - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) acc_s[kb][i] = kNegInf;
+      }
+    }
+    // Online softmax for this lane's query, in log2 units: the raw scores are
+    // maximised first (the scale is positive, so scaling commutes with max)
+    // and the scale is folded into the exponent, p = 2^(s sc - m), one FMA per
+    // score.
+    const float sc = a.scale_log2;
     float mt = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = acc_s[kb][i] * a.scale_log2;
-        if (need_mask && 32 * kb + 8 * (i >> 2) + (i & 3) > lim) s = kNegInf;
-        acc_s[kb][i] = s;
-        mt = fmaxf(mt, s);
-      }
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc_s[kb][i]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * sc;
     // Lazy rescale: the running max only moves when this tile raises it by
     // more than 8 (log2 domain), so probabilities stay <= 2^8 and the output
     // rescale is skipped whenever no lane of the wave needs it.  Subtracting
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(acc_s[kb][i] - m_new);
+        const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], sc, -m_new));
         acc_s[kb][i] = p;
         psum += p;
       }
@@ -274,7 +298,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const u32x4 vf = *reinterpret_cast<const u32x4 *>(
-                &sm.vt[(32 * db + col) * Smem<DT, D>::kVtStride + 32 * kb + 16 * t + 8 * h]);
+                &sm.vt[Smem<DT, D>::vt_row(32 * db + col) + 32 * kb + 16 * t + 8 * h]);
             acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pw), acc_o[db], 0, 0, 0);
           }
@@ -291,7 +315,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
+  };
+
+  // Only the last key tile can lie wholly above a wave's rows (its first key
+  // is at most q0 + 64), so every wave computes every earlier tile and the
+  // skip test sits outside the loop.
+  for (int kt = 0; kt < n_kt - 1; ++kt) {
+    stage(kt);
+    compute(kt);
   }
+  stage(n_kt - 1);
+  if ((n_kt - 1) * BN <= wave_last) compute(n_kt - 1);
 
   // Normalise and write O[qrow][d] for d = 32 db + 8 g + 4 h + 0..3.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -314,20 +348,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Register budgets: at D = 64, three workgroups per CU for bf16 and two for
+// fp32; D = 128 keeps one, since capping it would spill.
+template <int DT>
+__global__ __launch_bounds__(256, DT == KVC_BF16 ? 3 : 2) void prefill_kernel_d64(PrefillArgs a) {
+  prefill_tile<DT, 64>(a);
+}
+template <int DT>
+__global__ __launch_bounds__(256) void prefill_kernel_d128(PrefillArgs a) { prefill_tile<DT, 128>(a); }
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_layers * a.B * a.Hq), (unsigned)a.q_tiles);
   if (dtype == KVC_F32) {
     if (D == 64)
-      hipLaunchKernelGGL((prefill_kernel<KVC_F32, 64>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel_d64<KVC_F32>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_kernel<KVC_F32, 128>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel_d128<KVC_F32>), grid, dim3(256), 0, s, a);
   } else {
     if (D == 64)
-      hipLaunchKernelGGL((prefill_kernel<KVC_BF16, 64>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel_d64<KVC_BF16>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_kernel<KVC_BF16, 128>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel_d128<KVC_BF16>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
