@@ -186,6 +186,9 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32
       return fail(KVC_E_SHAPE, "%s: k_new / v_new must be 16-byte aligned", fn);
   }
   const DecodeGeometry g = decode_geometry(cache, n_layers, Hq, N);
+  if ((long long)n_layers * cache->Hkv * g.row_tiles > 65535)
+    return fail(KVC_E_UNSUPPORTED, "%s: %d layers x %d KV heads x %d row tiles exceed one launch", fn,
+                n_layers, cache->Hkv, g.row_tiles);
   if (!workspace) return fail(KVC_E_WORKSPACE, "%s: workspace is NULL", fn);
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(KVC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
@@ -214,6 +217,8 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32
   a.max_splits = g.max_splits;
   a.split_keys = g.split_keys;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.hkv_div = kvc::magic_for(cache->Hkv);
+  a.split_div = kvc::magic_for(g.split_keys);
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
     a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;

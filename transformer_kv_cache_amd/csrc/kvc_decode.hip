@@ -12,8 +12,8 @@
 // head (plain multi-head single-token decode); several rows per KV head (GQA
 // groups, chunked decode) go to the matrix-core kernel in kvc_decode_mfma.hip.
 // A workgroup (256 lanes, 4 waves) owns one (layer, sequence, KV head, split
-// of SPLIT consecutive keys); the code is written for a tile of RT rows but
-// instantiated with RT = 1.  Inside the workgroup:
+// of SPLIT consecutive keys) and the head's single query row.  Inside the
+// workgroup:
 //   * a key row of D elements is LPR = D*elem/16 lanes wide; each lane loads
 //     one 16-byte vector of it (global_load_dwordx4).  Consecutive lane groups
 //     take consecutive rows, so one wave-wide load covers 64*16 contiguous
@@ -26,11 +26,11 @@
 //     over its keys; the states are merged across the wave with cross-lane
 //     exchanges and across the 4 waves through LDS, rescaling by exp2 of
 //     the max difference (log2(e) is folded into the scale).
-// Fused step.  kvc_decode_step also performs the append: keys at positions
-// [P, P+N) are read straight from the new K/V rows instead of the cache, and
-// the workgroups of row tile 0 that hold them write them to their cache slots.
-// No workgroup reads those slots during the call, so the write is race-free,
-// and the step needs no separate append launch.
+// Fused step.  kvc_decode_step also performs the append: the new key P is
+// read straight from the new K/V row instead of the cache, and the workgroup
+// that holds it writes it to its cache slot.  No workgroup reads that slot
+// during the call, so the write is race-free, and the step needs no separate
+// append launch.
 // Combine.  With more than one split, each workgroup writes its (max, sum,
 // P.V) state to the workspace and a second, small kernel merges the splits of
 // every query row (rescaling by exp2 of the max difference) and writes the
@@ -58,6 +58,31 @@ __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+constexpr int kDppRowRor8 = 0x128;   // rotate by 8 inside each 16-lane row
+
+// x combined (sum, or max with MAX) with the value OFF lanes away, OFF in
+// {8, 16, 32}, every lane getting the result.  OFF = 8 is a DPP rotate inside
+// the 16-lane row; OFF = 16 and 32 use the gfx950 permlane swaps, which trade
+// rows (or half-waves) between two registers: swapping x with itself leaves
+// the two partners' values in the two results, so combining them gives the
+// pair's total in every lane, in VALU latency rather than an LDS round trip.
+template <int OFF, bool MAX = false>
+__device__ __forceinline__ float xor_combine(float x) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "partner distance");
+  float y0, y1;
+  if constexpr (OFF == 8) {
+    y0 = x;
+    y1 = dpp_mov<kDppRowRor8>(x);
+  } else {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = (OFF == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                               : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    y0 = __uint_as_float(r[0]);
+    y1 = __uint_as_float(r[1]);
+  }
+  return MAX ? fmaxf(y0, y1) : y0 + y1;
+}
+
 // Sum over the LPR lanes that hold one key row; every lane gets the total.
 // Lane groups are aligned blocks of LPR lanes.  After the two quad steps a
 // quad is uniform, so mirroring inside 8 (then 16) lanes pairs uniform blocks.
@@ -68,7 +93,7 @@ __device__ __forceinline__ float row_allreduce(float x) {
   x += dpp_mov<kDppQuadXor2>(x);
   x += dpp_mov<kDppHalfMirror>(x);
   if (LPR >= 16) x += dpp_mov<kDppRowMirror>(x);
-  if (LPR >= 32) x += __shfl_xor(x, 16);
+  if (LPR >= 32) x = xor_combine<16>(x);
   return x;
 }
 
@@ -92,7 +117,7 @@ __device__ __forceinline__ float rescale(float m, float M) {
   return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
-template <int DT, int D, int RT, int KPL, bool FUSED>
+template <int DT, int D, int KPL, bool FUSED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
   constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
@@ -106,170 +131,172 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int rg = tid / LPR;
   const int c = tid % LPR;
 
-  // Grid: x = split, y = (layer, KV head, row tile), z = sequence in the
-  // batch slice.  The sequence comes straight from blockIdx.z so its length
-  // can be fetched while the other indices are still being computed.
+  // Grid: x = split, y = (layer, KV head), z = sequence in the batch slice.
+  // The sequence comes straight from blockIdx.z so its length can be fetched
+  // while the other indices are still being computed.  One query row per KV
+  // head (G = N = 1), so the query row index equals the KV head index.
   const int split = blockIdx.x;
   const int bb = blockIdx.z;
+  const int lh = blockIdx.y;
+  // Every kernel argument the prologue needs, fetched in one scalar round:
+  // the empty asm takes them all as operands, so none of their loads can be
+  // deferred behind the early exit or the index arithmetic.
   const int P = a.hist[bb];
-  const int rt = (RT == 1) ? 0 : (int)blockIdx.y % a.row_tiles;
-  const int lh = (RT == 1) ? (int)blockIdx.y : (int)blockIdx.y / a.row_tiles;
-  const int hkv = lh % a.Hkv;
-  const int l = lh / a.Hkv;
-  const int b = a.b0 + bb;
-  const int nkeys = P + a.N;
-  const int nsplit = (nkeys + SPLIT - 1) / SPLIT;
+  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0;
+  const uint32_t hkv_div = a.hkv_div;
+  const char *k_cache = a.k_cache, *v_cache = a.v_cache, *qp = a.q;
+  asm volatile("" ::"s"(P), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(b0), "s"(hkv_div),
+               "s"(k_cache), "s"(v_cache), "s"(qp));
+  const int nsplit = (P + SPLIT) / SPLIT;  // keys 0 .. P
   if (split >= nsplit) return;
-  const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
-  const long long qrow0 = (((long long)l * a.B + b) * a.Hq + (long long)hkv * a.group) * a.N;
+  const int l = div_magic(lh, Hkv, hkv_div);
+  const int hkv = lh - l * Hkv;
+  const int b = b0 + bb;
+  // (layer, sequence, KV head) indices fit in 32 bits; only the row offsets
+  // need 64.
+  const uint32_t head = (uint32_t)(((layer0 + l) * B + b) * Hkv + hkv);
+  const size_t crow0 = (size_t)head * (uint32_t)Tmax;
+  const uint32_t row = (uint32_t)((l * B + b) * Hkv + hkv);  // (l, b, hq, i = 0), Hq = Hkv
 
   const int key0 = split * SPLIT;
-  const u32x4 *kc = reinterpret_cast<const u32x4 *>(a.k_cache) + crow0 * LPR + c;
-  const u32x4 *vc = reinterpret_cast<const u32x4 *>(a.v_cache) + crow0 * LPR + c;
-  const size_t nrow0 = (((size_t)l * a.B + b) * a.Hkv + hkv) * (size_t)a.N * LPR + c;
-  const u32x4 *kn = FUSED ? reinterpret_cast<const u32x4 *>(a.k_new) + nrow0 : nullptr;
-  const u32x4 *vn = FUSED ? reinterpret_cast<const u32x4 *>(a.v_new) + nrow0 : nullptr;
+  const int last = P - key0;  // offset of the last visible key (key P) in this split
+  // Uniform bases plus 32-bit per-lane byte offsets: global loads with an SGPR
+  // base take one VGPR per address.
+  const char *kc = k_cache + crow0 * (LPR * 16);
+  const char *vc = v_cache + crow0 * (LPR * 16);
 
-  // 1. Issue the query loads and every K and V load of this split up front.
-  //    Key indices past the sequence are clamped to its last row (always
-  //    valid) so that no load sits behind a branch; their scores are masked.
-  const int rr0 = rt * RT;
-  u32x4 qw[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int rr = (rr0 + r < a.rows) ? rr0 + r : a.rows - 1;
-    qw[r] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + rr) * LPR + c];
+  // 1. Issue the query load and every K and V load of this split up front.
+  //    Keys past P are clamped to P (a valid slot) so that no load sits
+  //    behind a branch; their scores are masked.
+  const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
+  // Fused step: key P is the new row, not yet in the cache; the workgroup
+  // whose split holds it reads it from k_new / v_new (all lanes load their
+  // column of it, the lanes of the row group that owns it keep it).
+  const bool has_new = FUSED && last < SPLIT;
+  u32x4 k_nw = {}, v_nw = {};
+  if (has_new) {
+    const size_t nrow = (((size_t)l * a.B + b) * a.Hkv + hkv) * LPR + c;
+    k_nw = stream_load(reinterpret_cast<const u32x4 *>(a.k_new) + nrow);
+    v_nw = stream_load(reinterpret_cast<const u32x4 *>(a.v_new) + nrow);
   }
   u32x4 kw[KPL], vw[KPL];
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {
-    const int key = key0 + kk * NRG + rg;
-    const int kidx = key < nkeys ? key : nkeys - 1;
-    const bool fresh = FUSED && kidx >= P;  // a new row: read it from k_new / v_new
-    const size_t nidx = (size_t)(fresh ? kidx - P : 0);
-    kw[kk] = stream_load(fresh ? kn + nidx * LPR : kc + (size_t)kidx * LPR);
-    vw[kk] = stream_load(fresh ? vn + nidx * LPR : vc + (size_t)kidx * LPR);
+    const int kr = kk * NRG + rg;  // key offset within the split
+    const uint32_t off = (uint32_t)((key0 + (kr < last ? kr : last)) * LPR + c) * 16u;
+    kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(kc + off));
+    vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off));
   }
   // Keep the scheduler from interleaving arithmetic (and its waits) into the
   // load burst: all loads of the split are in flight before the first wait.
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. Query fragments of the tile's rows (row rr = g*N + i of this KV head).
-  float qf[RT][EV];
+  if (has_new) {
+    // Swap the new row in for key P and for the masked keys past it (their
+    // clamped loads read slot P, which holds stale data: a non-finite value
+    // there would survive the zero weight).  Then write the new row to its
+    // cache slot; no workgroup reads that slot during the call.
 #pragma unroll
-  for (int r = 0; r < RT; ++r) unpack16<DT>(qw[r], qf[r]);
+    for (int kk = 0; kk < KPL; ++kk) {
+      if (kk * NRG + rg >= last) {
+        kw[kk] = k_nw;
+        vw[kk] = v_nw;
+      }
+    }
+    if (rg == last % NRG) {
+      const size_t slot = (crow0 + P) * LPR + c;
+      reinterpret_cast<u32x4 *>(a.k_cache)[slot] = k_nw;
+      reinterpret_cast<u32x4 *>(a.v_cache)[slot] = v_nw;
+    }
+  }
 
-  // 3. Scores in the log2 domain, masked keys at -inf.
-  float s[RT][KPL];
+  // 2. Scores in the log2 domain; key key0 + kk*NRG + rg is visible iff it is
+  //    at most P, a compare of rg against a uniform bound.
+  float qf[EV];
+  unpack16<DT>(qw, qf);
+  float s[KPL];
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {
     float kf[EV];
     unpack16<DT>(kw[kk], kf);
-    const int key = key0 + kk * NRG + rg;
+    float dot = 0.f;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) dot = fmaf(qf[r][e], kf[e], dot);
-      dot = row_allreduce<LPR>(dot);
-      const int i = (rr0 + r) % a.N;
-      const bool visible = (key < nkeys) && (key <= P + i) && (rr0 + r < a.rows);
-      s[r][kk] = visible ? dot * a.scale_log2 : kNegInf;
-    }
+    for (int e = 0; e < EV; ++e) dot = fmaf(qf[e], kf[e], dot);
+    dot = row_allreduce<LPR>(dot);
+    s[kk] = (rg <= last - kk * NRG) ? dot * a.scale_log2 : kNegInf;
   }
 
-  // 4. Per-row-group softmax state over its KPL keys.
-  float m[RT], lsum[RT], acc[RT][EV];
+  // 3. Per-row-group softmax state over its KPL keys.  Row group 0 always
+  //    holds key key0 <= P, so in the merged state the max is finite.
+  float m = s[0];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    float mx = s[r][0];
+  for (int kk = 1; kk < KPL; ++kk) m = fmaxf(m, s[kk]);
+  float lsum = 0.f, acc[EV];
 #pragma unroll
-    for (int kk = 1; kk < KPL; ++kk) mx = fmaxf(mx, s[r][kk]);
-    m[r] = mx;
-    lsum[r] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[r][e] = 0.f;
-  }
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {
     float vf[EV];
     unpack16<DT>(vw[kk], vf);
+    const float p = (m == kNegInf) ? 0.f : fast_exp2(s[kk] - m);
+    lsum += p;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const float p = (m[r] == kNegInf) ? 0.f : fast_exp2(s[r][kk] - m[r]);
-      lsum[r] += p;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[r][e] = fmaf(p, vf[e], acc[r][e]);
-    }
+    for (int e = 0; e < EV; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
   }
 
-  // 5. Merge the row groups of this wave (lanes with the same c).
+  // 4. Merge the row groups of this wave (lanes with the same c).
+  {
+    float M = m;
+    if constexpr (LPR <= 8) M = xor_combine<8, true>(M);
+    if constexpr (LPR <= 16) M = xor_combine<16, true>(M);
+    M = xor_combine<32, true>(M);
+    const float f = rescale(m, M);
+    lsum *= f;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    float M = m[r];
+    for (int e = 0; e < EV; ++e) acc[e] *= f;
+    if constexpr (LPR <= 8) {
+      lsum = xor_combine<8>(lsum);
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float f = rescale(m[r], M);
-    lsum[r] *= f;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[r][e] *= f;
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-      lsum[r] += __shfl_xor(lsum[r], off);
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[r][e] += __shfl_xor(acc[r][e], off);
+      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<8>(acc[e]);
     }
-    m[r] = M;
+    if constexpr (LPR <= 16) {
+      lsum = xor_combine<16>(lsum);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<16>(acc[e]);
+    }
+    lsum = xor_combine<32>(lsum);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = xor_combine<32>(acc[e]);
+    m = M;
   }
 
-  // Fused step: row tile 0 writes the new rows it holds into their slots.
-  if constexpr (FUSED) {
-    if (rt == 0) {
-      u32x4 *kd = reinterpret_cast<u32x4 *>(a.k_cache) + crow0 * LPR + c;
-      u32x4 *vd = reinterpret_cast<u32x4 *>(a.v_cache) + crow0 * LPR + c;
-#pragma unroll
-      for (int kk = 0; kk < KPL; ++kk) {
-        const int key = key0 + kk * NRG + rg;
-        if (key >= P && key < nkeys) {
-          kd[(size_t)key * LPR] = kw[kk];
-          vd[(size_t)key * LPR] = vw[kk];
-        }
-      }
-    }
-  }
-
-  // 6. Merge the four waves through LDS.
-  __shared__ float sh_o[4][RT][D];
-  __shared__ float sh_m[4][RT];
-  __shared__ float sh_l[4][RT];
+  // 5. Merge the four waves through LDS; write the output (one split) or this
+  //    split's state.
+  __shared__ float sh_o[4][D];
+  __shared__ float sh_m[4];
+  __shared__ float sh_l[4];
   if (lane < LPR) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-#pragma unroll
-      for (int e = 0; e < EV; ++e) sh_o[wave][r][c * EV + e] = acc[r][e];
-      if (c == 0) {
-        sh_m[wave][r] = m[r];
-        sh_l[wave][r] = lsum[r];
-      }
+    for (int e = 0; e < EV; ++e) sh_o[wave][c * EV + e] = acc[e];
+    if (c == 0) {
+      sh_m[wave] = m;
+      sh_l[wave] = lsum;
     }
   }
   __syncthreads();
 
-  for (int t = tid; t < RT * D; t += 256) {
-    const int r = t / D;
-    const int d = t % D;
-    if (rr0 + r >= a.rows) continue;
-    float M = sh_m[0][r];
+  if (tid < D) {
+    const int d = tid;
+    float M = sh_m[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh_m[w][r]);
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh_m[w]);
     float o = 0.f, L = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = rescale(sh_m[w][r], M);
-      o = fmaf(f, sh_o[w][r][d], o);
-      L = fmaf(f, sh_l[w][r], L);
+      const float f = rescale(sh_m[w], M);
+      o = fmaf(f, sh_o[w][d], o);
+      L = fmaf(f, sh_l[w], L);
     }
-    const long long row = qrow0 + rr0 + r;
     if (nsplit == 1) {
       const float val = o / L;
       store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
@@ -284,11 +311,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the split-K states of every query row whose sequence needed more
-// than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
-// per row, one output element per lane.  Splits are read in chunks of 8 with
-// every load of a chunk issued before any is used (indices clamped, extra
-// splits masked), merged online across chunks.
 // Merge of one query row's split states, element d of the output row.
 // Splits are read in chunks of 16 with every load of a chunk issued before any
 // is used (indices clamped, extra splits masked), merged online across chunks.
@@ -330,22 +352,21 @@ __device__ __forceinline__ void combine_row(const DecodeArgs &a, long long row, 
 
 // Merge of the split-K states of every query row whose sequence needed more
 // than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
-// per row, one output element per lane.
+// per row, one output element per lane.  Grid: x = blocks over the Hq * N
+// rows of one (layer, sequence), y = layer, z = sequence in the batch slice,
+// so that a row's index needs no division.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  constexpr int RPW = 256 / D;  // rows per workgroup
-  const int d = threadIdx.x % D;
-  const long long t = (long long)blockIdx.x * RPW + threadIdx.x / D;  // (l, bb, hq, i)
-  const long long rows_here = (long long)a.n_layers * a.nb * a.Hq * a.N;
-  if (t >= rows_here) return;
-  const int i = (int)(t % a.N);
-  const int hq = (int)((t / a.N) % a.Hq);
-  const int bb = (int)((t / ((long long)a.N * a.Hq)) % a.nb);
-  const int l = (int)(t / ((long long)a.N * a.Hq * a.nb));
-  const int b = a.b0 + bb;
-  const int nsplit = (a.hist[bb] + a.N + a.split_keys - 1) / a.split_keys;
+  const int bb = blockIdx.z;
+  const int l = blockIdx.y;
+  const int nsplit = div_magic(a.hist[bb] + a.N + a.split_keys - 1, a.split_keys, a.split_div);
   if (nsplit <= 1) return;  // written by the split kernel
-  combine_row<DT, D>(a, (((long long)l * a.B + b) * a.Hq + hq) * a.N + i, nsplit, d);
+  const int t = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int rloc = t / D;  // (hq, i) within the (layer, sequence)
+  if (rloc >= a.Hq * a.N) return;
+  const int b = a.b0 + bb;
+  const long long row = ((long long)l * a.B + b) * (a.Hq * a.N) + rloc;
+  combine_row<DT, D>(a, row, nsplit, t % D);
 }
 
 // Keys each lane group loads per split: a split covers 256 / LPR * this many
@@ -356,21 +377,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #endif
 constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
 
-template <int DT, int D, int RT>
-hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
-  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv * a.row_tiles), (unsigned)a.nb);
-  if (fused)
-    hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<DT, D, RT, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-// Several query rows per KV head run on the matrix-core kernel, so the vector
-// kernel is instantiated for one row per workgroup only.
 template <int DT, int D>
-hipError_t launch_rt(const DecodeArgs &a, int /*rt*/, int splits, bool fused, hipStream_t s) {
-  return launch_one<DT, D, 1>(a, splits, fused, s);
+hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
+  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
+  if (fused)
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -383,9 +397,8 @@ int decode_split_keys(int dtype, int D) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) {
-  const long long rows = (long long)a.n_layers * a.nb * a.Hq * a.N;
-  const long long blocks = (rows + 256 / D - 1) / (256 / D);
-  const dim3 grid((unsigned)blocks);
+  const int rows = a.Hq * a.N;  // per (layer, sequence)
+  const dim3 grid((unsigned)((rows * D + 255) / 256), (unsigned)a.n_layers, (unsigned)a.nb);
   if (dtype == KVC_F32) {
     if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_F32, 64>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((combine_kernel<KVC_F32, 128>), grid, dim3(256), 0, s, a);
@@ -396,14 +409,16 @@ hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile, int splits,
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int /*row_tile*/, int splits,
                          bool fused_append, hipStream_t s) {
+  // The vector kernel serves one query row per KV head (G = N = 1) only.
+  if (a.rows != 1 || a.N != 1 || a.group != 1) return hipErrorInvalidValue;
   if (dtype == KVC_F32) {
-    if (D == 64) return launch_rt<KVC_F32, 64>(a, row_tile, splits, fused_append, s);
-    return launch_rt<KVC_F32, 128>(a, row_tile, splits, fused_append, s);
+    if (D == 64) return launch_one<KVC_F32, 64>(a, splits, fused_append, s);
+    return launch_one<KVC_F32, 128>(a, splits, fused_append, s);
   }
-  if (D == 64) return launch_rt<KVC_BF16, 64>(a, row_tile, splits, fused_append, s);
-  return launch_rt<KVC_BF16, 128>(a, row_tile, splits, fused_append, s);
+  if (D == 64) return launch_one<KVC_BF16, 64>(a, splits, fused_append, s);
+  return launch_one<KVC_BF16, 128>(a, splits, fused_append, s);
 }
 
 }  // namespace kvc

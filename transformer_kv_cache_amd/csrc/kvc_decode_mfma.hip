@@ -90,8 +90,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int P = a.hist[bb];
   const int rt = blockIdx.y % a.row_tiles;
   const int lh = blockIdx.y / a.row_tiles;
-  const int hkv = lh % a.Hkv;
-  const int l = lh / a.Hkv;
+  const int l = div_magic(lh, a.Hkv, a.hkv_div);
+  const int hkv = lh - l * a.Hkv;
   const int b = a.b0 + bb;
   const int nkeys = P + a.N;
   const int nsplit = (nkeys + SPLIT - 1) / SPLIT;

@@ -93,8 +93,25 @@ struct DecodeArgs {
   int32_t split_keys;  // keys per split of the launched kernel
   int32_t b0, nb;
   float scale_log2;    // scale * log2(e)
+  uint32_t hkv_div;    // div_magic multiplier for Hkv
+  uint32_t split_div;  // div_magic multiplier for split_keys
   int32_t hist[kMaxBatchPerLaunch];
 };
+
+// floor(2^32 / d) capped at 2^32 - 1: the multiplier div_magic uses for d.
+inline uint32_t magic_for(int d) {
+  const unsigned long long m = (1ull << 32) / (unsigned long long)d;
+  return m > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)m;
+}
+
+// floor(n / d) for 0 <= n < 2^31 and d >= 1, with m = magic_for(d).  m falls
+// short of 2^32 / d by less than one, so n m / 2^32 lies in (n/d - 1, n/d]:
+// umulhi(n, m) is floor(n / d) or one less, and one compare fixes it.
+__device__ __forceinline__ int div_magic(int n, int d, uint32_t m) {
+  int q = (int)__umulhi((uint32_t)n, m);
+  if (n - q * d >= d) ++q;
+  return q;
+}
 
 struct PrefillArgs {
   char *k_cache, *v_cache;
