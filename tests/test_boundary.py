@@ -158,6 +158,11 @@ def test_decode_error_paths(lib):
     assert call(q=h.ptr(offset=8)) == E_SHAPE
     assert call(layer0=1) == E_SHAPE
     assert call(c=None) == E_NULL
+    # more (layer, KV head) units than one launch's grid holds
+    big = desc(h, L=2, B=1, Hkv=40000, Tmax=16)
+    need_big = lib.kvc_decode_workspace_bytes(ctypes.byref(big), 2, 40000, 1)
+    assert call(c=ctypes.byref(big), Hq=40000, N=1, hist=hist(2), ws=h.ptr(256), wsb=need_big) == E_UNSUPPORTED
+    assert "exceed one launch" in err(lib)
 
 
 def test_decode_step_error_paths(lib):
