@@ -182,7 +182,8 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
                        workspace=wss[r])
 
     def combine_only(r):
-        K.decode_combine(caches[r], outs[r], hist, w.L, w.Hq, N, workspace=wss[r])
+        K.decode_combine(caches[r], qs[r], hist, kns[r], vns[r], scale=w.scale, out=outs[r],
+                         workspace=wss[r])
 
     def append_only(r):
         K.append(caches[r], kns[r], vns[r], hist)
@@ -199,9 +200,15 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     res["append_us"] = GraphTimer(torch, append_only, rotate).time(steps)
     # the fused step reads the new rows from k_new/v_new and writes them once
     res["step_bytes"] = decode_bytes(w, N) + new_rows_bytes(w, N)
-    # split kernel alone: K/V (history from the cache, new rows from k_new/v_new)
-    # and q read, new rows written; outputs of multi-split rows come later
-    res["split_bytes"] = kv_read_bytes(w, N) + q_bytes(w, N) + new_rows_bytes(w, N)
+    # split kernel alone.  One query row per KV head (vector kernel): K/V of
+    # the cached keys [0, P) and q read; the combine pass adds key P from
+    # k_new/v_new and appends it.  Several rows per KV head (matrix-core
+    # kernel): K/V of all keys (new rows from k_new/v_new) and q read, new
+    # rows written.
+    if (w.Hq // w.Hkv) * N == 1:
+        res["split_bytes"] = kv_read_bytes(w, 0) + q_bytes(w, N)
+    else:
+        res["split_bytes"] = kv_read_bytes(w, N) + q_bytes(w, N) + new_rows_bytes(w, N)
     res["split_gbs"] = res["split_bytes"] / res["split_us"] / 1e3
     res["step_gbs"] = res["step_bytes"] / res["step_us"] / 1e3
     res["attn_decode_bytes"] = decode_bytes(w, N)
@@ -394,7 +401,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_kernel<f32,D64,RT1,fused> (split-K pass, kvc_decode_split)",
+                     "kernel": "decode_kernel<f32,D64,KPL4> (split-K pass over the cached keys, "
+                               "kvc_decode_split)",
                      "launch_us": round(head["split_us"], 3),
                      "algorithmic_bytes": head["split_bytes"],
                      "combine_kernel_us": round(head["combine_us"], 3),

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -154,8 +154,8 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0,
  * positions [hist_len[b], hist_len[b] + N) followed by kvc_attn_decode with
  * the same hist_len, with identical results (cache bytes bit for bit,
  * outputs as kvc_attn_decode computes them).  The new rows are read once,
- * straight from k_new / v_new, and written into their slots by the attention
- * kernel itself, so the step needs no separate append launch.  This is the
+ * straight from k_new / v_new, and written into their slots by the decode
+ * kernels themselves, so the step needs no separate append launch.  This is the
  * decode graph's "one token + cache in, output + updated cache out" ([KV-1]
  * "Prefill/Decode 双图"; [KV-2] "一个很容易漏掉的错误": append on the sequence
  * axis, then attend with the offset mask).
@@ -174,19 +174,22 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0,
 /*
  * The two phases of kvc_attn_decode / kvc_decode_step as separate calls, for
  * callers that want to place other work between them (or time them apart).
+ * Both take the arguments of kvc_decode_step; with k_new and v_new both NULL
+ * they are the phases of kvc_attn_decode (rows [P, P+N) already appended),
+ * with both given the phases of kvc_decode_step.  Call kvc_decode_combine
+ * with the same arguments as kvc_decode_split, on the same stream, before
+ * anything else uses the workspace; together they equal the one-call form.
  *
- * kvc_decode_split runs the split-K pass: with k_new and v_new both NULL it
- * is the first phase of kvc_attn_decode (rows [P, P+N) already appended);
- * with both given it is the first phase of kvc_decode_step and also writes
- * the new rows into their slots.  Query rows of sequences whose P + N keys
- * fit one split get their output in `o` at once; the others get their
- * per-split softmax states (max, sum, unnormalised output) in `workspace`.
- * kvc_decode_combine then merges those states and writes the remaining
- * outputs: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
- * M = max_s m_s (the rescaling that makes split softmax states additive;
- * the result is the same softmax-weighted sum [KV-4] "Decode 阶段" defines).
- * Call it on the same stream with the same cache, layer range, Hq, N,
- * hist_len, o and workspace, before anything else uses the workspace.
+ * kvc_decode_split runs the split-K pass: each (layer, sequence, KV head,
+ * split of the keys) computes the softmax state (max, sum, unnormalised
+ * output) of its keys, into `workspace`, or straight into `o` for query rows
+ * whose keys fit one split when nothing is left to merge.
+ * kvc_decode_combine merges the states of every remaining query row and
+ * writes its output: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
+ * M = max_s m_s (the rescaling that makes split softmax states additive; the
+ * result is the same softmax-weighted sum [KV-4] "Decode 阶段" defines).
+ * Which phase writes the new K/V rows into the cache in the k_new form is an
+ * implementation detail: after both phases they are in their slots.
  * Arguments, errors and workspace rules as kvc_attn_decode / kvc_decode_step;
  * passing only one of k_new / v_new is KVC_E_NULL.
  */
@@ -197,10 +200,11 @@ kvc_status kvc_decode_split(const kvc_cache *cache, int32_t layer0,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
 kvc_status kvc_decode_combine(const kvc_cache *cache, int32_t layer0,
-                              int32_t n_layers, int32_t Hq, int32_t N,
-                              const int32_t *hist_len, void *o,
-                              void *workspace, size_t workspace_bytes,
-                              void *stream);
+                              int32_t n_layers, const void *q,
+                              const void *k_new, const void *v_new,
+                              int32_t Hq, int32_t N, const int32_t *hist_len,
+                              float scale, void *o, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * attn_prefill: causal self-attention over an S-token prompt that starts an

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == 1
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 2
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -202,11 +202,18 @@ def test_split_and_combine_error_paths(lib):
     assert split(ctypes.byref(d), 0, 2, q, None, None, 4, 3, hist(2, 14), 0.125, o, ws, need, None) == E_CAPACITY
     assert split(ctypes.byref(d), 0, 2, q, None, None, 4, 3, hist(2, 5), 0.125, o, ws, 0, None) == E_WORKSPACE
     comb = lib.kvc_decode_combine
-    assert comb(ctypes.byref(d), 0, 2, 4, 3, hist(2, 5), None, ws, need, None) == E_NULL
-    assert comb(ctypes.byref(d), 0, 2, 4, 3, hist(2, 5), o, None, need, None) == E_WORKSPACE
-    assert comb(ctypes.byref(d), 0, 2, 3, 3, hist(2, 5), o, ws, need, None) == E_SHAPE
-    assert comb(ctypes.byref(d), 0, 2, 4, 3, hist(2, 15), o, ws, need, None) == E_CAPACITY
-    assert comb(ctypes.byref(d), 0, 2, 4, 0, hist(2, 5), None, None, 0, None) == OK
+    args = lambda **kw: (ctypes.byref(kw.get("d", d)), 0, 2, kw.get("q", q), kw.get("kn", None),
+                         kw.get("vn", None), kw.get("Hq", 4), kw.get("N", 3),
+                         kw.get("hist", hist(2, 5)), 0.125, kw.get("o", o), kw.get("ws", ws),
+                         kw.get("wsb", need), None)
+    assert comb(*args(o=None)) == E_NULL
+    assert comb(*args(q=None)) == E_NULL
+    assert comb(*args(kn=kn)) == E_NULL
+    assert comb(*args(vn=kn)) == E_NULL
+    assert comb(*args(ws=None)) == E_WORKSPACE
+    assert comb(*args(Hq=3)) == E_SHAPE
+    assert comb(*args(hist=hist(2, 15))) == E_CAPACITY
+    assert comb(*args(N=0, q=None, o=None, ws=None, wsb=0)) == OK
 
 
 def test_prefill_error_paths(lib):

@@ -232,11 +232,11 @@ def test_split_then_combine_equals_one_call(case):
             o = K.decode_step(cache, qd, kd, vd, w.hist)
         elif mode == "two_phases":
             o = K.decode_split(cache, qd, w.hist, kd, vd)
-            K.decode_combine(cache, o, w.hist, w.L, w.Hq, q.shape[3])
+            K.decode_combine(cache, qd, w.hist, kd, vd, out=o)
         else:
             K.append(cache, kd, vd, w.hist)
             o = K.decode_split(cache, qd, w.hist)
-            K.decode_combine(cache, o, w.hist, w.L, w.Hq, q.shape[3])
+            K.decode_combine(cache, qd, w.hist, out=o)
         outs[mode] = (to_host(o), to_host(cache.k))
     for mode in ("two_phases", "two_phases_unfused"):
         assert np.array_equal(bits(outs[mode][0]), bits(outs["one_call"][0])), mode

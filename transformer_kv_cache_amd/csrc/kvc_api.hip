@@ -177,8 +177,8 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32
   if ((st = check_hist(cache, hist_len, N, fn)) != KVC_OK) return st;
   if (N == 0 || n_layers == 0 || cache->B == 0) return ok();
   if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
-  if (((phases & kSplit) && !q) || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
-  if (((phases & kSplit) && !aligned16(q)) || !aligned16(o))
+  if (!q || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
+  if (!aligned16(q) || !aligned16(o))
     return fail(KVC_E_SHAPE, "%s: q / o must be 16-byte aligned", fn);
   if (fused) {
     if (!k_new || !v_new) return fail(KVC_E_NULL, "%s: k_new or v_new is NULL", fn);
@@ -219,22 +219,26 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32
   a.scale_log2 = scale * 1.4426950408889634f;
   a.hkv_div = kvc::magic_for(cache->Hkv);
   a.split_div = kvc::magic_for(g.split_keys);
+  // Vector kernel: the split pass covers keys [0, P) and the combine pass
+  // adds key P (from k_new / v_new in the fused step, which it then writes to
+  // the cache, else from the cache), so both forms do the same arithmetic.
+  a.tail = g.mfma ? 0 : 1;
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
     a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
-    int max_keys = 0;
+    int max_keys = 0;  // keys the split pass covers, longest sequence
     for (int i = 0; i < a.nb; ++i) {
       a.hist[i] = hist_len[b0 + i];
-      if (hist_len[b0 + i] + N > max_keys) max_keys = hist_len[b0 + i] + N;
+      const int keys = hist_len[b0 + i] + (a.tail ? 0 : N);
+      if (keys > max_keys) max_keys = keys;
     }
     const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
     hipError_t e = hipSuccess;
-    if (phases & kSplit)
+    if ((phases & kSplit) && splits > 0)
       e = g.mfma ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused,
                                            (hipStream_t)stream)
-                 : kvc::launch_decode(a, cache->dtype, cache->D, g.row_tile, splits, fused,
-                                      (hipStream_t)stream);
-    if (e == hipSuccess && (phases & kCombine) && splits > 1)
+                 : kvc::launch_decode(a, cache->dtype, cache->D, splits, (hipStream_t)stream);
+    if (e == hipSuccess && (phases & kCombine) && (a.tail || splits > 1))
       e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
@@ -271,11 +275,15 @@ kvc_status kvc_decode_split(const kvc_cache *cache, int32_t layer0, int32_t n_la
                      stream);
 }
 
-kvc_status kvc_decode_combine(const kvc_cache *cache, int32_t layer0, int32_t n_layers, int32_t Hq,
-                              int32_t N, const int32_t *hist_len, void *o, void *workspace,
-                              size_t workspace_bytes, void *stream) {
-  return decode_impl("kvc_decode_combine", kCombine, cache, layer0, n_layers, nullptr, nullptr,
-                     nullptr, false, Hq, N, hist_len, 1.0f, o, workspace, workspace_bytes, stream);
+kvc_status kvc_decode_combine(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                              const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                              int32_t N, const int32_t *hist_len, float scale, void *o,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(KVC_E_NULL, "kvc_decode_combine: k_new and v_new must both be given or both NULL");
+  return decode_impl("kvc_decode_combine", kCombine, cache, layer0, n_layers, q, k_new, v_new,
+                     k_new != nullptr, Hq, N, hist_len, scale, o, workspace, workspace_bytes,
+                     stream);
 }
 
 kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,

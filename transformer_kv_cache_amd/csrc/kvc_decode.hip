@@ -26,19 +26,19 @@
 //     over its keys; the states are merged across the wave with cross-lane
 //     exchanges and across the 4 waves through LDS, rescaling by exp2 of
 //     the max difference (log2(e) is folded into the scale).
-// Fused step.  kvc_decode_step also performs the append: the new key P is
-// read straight from the new K/V row instead of the cache, and the workgroup
-// that holds it writes it to its cache slot.  No workgroup reads that slot
-// during the call, so the write is race-free, and the step needs no separate
-// append launch.
-// Combine.  With more than one split, each workgroup writes its (max, sum,
-// P.V) state to the workspace and a second, small kernel merges the splits of
-// every query row (rescaling by exp2 of the max difference) and writes the
-// output; with a single split the workgroup writes the output itself.  The
-// merge is a separate launch rather than a last-workgroup ticket: the ticket
-// needs a device-scope release fence in every workgroup, which on gfx950 is an
-// L2 write-back (buffer_wbl2), and that measured about ten times slower than
-// the extra launch.
+// Combine.  Each workgroup writes its (max, sum, P.V) state to the
+// workspace and a second, small kernel merges the states of every query row
+// (rescaling by exp2 of the max difference) and writes the output.  The
+// split kernel covers keys [0, P); the combine kernel adds the last key P as
+// one more state, read from the new K/V row in the fused step (kvc_decode_step,
+// which also writes that row to its cache slot there) and from the cache
+// otherwise, so the fused and the two-call forms do the same arithmetic.
+// Every split workgroup thus runs one uniform code path: none waits on the
+// new row or on a store before its arithmetic, which would lengthen the
+// slowest workgroup.  The merge is a separate launch rather than a
+// last-workgroup ticket: the ticket needs a device-scope release fence in
+// every workgroup, which on gfx950 is an L2 write-back (buffer_wbl2), and
+// that measured about ten times slower than the extra launch.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -117,7 +117,7 @@ __device__ __forceinline__ float rescale(float m, float M) {
   return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
-template <int DT, int D, int KPL, bool FUSED>
+template <int DT, int D, int KPL>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
   constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
@@ -142,12 +142,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // the empty asm takes them all as operands, so none of their loads can be
   // deferred behind the early exit or the index arithmetic.
   const int P = a.hist[bb];
-  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0;
+  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0, tail = a.tail;
   const uint32_t hkv_div = a.hkv_div;
   const char *k_cache = a.k_cache, *v_cache = a.v_cache, *qp = a.q;
-  asm volatile("" ::"s"(P), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(b0), "s"(hkv_div),
-               "s"(k_cache), "s"(v_cache), "s"(qp));
-  const int nsplit = (P + SPLIT) / SPLIT;  // keys 0 .. P
+  asm volatile("" ::"s"(P), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(b0), "s"(tail),
+               "s"(hkv_div), "s"(k_cache), "s"(v_cache), "s"(qp));
+  // Keys of this pass: 0 .. P-1 when the combine pass adds key P (always,
+  // as launched), else 0 .. P.
+  const int nk = P + 1 - tail;
+  const int nsplit = (nk + SPLIT - 1) / SPLIT;
   if (split >= nsplit) return;
   const int l = div_magic(lh, Hkv, hkv_div);
   const int hkv = lh - l * Hkv;
@@ -159,26 +162,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint32_t row = (uint32_t)((l * B + b) * Hkv + hkv);  // (l, b, hq, i = 0), Hq = Hkv
 
   const int key0 = split * SPLIT;
-  const int last = P - key0;  // offset of the last visible key (key P) in this split
+  const int last = nk - 1 - key0;  // offset of the last visible key in this split
   // Uniform bases plus 32-bit per-lane byte offsets: global loads with an SGPR
   // base take one VGPR per address.
   const char *kc = k_cache + crow0 * (LPR * 16);
   const char *vc = v_cache + crow0 * (LPR * 16);
 
   // 1. Issue the query load and every K and V load of this split up front.
-  //    Keys past P are clamped to P (a valid slot) so that no load sits
-  //    behind a branch; their scores are masked.
+  //    Keys past the last visible one are clamped to it (a valid, written
+  //    slot) so that no load sits behind a branch; their scores are masked.
   const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
-  // Fused step: key P is the new row, not yet in the cache; the workgroup
-  // whose split holds it reads it from k_new / v_new (all lanes load their
-  // column of it, the lanes of the row group that owns it keep it).
-  const bool has_new = FUSED && last < SPLIT;
-  u32x4 k_nw = {}, v_nw = {};
-  if (has_new) {
-    const size_t nrow = (((size_t)l * a.B + b) * a.Hkv + hkv) * LPR + c;
-    k_nw = stream_load(reinterpret_cast<const u32x4 *>(a.k_new) + nrow);
-    v_nw = stream_load(reinterpret_cast<const u32x4 *>(a.v_new) + nrow);
-  }
   u32x4 kw[KPL], vw[KPL];
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {
@@ -191,27 +184,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // load burst: all loads of the split are in flight before the first wait.
   __builtin_amdgcn_sched_barrier(0);
 
-  if (has_new) {
-    // Swap the new row in for key P and for the masked keys past it (their
-    // clamped loads read slot P, which holds stale data: a non-finite value
-    // there would survive the zero weight).  Then write the new row to its
-    // cache slot; no workgroup reads that slot during the call.
-#pragma unroll
-    for (int kk = 0; kk < KPL; ++kk) {
-      if (kk * NRG + rg >= last) {
-        kw[kk] = k_nw;
-        vw[kk] = v_nw;
-      }
-    }
-    if (rg == last % NRG) {
-      const size_t slot = (crow0 + P) * LPR + c;
-      reinterpret_cast<u32x4 *>(a.k_cache)[slot] = k_nw;
-      reinterpret_cast<u32x4 *>(a.v_cache)[slot] = v_nw;
-    }
-  }
-
-  // 2. Scores in the log2 domain; key key0 + kk*NRG + rg is visible iff it is
-  //    at most P, a compare of rg against a uniform bound.
+  // 2. Scores in the log2 domain; key key0 + kk*NRG + rg is visible iff its
+  //    offset is at most `last`, a compare of rg against a uniform bound.
   float qf[EV];
   unpack16<DT>(qw, qf);
   float s[KPL];
@@ -227,7 +201,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // 3. Per-row-group softmax state over its KPL keys.  Row group 0 always
-  //    holds key key0 <= P, so in the merged state the max is finite.
+  //    holds key key0, which is visible, so in the merged state the max is
+  //    finite.
   float m = s[0];
 #pragma unroll
   for (int kk = 1; kk < KPL; ++kk) m = fmaxf(m, s[kk]);
@@ -270,8 +245,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     m = M;
   }
 
-  // 5. Merge the four waves through LDS; write the output (one split) or this
-  //    split's state.
+  // 5. Merge the four waves through LDS; write this split's state (or the
+  //    output, for a single split with no key left to the combine pass).
   __shared__ float sh_o[4][D];
   __shared__ float sh_m[4];
   __shared__ float sh_l[4];
@@ -297,7 +272,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       o = fmaf(f, sh_o[w][d], o);
       L = fmaf(f, sh_l[w], L);
     }
-    if (nsplit == 1) {
+    if (!tail && nsplit == 1) {
       const float val = o / L;
       store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
     } else {
@@ -311,62 +286,141 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of one query row's split states, element d of the output row.
-// Splits are read in chunks of 16 with every load of a chunk issued before any
-// is used (indices clamped, extra splits masked), merged online across chunks.
+// One element of a row in the cache dtype: raw bits, and widened to fp32.
+template <int DT> struct Elem;
+template <> struct Elem<KVC_F32> {
+  typedef uint32_t bits;
+  static __device__ __forceinline__ float widen(bits u) { return __uint_as_float(u); }
+};
+template <> struct Elem<KVC_BF16> {
+  typedef uint16_t bits;
+  static __device__ __forceinline__ float widen(bits u) { return __uint_as_float((uint32_t)u << 16); }
+};
+
+// Merge of the split-K states of query rows: o = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s with M = max_s m_s.  One wave per row, lane j holding
+// elements j, j + 64, ... of it.  Grid: x = blocks of 4 rows over the Hq * N
+// rows of one (layer, sequence), y = layer, z = sequence in the batch slice,
+// so that a row's index needs no division.
+//   Without `tail` only rows whose sequence needed more than one split are
+// merged (the split kernel wrote the others).  With `tail` (one query row per
+// KV head) the split states cover keys [0, P) and this pass adds key P: its
+// state is (m, l, o) = (scale log2(e) q.k_P, 1, v_P), merged like any split.
+// In the fused step k_P, v_P come from k_new / v_new and this pass then
+// writes them to cache slot P (read by no kernel of the step, so the write
+// is race-free); otherwise they are read from slot P.
 template <int DT, int D>
-__device__ __forceinline__ void combine_row(const DecodeArgs &a, long long row, int nsplit, int d) {
-  constexpr int CH = 16;
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  constexpr int EPL = D / 64;  // elements per lane
+  typedef typename Elem<DT>::bits bits;
+  const int lane = threadIdx.x & 63;
+  // (hq, i); wave-uniform, so a row's split (max, sum) pairs are scalar loads
+  const int rloc = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int bb = blockIdx.z;
+  const int l = blockIdx.y;
+  if (rloc >= a.Hq * a.N) return;
+  const int P = a.hist[bb];
+  const int tail = a.tail;
+  const int nk = tail ? P : P + a.N;  // keys covered by split states
+  const int nsplit = div_magic(nk + a.split_keys - 1, a.split_keys, a.split_div);
+  if (!tail && nsplit <= 1) return;  // written by the split kernel
+  const int b = a.b0 + bb;
+  const long long row = ((long long)l * a.B + b) * (a.Hq * a.N) + rloc;
   const size_t ws0 = (size_t)row * a.max_splits;
-  float M = kNegInf, o = 0.f, L = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += CH) {
-    float mv[CH], lv[CH], ov[CH];
+
+  // Cache slot P of this row's (layer, sequence, KV head); rows are
+  // (l, b, hkv) in tail mode (G = N = 1), so q, k_new and v_new share the
+  // row index.
+  const size_t slot = ((((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + rloc) * a.Tmax + P) * D;
+  const bool fused = a.k_new != nullptr;
+
+  // Splits in chunks of CH, every load of a chunk issued before any is used
+  // (indices clamped, extra splits masked), merged online across chunks.  The
+  // key-P rows and the first chunk are loaded together.
+  constexpr int CH = 16;
+  float mv[CH], lv[CH], ov[CH][EPL];
+  auto load_chunk = [&](int s0) {
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int sp = (s0 + j < nsplit) ? s0 + j : nsplit - 1;
-      mv[j] = a.ws_ml[(ws0 + sp) * 2];
-      lv[j] = a.ws_ml[(ws0 + sp) * 2 + 1];
-      ov[j] = a.ws_o[(ws0 + sp) * D + d];
+    for (int t = 0; t < CH; ++t) {
+      const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
+      mv[t] = a.ws_ml[(ws0 + sp) * 2];
+      lv[t] = a.ws_ml[(ws0 + sp) * 2 + 1];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ov[t][j] = a.ws_o[(ws0 + sp) * D + lane + 64 * j];
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Key P's rows (loaded unconditionally, from q itself when unused, so that
+  // no load sits behind a branch the compiler could fill with their use).
+  const bits *qb = reinterpret_cast<const bits *>(a.q) + (size_t)row * D;
+  const bits *kb = !tail ? qb
+                   : fused ? reinterpret_cast<const bits *>(a.k_new) + (size_t)row * D
+                           : reinterpret_cast<const bits *>(a.k_cache) + slot;
+  const bits *vb = !tail ? qb
+                   : fused ? reinterpret_cast<const bits *>(a.v_new) + (size_t)row * D
+                           : reinterpret_cast<const bits *>(a.v_cache) + slot;
+  bits qn[EPL], kn[EPL], vn[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    qn[j] = qb[lane + 64 * j];
+    kn[j] = kb[lane + 64 * j];
+    vn[j] = vb[lane + 64 * j];
+  }
+  if (nsplit > 0) load_chunk(0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (tail && fused) {
+    // the append of the new row, issued before the merge arithmetic
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      reinterpret_cast<bits *>(a.k_cache)[slot + lane + 64 * j] = kn[j];
+      reinterpret_cast<bits *>(a.v_cache)[slot + lane + 64 * j] = vn[j];
+    }
+  }
+
+  float M = kNegInf, L = 0.f, o[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) o[j] = 0.f;
+  if (tail) {
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) dot = fmaf(Elem<DT>::widen(qn[j]), Elem<DT>::widen(kn[j]), dot);
+    dot = row_allreduce<16>(dot);
+    dot = xor_combine<16>(dot);
+    dot = xor_combine<32>(dot);
+    M = dot * a.scale_log2;
+    L = 1.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) o[j] = Elem<DT>::widen(vn[j]);
+  }
+  for (int s0 = 0; s0 < nsplit; s0 += CH) {
+    if (s0 > 0) {
+      load_chunk(s0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     float Mc = M;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (s0 + j >= nsplit) mv[j] = kNegInf;
-      Mc = fmaxf(Mc, mv[j]);
+    for (int t = 0; t < CH; ++t) {
+      if (s0 + t >= nsplit) mv[t] = kNegInf;
+      Mc = fmaxf(Mc, mv[t]);
     }
     const float fr = rescale(M, Mc);
-    o *= fr;
     L *= fr;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const float f = rescale(mv[j], Mc);
-      o = fmaf(f, ov[j], o);
-      L = fmaf(f, lv[j], L);
+    for (int j = 0; j < EPL; ++j) o[j] *= fr;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const float f = rescale(mv[t], Mc);
+      L = fmaf(f, lv[t], L);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) o[j] = fmaf(f, ov[t][j], o[j]);
     }
     M = Mc;
   }
-  const float val = o / L;
-  store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
-}
-
-// Merge of the split-K states of every query row whose sequence needed more
-// than one split: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  D lanes
-// per row, one output element per lane.  Grid: x = blocks over the Hq * N
-// rows of one (layer, sequence), y = layer, z = sequence in the batch slice,
-// so that a row's index needs no division.
-template <int DT, int D>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  const int bb = blockIdx.z;
-  const int l = blockIdx.y;
-  const int nsplit = div_magic(a.hist[bb] + a.N + a.split_keys - 1, a.split_keys, a.split_div);
-  if (nsplit <= 1) return;  // written by the split kernel
-  const int t = (int)blockIdx.x * 256 + (int)threadIdx.x;
-  const int rloc = t / D;  // (hq, i) within the (layer, sequence)
-  if (rloc >= a.Hq * a.N) return;
-  const int b = a.b0 + bb;
-  const long long row = ((long long)l * a.B + b) * (a.Hq * a.N) + rloc;
-  combine_row<DT, D>(a, row, nsplit, t % D);
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const float val = o[j] * inv;
+    store_elems<DT>(a.o, (size_t)row * D + lane + 64 * j, &val, 1);
+  }
 }
 
 // Keys each lane group loads per split: a split covers 256 / LPR * this many
@@ -378,12 +432,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
 
 template <int DT, int D>
-hipError_t launch_one(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
+hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
-  if (fused)
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -397,8 +448,8 @@ int decode_split_keys(int dtype, int D) {
 }
 
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) {
-  const int rows = a.Hq * a.N;  // per (layer, sequence)
-  const dim3 grid((unsigned)((rows * D + 255) / 256), (unsigned)a.n_layers, (unsigned)a.nb);
+  const int rows = a.Hq * a.N;  // per (layer, sequence); one wave each
+  const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)a.n_layers, (unsigned)a.nb);
   if (dtype == KVC_F32) {
     if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_F32, 64>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((combine_kernel<KVC_F32, 128>), grid, dim3(256), 0, s, a);
@@ -409,16 +460,15 @@ hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int /*row_tile*/, int splits,
-                         bool fused_append, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s) {
   // The vector kernel serves one query row per KV head (G = N = 1) only.
   if (a.rows != 1 || a.N != 1 || a.group != 1) return hipErrorInvalidValue;
   if (dtype == KVC_F32) {
-    if (D == 64) return launch_one<KVC_F32, 64>(a, splits, fused_append, s);
-    return launch_one<KVC_F32, 128>(a, splits, fused_append, s);
+    if (D == 64) return launch_one<KVC_F32, 64>(a, splits, s);
+    return launch_one<KVC_F32, 128>(a, splits, s);
   }
-  if (D == 64) return launch_one<KVC_BF16, 64>(a, splits, fused_append, s);
-  return launch_one<KVC_BF16, 128>(a, splits, fused_append, s);
+  if (D == 64) return launch_one<KVC_BF16, 64>(a, splits, s);
+  return launch_one<KVC_BF16, 128>(a, splits, s);
 }
 
 }  // namespace kvc

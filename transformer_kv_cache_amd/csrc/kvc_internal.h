@@ -95,6 +95,8 @@ struct DecodeArgs {
   float scale_log2;    // scale * log2(e)
   uint32_t hkv_div;    // div_magic multiplier for Hkv
   uint32_t split_div;  // div_magic multiplier for split_keys
+  int32_t tail;        // 1 (vector kernel): the split states cover keys
+                       // [0, P) and the combine adds key P
   int32_t hist[kMaxBatchPerLaunch];
 };
 
@@ -127,8 +129,7 @@ struct PrefillArgs {
 // Host launchers (one translation unit each).  They assume validated
 // arguments and return the launch status.
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int row_tile,
-                         int splits, bool fused_append, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s);

@@ -26,6 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
+ABI_VERSION = 2  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -67,6 +68,10 @@ def library(path: str | None = None) -> ctypes.CDLL:
         cp = ctypes.POINTER(CacheDesc)
         ip = ctypes.POINTER(ctypes.c_int32)
         lib.kvc_abi_version.argtypes, lib.kvc_abi_version.restype = [], i32
+        if lib.kvc_abi_version() != ABI_VERSION:
+            raise KVCacheLibraryMissing(
+                f"{p} has ABI version {lib.kvc_abi_version()}, this binding needs {ABI_VERSION}; "
+                "rebuild with `python -m transformer_kv_cache_amd.build`")
         lib.kvc_last_error.argtypes, lib.kvc_last_error.restype = [], ctypes.c_char_p
         lib.kvc_cache_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
         lib.kvc_cache_bytes.restype = ctypes.c_uint64
@@ -82,7 +87,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_split.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ip, ctypes.c_float, vp,
                                          vp, sz, vp]
         lib.kvc_decode_split.restype = i32
-        lib.kvc_decode_combine.argtypes = [cp, i32, i32, i32, i32, ip, vp, vp, sz, vp]
+        lib.kvc_decode_combine.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ip, ctypes.c_float, vp,
+                                           vp, sz, vp]
         lib.kvc_decode_combine.restype = i32
         lib.kvc_attn_prefill.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
         lib.kvc_attn_prefill.restype = i32
@@ -252,10 +258,8 @@ def decode_step(cache: KVCache, q, k_new, v_new, hist_len, scale: float | None =
     return out
 
 
-def decode_split(cache: KVCache, q, hist_len, k_new=None, v_new=None, scale: float | None = None,
-                 out=None, layer0: int = 0, workspace=None, stream=None):
-    """First phase of attn_decode (k_new/v_new None) or decode_step (both
-    given): outputs of single-split sequences, split states for the rest."""
+def _decode_phase(fn_name, cache, q, hist_len, k_new, v_new, scale, out, layer0, workspace,
+                  stream):
     n_layers, _, Hq, N, _ = q.shape
     shape = (n_layers, cache.B, Hq, N, cache.D)
     _check_tensor("q", q, cache, shape)
@@ -274,7 +278,7 @@ def decode_split(cache: KVCache, q, hist_len, k_new=None, v_new=None, scale: flo
     if workspace is None:
         workspace = _default_workspace(cache, n_layers, Hq, N, stream)
     d = cache.desc()
-    _check(library().kvc_decode_split(
+    _check(getattr(library(), fn_name)(
         ctypes.byref(d), layer0, n_layers, q.data_ptr(),
         None if k_new is None else k_new.data_ptr(), None if v_new is None else v_new.data_ptr(),
         Hq, N, hp, float(scale), out.data_ptr(), workspace.data_ptr(),
@@ -282,18 +286,22 @@ def decode_split(cache: KVCache, q, hist_len, k_new=None, v_new=None, scale: flo
     return out
 
 
-def decode_combine(cache: KVCache, out, hist_len, n_layers: int, Hq: int, N: int,
-                   layer0: int = 0, workspace=None, stream=None):
-    """Second phase: merge the split states left by decode_split into `out`."""
-    _check_tensor("out", out, cache, (n_layers, cache.B, Hq, N, cache.D))
-    _, hp = _hist(hist_len, cache.B)
-    if workspace is None:
-        workspace = _default_workspace(cache, n_layers, Hq, N, stream)
-    d = cache.desc()
-    _check(library().kvc_decode_combine(
-        ctypes.byref(d), layer0, n_layers, Hq, N, hp, out.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(cache.device, stream)))
-    return out
+def decode_split(cache: KVCache, q, hist_len, k_new=None, v_new=None, scale: float | None = None,
+                 out=None, layer0: int = 0, workspace=None, stream=None):
+    """First phase of attn_decode (k_new/v_new None) or decode_step (both
+    given): per-split softmax states, or outputs where nothing is left to
+    merge."""
+    return _decode_phase("kvc_decode_split", cache, q, hist_len, k_new, v_new, scale, out,
+                         layer0, workspace, stream)
+
+
+def decode_combine(cache: KVCache, q, hist_len, k_new=None, v_new=None,
+                   scale: float | None = None, out=None, layer0: int = 0, workspace=None,
+                   stream=None):
+    """Second phase: takes the same arguments as the decode_split call it
+    completes and merges its split states into `out`."""
+    return _decode_phase("kvc_decode_combine", cache, q, hist_len, k_new, v_new, scale, out,
+                         layer0, workspace, stream)
 
 
 def attn_prefill(cache: KVCache, q, k, v, scale: float | None = None, out=None,
