@@ -318,21 +318,31 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int rloc = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int bb = blockIdx.z;
   const int l = blockIdx.y;
-  if (rloc >= a.Hq * a.N) return;
+  // Every kernel argument, fetched in one scalar round (the empty asm takes
+  // them all as operands, so no load is deferred behind a branch).
   const int P = a.hist[bb];
-  const int tail = a.tail;
-  const int nk = tail ? P : P + a.N;  // keys covered by split states
-  const int nsplit = div_magic(nk + a.split_keys - 1, a.split_keys, a.split_div);
+  const int Hq = a.Hq, N = a.N, tail = a.tail, split_keys = a.split_keys, B = a.B, Hkv = a.Hkv;
+  const int Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0, max_splits = a.max_splits;
+  const uint32_t split_div = a.split_div;
+  const char *qp = a.q, *knp = a.k_new, *vnp = a.v_new;
+  char *kcp = a.k_cache, *vcp = a.v_cache;
+  const float *ws_o = a.ws_o, *ws_ml = a.ws_ml;
+  asm volatile("" ::"s"(P), "s"(Hq), "s"(N), "s"(tail), "s"(split_keys), "s"(B), "s"(Hkv),
+               "s"(Tmax), "s"(layer0), "s"(b0), "s"(max_splits), "s"(split_div), "s"(qp),
+               "s"(knp), "s"(vnp), "s"(kcp), "s"(vcp), "s"(ws_o), "s"(ws_ml));
+  if (rloc >= Hq * N) return;
+  const int nk = tail ? P : P + N;  // keys covered by split states
+  const int nsplit = div_magic(nk + split_keys - 1, split_keys, split_div);
   if (!tail && nsplit <= 1) return;  // written by the split kernel
-  const int b = a.b0 + bb;
-  const long long row = ((long long)l * a.B + b) * (a.Hq * a.N) + rloc;
-  const size_t ws0 = (size_t)row * a.max_splits;
+  const int b = b0 + bb;
+  const long long row = ((long long)l * B + b) * (Hq * N) + rloc;
+  const size_t ws0 = (size_t)row * max_splits;
 
   // Cache slot P of this row's (layer, sequence, KV head); rows are
   // (l, b, hkv) in tail mode (G = N = 1), so q, k_new and v_new share the
   // row index.
-  const size_t slot = ((((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + rloc) * a.Tmax + P) * D;
-  const bool fused = a.k_new != nullptr;
+  const size_t slot = ((((size_t)(layer0 + l) * B + b) * Hkv + rloc) * Tmax + P) * D;
+  const bool fused = knp != nullptr;
 
   // Splits in chunks of CH, every load of a chunk issued before any is used
   // (indices clamped, extra splits masked), merged online across chunks.  The
@@ -343,21 +353,21 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
       const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
-      mv[t] = a.ws_ml[(ws0 + sp) * 2];
-      lv[t] = a.ws_ml[(ws0 + sp) * 2 + 1];
+      mv[t] = ws_ml[(ws0 + sp) * 2];
+      lv[t] = ws_ml[(ws0 + sp) * 2 + 1];
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) ov[t][j] = a.ws_o[(ws0 + sp) * D + lane + 64 * j];
+      for (int j = 0; j < EPL; ++j) ov[t][j] = ws_o[(ws0 + sp) * D + lane + 64 * j];
     }
   };
   // Key P's rows (loaded unconditionally, from q itself when unused, so that
   // no load sits behind a branch the compiler could fill with their use).
-  const bits *qb = reinterpret_cast<const bits *>(a.q) + (size_t)row * D;
+  const bits *qb = reinterpret_cast<const bits *>(qp) + (size_t)row * D;
   const bits *kb = !tail ? qb
-                   : fused ? reinterpret_cast<const bits *>(a.k_new) + (size_t)row * D
-                           : reinterpret_cast<const bits *>(a.k_cache) + slot;
+                   : fused ? reinterpret_cast<const bits *>(knp) + (size_t)row * D
+                           : reinterpret_cast<const bits *>(kcp) + slot;
   const bits *vb = !tail ? qb
-                   : fused ? reinterpret_cast<const bits *>(a.v_new) + (size_t)row * D
-                           : reinterpret_cast<const bits *>(a.v_cache) + slot;
+                   : fused ? reinterpret_cast<const bits *>(vnp) + (size_t)row * D
+                           : reinterpret_cast<const bits *>(vcp) + slot;
   bits qn[EPL], kn[EPL], vn[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
@@ -371,8 +381,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     // the append of the new row, issued before the merge arithmetic
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-      reinterpret_cast<bits *>(a.k_cache)[slot + lane + 64 * j] = kn[j];
-      reinterpret_cast<bits *>(a.v_cache)[slot + lane + 64 * j] = vn[j];
+      reinterpret_cast<bits *>(kcp)[slot + lane + 64 * j] = kn[j];
+      reinterpret_cast<bits *>(vcp)[slot + lane + 64 * j] = vn[j];
     }
   }
 
