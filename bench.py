@@ -393,7 +393,7 @@ def main():
         "config": {"workload": "GPT-2 Small KV-cache decode step, 12 layers, fp32, B=1, H=12, "
                                "D=64, Tmax=1024, history 1023 + 1 new token (T=1024)",
                    "layers": 12, "batch": 1, "heads": 12, "head_dim": 64, "context": 1024,
-                   "step": "kvc_decode_step: split-K kernel (writes the new rows) + combine",
+                   "step": "kvc_decode_step: split-K kernel over the cached keys + combine kernel (adds the new key, appends its row)",
                    "rotating_cache_replicas": args.rotate},
         "decode_us_per_step": round(step_us, 3),
         "step_bytes": step_bytes,
