@@ -20,8 +20,10 @@
 // waves) covers 16 query rows and a split of 4 x KPW keys; the per-row softmax
 // states of the waves merge in LDS and then follow the same path as the
 // vector kernel: the output directly, or (max, sum, partial output) into the
-// workspace for the split-combine kernel.  The fused step (append inside the
-// kernel) works as in kvc_decode.hip.
+// workspace for the split-combine kernel.  In the fused step keys [P, P+N)
+// are read straight from k_new / v_new, and the workgroups of row tile 0 that
+// hold them write them to their cache slots (no workgroup reads those slots
+// during the call).
 #include "kvc_internal.h"
 
 namespace kvc {
