@@ -12,6 +12,8 @@ Array conventions (numpy, C-contiguous):
     ``np.uint16`` (the high half of an fp32).
   * caches are ``[L, B, Hkv, Tmax, D]``; new rows and queries are
     ``[n_layers, B, H, N, D]``; ``hist_len`` is ``int32[B]``.
+  * paged caches are pools ``[L, num_blocks, Hkv, block_size, D]`` with an
+    ``int32[B, max_blocks]`` block table.
 """
 from __future__ import annotations
 
@@ -75,6 +77,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attention.restype = i32
     lib.oracle_prefill.argtypes = [vp, vp] + [i32] * 8 + [vp, vp, vp, i32, i32, dbl, vp]
     lib.oracle_prefill.restype = i32
+    lib.oracle_paged_append.argtypes = [vp, vp] + [i32] * 8 + [vp, vp, i32, i32, vp, vp, i32]
+    lib.oracle_paged_append.restype = i32
+    lib.oracle_paged_attention.argtypes = [vp, vp, vp] + [i32] * 11 + [vp, vp, i32, dbl, vp]
+    lib.oracle_paged_attention.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_set_threads.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -158,6 +164,56 @@ def prefill(k_cache, v_cache, q, k, v, scale, layer0=0, lib=None) -> np.ndarray:
     rc = lib.oracle_prefill(_ptr(k_cache), _ptr(v_cache), L, B, Hkv, Tmax, D, dt, layer0,
                             n_layers, _ptr(q), _ptr(k), _ptr(v), Hq, S, float(scale), _ptr(out))
     _check(rc, "oracle_prefill")
+    return out
+
+
+def _paged_shapes(k_pool, v_pool, block_table, what):
+    L, num_blocks, Hkv, bs, D = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError(f"{what}: shape mismatch")
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    if bt.ndim != 2:
+        raise ValueError(f"{what}: block_table must be [B, max_blocks]")
+    return L, num_blocks, Hkv, bs, D, bt
+
+
+def paged_append(k_pool, v_pool, k_new, v_new, hist_len, block_table, layer0=0, lib=None) -> None:
+    """In-place append into a paged cache: pools [L, num_blocks, Hkv,
+    block_size, D], new rows [n_layers, B, Hkv, N, D], block_table int32
+    [B, max_blocks]."""
+    lib = lib or load()
+    L, nblk, Hkv, bs, D, bt = _paged_shapes(k_pool, v_pool, block_table, "paged_append")
+    n_layers, B, H2, N, D2 = k_new.shape
+    if (H2, D2) != (Hkv, D) or v_new.shape != k_new.shape or bt.shape[0] != B:
+        raise ValueError("paged_append: shape mismatch")
+    dt = _dtype_code(k_pool)
+    for a in (v_pool, k_new, v_new):
+        if _dtype_code(a) != dt:
+            raise TypeError("paged_append: dtype mismatch")
+    hist = np.ascontiguousarray(hist_len, dtype=np.int32)
+    rc = lib.oracle_paged_append(_ptr(k_pool), _ptr(v_pool), L, nblk, Hkv, bs, D, dt, layer0,
+                                 n_layers, _ptr(k_new), _ptr(v_new), B, N, _ptr(hist), _ptr(bt),
+                                 bt.shape[1])
+    _check(rc, "oracle_paged_append")
+
+
+def paged_attention(q, k_pool, v_pool, hist_len, block_table, scale, layer0=0, lib=None) -> np.ndarray:
+    """Attention of q ([n_layers,B,Hq,N,D]) against a paged cache, new row i
+    of sequence b seeing positions 0..hist_len[b]+i.  Returns float64."""
+    lib = lib or load()
+    L, nblk, Hkv, bs, D, bt = _paged_shapes(k_pool, v_pool, block_table, "paged_attention")
+    n_layers, B, Hq, N, D2 = q.shape
+    if D2 != D or bt.shape[0] != B:
+        raise ValueError("paged_attention: shape mismatch")
+    dt = _dtype_code(k_pool)
+    if _dtype_code(q) != dt or _dtype_code(v_pool) != dt:
+        raise TypeError("paged_attention: dtype mismatch")
+    hist = np.ascontiguousarray(hist_len, dtype=np.int32)
+    out = np.zeros(q.shape, dtype=np.float64)
+    rc = lib.oracle_paged_attention(_ptr(q), _ptr(k_pool), _ptr(v_pool), L, nblk, Hkv, bs, D, dt,
+                                    layer0, n_layers, Hq, B, N, _ptr(hist), _ptr(bt), bt.shape[1],
+                                    float(scale), _ptr(out))
+    _check(rc, "oracle_paged_attention")
     return out
 
 

@@ -235,6 +235,131 @@ int oracle_prefill(void *k_cache, void *v_cache, int L, int B, int Hkv,
   return rc;
 }
 
+/*
+ * Paged cache.  [KV-2] "显存测量最容易被分配器误导" (production engines
+ * preallocate and manage the cache in pages or blocks instead of
+ * concatenating) and [KV-4] "Decode 阶段" (the note after listing 1-2: real
+ * implementations write each step's K/V in place, slot by slot, with
+ * PagedAttention).  The pages give no layout; the reading taken is the usual
+ * one for such a cache:
+ *   * K and V are each a pool [L, num_blocks, Hkv, block_size, D]: a block
+ *     holds block_size consecutive positions of every KV head of one layer;
+ *   * block_table[b][j] (int32 [B, max_blocks]) names the block that holds
+ *     positions j*block_size .. j*block_size + block_size - 1 of sequence b;
+ *   * position t of sequence b is row t % block_size of block
+ *     block_table[b][t / block_size].
+ * Attention over a paged cache is the attention above over the sequence's
+ * rows in position order; which physical block holds them changes nothing.
+ */
+
+/* Flat element index of pool[l][blk][h][r][0]. */
+static size_t paged_row(int l, int blk, int h, int r, int num_blocks, int Hkv,
+                        int block_size, int D) {
+  return ((((size_t)l * num_blocks + blk) * Hkv + h) * (size_t)block_size +
+          (size_t)r) *
+         (size_t)D;
+}
+
+/* Checks shared by the paged functions: positions [0, hist_len[b] + N) must
+ * fit the table row, and every block id they use must name a block. */
+static int paged_check(int L, int num_blocks, int Hkv, int block_size, int D,
+                       int layer0, int n_layers, int B, int N,
+                       const int32_t *hist_len, const int32_t *block_table,
+                       int max_blocks) {
+  if (L < 0 || num_blocks < 0 || Hkv <= 0 || block_size <= 0 || D <= 0 ||
+      B < 0 || N < 0 || max_blocks < 0 || layer0 < 0 || n_layers < 0 ||
+      layer0 + n_layers > L)
+    return ORACLE_E_ARG;
+  for (int b = 0; b < B; ++b) {
+    if (hist_len[b] < 0) return ORACLE_E_ARG;
+    const int64_t end = (int64_t)hist_len[b] + N;
+    if (end > (int64_t)max_blocks * block_size) return ORACLE_E_CAPACITY;
+    for (int64_t j = 0; j * block_size < end; ++j) {
+      const int32_t blk = block_table[(size_t)b * max_blocks + j];
+      if (blk < 0 || blk >= num_blocks) return ORACLE_E_ARG;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Write the N new K/V rows of layers [layer0, layer0+n_layers) at positions
+ * [P_b, P_b+N) of each sequence b, each into its slot: row (P_b+i) %
+ * block_size of block block_table[b][(P_b+i) / block_size].  Nothing else in
+ * the pools changes; rows are copied byte for byte.  Returns
+ * ORACLE_E_CAPACITY (P_b + N beyond the table row) or ORACLE_E_ARG (a block
+ * id out of range) and writes nothing.
+ */
+int oracle_paged_append(void *k_pool, void *v_pool, int L, int num_blocks,
+                        int Hkv, int block_size, int D, int dtype, int layer0,
+                        int n_layers, const void *k_new, const void *v_new,
+                        int B, int N, const int32_t *hist_len,
+                        const int32_t *block_table, int max_blocks) {
+  int rc = paged_check(L, num_blocks, Hkv, block_size, D, layer0, n_layers, B,
+                       N, hist_len, block_table, max_blocks);
+  if (rc != ORACLE_OK) return rc;
+  const size_t es = elem_size(dtype);
+  for (int l = 0; l < n_layers; ++l)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < Hkv; ++h)
+        for (int i = 0; i < N; ++i) {
+          const int t = hist_len[b] + i;
+          const int blk = block_table[(size_t)b * max_blocks + t / block_size];
+          const size_t dst = paged_row(layer0 + l, blk, h, t % block_size,
+                                       num_blocks, Hkv, block_size, D);
+          const size_t src = step_row(l, b, h, i, B, Hkv, N, D);
+          memcpy((char *)k_pool + dst * es, (const char *)k_new + src * es,
+                 (size_t)D * es);
+          memcpy((char *)v_pool + dst * es, (const char *)v_new + src * es,
+                 (size_t)D * es);
+        }
+  return ORACLE_OK;
+}
+
+/*
+ * Attention over a paged cache: gather each sequence's rows 0 ..
+ * hist_len[b]+N-1 in position order into a contiguous [n_layers, B, Hkv,
+ * Tlog, D] copy (Tlog = max_blocks * block_size), then oracle_attention on
+ * it -- the same definition, keys visited in the same order.
+ */
+int oracle_paged_attention(const void *q, const void *k_pool,
+                           const void *v_pool, int L, int num_blocks, int Hkv,
+                           int block_size, int D, int dtype, int layer0,
+                           int n_layers, int Hq, int B, int N,
+                           const int32_t *hist_len, const int32_t *block_table,
+                           int max_blocks, double scale, double *out) {
+  int rc = paged_check(L, num_blocks, Hkv, block_size, D, layer0, n_layers, B,
+                       N, hist_len, block_table, max_blocks);
+  if (rc != ORACLE_OK) return rc;
+  if (Hq <= 0 || Hq % Hkv != 0) return ORACLE_E_ARG;
+  const int Tlog = max_blocks * block_size;
+  const size_t es = elem_size(dtype);
+  const size_t n = (size_t)n_layers * B * Hkv * (size_t)Tlog * D;
+  char *kc = (char *)calloc(n > 0 ? n : 1, es);
+  char *vc = (char *)calloc(n > 0 ? n : 1, es);
+  if (!kc || !vc) {
+    free(kc);
+    free(vc);
+    return ORACLE_E_ARG;
+  }
+  for (int l = 0; l < n_layers; ++l)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < Hkv; ++h)
+        for (int pos = 0; pos < hist_len[b] + N; ++pos) {
+          const int blk = block_table[(size_t)b * max_blocks + pos / block_size];
+          const size_t src = paged_row(layer0 + l, blk, h, pos % block_size,
+                                       num_blocks, Hkv, block_size, D);
+          const size_t dst = cache_row(l, b, h, pos, B, Hkv, Tlog, D);
+          memcpy(kc + dst * es, (const char *)k_pool + src * es, (size_t)D * es);
+          memcpy(vc + dst * es, (const char *)v_pool + src * es, (size_t)D * es);
+        }
+  rc = oracle_attention(q, kc, vc, n_layers, B, Hkv, Tlog, D, dtype, 0,
+                        n_layers, Hq, N, hist_len, scale, out);
+  free(kc);
+  free(vc);
+  return rc;
+}
+
 /* Thread control for the timed CPU baseline (independent (l, b, hq) units). */
 void oracle_set_threads(int n) {
 #ifdef _OPENMP

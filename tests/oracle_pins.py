@@ -361,6 +361,163 @@ def pin_bf16_decode_exact(lib):
     assert np.array_equal(out.reshape(-1), expect)
 
 
+# ---------------------------------------------------------------- paged cache
+# Reading of [KV-2] "显存测量最容易被分配器误导" and [KV-4] "Decode 阶段" (in-place
+# writes by slot): pools [L, num_blocks, Hkv, block_size, D], position t of
+# sequence b in row t % block_size of block block_table[b][t // block_size].
+
+
+def _paged_canary(L, nblk, H, bs, D, dtype="f32"):
+    return _empty_cache(L, nblk, H, bs, D, dtype)
+
+
+def pin_paged_identity_is_contiguous(lib):
+    """With one KV head and the identity table (sequence b's j-th block is
+    block b*max_blocks + j), the pool's bytes are the contiguous cache's bytes
+    ([L, B, 1, max_blocks*block_size, D] read as [L, B*max_blocks, 1,
+    block_size, D]): a paged decode step must leave the same bytes as the
+    contiguous append and give the same outputs as the contiguous attention,
+    bit for bit."""
+    rng = _rng(61)
+    L, B, D, bs, mb = 2, 3, 8, 4, 5
+    T = bs * mb
+    hist = np.array([0, 7, 13], np.int32)  # empty, inside a block, block boundary +1
+    kc, vc = _empty_cache(L, B, 1, T, D)
+    _fill_history(kc, vc, hist, rng)
+    kp = np.ascontiguousarray(kc.reshape(L, B * mb, 1, bs, D))
+    vp = np.ascontiguousarray(vc.reshape(L, B * mb, 1, bs, D))
+    bt = np.arange(B * mb, dtype=np.int32).reshape(B, mb)
+    for N in (1, 3, 6):
+        q = rng.standard_normal((L, B, 2, N, D), dtype=np.float32)
+        k = rng.standard_normal((L, B, 1, N, D), dtype=np.float32)
+        v = rng.standard_normal((L, B, 1, N, D), dtype=np.float32)
+        kc2, vc2, kp2, vp2 = kc.copy(), vc.copy(), kp.copy(), vp.copy()
+        ref = _decode(lib, kc2, vc2, q, k, v, hist, 0.4)
+        oracle.paged_append(kp2, vp2, k, v, hist, bt, lib=lib)
+        got = oracle.paged_attention(q, kp2, vp2, hist, bt, 0.4, lib=lib)
+        assert np.array_equal(kp2.reshape(kc2.shape).view(np.uint32), kc2.view(np.uint32)), N
+        assert np.array_equal(vp2.reshape(vc2.shape).view(np.uint32), vc2.view(np.uint32)), N
+        assert np.array_equal(got, ref), N
+
+
+def _paged_from_history(lib, kc, vc, hist, bt, nblk, bs, dtype="f32", layer0=0):
+    """Pools holding the contiguous history rows of layers [layer0, L), written
+    by the paged append itself (P = 0, N = longest history; rows past a
+    sequence's own history are written too and never read)."""
+    L, B, H, T, D = kc.shape
+    kp, vp = _paged_canary(L, nblk, H, bs, D, dtype)
+    n = int(hist.max())
+    if n:
+        kn = np.ascontiguousarray(kc[layer0:, :, :, :n])
+        vn = np.ascontiguousarray(vc[layer0:, :, :, :n])
+        oracle.paged_append(kp, vp, kn, vn, np.zeros(B, np.int32), bt, layer0=layer0, lib=lib)
+    return kp, vp
+
+
+def pin_paged_block_permutation(lib):
+    """Which physical block holds a logical block changes nothing: paged
+    decode over a shuffled table (blocks scattered through a larger pool,
+    GQA, layers from layer0 = 1 on) equals the contiguous decode, outputs bit
+    for bit, and the new rows land where the table says."""
+    rng = _rng(62)
+    L, B, Hkv, G, D, bs, mb = 3, 3, 2, 2, 8, 4, 6
+    nblk = B * mb + 5
+    hist = np.array([9, 0, 17], np.int32)
+    kc, vc = _empty_cache(L, B, Hkv, bs * mb, D)
+    _fill_history(kc, vc, hist, rng)
+    bt = rng.permutation(nblk)[: B * mb].astype(np.int32).reshape(B, mb)
+    kp, vp = _paged_from_history(lib, kc, vc, hist, bt, nblk, bs, layer0=1)
+    N = 4
+    q = rng.standard_normal((L - 1, B, Hkv * G, N, D), dtype=np.float32)
+    k = rng.standard_normal((L - 1, B, Hkv, N, D), dtype=np.float32)
+    v = rng.standard_normal((L - 1, B, Hkv, N, D), dtype=np.float32)
+    ref = _decode(lib, kc, vc, q, k, v, hist, 0.3, layer0=1)
+    oracle.paged_append(kp, vp, k, v, hist, bt, layer0=1, lib=lib)
+    got = oracle.paged_attention(q, kp, vp, hist, bt, 0.3, layer0=1, lib=lib)
+    assert np.array_equal(got, ref)
+    assert synth.is_canary(kp[0]).all() and synth.is_canary(vp[0]).all()  # layer 0 untouched
+    # the table's unused blocks are untouched
+    unused = np.setdiff1d(np.arange(nblk), bt)
+    assert synth.is_canary(kp[:, unused]).all() and synth.is_canary(vp[:, unused]).all()
+
+
+def pin_paged_heads_are_independent(lib):
+    """A block holds every KV head's rows: appending two KV heads at once
+    leaves, for each head, the bytes that appending that head alone into a
+    one-head pool leaves; attention per head is unchanged by the other head."""
+    rng = _rng(63)
+    L, B, Hkv, D, bs, mb = 1, 2, 2, 4, 4, 3
+    nblk = 7
+    bt = np.array([[5, 0, 3], [6, 2, 1]], np.int32)
+    hist = np.array([5, 2], np.int32)
+    N = 3
+    k = rng.standard_normal((L, B, Hkv, N, D), dtype=np.float32)
+    v = rng.standard_normal((L, B, Hkv, N, D), dtype=np.float32)
+    q = rng.standard_normal((L, B, Hkv, N, D), dtype=np.float32)
+    kp, vp = _paged_canary(L, nblk, Hkv, bs, D)
+    oracle.paged_append(kp, vp, k, v, hist, bt, lib=lib)
+    for h in range(Hkv):
+        kh, vh = _paged_canary(L, nblk, 1, bs, D)
+        oracle.paged_append(kh, vh, np.ascontiguousarray(k[:, :, h:h + 1]),
+                            np.ascontiguousarray(v[:, :, h:h + 1]), hist, bt, lib=lib)
+        assert np.array_equal(kp[:, :, h:h + 1].view(np.uint32), kh.view(np.uint32)), h
+        assert np.array_equal(vp[:, :, h:h + 1].view(np.uint32), vh.view(np.uint32)), h
+    # attention: the N rows as a prompt (positions 0 .. N-1), all heads at
+    # once against each head alone
+    h0 = np.zeros(B, np.int32)
+    kp2, vp2 = _paged_canary(L, nblk, Hkv, bs, D)
+    oracle.paged_append(kp2, vp2, k, v, h0, bt, lib=lib)
+    full = oracle.paged_attention(q, kp2, vp2, h0, bt, 0.5, lib=lib)
+    for h in range(Hkv):
+        kh, vh = _paged_canary(L, nblk, 1, bs, D)
+        oracle.paged_append(kh, vh, np.ascontiguousarray(k[:, :, h:h + 1]),
+                            np.ascontiguousarray(v[:, :, h:h + 1]), h0, bt, lib=lib)
+        one = oracle.paged_attention(np.ascontiguousarray(q[:, :, h:h + 1]), kh, vh, h0, bt, 0.5,
+                                     lib=lib)
+        assert np.array_equal(full[:, :, h:h + 1], one), h
+
+
+def pin_paged_shared_prefix(lib):
+    """Two sequences whose tables share the blocks of a common prefix give
+    the outputs of two sequences holding private copies of it."""
+    rng = _rng(64)
+    L, Hkv, D, bs = 1, 1, 8, 4
+    prefix = rng.standard_normal((L, 1, Hkv, 8, D), dtype=np.float32)  # two full blocks
+    tails = rng.standard_normal((L, 2, Hkv, 3, D), dtype=np.float32)
+    hist = np.array([11, 11], np.int32)
+    N = 1
+    q = rng.standard_normal((L, 2, Hkv, N, D), dtype=np.float32)
+    k = rng.standard_normal((L, 2, Hkv, N, D), dtype=np.float32)
+    v = rng.standard_normal((L, 2, Hkv, N, D), dtype=np.float32)
+    outs = []
+    for shared in (True, False):
+        bt = np.array([[0, 1, 2], [0, 1, 3]], np.int32) if shared else \
+            np.array([[0, 1, 2], [4, 5, 3]], np.int32)
+        kp, vp = _paged_canary(L, 6, Hkv, bs, D)
+        both = np.ascontiguousarray(np.concatenate([prefix, prefix], axis=1))
+        oracle.paged_append(kp, vp, both, both * 0.5, np.zeros(2, np.int32), bt, lib=lib)
+        oracle.paged_append(kp, vp, tails, tails * 0.5, np.array([8, 8], np.int32), bt, lib=lib)
+        oracle.paged_append(kp, vp, k, v, hist, bt, lib=lib)
+        outs.append(oracle.paged_attention(q, kp, vp, hist, bt, 0.35, lib=lib))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def pin_paged_refusals(lib):
+    """Positions past the table row, or a block id outside the pool, are
+    refused and nothing is written."""
+    kp, vp = _paged_canary(1, 4, 1, 4, 4)
+    kn = np.ones((1, 1, 1, 2, 4), np.float32)
+    for hist, bt in ((np.array([7], np.int32), np.array([[0, 1]], np.int32)),     # 7 + 2 > 8
+                     (np.array([3], np.int32), np.array([[0, 4]], np.int32)),     # block 4 of 4
+                     (np.array([3], np.int32), np.array([[0, -1]], np.int32))):
+        try:
+            oracle.paged_append(kp, vp, kn, kn, hist, bt, lib=lib)
+            raise AssertionError(f"accepted hist={hist} table={bt}")
+        except oracle.OracleError:
+            pass
+        assert synth.is_canary(kp).all() and synth.is_canary(vp).all()
+
+
 ALL_PINS = [
     pin_cache_bytes_golden,
     pin_single_key_exact,
@@ -375,4 +532,9 @@ ALL_PINS = [
     pin_gqa_equals_repeated_mha,
     pin_append_positions_and_canaries,
     pin_bf16_decode_exact,
+    pin_paged_identity_is_contiguous,
+    pin_paged_block_permutation,
+    pin_paged_heads_are_independent,
+    pin_paged_shared_prefix,
+    pin_paged_refusals,
 ]

@@ -3,16 +3,40 @@
 Each mutant is a copy of oracle/kvc_oracle.c with one textual change (a
 dropped term, a wrong sign or index, a transposed operand, a wrong head
 mapping, an off-by-one in the mask or the append), compiled with gcc into a
-temporary directory.  The pins are then run against the mutant; the test
-fails if all of them still pass.  The real oracle is never modified.
+temporary directory.  The pins are then run against the mutant in a child
+process (a wrong index can write outside the test's arrays, which must not
+corrupt this process); the test fails if all of them still pass.  The real
+oracle is never modified.
 """
+import json
 import os
 import shutil
+import subprocess
+import sys
 
 import pytest
 
 import oracle
+
+TESTS = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(TESTS)
+
+# Runs every pin against the library named on the command line and prints
+# the names of the pins that tripped as one JSON line.
+RUN_PINS = """
+import json, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle
 from oracle_pins import ALL_PINS
+lib = oracle.load(sys.argv[1])
+caught = []
+for pin in ALL_PINS:
+    try:
+        pin(lib)
+    except (AssertionError, oracle.OracleError, ValueError, FloatingPointError):
+        caught.append(pin.__name__)
+print(json.dumps(caught), flush=True)
+""".format(root=ROOT, tests=TESTS)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "kvc_oracle.c")
@@ -47,6 +71,23 @@ MUTANTS = {
     "bf16_wrong_shift": ("uint32_t bits = (uint32_t)hi << 16;", "uint32_t bits = (uint32_t)hi << 15;"),
     # the size formula
     "size_formula_drops_kv_factor": ("return (uint64_t)(2 * layers *", "return (uint64_t)(1 * layers *"),
+    # the paged cache: block-table lookup, row inside the block, head, layer
+    "paged_append_block_from_offset": ("block_table[(size_t)b * max_blocks + t / block_size]",
+                                       "block_table[(size_t)b * max_blocks + t % block_size]"),
+    "paged_append_row_from_block_index": ("paged_row(layer0 + l, blk, h, t % block_size,",
+                                          "paged_row(layer0 + l, blk, h, t / block_size % block_size,"),
+    "paged_gather_row_off_by_one": ("paged_row(layer0 + l, blk, h, pos % block_size,",
+                                    "paged_row(layer0 + l, blk, h, (pos + 1) % block_size,"),
+    "paged_gather_ignores_layer0": ("paged_row(layer0 + l, blk, h, pos % block_size,",
+                                    "paged_row(l, blk, h, pos % block_size,"),
+    "paged_table_row_of_first_sequence": ("block_table[(size_t)b * max_blocks + pos / block_size]",
+                                          "block_table[pos / block_size]"),
+    "paged_ignores_head": ("((((size_t)l * num_blocks + blk) * Hkv + h)",
+                           "((((size_t)l * num_blocks + blk) * Hkv + 0)"),
+    "paged_head_and_row_swapped": ("((((size_t)l * num_blocks + blk) * Hkv + h) * (size_t)block_size +\n          (size_t)r)",
+                                   "((((size_t)l * num_blocks + blk) * (size_t)block_size + r) * Hkv +\n          (size_t)h)"),
+    "paged_capacity_unchecked": ("if (end > (int64_t)max_blocks * block_size) return ORACLE_E_CAPACITY;",
+                                 "if (end > (int64_t)max_blocks * block_size + block_size) return ORACLE_E_CAPACITY;"),
 }
 
 
@@ -66,11 +107,14 @@ def test_mutant_is_caught(name, source, tmp_path):
     src.write_text(source.replace(old, new))
     so = str(tmp_path / "libmutant.so")
     oracle.compile_library(str(src), so)
-    lib = oracle.load(so)
-    caught = []
-    for pin in ALL_PINS:
-        try:
-            pin(lib)
-        except (AssertionError, oracle.OracleError, ValueError, FloatingPointError):
-            caught.append(pin.__name__)
+    r = subprocess.run([sys.executable, "-c", RUN_PINS, so], capture_output=True, text=True,
+                       timeout=600, env=dict(os.environ, OMP_NUM_THREADS="2"))
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("[")]
+    if lines:
+        caught = json.loads(lines[-1])
+    else:
+        # the mutant crashed the child before the pins finished: a visible
+        # failure no correct oracle shows, so the mistake did not go unnoticed
+        assert r.returncode != 0, r.stderr[-2000:]
+        caught = [f"crash ({r.returncode})"]
     assert caught, f"planted mistake {name!r} passed every pin"
