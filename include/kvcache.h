@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -225,6 +225,75 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0,
                             int32_t n_layers, const void *q, const void *k,
                             const void *v, int32_t Hq, int32_t S, float scale,
                             void *o, void *stream);
+
+/*
+ * ---- paged cache ---------------------------------------------------------
+ * The cache as pools of fixed-size blocks shared by all sequences, each
+ * sequence owning a list of blocks (its block table).  [KV-2]
+ * "显存测量最容易被分配器误导" (production engines manage the cache in pages or
+ * blocks instead of concatenating) and [KV-4] "Decode 阶段" (the note after
+ * listing 1-2: real implementations write each step's K/V in place, slot by
+ * slot, with PagedAttention).  The pages give no layout; this one is:
+ *   k, v        : device, [L, num_blocks, Hkv, block_size, D] each, the
+ *                 cache dtype; a block holds block_size consecutive positions
+ *                 of every KV head of one layer
+ *   block_table : device int32 [B, max_blocks], caller-owned; position t of
+ *                 sequence b lives in row t % block_size of block
+ *                 block_table[b][t / block_size]
+ * block_size is a power of two in [1, 1024]; D in {64, 128}.  Sequences may
+ * share blocks (a common prefix); a call must not write a block that another
+ * sequence still reads.  The library cannot check the table's contents
+ * without a device sync: block ids outside [0, num_blocks) are clamped into
+ * the pools (wrong results, never an access outside them).  Everything else
+ * -- argument checks before any enqueue, hist_len on the host, no
+ * allocation, caller workspace, stream -- is as for the contiguous cache,
+ * with capacity max_blocks * block_size positions per sequence.
+ */
+typedef struct {
+  void *k, *v;          /* device pools [L, num_blocks, Hkv, block_size, D] */
+  int32_t L, num_blocks, Hkv, block_size, D;
+  int32_t dtype;        /* kvc_dtype */
+} kvc_paged_cache;
+
+/* 2 x L x num_blocks x Hkv x block_size x D x element size; 0 on bad input. */
+uint64_t kvc_paged_cache_bytes(int64_t L, int64_t num_blocks, int64_t Hkv,
+                               int64_t block_size, int64_t D, int32_t dtype);
+
+/* kvc_append into a paged cache: row i of k_new / v_new ([n_layers, B, Hkv,
+ * N, D]) goes to position hist_len[b] + i, i.e. its slot in the block the
+ * table names.  Positions past max_blocks * block_size: KVC_E_CAPACITY. */
+kvc_status kvc_paged_append(const kvc_paged_cache *cache, int32_t layer0,
+                            int32_t n_layers, const void *k_new,
+                            const void *v_new, int32_t B, int32_t N,
+                            const int32_t *hist_len,
+                            const int32_t *block_table, int32_t max_blocks,
+                            void *stream);
+
+/* Workspace bytes for the paged decode calls with these arguments. */
+size_t kvc_paged_decode_workspace_bytes(const kvc_paged_cache *cache,
+                                        int32_t n_layers, int32_t B, int32_t Hq,
+                                        int32_t N, int32_t max_blocks);
+
+/* kvc_attn_decode over a paged cache: keys 0 .. hist_len[b] + i of sequence
+ * b, read through its block table; q, o [n_layers, B, Hq, N, D]. */
+kvc_status kvc_paged_attn_decode(const kvc_paged_cache *cache, int32_t layer0,
+                                 int32_t n_layers, const void *q, int32_t Hq,
+                                 int32_t B, int32_t N, const int32_t *hist_len,
+                                 const int32_t *block_table, int32_t max_blocks,
+                                 float scale, void *o, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* kvc_decode_step over a paged cache: kvc_paged_append followed by
+ * kvc_paged_attn_decode, with the same results, in the same launches as
+ * kvc_decode_step. */
+kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0,
+                                 int32_t n_layers, const void *q,
+                                 const void *k_new, const void *v_new,
+                                 int32_t Hq, int32_t B, int32_t N,
+                                 const int32_t *hist_len,
+                                 const int32_t *block_table, int32_t max_blocks,
+                                 float scale, void *o, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvc_last_error(void);

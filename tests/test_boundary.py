@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 2
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 3
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -247,3 +247,67 @@ def test_workspace_size_is_length_independent(lib):
     assert 0 < small < big
     assert lib.kvc_decode_workspace_bytes(ctypes.byref(desc(h)), 2, 3, 1) == 0
     assert lib.kvc_decode_workspace_bytes(None, 2, 2, 1) == 0
+
+
+def pdesc(h, L=2, nblk=8, Hkv=2, bs=4, D=64, dtype=0):
+    return K.PagedCacheDesc(h.ptr().value, h.ptr().value, L, nblk, Hkv, bs, D, dtype)
+
+
+def test_paged_cache_bytes(lib):
+    assert lib.kvc_paged_cache_bytes(12, 64, 12, 16, 64, 0) == 2 * 12 * 64 * 12 * 16 * 64 * 4
+    assert lib.kvc_paged_cache_bytes(1, 1, 1, 1, 64, 1) == 256
+    assert lib.kvc_paged_cache_bytes(1, -1, 1, 1, 64, 0) == 0
+    assert lib.kvc_paged_cache_bytes(1, 1, 1, 1, 64, 5) == 0
+
+
+def test_paged_error_paths(lib):
+    h = Host()
+    d = pdesc(h)
+    bt = h.ptr()
+    q, o, kn = h.ptr(), h.ptr(), h.ptr()
+    need = lib.kvc_paged_decode_workspace_bytes(ctypes.byref(d), 2, 2, 4, 3, 4)
+    assert need > 0 and need % 256 == 0
+    ws = h.ptr(need)
+
+    def app(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, k=kn, v=kn, B=2, N=3, hist=hist(2, 5),
+                 bt=bt, mb=4)
+        a.update(kw)
+        return lib.kvc_paged_append(a["c"], a["layer0"], a["n_layers"], a["k"], a["v"], a["B"],
+                                    a["N"], a["hist"], a["bt"], a["mb"], None)
+
+    assert app(hist=hist(2, 14)) == E_CAPACITY            # 14 + 3 > 4 blocks x 4
+    assert "exceeds" in err(lib)
+    assert app(bt=None) == E_NULL
+    assert app(bt=h.ptr(offset=2)) == E_NULL              # misaligned table
+    assert app(c=ctypes.byref(pdesc(h, bs=6))) == E_SHAPE  # not a power of two
+    assert app(c=ctypes.byref(pdesc(h, bs=2048))) == E_SHAPE
+    assert app(c=ctypes.byref(pdesc(h, nblk=0))) == E_SHAPE
+    assert app(c=ctypes.byref(pdesc(h, D=96))) == E_UNSUPPORTED
+    assert app(c=None) == E_NULL
+    assert app(layer0=1) == E_SHAPE
+    assert app(N=0, k=None, v=None) == OK
+    assert app(B=0, hist=None, bt=None) == OK
+
+    def dec(step=False, **kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=q, Hq=4, B=2, N=3, hist=hist(2, 5),
+                 bt=bt, mb=4, scale=0.125, o=o, ws=ws, wsb=need)
+        a.update(kw)
+        if step:
+            return lib.kvc_paged_decode_step(a["c"], a["layer0"], a["n_layers"], a["q"], kn, kn,
+                                             a["Hq"], a["B"], a["N"], a["hist"], a["bt"], a["mb"],
+                                             a["scale"], a["o"], a["ws"], a["wsb"], None)
+        return lib.kvc_paged_attn_decode(a["c"], a["layer0"], a["n_layers"], a["q"], a["Hq"],
+                                         a["B"], a["N"], a["hist"], a["bt"], a["mb"], a["scale"],
+                                         a["o"], a["ws"], a["wsb"], None)
+
+    for step in (False, True):
+        assert dec(step, Hq=3) == E_SHAPE
+        assert dec(step, hist=hist(2, 15)) == E_CAPACITY
+        assert dec(step, bt=None) == E_NULL
+        assert dec(step, q=None) == E_NULL
+        assert dec(step, wsb=need - 256) == E_WORKSPACE
+        assert dec(step, scale=float("nan")) == E_SHAPE
+        assert dec(step, mb=-1) == E_SHAPE
+        assert dec(step, N=0, q=None, o=None, ws=None) == OK
+

@@ -99,23 +99,11 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
   return g;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
-
-const char *kvc_last_error(void) { return g_last_error; }
-
-uint64_t kvc_cache_bytes(int64_t L, int64_t B, int64_t Hkv, int64_t Tmax, int64_t D, int32_t dtype) {
-  if (L < 0 || B < 0 || Hkv < 0 || Tmax < 0 || D < 0) return 0;
-  if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
-  return (uint64_t)2 * L * Hkv * D * Tmax * B * elem_bytes(dtype);
-}
-
-kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *k_new,
-                      const void *v_new, int32_t N, const int32_t *hist_len, void *stream) {
-  static const char *fn = "kvc_append";
+// Shared by kvc_append and kvc_paged_append (pg.block_table set: `cache` is
+// the logical view of the pools, Tmax = max_blocks * block_size).
+kvc_status append_impl(const char *fn, const kvc_cache *cache, const kvc::PagedGeom &pg,
+                       int32_t layer0, int32_t n_layers, const void *k_new, const void *v_new,
+                       int32_t N, const int32_t *hist_len, void *stream) {
   kvc_status st = check_cache(cache, layer0, n_layers, fn);
   if (st != KVC_OK) return st;
   if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
@@ -138,6 +126,7 @@ kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers, 
   a.n_layers = n_layers;
   a.N = N;
   a.row_vec16 = cache->D * elem_bytes(cache->dtype) / 16;
+  a.pg = pg;
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
     a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
@@ -146,6 +135,47 @@ kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers, 
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
+}
+
+// A paged cache descriptor checked and turned into the logical view the
+// shared implementations take: B sequences of max_blocks * block_size
+// positions each, plus the block-table geometry.
+kvc_status paged_view(const kvc_paged_cache *pc, int32_t B, const int32_t *block_table,
+                      int32_t max_blocks, const char *fn, kvc_cache *view, kvc::PagedGeom *pg) {
+  if (!pc) return fail(KVC_E_NULL, "%s: cache descriptor is NULL", fn);
+  if (pc->num_blocks <= 0 || pc->block_size <= 0 || (pc->block_size & (pc->block_size - 1)) ||
+      pc->block_size > 1024)
+    return fail(KVC_E_SHAPE, "%s: num_blocks = %d must be > 0 and block_size = %d a power of two "
+                "in [1, 1024]", fn, pc->num_blocks, pc->block_size);
+  if (B < 0 || max_blocks < 0 || (int64_t)max_blocks * pc->block_size > 2147483647LL)
+    return fail(KVC_E_SHAPE, "%s: B = %d, max_blocks = %d", fn, B, max_blocks);
+  if (B > 0 && max_blocks > 0 && (!block_table || ((uintptr_t)block_table & 3u)))
+    return fail(KVC_E_NULL, "%s: block_table is NULL or misaligned", fn);
+  *view = kvc_cache{pc->k, pc->v, pc->L, B, pc->Hkv, max_blocks * pc->block_size, pc->D, pc->dtype};
+  int log2 = 0;
+  while ((1 << log2) < pc->block_size) ++log2;
+  *pg = kvc::PagedGeom{block_table, max_blocks, pc->num_blocks, log2};
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char *kvc_last_error(void) { return g_last_error; }
+
+uint64_t kvc_cache_bytes(int64_t L, int64_t B, int64_t Hkv, int64_t Tmax, int64_t D, int32_t dtype) {
+  if (L < 0 || B < 0 || Hkv < 0 || Tmax < 0 || D < 0) return 0;
+  if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
+  return (uint64_t)2 * L * Hkv * D * Tmax * B * elem_bytes(dtype);
+}
+
+kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *k_new,
+                      const void *v_new, int32_t N, const int32_t *hist_len, void *stream) {
+  return append_impl("kvc_append", cache, kvc::PagedGeom{}, layer0, n_layers, k_new, v_new, N,
+                     hist_len, stream);
 }
 
 size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers, int32_t Hq, int32_t N) {
@@ -164,10 +194,11 @@ enum Phases { kSplit = 1, kCombine = 2, kBoth = 3 };
 
 // Shared by kvc_attn_decode, kvc_decode_step (fused: k_new / v_new given),
 // kvc_decode_split and kvc_decode_combine.
-kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32_t layer0,
-                       int32_t n_layers, const void *q, const void *k_new, const void *v_new,
-                       bool fused, int32_t Hq, int32_t N, const int32_t *hist_len, float scale,
-                       void *o, void *workspace, size_t workspace_bytes, void *stream) {
+kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
+                       const kvc::PagedGeom &pg, int32_t layer0, int32_t n_layers, const void *q,
+                       const void *k_new, const void *v_new, bool fused, int32_t Hq, int32_t N,
+                       const int32_t *hist_len, float scale, void *o, void *workspace,
+                       size_t workspace_bytes, void *stream) {
   kvc_status st = check_cache(cache, layer0, n_layers, fn);
   if (st != KVC_OK) return st;
   if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
@@ -223,6 +254,7 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache, int32
   // adds key P (from k_new / v_new in the fused step, which it then writes to
   // the cache, else from the cache), so both forms do the same arithmetic.
   a.tail = g.mfma ? 0 : 1;
+  a.pg = pg;
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
     a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
@@ -252,7 +284,7 @@ extern "C" {
 kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,
                            int32_t Hq, int32_t N, const int32_t *hist_len, float scale, void *o,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_impl("kvc_attn_decode", kBoth, cache, layer0, n_layers, q, nullptr, nullptr, false,
+  return decode_impl("kvc_attn_decode", kBoth, cache, kvc::PagedGeom{}, layer0, n_layers, q, nullptr, nullptr, false,
                      Hq, N, hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
@@ -260,7 +292,7 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0, int32_t n_lay
                            const void *k_new, const void *v_new, int32_t Hq, int32_t N,
                            const int32_t *hist_len, float scale, void *o, void *workspace,
                            size_t workspace_bytes, void *stream) {
-  return decode_impl("kvc_decode_step", kBoth, cache, layer0, n_layers, q, k_new, v_new, true, Hq,
+  return decode_impl("kvc_decode_step", kBoth, cache, kvc::PagedGeom{}, layer0, n_layers, q, k_new, v_new, true, Hq,
                      N, hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
@@ -270,7 +302,7 @@ kvc_status kvc_decode_split(const kvc_cache *cache, int32_t layer0, int32_t n_la
                             size_t workspace_bytes, void *stream) {
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(KVC_E_NULL, "kvc_decode_split: k_new and v_new must both be given or both NULL");
-  return decode_impl("kvc_decode_split", kSplit, cache, layer0, n_layers, q, k_new, v_new,
+  return decode_impl("kvc_decode_split", kSplit, cache, kvc::PagedGeom{}, layer0, n_layers, q, k_new, v_new,
                      k_new != nullptr, Hq, N, hist_len, scale, o, workspace, workspace_bytes,
                      stream);
 }
@@ -281,7 +313,7 @@ kvc_status kvc_decode_combine(const kvc_cache *cache, int32_t layer0, int32_t n_
                               void *workspace, size_t workspace_bytes, void *stream) {
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(KVC_E_NULL, "kvc_decode_combine: k_new and v_new must both be given or both NULL");
-  return decode_impl("kvc_decode_combine", kCombine, cache, layer0, n_layers, q, k_new, v_new,
+  return decode_impl("kvc_decode_combine", kCombine, cache, kvc::PagedGeom{}, layer0, n_layers, q, k_new, v_new,
                      k_new != nullptr, Hq, N, hist_len, scale, o, workspace, workspace_bytes,
                      stream);
 }
@@ -324,6 +356,69 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_la
   a.q_tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(kvc::launch_prefill(a, cache->dtype, cache->D, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"
+
+// ---- paged cache -----------------------------------------------------------
+
+extern "C" {
+
+uint64_t kvc_paged_cache_bytes(int64_t L, int64_t num_blocks, int64_t Hkv, int64_t block_size,
+                               int64_t D, int32_t dtype) {
+  if (L < 0 || num_blocks < 0 || Hkv < 0 || block_size < 0 || D < 0) return 0;
+  if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
+  return (uint64_t)2 * L * num_blocks * Hkv * block_size * D * elem_bytes(dtype);
+}
+
+kvc_status kvc_paged_append(const kvc_paged_cache *cache, int32_t layer0, int32_t n_layers,
+                            const void *k_new, const void *v_new, int32_t B, int32_t N,
+                            const int32_t *hist_len, const int32_t *block_table,
+                            int32_t max_blocks, void *stream) {
+  static const char *fn = "kvc_paged_append";
+  kvc_cache view;
+  kvc::PagedGeom pg;
+  kvc_status st = paged_view(cache, B, block_table, max_blocks, fn, &view, &pg);
+  if (st != KVC_OK) return st;
+  return append_impl(fn, &view, pg, layer0, n_layers, k_new, v_new, N, hist_len, stream);
+}
+
+size_t kvc_paged_decode_workspace_bytes(const kvc_paged_cache *cache, int32_t n_layers, int32_t B,
+                                        int32_t Hq, int32_t N, int32_t max_blocks) {
+  if (!cache || cache->block_size <= 0 || B < 0 || max_blocks < 0 ||
+      (int64_t)max_blocks * cache->block_size > 2147483647LL)
+    return 0;
+  const kvc_cache view{cache->k, cache->v, cache->L, B, cache->Hkv,
+                       max_blocks * cache->block_size, cache->D, cache->dtype};
+  return kvc_decode_workspace_bytes(&view, n_layers, Hq, N);
+}
+
+kvc_status kvc_paged_attn_decode(const kvc_paged_cache *cache, int32_t layer0, int32_t n_layers,
+                                 const void *q, int32_t Hq, int32_t B, int32_t N,
+                                 const int32_t *hist_len, const int32_t *block_table,
+                                 int32_t max_blocks, float scale, void *o, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  static const char *fn = "kvc_paged_attn_decode";
+  kvc_cache view;
+  kvc::PagedGeom pg;
+  kvc_status st = paged_view(cache, B, block_table, max_blocks, fn, &view, &pg);
+  if (st != KVC_OK) return st;
+  return decode_impl(fn, kBoth, &view, pg, layer0, n_layers, q, nullptr, nullptr, false, Hq, N,
+                     hist_len, scale, o, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0, int32_t n_layers,
+                                 const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                                 int32_t B, int32_t N, const int32_t *hist_len,
+                                 const int32_t *block_table, int32_t max_blocks, float scale,
+                                 void *o, void *workspace, size_t workspace_bytes, void *stream) {
+  static const char *fn = "kvc_paged_decode_step";
+  kvc_cache view;
+  kvc::PagedGeom pg;
+  kvc_status st = paged_view(cache, B, block_table, max_blocks, fn, &view, &pg);
+  if (st != KVC_OK) return st;
+  return decode_impl(fn, kBoth, &view, pg, layer0, n_layers, q, k_new, v_new, true, Hq, N,
+                     hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -6,7 +6,9 @@
 // new rows into their slots in place instead of concatenating.  Here the
 // cache is allocated once at Tmax rows and a step writes rows
 // [P_b, P_b + N) of each (layer, sequence, KV head): a pure byte copy, so it is
-// bit-exact for every element type.
+// bit-exact for every element type.  For a paged cache (pools of fixed-size
+// blocks and a per-sequence block table) each row goes to its slot, row
+// t % block_size of block block_table[b][t / block_size].
 //
 // Roofline: HBM, 2 x rows x D x elem bytes read and the same written.
 #include "kvc_internal.h"
@@ -28,9 +30,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, long long tot
     const int l = (int)(r / a.nb);
     const int b = a.b0 + bb;
     const long long src = ((((long long)l * a.B + b) * a.Hkv + h) * a.N + i) * a.row_vec16 + c;
-    const long long dst =
-        ((((long long)(a.layer0 + l) * a.B + b) * a.Hkv + h) * a.Tmax + (a.hist[bb] + i)) *
-            a.row_vec16 + c;
+    const int t_pos = a.hist[bb] + i;
+    const long long row =
+        a.pg.block_table
+            ? (long long)paged_row(a.pg, b, t_pos, a.layer0 + l, h, a.Hkv)
+            : (((long long)(a.layer0 + l) * a.B + b) * a.Hkv + h) * a.Tmax + t_pos;
+    const long long dst = row * a.row_vec16 + c;
     const u32x4 kv = reinterpret_cast<const u32x4 *>(a.k_new)[src];
     const u32x4 vv = reinterpret_cast<const u32x4 *>(a.v_new)[src];
     reinterpret_cast<u32x4 *>(a.k_cache)[dst] = kv;

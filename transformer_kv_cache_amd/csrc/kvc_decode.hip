@@ -117,7 +117,7 @@ __device__ __forceinline__ float rescale(float m, float M) {
   return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
-template <int DT, int D, int KPL>
+template <int DT, int D, int KPL, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
   constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
@@ -171,14 +171,30 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // 1. Issue the query load and every K and V load of this split up front.
   //    Keys past the last visible one are clamped to it (a valid, written
   //    slot) so that no load sits behind a branch; their scores are masked.
+  //    A paged cache first looks up each key's block (one load per key, all
+  //    issued together), then streams the rows from their blocks.
   const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
   u32x4 kw[KPL], vw[KPL];
+  if constexpr (PAGED) {
+    size_t prow[KPL];
 #pragma unroll
-  for (int kk = 0; kk < KPL; ++kk) {
-    const int kr = kk * NRG + rg;  // key offset within the split
-    const uint32_t off = (uint32_t)((key0 + (kr < last ? kr : last)) * LPR + c) * 16u;
-    kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(kc + off));
-    vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off));
+    for (int kk = 0; kk < KPL; ++kk) {
+      const int kr = kk * NRG + rg;
+      prow[kk] = paged_row(a.pg, b, key0 + (kr < last ? kr : last), layer0 + l, hkv, Hkv);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(k_cache) + prow[kk] * LPR + c);
+      vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(v_cache) + prow[kk] * LPR + c);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      const int kr = kk * NRG + rg;  // key offset within the split
+      const uint32_t off = (uint32_t)((key0 + (kr < last ? kr : last)) * LPR + c) * 16u;
+      kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(kc + off));
+      vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off));
+    }
   }
   // Keep the scheduler from interleaving arithmetic (and its waits) into the
   // load burst: all loads of the split are in flight before the first wait.
@@ -341,7 +357,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   // Cache slot P of this row's (layer, sequence, KV head); rows are
   // (l, b, hkv) in tail mode (G = N = 1), so q, k_new and v_new share the
   // row index.
-  const size_t slot = ((((size_t)(layer0 + l) * B + b) * Hkv + rloc) * Tmax + P) * D;
+  const size_t slot = (a.pg.block_table ? paged_row(a.pg, b, P, layer0 + l, rloc, Hkv)
+                                         : (((size_t)(layer0 + l) * B + b) * Hkv + rloc) * Tmax + P) *
+                      D;
   const bool fused = knp != nullptr;
 
   // Splits in chunks of CH, every load of a chunk issued before any is used
@@ -444,7 +462,10 @@ constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
 template <int DT, int D>
 hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
-  hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane>), grid, dim3(256), 0, s, a);
+  if (a.pg.block_table)
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

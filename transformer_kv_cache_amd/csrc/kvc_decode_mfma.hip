@@ -65,7 +65,7 @@ __device__ __forceinline__ int vec_index(int j, int g) {
 }
 
 // KPW keys per wave (a multiple of 16), RM = 16 query rows per workgroup.
-template <int DT, int D, int KPW, bool FUSED>
+template <int DT, int D, int KPW, bool FUSED, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int EB = Dtype<DT>::kBytes;
   constexpr int EV = Dtype<DT>::kPer16B;   // elements per 16-byte vector
@@ -121,14 +121,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   }
   const int keyw = split * SPLIT + wave * KPW;  // first key of this wave
   u32x4 kw[NB][J], vw[NB][J];
+  // Paged cache: each key's row index in the pools, looked up through the
+  // block table (all lookups issued before any K/V load).
+  size_t prow[NB];
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int key = keyw + 16 * nb + c16;
+      prow[nb] = paged_row(a.pg, b, key < nkeys ? key : nkeys - 1, a.layer0 + l, hkv, a.Hkv);
+    }
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int key = keyw + 16 * nb + c16;
     const int kidx = key < nkeys ? key : nkeys - 1;
     const bool fresh = FUSED && kidx >= P;
     const size_t nidx = (size_t)(fresh ? kidx - P : 0);
-    const u32x4 *kp = fresh ? kn + nidx * LPR : kc + (size_t)kidx * LPR;
-    const u32x4 *vp = fresh ? vn + nidx * LPR : vc + (size_t)kidx * LPR;
+    const size_t crow = PAGED ? prow[nb] : (size_t)kidx;  // row within the K/V base below
+    const u32x4 *kbase = PAGED ? reinterpret_cast<const u32x4 *>(a.k_cache) : kc;
+    const u32x4 *vbase = PAGED ? reinterpret_cast<const u32x4 *>(a.v_cache) : vc;
+    const u32x4 *kp = fresh ? kn + nidx * LPR : kbase + crow * LPR;
+    const u32x4 *vp = fresh ? vn + nidx * LPR : vbase + crow * LPR;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       kw[nb][j] = stream_load(kp + vec_index<J>(j, g));
@@ -140,16 +153,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // Fused step: row tile 0 writes the new rows it read from k_new / v_new.
   if constexpr (FUSED) {
     if (rt == 0) {
-      u32x4 *kd = reinterpret_cast<u32x4 *>(a.k_cache) + crow0 * LPR;
-      u32x4 *vd = reinterpret_cast<u32x4 *>(a.v_cache) + crow0 * LPR;
+      u32x4 *kd = reinterpret_cast<u32x4 *>(a.k_cache) + (PAGED ? 0 : crow0 * LPR);
+      u32x4 *vd = reinterpret_cast<u32x4 *>(a.v_cache) + (PAGED ? 0 : crow0 * LPR);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int key = keyw + 16 * nb + c16;
         if (key >= P && key < nkeys) {
+          const size_t drow = PAGED ? prow[nb] : (size_t)key;
 #pragma unroll
           for (int j = 0; j < J; ++j) {
-            kd[(size_t)key * LPR + vec_index<J>(j, g)] = kw[nb][j];
-            vd[(size_t)key * LPR + vec_index<J>(j, g)] = vw[nb][j];
+            kd[drow * LPR + vec_index<J>(j, g)] = kw[nb][j];
+            vd[drow * LPR + vec_index<J>(j, g)] = vw[nb][j];
           }
         }
       }
@@ -277,10 +291,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 template <int DT, int D, int KPW>
 hipError_t launch_kpw(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv * a.row_tiles), (unsigned)a.nb);
-  if (fused)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true>), grid, dim3(256), 0, s, a);
+  const bool paged = a.pg.block_table != nullptr;
+  if (fused && paged)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, true>), grid, dim3(256), 0, s, a);
+  else if (fused)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, false>), grid, dim3(256), 0, s, a);
+  else if (paged)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

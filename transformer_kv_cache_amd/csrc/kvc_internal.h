@@ -67,6 +67,27 @@ __device__ __forceinline__ void store_elems<KVC_BF16>(void *base, size_t index, 
 
 // ---- launch descriptors (passed by value as kernel arguments) -------------
 
+// Paged cache geometry: K and V are pools [L][num_blocks][Hkv][block_size][D]
+// and position t of sequence b is row t % block_size of block
+// block_table[b][t / block_size].  block_table == nullptr for the contiguous
+// [L][B][Hkv][Tmax][D] cache.
+struct PagedGeom {
+  const int32_t *block_table;  // device, [B][max_blocks]
+  int32_t max_blocks, num_blocks, bs_log2;
+};
+
+// Row index (in rows of D elements) of position t of sequence b, KV head h,
+// layer `layer` of a paged pool.  Block ids outside [0, num_blocks) are
+// clamped, so a bad table can give wrong results but never reads or writes
+// outside the pools.
+__device__ __forceinline__ size_t paged_row(const PagedGeom &p, int b, int t, int layer, int h,
+                                            int Hkv) {
+  int blk = p.block_table[(size_t)b * p.max_blocks + (t >> p.bs_log2)];
+  blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+  return ((((size_t)layer * p.num_blocks + blk) * Hkv + h) << p.bs_log2) +
+         (size_t)(t & ((1 << p.bs_log2) - 1));
+}
+
 struct AppendArgs {
   char *k_cache, *v_cache;
   const char *k_new, *v_new;
@@ -74,6 +95,7 @@ struct AppendArgs {
   int32_t layer0, n_layers, N;
   int32_t b0, nb;       // batch slice [b0, b0+nb) of this launch
   int32_t row_vec16;    // 16-byte vectors per row (D * elem / 16)
+  PagedGeom pg;         // paged cache, else block_table == nullptr
   int32_t hist[kMaxBatchPerLaunch];
 };
 
@@ -97,6 +119,7 @@ struct DecodeArgs {
   uint32_t split_div;  // div_magic multiplier for split_keys
   int32_t tail;        // 1 (vector kernel): the split states cover keys
                        // [0, P) and the combine adds key P
+  PagedGeom pg;        // paged cache, else block_table == nullptr
   int32_t hist[kMaxBatchPerLaunch];
 };
 

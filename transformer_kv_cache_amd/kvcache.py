@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 2  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 3  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -47,6 +47,13 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("L", ctypes.c_int32), ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("Tmax", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class PagedCacheDesc(ctypes.Structure):
+    """Mirror of ``kvc_paged_cache``."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("L", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,6 +99,20 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_combine.restype = i32
         lib.kvc_attn_prefill.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
         lib.kvc_attn_prefill.restype = i32
+        pp = ctypes.POINTER(PagedCacheDesc)
+        f32 = ctypes.c_float
+        lib.kvc_paged_cache_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+        lib.kvc_paged_cache_bytes.restype = ctypes.c_uint64
+        lib.kvc_paged_append.argtypes = [pp, i32, i32, vp, vp, i32, i32, ip, vp, i32, vp]
+        lib.kvc_paged_append.restype = i32
+        lib.kvc_paged_decode_workspace_bytes.argtypes = [pp, i32, i32, i32, i32, i32]
+        lib.kvc_paged_decode_workspace_bytes.restype = sz
+        lib.kvc_paged_attn_decode.argtypes = [pp, i32, i32, vp, i32, i32, i32, ip, vp, i32, f32, vp,
+                                              vp, sz, vp]
+        lib.kvc_paged_attn_decode.restype = i32
+        lib.kvc_paged_decode_step.argtypes = [pp, i32, i32, vp, vp, vp, i32, i32, i32, ip, vp, i32,
+                                              f32, vp, vp, sz, vp]
+        lib.kvc_paged_decode_step.restype = i32
         if path is None:
             _lib = lib
     return lib
@@ -191,14 +212,22 @@ def new_decode_workspace(cache: KVCache, n_layers: int, Hq: int, N: int) -> torc
 _ws_cache: dict = {}
 
 
-def _default_workspace(cache, n_layers, Hq, N, stream):
+def _aligned_workspace(nbytes, device):
+    n = max(int(nbytes), 256)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def _default_workspace(cache, n_layers, Hq, N, stream, need=None):
     """One growing scratch workspace per (device, stream): calls on one
     stream run one after another, so they can share it."""
-    need = decode_workspace_bytes(cache, n_layers, Hq, N)
+    if need is None:
+        need = decode_workspace_bytes(cache, n_layers, Hq, N)
     key = (cache.device, int(_stream(cache.device, stream).value or 0))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = new_decode_workspace(cache, n_layers, Hq, N)
+        ws = _aligned_workspace(need, cache.device)
         _ws_cache[key] = ws
     return ws
 
@@ -322,3 +351,131 @@ def attn_prefill(cache: KVCache, q, k, v, scale: float | None = None, out=None,
         ctypes.byref(d), layer0, n_layers, q.data_ptr(), k.data_ptr(), v.data_ptr(), Hq, S,
         float(scale), out.data_ptr(), _stream(cache.device, stream)))
     return out
+
+
+# ---- paged cache ------------------------------------------------------------
+
+def paged_cache_bytes(L, num_blocks, Hkv, block_size, D, dtype=torch.float32) -> int:
+    """2 x L x num_blocks x Hkv x block_size x D x element size."""
+    return int(library().kvc_paged_cache_bytes(L, num_blocks, Hkv, block_size, D,
+                                               _DTYPE_CODE[dtype]))
+
+
+class PagedKVCache:
+    """Block pools ``k``, ``v`` of shape [L, num_blocks, Hkv, block_size, D]
+    on one GPU, shared by all sequences; each call takes the sequences'
+    block table (int32 [B, max_blocks] on the same device): position t of
+    sequence b is row t % block_size of block block_table[b, t // block_size]."""
+
+    def __init__(self, L, num_blocks, Hkv, block_size, D, dtype=torch.float32, device="cuda",
+                 k=None, v=None):
+        if dtype not in _DTYPE_CODE:
+            raise TypeError(f"unsupported cache dtype {dtype}")
+        shape = (L, num_blocks, Hkv, block_size, D)
+        self.k = k if k is not None else torch.empty(shape, dtype=dtype, device=device)
+        self.v = v if v is not None else torch.empty(shape, dtype=dtype, device=device)
+        for t in (self.k, self.v):
+            if tuple(t.shape) != shape or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("pool tensors must be contiguous CUDA tensors of shape "
+                                 f"{shape} and dtype {dtype}")
+        self.L, self.num_blocks, self.Hkv, self.block_size, self.D = L, num_blocks, Hkv, block_size, D
+        self.dtype = dtype
+
+    @property
+    def device(self):
+        return self.k.device
+
+    def desc(self) -> PagedCacheDesc:
+        return PagedCacheDesc(self.k.data_ptr(), self.v.data_ptr(), self.L, self.num_blocks,
+                              self.Hkv, self.block_size, self.D, _DTYPE_CODE[self.dtype])
+
+
+def _check_table(cache, block_table):
+    if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32
+            or block_table.device != cache.device or block_table.dim() != 2
+            or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 [B, max_blocks] tensor on "
+                         f"{cache.device}")
+    return block_table.shape[0], block_table.shape[1]
+
+
+def paged_append(cache: PagedKVCache, k_new, v_new, hist_len, block_table, layer0: int = 0,
+                 stream=None) -> None:
+    """Write k_new/v_new ([n_layers,B,Hkv,N,D]) at positions hist_len[b] ..
+    of each sequence, into the slots its block table names."""
+    B, mb = _check_table(cache, block_table)
+    n_layers, _, _, N, _ = k_new.shape
+    shape = (n_layers, B, cache.Hkv, N, cache.D)
+    _check_tensor("k_new", k_new, cache, shape)
+    _check_tensor("v_new", v_new, cache, shape)
+    _, hp = _hist(hist_len, B)
+    d = cache.desc()
+    _check(library().kvc_paged_append(ctypes.byref(d), layer0, n_layers, k_new.data_ptr(),
+                                      v_new.data_ptr(), B, N, hp, block_table.data_ptr(), mb,
+                                      _stream(cache.device, stream)))
+
+
+def paged_decode_workspace_bytes(cache: PagedKVCache, n_layers, B, Hq, N, max_blocks) -> int:
+    d = cache.desc()
+    return int(library().kvc_paged_decode_workspace_bytes(ctypes.byref(d), n_layers, B, Hq, N,
+                                                          max_blocks))
+
+
+def new_paged_decode_workspace(cache: PagedKVCache, n_layers, B, Hq, N, max_blocks):
+    return _aligned_workspace(paged_decode_workspace_bytes(cache, n_layers, B, Hq, N, max_blocks),
+                              cache.device)
+
+
+def _paged_decode(fn_name, cache, q, k_new, v_new, hist_len, block_table, scale, out, layer0,
+                  workspace, stream):
+    B, mb = _check_table(cache, block_table)
+    n_layers, _, Hq, N, _ = q.shape
+    shape = (n_layers, B, Hq, N, cache.D)
+    _check_tensor("q", q, cache, shape)
+    if k_new is not None:
+        kshape = (n_layers, B, cache.Hkv, N, cache.D)
+        _check_tensor("k_new", k_new, cache, kshape)
+        _check_tensor("v_new", v_new, cache, kshape)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, B)
+    if workspace is None:
+        need = paged_decode_workspace_bytes(cache, n_layers, B, Hq, N, mb)
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream, need=need)
+    if workspace.device != cache.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the cache's device")
+    d = cache.desc()
+    lib = library()
+    wsb = workspace.numel() * workspace.element_size()
+    st = _stream(cache.device, stream)
+    if k_new is None:
+        status = lib.kvc_paged_attn_decode(ctypes.byref(d), layer0, n_layers, q.data_ptr(), Hq, B,
+                                           N, hp, block_table.data_ptr(), mb, float(scale),
+                                           out.data_ptr(), workspace.data_ptr(), wsb, st)
+    else:
+        status = lib.kvc_paged_decode_step(ctypes.byref(d), layer0, n_layers, q.data_ptr(),
+                                           k_new.data_ptr(), v_new.data_ptr(), Hq, B, N, hp,
+                                           block_table.data_ptr(), mb, float(scale),
+                                           out.data_ptr(), workspace.data_ptr(), wsb, st)
+    _check(status)
+    return out
+
+
+def paged_attn_decode(cache: PagedKVCache, q, hist_len, block_table, scale: float | None = None,
+                      out=None, layer0: int = 0, workspace=None, stream=None):
+    """attn_decode over a paged cache (the N new rows already appended)."""
+    return _paged_decode("attn", cache, q, None, None, hist_len, block_table, scale, out, layer0,
+                         workspace, stream)
+
+
+def paged_decode_step(cache: PagedKVCache, q, k_new, v_new, hist_len, block_table,
+                      scale: float | None = None, out=None, layer0: int = 0, workspace=None,
+                      stream=None):
+    """paged_append + paged_attn_decode in the decode step's launches."""
+    if k_new is None or v_new is None:
+        raise ValueError("paged_decode_step needs k_new and v_new")
+    return _paged_decode("step", cache, q, k_new, v_new, hist_len, block_table, scale, out, layer0,
+                         workspace, stream)

@@ -191,3 +191,87 @@ def batched_decode(seed=0, gqa=False, B=8, L=12) -> Workload:
     return make_workload("batched_decode_mha", seed=seed, dtype="bf16", L=L, B=B,
                          Hq=12, Hkv=12, D=64, Tmax=1024, draw_lengths=(1, 1024),
                          step_lens=(1,))
+
+
+# ---- paged cache inputs -----------------------------------------------------
+
+@dataclass
+class PagedWorkload:
+    """Seeded inputs for a paged cache: pools ``k_pool``/``v_pool`` of shape
+    ``[L, num_blocks, Hkv, block_size, D]`` and a block table ``int32[B,
+    max_blocks]``.  Every block a table names holds N(0,1) rows; the blocks no
+    table names hold the canary.  Which rows make up a sequence's history is
+    up to the code under test -- this module only draws bytes and block ids.
+    ``steps`` as in ``Workload``."""
+    name: str
+    dtype: str
+    L: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    block_size: int
+    num_blocks: int
+    max_blocks: int
+    hist: np.ndarray
+    block_table: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    steps: list = field(default_factory=list)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+def make_paged_workload(name, *, seed, dtype, L, B, Hq, Hkv, D, block_size, max_blocks,
+                        hist=None, step_lens=(1,), draw_lengths=None, spare_blocks=7,
+                        shared_prefix_blocks=0) -> PagedWorkload:
+    """Each sequence gets ``max_blocks`` distinct blocks drawn from a shuffled
+    pool of ``B * max_blocks + spare_blocks`` (the first
+    ``shared_prefix_blocks`` entries of every row are the same blocks, as for
+    a common prompt).  ``hist``/``draw_lengths`` as in ``make_workload``."""
+    rng = np.random.default_rng(seed)
+    if draw_lengths is not None:
+        lo, hi = draw_lengths
+        hist = (rng.integers(lo, hi + 1, size=B) - 1).astype(np.int32)
+    elif hist is None:
+        hist = np.zeros(B, dtype=np.int32)
+    hist = np.asarray(hist, dtype=np.int32).copy()
+    if hist.shape != (B,):
+        hist = np.full(B, int(hist.reshape(-1)[0]), dtype=np.int32)
+    sp = shared_prefix_blocks
+    num_blocks = sp + B * (max_blocks - sp) + spare_blocks
+    ids = rng.permutation(num_blocks).astype(np.int32)
+    table = np.empty((B, max_blocks), np.int32)
+    table[:, :sp] = ids[:sp]
+    table[:, sp:] = ids[sp:sp + B * (max_blocks - sp)].reshape(B, max_blocks - sp)
+    shape = (L, num_blocks, Hkv, block_size, D)
+    kp = canary_cache(shape, dtype)
+    vp = canary_cache(shape, dtype)
+    used = np.unique(table)
+    kp[:, used] = as_dtype(_normal(rng, (L, used.size, Hkv, block_size, D)), dtype)
+    vp[:, used] = as_dtype(_normal(rng, (L, used.size, Hkv, block_size, D)), dtype)
+    steps = [tuple(as_dtype(_normal(rng, (L, B, H, n, D)), dtype) for H in (Hq, Hkv, Hkv))
+             for n in step_lens]
+    return PagedWorkload(name, dtype, L, B, Hq, Hkv, D, block_size, num_blocks, max_blocks,
+                         hist, table, kp, vp, steps)
+
+
+def paged_decode_12layer(P, block_size=16, seed=0, dtype="f32", N=1) -> PagedWorkload:
+    """The 12-layer decode workload (B=1, H=12, D=64, 1024 positions) on a
+    paged cache of ``block_size``-position blocks."""
+    return make_paged_workload(f"paged_decode_12layer_P{P}_bs{block_size}_N{N}", seed=seed,
+                               dtype=dtype, L=12, B=1, Hq=12, Hkv=12, D=64,
+                               block_size=block_size, max_blocks=1024 // block_size, hist=[P],
+                               step_lens=(N,))
+
+
+def paged_batched_decode(seed=0, gqa=False, block_size=16, B=8, L=12) -> PagedWorkload:
+    """The batched bf16 decode workload (visible keys U[1, 1024]) on a paged
+    cache; MHA (H=12, D=64) or GQA (32 query heads, 8 KV heads, D=128)."""
+    Hq, Hkv, D = (32, 8, 128) if gqa else (12, 12, 64)
+    return make_paged_workload(f"paged_batched_{'gqa' if gqa else 'mha'}_bs{block_size}",
+                               seed=seed, dtype="bf16", L=L, B=B, Hq=Hq, Hkv=Hkv, D=D,
+                               block_size=block_size, max_blocks=1024 // block_size,
+                               draw_lengths=(1, 1024))
