@@ -239,6 +239,44 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     return res
 
 
+def bench_paged_decode(torch, K, w, steps, warmup, rotate):
+    """Time the paged decode step of paged workload `w` (one step of N rows),
+    pools and inputs rotated over `rotate` replicas like bench_decode."""
+    from gpu_common import to_dev, torch_dtype
+    q_np, k_np, v_np = w.steps[0]
+    N = q_np.shape[3]
+    dt = torch_dtype(w.dtype)
+    base_k, base_v = to_dev(w.k_pool), to_dev(w.v_pool)
+    caches = [K.PagedKVCache(w.L, w.num_blocks, w.Hkv, w.block_size, w.D, dt, k=kk, v=vv)
+              for kk, vv in zip(replicate(torch, base_k, rotate), replicate(torch, base_v, rotate))]
+    qs = replicate(torch, to_dev(q_np), rotate)
+    kns = replicate(torch, to_dev(k_np), rotate)
+    vns = replicate(torch, to_dev(v_np), rotate)
+    bt = torch.from_numpy(w.block_table).cuda()
+    outs = [torch.empty_like(qs[0]) for _ in range(rotate)]
+    wss = [K.new_paged_decode_workspace(caches[0], w.L, w.B, w.Hq, N, w.max_blocks)
+           for _ in range(rotate)]
+    hist = w.hist.copy()
+
+    def step(r):
+        K.paged_decode_step(caches[r], qs[r], kns[r], vns[r], hist, bt, scale=w.scale,
+                            out=outs[r], workspace=wss[r])
+
+    for i in range(warmup):
+        step(i % rotate)
+    torch.cuda.synchronize()
+    res = {"step_us": GraphTimer(torch, step, rotate).time(steps)}
+    # algorithmic bytes as for the contiguous step, plus the block-table reads
+    e = elem_bytes(w.dtype)
+    kv = 2 * w.L * w.Hkv * w.D * e * int(np.sum(w.hist + N))
+    qo = 2 * w.L * w.B * w.Hq * N * w.D * e
+    new_rows = 2 * w.L * w.B * w.Hkv * N * w.D * e
+    res["step_bytes"] = kv + qo + new_rows
+    res["step_gbs"] = res["step_bytes"] / res["step_us"] / 1e3
+    res["block_size"] = w.block_size
+    return res
+
+
 def bench_prefill(torch, K, S, dtype, reps, rotate=4):
     from gpu_common import to_dev, torch_dtype
     from transformer_kv_cache_amd import synth
@@ -367,6 +405,21 @@ def main():
             r = {k: round(v, 3) for k, v in r.items()}
             r["lengths"] = (wb.hist + 1).tolist()
             extras[name] = r
+        paged = {}
+        for bs in (16, 64):
+            log(f"paged decode 12-layer fp32 T=1024, block size {bs}")
+            r = bench_paged_decode(torch, K, synth.paged_decode_12layer(1023, block_size=bs),
+                                   args.steps, args.warmup, args.rotate)
+            paged[f"fp32_12layer_T1024_bs{bs}"] = {k: round(v, 3) for k, v in r.items()}
+        for gqa in (False, True):
+            name = "bf16_" + ("gqa32q8kv_D128" if gqa else "mha12_D64") + "_bs16"
+            log(f"paged decode {name}")
+            wp = synth.paged_batched_decode(seed=3, gqa=gqa, block_size=16)
+            r = {k: round(v, 3) for k, v in
+                 bench_paged_decode(torch, K, wp, args.steps, args.warmup, 4).items()}
+            r["lengths"] = (wp.hist + 1).tolist()
+            paged[name] = r
+        extras["paged_decode"] = paged
         pre = []
         for dtype in ("f32", "bf16"):
             for S in (256, 1024):
