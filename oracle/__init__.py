@@ -77,6 +77,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attention.restype = i32
     lib.oracle_prefill.argtypes = [vp, vp] + [i32] * 8 + [vp, vp, vp, i32, i32, dbl, vp]
     lib.oracle_prefill.restype = i32
+    lib.oracle_prefill_varlen.argtypes = [vp, vp] + [i32] * 8 + [vp, vp, vp, i32, vp, vp, dbl, vp]
+    lib.oracle_prefill_varlen.restype = i32
     lib.oracle_paged_append.argtypes = [vp, vp] + [i32] * 8 + [vp, vp, i32, i32, vp, vp, i32]
     lib.oracle_paged_append.restype = i32
     lib.oracle_paged_attention.argtypes = [vp, vp, vp] + [i32] * 11 + [vp, vp, i32, dbl, vp]
@@ -164,6 +166,33 @@ def prefill(k_cache, v_cache, q, k, v, scale, layer0=0, lib=None) -> np.ndarray:
     rc = lib.oracle_prefill(_ptr(k_cache), _ptr(v_cache), L, B, Hkv, Tmax, D, dt, layer0,
                             n_layers, _ptr(q), _ptr(k), _ptr(v), Hq, S, float(scale), _ptr(out))
     _check(rc, "oracle_prefill")
+    return out
+
+
+def prefill_varlen(k_cache, v_cache, q, k, v, cu_seqlens, hist_len, scale, layer0=0,
+                   lib=None) -> np.ndarray:
+    """Packed variable-length prefill with history: q [n_layers, T, Hq, D],
+    k/v [n_layers, T, Hkv, D] token-major, sequence b's new tokens at
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 going to cache positions hist_len[b]
+    ..  Returns float64 [n_layers, T, Hq, D]."""
+    lib = lib or load()
+    L, B, Hkv, Tmax, D = k_cache.shape
+    n_layers, T, Hq, D2 = q.shape
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if D2 != D or k.shape != (n_layers, T, Hkv, D) or v.shape != k.shape or cu.shape != (B + 1,):
+        raise ValueError("prefill_varlen: shape mismatch")
+    if int(cu[-1]) != T:
+        raise ValueError("prefill_varlen: cu_seqlens[B] must equal the packed token count")
+    dt = _dtype_code(k_cache)
+    for a in (v_cache, q, k, v):
+        if _dtype_code(a) != dt:
+            raise TypeError("prefill_varlen: dtype mismatch")
+    hist = np.ascontiguousarray(hist_len, dtype=np.int32)
+    out = np.zeros(q.shape, dtype=np.float64)
+    rc = lib.oracle_prefill_varlen(_ptr(k_cache), _ptr(v_cache), L, B, Hkv, Tmax, D, dt, layer0,
+                                   n_layers, _ptr(q), _ptr(k), _ptr(v), Hq, _ptr(cu), _ptr(hist),
+                                   float(scale), _ptr(out))
+    _check(rc, "oracle_prefill_varlen")
     return out
 
 

@@ -150,6 +150,37 @@ int oracle_append(void *k_cache, void *v_cache, int L, int B, int Hkv,
  * double.  Returns ORACLE_E_ARG on bad shapes, ORACLE_E_CAPACITY if any
  * P_b + N > Tmax; out is then untouched.
  */
+/*
+ * One query row against the n visible keys 0 .. n-1 of cache head
+ * (layer, b, hkv): the definition above, written once and used by every
+ * attention function here.  q_row and out_row point at the row's D
+ * elements; s and acc are scratch of n and D doubles.
+ */
+static void attend_row(const void *q, size_t q_row, const void *k_cache,
+                       const void *v_cache, int layer, int b, int hkv, int B,
+                       int Hkv, int Tmax, int D, int dtype, int n,
+                       double scale, double *s, double *acc, double *out_row) {
+  for (int j = 0; j < n; ++j) {
+    const size_t krow = cache_row(layer, b, hkv, j, B, Hkv, Tmax, D);
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += load_elem(q, q_row + d, dtype) * load_elem(k_cache, krow + d, dtype);
+    s[j] = scale * dot;
+  }
+  double m = -INFINITY;
+  for (int j = 0; j < n; ++j)
+    if (s[j] > m) m = s[j];
+  double denom = 0.0;
+  for (int d = 0; d < D; ++d) acc[d] = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const double w = exp(s[j] - m);
+    const size_t vrow = cache_row(layer, b, hkv, j, B, Hkv, Tmax, D);
+    denom += w;
+    for (int d = 0; d < D; ++d) acc[d] += w * load_elem(v_cache, vrow + d, dtype);
+  }
+  for (int d = 0; d < D; ++d) out_row[d] = acc[d] / denom;
+}
+
 int oracle_attention(const void *q, const void *k_cache, const void *v_cache,
                      int L, int B, int Hkv, int Tmax, int D, int dtype,
                      int layer0, int n_layers, int Hq, int N,
@@ -183,26 +214,8 @@ int oracle_attention(const void *q, const void *k_cache, const void *v_cache,
     for (int i = 0; i < N; ++i) {
       const int n = hist_len[b] + i + 1;
       const size_t qrow = step_row(l, b, hq, i, B, Hq, N, D);
-      for (int j = 0; j < n; ++j) {
-        const size_t krow = cache_row(layer0 + l, b, hkv, j, B, Hkv, Tmax, D);
-        double dot = 0.0;
-        for (int d = 0; d < D; ++d)
-          dot += load_elem(q, qrow + d, dtype) *
-                 load_elem(k_cache, krow + d, dtype);
-        s[j] = scale * dot;
-      }
-      double m = -INFINITY;
-      for (int j = 0; j < n; ++j)
-        if (s[j] > m) m = s[j];
-      double denom = 0.0;
-      for (int d = 0; d < D; ++d) acc[d] = 0.0;
-      for (int j = 0; j < n; ++j) {
-        const double w = exp(s[j] - m);
-        const size_t vrow = cache_row(layer0 + l, b, hkv, j, B, Hkv, Tmax, D);
-        denom += w;
-        for (int d = 0; d < D; ++d) acc[d] += w * load_elem(v_cache, vrow + d, dtype);
-      }
-      for (int d = 0; d < D; ++d) out[qrow + d] = acc[d] / denom;
+      attend_row(q, qrow, k_cache, v_cache, layer0 + l, b, hkv, B, Hkv, Tmax, D,
+                 dtype, n, scale, s, acc, out + qrow);
     }
     free(s);
     free(acc);
@@ -233,6 +246,79 @@ int oracle_prefill(void *k_cache, void *v_cache, int L, int B, int Hkv,
                           layer0, n_layers, Hq, S, zeros, scale, out);
   free(zeros);
   return rc;
+}
+
+/*
+ * Packed variable-length prefill with history.  [KV-4] "Prefill 阶段": a
+ * batch of prompts is packed along the token axis ([total_tokens, hidden],
+ * cu_seqlens marking where each sequence starts) so one launch covers the
+ * whole batch; a long prompt is prefilled in chunks, and a prompt whose
+ * prefix is already cached only prefills the increment.  So sequence b
+ * brings S_b = cu_seqlens[b+1] - cu_seqlens[b] new tokens on top of P_b =
+ * hist_len[b] cached ones: they are appended at positions [P_b, P_b + S_b)
+ * and new token i attends to positions 0 .. P_b + i ([KV-2]
+ * "一个很容易漏掉的错误": the causal mask offset by the history length).
+ * That is exactly append then attention as above, one sequence at a time.
+ *
+ * Packed tensors are token-major per layer, as the page's packed batch:
+ * q and out [n_layers, T, Hq, D], k and v [n_layers, T, Hkv, D], T =
+ * cu_seqlens[B]; token cu_seqlens[b] + i is new token i of sequence b.
+ * Returns ORACLE_E_CAPACITY if any P_b + S_b > Tmax, ORACLE_E_ARG on bad
+ * shapes (cu_seqlens not non-decreasing from 0); nothing is written then.
+ */
+int oracle_prefill_varlen(void *k_cache, void *v_cache, int L, int B, int Hkv,
+                          int Tmax, int D, int dtype, int layer0,
+                          int n_layers, const void *q, const void *k,
+                          const void *v, int Hq, const int32_t *cu_seqlens,
+                          const int32_t *hist_len, double scale, double *out) {
+  if (L < 0 || B < 0 || Hkv <= 0 || Tmax < 0 || D <= 0 || Hq <= 0 ||
+      Hq % Hkv != 0 || layer0 < 0 || n_layers < 0 || layer0 + n_layers > L ||
+      cu_seqlens[0] != 0)
+    return ORACLE_E_ARG;
+  for (int b = 0; b < B; ++b) {
+    if (hist_len[b] < 0 || cu_seqlens[b + 1] < cu_seqlens[b]) return ORACLE_E_ARG;
+    if ((int64_t)hist_len[b] + (cu_seqlens[b + 1] - cu_seqlens[b]) > Tmax)
+      return ORACLE_E_CAPACITY;
+  }
+  const int T = cu_seqlens[B];
+  const size_t es = elem_size(dtype);
+  /* append: token cu[b] + i of head h to cache position P_b + i */
+  for (int l = 0; l < n_layers; ++l)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < Hkv; ++h)
+        for (int i = 0; i < cu_seqlens[b + 1] - cu_seqlens[b]; ++i) {
+          const int pos = hist_len[b] + i;
+          const size_t src = (((size_t)l * T + cu_seqlens[b] + i) * Hkv + h) * (size_t)D;
+          const size_t dst = cache_row(layer0 + l, b, h, pos, B, Hkv, Tmax, D);
+          memcpy((char *)k_cache + dst * es, (const char *)k + src * es, (size_t)D * es);
+          memcpy((char *)v_cache + dst * es, (const char *)v + src * es, (size_t)D * es);
+        }
+  /* attention: new token i of sequence b sees P_b + i + 1 keys */
+  const int group = Hq / Hkv;
+  const long units = (long)n_layers * B * Hq;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+  for (long u = 0; u < units; ++u) {
+    const int hq = (int)(u % Hq);
+    const int b = (int)((u / Hq) % B);
+    const int l = (int)(u / ((long)Hq * B));
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Tmax > 0 ? Tmax : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+      free(s);
+      free(acc);
+      failed = 1;
+      continue;
+    }
+    for (int i = 0; i < cu_seqlens[b + 1] - cu_seqlens[b]; ++i) {
+      const size_t qrow = (((size_t)l * T + cu_seqlens[b] + i) * Hq + hq) * (size_t)D;
+      attend_row(q, qrow, k_cache, v_cache, layer0 + l, b, hq / group, B, Hkv,
+                 Tmax, D, dtype, hist_len[b] + i + 1, scale, s, acc, out + qrow);
+    }
+    free(s);
+    free(acc);
+  }
+  return failed ? ORACLE_E_ARG : ORACLE_OK;
 }
 
 /*

@@ -506,16 +506,111 @@ def pin_paged_refusals(lib):
     """Positions past the table row, or a block id outside the pool, are
     refused and nothing is written."""
     kp, vp = _paged_canary(1, 4, 1, 4, 4)
-    kn = np.ones((1, 1, 1, 2, 4), np.float32)
-    for hist, bt in ((np.array([7], np.int32), np.array([[0, 1]], np.int32)),     # 7 + 2 > 8
-                     (np.array([3], np.int32), np.array([[0, 4]], np.int32)),     # block 4 of 4
-                     (np.array([3], np.int32), np.array([[0, -1]], np.int32))):
+    kn = np.ones((1, 2, 1, 2, 4), np.float32)
+    # sequence 0 overflows its two-block row (7 + 2 > 8); the entry past the
+    # row is the next row's first, a valid id, so only the capacity check
+    # stands between the call and a write into block 2
+    for hist, bt in ((np.array([7, 0], np.int32), np.array([[0, 1], [2, 3]], np.int32)),
+                     (np.array([3, 0], np.int32), np.array([[0, 4], [2, 3]], np.int32)),
+                     (np.array([3, 0], np.int32), np.array([[0, -1], [2, 3]], np.int32))):
         try:
             oracle.paged_append(kp, vp, kn, kn, hist, bt, lib=lib)
             raise AssertionError(f"accepted hist={hist} table={bt}")
         except oracle.OracleError:
             pass
         assert synth.is_canary(kp).all() and synth.is_canary(vp).all()
+
+
+# ---------------------------------------------------------------- packed varlen prefill
+# [KV-4] "Prefill 阶段": prompts packed along the token axis (token-major
+# [n_layers, T, H, D], cu_seqlens boundaries), each with its own cached prefix.
+
+
+def _pack(x, lens):
+    """[n_layers, B, H, Smax, D] padded rows -> token-major packed
+    [n_layers, sum(lens), H, D] (sequence b's first lens[b] rows)."""
+    parts = [np.transpose(x[:, b, :, :n], (0, 2, 1, 3)) for b, n in enumerate(lens)]
+    return np.ascontiguousarray(np.concatenate(parts, axis=1))
+
+
+def _unpack(y, lens):
+    """Inverse of _pack for outputs: list of [n_layers, H, lens[b], D]."""
+    out, t = [], 0
+    for n in lens:
+        out.append(np.transpose(y[:, t:t + n], (0, 2, 1, 3)))
+        t += n
+    return out
+
+
+def pin_varlen_equals_padded(lib):
+    """Equal lengths and histories: the packed call leaves the cache bytes and
+    gives the outputs (bit for bit) of append + attention on the padded
+    layout with N = S."""
+    rng = _rng(71)
+    L, B, Hkv, G, D, T = 2, 3, 2, 2, 8, 24
+    S, P = 5, 7
+    hist = np.full(B, P, np.int32)
+    kc, vc = _empty_cache(L, B, Hkv, T, D)
+    _fill_history(kc, vc, hist, rng)
+    q = rng.standard_normal((L, B, Hkv * G, S, D), dtype=np.float32)
+    k = rng.standard_normal((L, B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((L, B, Hkv, S, D), dtype=np.float32)
+    kc2, vc2 = kc.copy(), vc.copy()
+    ref = _decode(lib, kc, vc, q, k, v, hist, 0.3)
+    lens = [S] * B
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    got = oracle.prefill_varlen(kc2, vc2, _pack(q, lens), _pack(k, lens), _pack(v, lens), cu,
+                                hist, 0.3, lib=lib)
+    assert np.array_equal(kc2.view(np.uint32), kc.view(np.uint32))
+    assert np.array_equal(vc2.view(np.uint32), vc.view(np.uint32))
+    for b, ob in enumerate(_unpack(got, lens)):
+        assert np.array_equal(ob, ref[:, b]), b
+
+
+def pin_varlen_ragged_equals_per_sequence(lib):
+    """Different lengths (one empty) and histories in one packed call equal
+    each sequence's own padded append + attention, bit for bit; layer0 = 1."""
+    rng = _rng(72)
+    L, B, Hkv, G, D, T = 3, 4, 1, 3, 8, 32
+    lens = [3, 0, 9, 1]
+    hist = np.array([0, 5, 11, 30], np.int32)
+    kc, vc = _empty_cache(L, B, Hkv, T, D)
+    _fill_history(kc, vc, hist, rng)
+    Smax = max(lens)
+    q = rng.standard_normal((L - 1, B, Hkv * G, Smax, D), dtype=np.float32)
+    k = rng.standard_normal((L - 1, B, Hkv, Smax, D), dtype=np.float32)
+    v = rng.standard_normal((L - 1, B, Hkv, Smax, D), dtype=np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kc2, vc2 = kc.copy(), vc.copy()
+    got = _unpack(oracle.prefill_varlen(kc2, vc2, _pack(q, lens), _pack(k, lens), _pack(v, lens),
+                                        cu, hist, 0.45, layer0=1, lib=lib), lens)
+    for b, n in enumerate(lens):
+        kb, vb = np.ascontiguousarray(kc[:, b:b + 1]), np.ascontiguousarray(vc[:, b:b + 1])
+        sl = (slice(None), slice(b, b + 1), slice(None), slice(0, n))
+        ref = _decode(lib, kb, vb, np.ascontiguousarray(q[sl]), np.ascontiguousarray(k[sl]),
+                      np.ascontiguousarray(v[sl]), hist[b:b + 1], 0.45, layer0=1)
+        assert np.array_equal(got[b], ref[:, 0]), b
+        assert np.array_equal(kc2[:, b:b + 1].view(np.uint32), kb.view(np.uint32)), b
+        assert np.array_equal(vc2[:, b:b + 1].view(np.uint32), vb.view(np.uint32)), b
+
+
+def pin_varlen_refusals(lib):
+    """A sequence whose history plus new tokens passes Tmax, or boundaries
+    that do not start at 0 or go backwards, are refused; nothing is written."""
+    kc, vc = _empty_cache(1, 2, 1, 8, 4)
+    q = np.ones((1, 6, 1, 4), np.float32)
+    for cu, hist in (([0, 2, 6], [1, 5]),     # 5 + 4 > 8
+                     ([1, 2, 6], [0, 0]),     # does not start at 0
+                     ([0, 4, 3], [0, 0])):    # goes backwards (T = 3 rows given)
+        cu = np.array(cu, np.int32)
+        T = int(cu[-1])
+        try:
+            oracle.prefill_varlen(kc, vc, q[:, :T], q[:, :T], q[:, :T], cu,
+                                  np.array(hist, np.int32), 0.5, lib=lib)
+            raise AssertionError(f"accepted cu={cu.tolist()} hist={hist}")
+        except (oracle.OracleError, ValueError):
+            pass
+        assert synth.is_canary(kc).all() and synth.is_canary(vc).all()
 
 
 ALL_PINS = [
@@ -537,4 +632,7 @@ ALL_PINS = [
     pin_paged_heads_are_independent,
     pin_paged_shared_prefix,
     pin_paged_refusals,
+    pin_varlen_equals_padded,
+    pin_varlen_ragged_equals_per_sequence,
+    pin_varlen_refusals,
 ]

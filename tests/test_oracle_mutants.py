@@ -53,10 +53,10 @@ MUTANTS = {
     "scale_inverted": ("s[j] = scale * dot;", "s[j] = dot / scale;"),
     "scores_from_values": ("load_elem(k_cache, krow + d, dtype);", "load_elem(v_cache, krow + d, dtype);"),
     "key_index_transposed": ("load_elem(k_cache, krow + d, dtype);",
-                             "load_elem(k_cache, cache_row(layer0 + l, b, hkv, d % n, B, Hkv, Tmax, D) + j % D, dtype);"),
+                             "load_elem(k_cache, cache_row(layer, b, hkv, d % n, B, Hkv, Tmax, D) + j % D, dtype);"),
     # the softmax
     "exp_sign_flipped": ("const double w = exp(s[j] - m);", "const double w = exp(m - s[j]);"),
-    "no_normalisation": ("out[qrow + d] = acc[d] / denom;", "out[qrow + d] = acc[d];"),
+    "no_normalisation": ("out_row[d] = acc[d] / denom;", "out_row[d] = acc[d];"),
     "denominator_counts_keys": ("denom += w;", "denom += 1.0;"),
     "weights_not_applied": ("acc[d] += w * load_elem(v_cache, vrow + d, dtype);",
                             "acc[d] += load_elem(v_cache, vrow + d, dtype) / n;"),
@@ -71,6 +71,14 @@ MUTANTS = {
     "bf16_wrong_shift": ("uint32_t bits = (uint32_t)hi << 16;", "uint32_t bits = (uint32_t)hi << 15;"),
     # the size formula
     "size_formula_drops_kv_factor": ("return (uint64_t)(2 * layers *", "return (uint64_t)(1 * layers *"),
+    # packed variable-length prefill: token offsets, history offset, head
+    "varlen_mask_without_history": ("hist_len[b] + i + 1, scale, s, acc, out + qrow);",
+                                    "i + 1, scale, s, acc, out + qrow);"),
+    "varlen_append_at_position_i": ("const int pos = hist_len[b] + i;", "const int pos = i;"),
+    "varlen_query_head_major": ("const size_t qrow = (((size_t)l * T + cu_seqlens[b] + i) * Hq + hq) * (size_t)D;",
+                                "const size_t qrow = (((size_t)l * Hq + hq) * T + cu_seqlens[b] + i) * (size_t)D;"),
+    "varlen_tokens_head_major": ("const size_t src = (((size_t)l * T + cu_seqlens[b] + i) * Hkv + h) * (size_t)D;",
+                                 "const size_t src = (((size_t)l * Hkv + h) * T + cu_seqlens[b] + i) * (size_t)D;"),
     # the paged cache: block-table lookup, row inside the block, head, layer
     "paged_append_block_from_offset": ("block_table[(size_t)b * max_blocks + t / block_size]",
                                        "block_table[(size_t)b * max_blocks + t % block_size]"),
