@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum {
   KVC_OK = 0,
@@ -225,6 +225,35 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0,
                             int32_t n_layers, const void *q, const void *k,
                             const void *v, int32_t Hq, int32_t S, float scale,
                             void *o, void *stream);
+
+/*
+ * attn_prefill_varlen: a batch of prompts packed along the token axis, each
+ * with its own cached prefix, in one call.  [KV-4] "Prefill 阶段": the packed
+ * batch ([total_tokens, hidden] with cu_seqlens marking where each sequence
+ * starts) lets one launch cover the whole batch; long prompts are prefilled
+ * in chunks, and a prompt whose prefix is already cached prefills only the
+ * increment.  Sequence b brings S_b = cu_seqlens[b+1] - cu_seqlens[b] new
+ * tokens on top of P_b = hist_len[b] cached positions: their K/V are written
+ * to cache positions [P_b, P_b + S_b) and new token i attends to positions
+ * 0 .. P_b + i ([KV-2] "一个很容易漏掉的错误": the causal mask offset by the
+ * history).  Same result as kvc_append + kvc_attn_decode per sequence with
+ * N = S_b.
+ *   q, o       : device, [n_layers, T, Hq, D], token-major (token
+ *                cu_seqlens[b] + i is new token i of sequence b), T =
+ *                cu_seqlens[B]
+ *   k, v       : device, [n_layers, T, Hkv, D]
+ *   cu_seqlens : host int32 [B + 1], cu_seqlens[0] = 0, non-decreasing
+ *                (S_b = 0 is allowed: that sequence is left alone)
+ *   hist_len   : host int32 [B], P_b >= 0; P_b + S_b > Tmax is
+ *                KVC_E_CAPACITY and nothing is written
+ * Other rules as kvc_attn_prefill.  Computed on the matrix cores like it.
+ */
+kvc_status kvc_attn_prefill_varlen(const kvc_cache *cache, int32_t layer0,
+                                   int32_t n_layers, const void *q,
+                                   const void *k, const void *v, int32_t Hq,
+                                   const int32_t *cu_seqlens,
+                                   const int32_t *hist_len, float scale,
+                                   void *o, void *stream);
 
 /*
  * ---- paged cache ---------------------------------------------------------

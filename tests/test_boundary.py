@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 3
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 4
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -310,4 +310,32 @@ def test_paged_error_paths(lib):
         assert dec(step, scale=float("nan")) == E_SHAPE
         assert dec(step, mb=-1) == E_SHAPE
         assert dec(step, N=0, q=None, o=None, ws=None) == OK
+
+
+def test_varlen_prefill_error_paths(lib):
+    h = Host()
+    d = desc(h)  # L=2, B=2, Hkv=2, Tmax=16, D=64
+    p = h.ptr()
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=p, k=p, v=p, Hq=4, cu=hist(0, 3, 7),
+                 hist=hist(2, 5), scale=0.125, o=p)
+        a.update(kw)
+        return lib.kvc_attn_prefill_varlen(a["c"], a["layer0"], a["n_layers"], a["q"], a["k"],
+                                           a["v"], a["Hq"], a["cu"], a["hist"], a["scale"], a["o"],
+                                           None)
+
+    assert call(cu=hist(1, 3, 7)) == E_SHAPE              # does not start at 0
+    assert call(cu=hist(0, 5, 3)) == E_SHAPE              # decreases
+    assert call(cu=None) == E_NULL
+    assert call(hist=hist(2, 13)) == E_CAPACITY           # 13 + 4 > 16
+    assert "exceeds" in err(lib)
+    assert call(hist=hist(-1, 0)) == E_SHAPE
+    assert call(hist=None) == E_NULL
+    assert call(Hq=3) == E_SHAPE
+    assert call(q=None) == E_NULL
+    assert call(o=h.ptr(offset=4)) == E_SHAPE
+    assert call(scale=float("inf")) == E_SHAPE
+    assert call(c=ctypes.byref(desc(h, D=32))) == E_UNSUPPORTED
+    assert call(cu=hist(0, 0, 0), q=None, k=None, v=None, o=None) == OK  # no tokens: no-op
 

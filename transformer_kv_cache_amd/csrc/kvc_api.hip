@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "kvc_internal.h"
 
@@ -156,6 +157,35 @@ kvc_status paged_view(const kvc_paged_cache *pc, int32_t B, const int32_t *block
   while ((1 << log2) < pc->block_size) ++log2;
   *pg = kvc::PagedGeom{block_table, max_blocks, pc->num_blocks, log2};
   return KVC_OK;
+}
+
+// Fields of a prefill launch shared by the padded and the packed entry
+// points (validated arguments).
+kvc::PrefillArgs prefill_args(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                              const void *q, const void *k, const void *v, int32_t Hq, float scale,
+                              void *o) {
+  kvc::PrefillArgs a{};
+  a.k_cache = (char *)cache->k;
+  a.v_cache = (char *)cache->v;
+  a.q = (const char *)q;
+  a.k = (const char *)k;
+  a.v = (const char *)v;
+  a.o = (char *)o;
+  a.B = cache->B;
+  a.Hkv = cache->Hkv;
+  a.Hq = Hq;
+  a.Tmax = cache->Tmax;
+  a.layer0 = layer0;
+  a.n_layers = n_layers;
+  a.group = Hq / cache->Hkv;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+void set_slice(kvc::PrefillArgs *a, int b0, int B) {
+  a->b0 = b0;
+  a->nb = B - b0 < kvc::kMaxBatchPerLaunch ? B - b0 : kvc::kMaxBatchPerLaunch;
+  a->nb_div = kvc::magic_for(a->nb);
 }
 
 }  // namespace
@@ -335,27 +365,99 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_la
   if (!q || !k || !v || !o) return fail(KVC_E_NULL, "%s: q, k, v or o is NULL", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
-  if ((int64_t)n_layers * cache->B * Hq > 2147483647LL)
-    return fail(KVC_E_UNSUPPORTED, "%s: too many heads for one launch", fn);
+  const int64_t tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+  const int64_t slice = cache->B < kvc::kMaxBatchPerLaunch ? cache->B : kvc::kMaxBatchPerLaunch;
+  if (tiles * slice > 65535 || (int64_t)cache->B * Hq * S >= 4294967296LL)
+    return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or rows for one launch", fn);
 
-  kvc::PrefillArgs a{};
-  a.k_cache = (char *)cache->k;
-  a.v_cache = (char *)cache->v;
-  a.q = (const char *)q;
-  a.k = (const char *)k;
-  a.v = (const char *)v;
-  a.o = (char *)o;
-  a.B = cache->B;
-  a.Hkv = cache->Hkv;
-  a.Hq = Hq;
-  a.Tmax = cache->Tmax;
-  a.S = S;
-  a.layer0 = layer0;
-  a.n_layers = n_layers;
-  a.group = Hq / cache->Hkv;
-  a.q_tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(kvc::launch_prefill(a, cache->dtype, cache->D, (hipStream_t)stream), fn);
+  // Padded layout [n_layers, B, H, S, D]: no history, S new tokens each.
+  const int64_t B = cache->B;
+  kvc::PrefillArgs a = prefill_args(cache, layer0, n_layers, q, k, v, Hq, scale, o);
+  a.q_sl = B * Hq * S;
+  a.q_sh = S;
+  a.q_si = 1;
+  a.kv_sl = B * cache->Hkv * S;
+  a.kv_sh = S;
+  a.kv_si = 1;
+  for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
+    set_slice(&a, b0, cache->B);
+    for (int i = 0; i < a.nb; ++i) {
+      a.hist[i] = 0;
+      a.len[i] = S;
+      a.q_row0[i] = (uint32_t)((int64_t)(b0 + i) * Hq * S);
+      a.kv_row0[i] = (uint32_t)((int64_t)(b0 + i) * cache->Hkv * S);
+    }
+    a.q_tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, false, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
+}
+
+kvc_status kvc_attn_prefill_varlen(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                                   const void *q, const void *k, const void *v, int32_t Hq,
+                                   const int32_t *cu_seqlens, const int32_t *hist_len, float scale,
+                                   void *o, void *stream) {
+  static const char *fn = "kvc_attn_prefill_varlen";
+  kvc_status st = check_cache(cache, layer0, n_layers, fn);
+  if (st != KVC_OK) return st;
+  if (Hq <= 0 || Hq % cache->Hkv != 0)
+    return fail(KVC_E_SHAPE, "%s: Hq = %d is not a positive multiple of Hkv = %d", fn, Hq, cache->Hkv);
+  if (!std::isfinite(scale)) return fail(KVC_E_SHAPE, "%s: scale is not finite", fn);
+  if (!cu_seqlens) return fail(KVC_E_NULL, "%s: cu_seqlens is NULL", fn);
+  if (cu_seqlens[0] != 0) return fail(KVC_E_SHAPE, "%s: cu_seqlens[0] = %d, not 0", fn, cu_seqlens[0]);
+  for (int b = 0; b < cache->B; ++b)
+    if (cu_seqlens[b + 1] < cu_seqlens[b])
+      return fail(KVC_E_SHAPE, "%s: cu_seqlens decreases at %d", fn, b + 1);
+  const int64_t T = cu_seqlens[cache->B];
+  std::vector<int32_t> lens(cache->B);
+  for (int b = 0; b < cache->B; ++b) lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+  // capacity: hist_len[b] + S_b <= Tmax, checked per sequence
+  if (cache->B > 0 && !hist_len) return fail(KVC_E_NULL, "%s: hist_len is NULL", fn);
+  for (int b = 0; b < cache->B; ++b) {
+    if (hist_len[b] < 0) return fail(KVC_E_SHAPE, "%s: hist_len[%d] = %d < 0", fn, b, hist_len[b]);
+    if ((int64_t)hist_len[b] + lens[b] > cache->Tmax)
+      return fail(KVC_E_CAPACITY, "%s: hist_len[%d] + S_%d = %d + %d exceeds Tmax = %d", fn, b, b,
+                  hist_len[b], lens[b], cache->Tmax);
+  }
+  if (T == 0 || n_layers == 0 || cache->B == 0) return ok();
+  if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
+  if (!q || !k || !v || !o) return fail(KVC_E_NULL, "%s: q, k, v or o is NULL", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
+  int max_len = 0;
+  for (int b = 0; b < cache->B; ++b) max_len = lens[b] > max_len ? lens[b] : max_len;
+  const int64_t tiles = (max_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+  const int64_t slice = cache->B < kvc::kMaxBatchPerLaunch ? cache->B : kvc::kMaxBatchPerLaunch;
+  if (tiles * slice > 65535 || T * Hq >= 4294967296LL)
+    return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or tokens for one launch", fn);
+
+  // Packed token-major layout [n_layers, T, H, D].
+  kvc::PrefillArgs a = prefill_args(cache, layer0, n_layers, q, k, v, Hq, scale, o);
+  a.q_sl = T * Hq;
+  a.q_sh = 1;
+  a.q_si = Hq;
+  a.kv_sl = T * cache->Hkv;
+  a.kv_sh = 1;
+  a.kv_si = cache->Hkv;
+  for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
+    set_slice(&a, b0, cache->B);
+    int slice_len = 0;
+    bool history = false;
+    for (int i = 0; i < a.nb; ++i) {
+      const int b = b0 + i;
+      a.hist[i] = hist_len[b];
+      a.len[i] = lens[b];
+      a.q_row0[i] = (uint32_t)((int64_t)cu_seqlens[b] * Hq);
+      a.kv_row0[i] = (uint32_t)((int64_t)cu_seqlens[b] * cache->Hkv);
+      if (lens[b] > slice_len) slice_len = lens[b];
+      if (hist_len[b] > 0 && lens[b] > 0) history = true;
+    }
+    a.q_tiles = (slice_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, history, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
 }
 
 }  // extern "C"

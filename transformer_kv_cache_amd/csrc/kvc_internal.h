@@ -138,15 +138,28 @@ __device__ __forceinline__ int div_magic(int n, int d, uint32_t m) {
   return q;
 }
 
+// Prefill of S_b new tokens per sequence on top of P_b cached positions,
+// for a batch slice [b0, b0 + nb).  q / o and the new k / v rows are
+// addressed through strides, in rows of D elements:
+//   row(l, sequence, h, i) = l * sl + h * sh + row0[sequence] + i * si
+// which covers both the padded [n_layers, B, H, S, D] layout and the packed
+// token-major [n_layers, T, H, D] one.
 struct PrefillArgs {
   char *k_cache, *v_cache;
   const char *q, *k, *v;
   char *o;
-  int32_t B, Hkv, Hq, Tmax, S;
-  int32_t layer0, n_layers;
-  int32_t group;
-  int32_t q_tiles;
+  int32_t B, Hkv, Hq, Tmax;
+  int32_t layer0, n_layers, group;
+  int32_t b0, nb;
+  int32_t q_tiles;      // most query tiles of one sequence in the slice
+  uint32_t nb_div;      // div_magic multiplier for nb
   float scale_log2;
+  int64_t q_sl, kv_sl;
+  int32_t q_sh, q_si, kv_sh, kv_si;
+  int32_t hist[kMaxBatchPerLaunch];     // P_b
+  int32_t len[kMaxBatchPerLaunch];      // S_b
+  uint32_t q_row0[kMaxBatchPerLaunch];  // row0 of q / o
+  uint32_t kv_row0[kMaxBatchPerLaunch]; // row0 of k / v
 };
 
 // Host launchers (one translation unit each).  They assume validated
@@ -156,7 +169,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipS
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, hipStream_t s);
 
 // Geometry shared by kvc_decode_workspace_bytes and the decode launchers.
 // One query row per KV head runs on the vector kernel; more rows (GQA groups,

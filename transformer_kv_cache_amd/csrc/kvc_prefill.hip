@@ -7,9 +7,18 @@
 // in cache rows [0, S).  Unlike decode this is a dense contraction (two
 // S x S x D products per head), so it runs on MFMA.
 //
+// The same kernel serves kvc_attn_prefill_varlen ([KV-4] "Prefill 阶段":
+// prompts packed along the token axis, each with its own cached prefix):
+// sequence b brings S_b new tokens on top of P_b cached positions, new token
+// i sits at position P_b + i and attends to positions 0 .. P_b + i; keys
+// below P_b come from the cache, the others from the new K/V rows.  Rows of
+// q / o / k / v are addressed through strides, so the padded layout of
+// kvc_attn_prefill and the packed token-major one share the code; without
+// history (every P_b = 0) a template switch drops the cache reads.
+//
 // Tiling.  A workgroup of 4 waves owns one (layer, sequence, query head) and a
-// tile of BM = 128 query rows (32 per wave); it walks key tiles of BN = 64
-// rows up to the diagonal, staging each K/V tile in LDS once for all four
+// tile of BM = 128 new tokens (32 per wave); it walks key tiles of BN = 64
+// positions up to the diagonal, staging each K/V tile in LDS once for all four
 // waves.  Per wave and key tile:
 //   S^T = K_tile . Q^T   (keys x queries; 32x32 MFMA blocks, Q held in
 //                          registers for the whole kernel)
@@ -26,8 +35,8 @@
 //   fp32: v_mfma_f32_32x32x2_f32, everything in fp32 (no reduced precision).
 // Tiles above the diagonal are never loaded; a wave skips key tiles that lie
 // entirely above its own 32 rows.  Grid order puts the longest (last) query
-// tiles of every head first, and with a head count that is a multiple of 8
-// all tiles of one head land on the same XCD and share its L2.
+// tiles of every sequence first, and with a (layer, head) count that is a
+// multiple of 8 all tiles of one head land on the same XCD and share its L2.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -83,11 +92,12 @@ template <int D> struct Smem<KVC_F32, D> {
   alignas(16) float v[BN * kVStride];
 };
 
-template <int DT, int D>
+template <int DT, int D, bool HIST>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   constexpr int EB = Dtype<DT>::kBytes;
   constexpr int EV = Dtype<DT>::kPer16B;
-  constexpr int LPR = D * EB / 16;             // 16-byte vectors per row
+  constexpr int RB = D * EB;                   // bytes per row
+  constexpr int LPR = RB / 16;                 // 16-byte vectors per row
   constexpr int TILE_VECS = BN * LPR;          // 16-byte vectors per K (or V) tile
   constexpr int VPT = TILE_VECS / 256;         // per thread
   constexpr int DB = D / 32;                   // 32-wide d blocks of O^T
@@ -101,24 +111,38 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   const int h = lane >> 5;     // half-wave
   const int col = lane & 31;   // MFMA column / row within a 32 block
 
-  const int head = blockIdx.x;  // (l, b, hq)
-  const int qt = a.q_tiles - 1 - (int)blockIdx.y;
+  // Grid: x = (layer, query head); y = (tile rank, sequence in the slice),
+  // sequence fastest, so that every sequence's longest (last) query tiles
+  // come first.
+  const int head = blockIdx.x;
   const int hq = head % a.Hq;
-  const int b = (head / a.Hq) % a.B;
-  const int l = head / (a.Hq * a.B);
+  const int l = head / a.Hq;
+  const int rank = div_magic((int)blockIdx.y, a.nb, a.nb_div);
+  const int bb = (int)blockIdx.y - rank * a.nb;
+  const int S = a.len[bb];   // new tokens of this sequence
+  const int P = HIST ? a.hist[bb] : 0;  // positions already cached
+  const int qt = (S + BM - 1) / BM - 1 - rank;
+  if (qt < 0) return;
+  const int b = a.b0 + bb;
   const int hkv = hq / a.group;
   const bool writer = (hq % a.group) == 0;
-  const int S = a.S;
   const int q0 = qt * BM;
-  const int qrow = q0 + wave * 32 + col;  // this lane's query row
-  const int wave_last = q0 + wave * 32 + 31;
+  const int qrow = q0 + wave * 32 + col;            // this lane's new token
+  const int wave_last = P + q0 + wave * 32 + 31;    // last position the wave's rows see
+  const int q_end = (q0 + BM < S) ? q0 + BM : S;
+  const int kv_end = P + q_end;                     // positions this tile needs
 
-  const size_t step_head = ((size_t)l * a.B + b);
-  const char *qbase = a.q + ((step_head * a.Hq + hq) * (size_t)S) * D * EB;
-  const char *kbase = a.k + ((step_head * a.Hkv + hkv) * (size_t)S) * D * EB;
-  const char *vbase = a.v + ((step_head * a.Hkv + hkv) * (size_t)S) * D * EB;
-  char *kcache = a.k_cache + (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax * D * EB;
-  char *vcache = a.v_cache + (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax * D * EB;
+  // New token i of this sequence: q / o at qbase + i * q_stride, its k / v
+  // at kin / vin + i * kv_stride.  Cached position j at kcache / vcache + j * RB.
+  const char *qbase = a.q + ((size_t)l * a.q_sl + (size_t)hq * a.q_sh + a.q_row0[bb]) * RB;
+  const size_t q_stride = (size_t)a.q_si * RB;
+  const size_t kv_in = ((size_t)l * a.kv_sl + (size_t)hkv * a.kv_sh + a.kv_row0[bb]) * RB;
+  const char *kin = a.k + kv_in;
+  const char *vin = a.v + kv_in;
+  const size_t kv_stride = (size_t)a.kv_si * RB;
+  const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
+  char *kcache = a.k_cache + crow0 * RB;
+  char *vcache = a.v_cache + crow0 * RB;
 
   // Q fragments, resident for the whole kernel.
   //   bf16: qv[ds] = Q[qrow][16 ds + 8 h .. +7]        (B operand of 32x32x16)
@@ -130,7 +154,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     qv[j] = u32x4{0u, 0u, 0u, 0u};
     if (qrow < S) {
       const int d0 = (DT == KVC_BF16) ? 16 * j + 8 * h : 8 * j + 4 * h;
-      qv[j] = *reinterpret_cast<const u32x4 *>(qbase + ((size_t)qrow * D + d0) * EB);
+      qv[j] = *reinterpret_cast<const u32x4 *>(qbase + (size_t)qrow * q_stride + d0 * EB);
     }
   }
 
@@ -140,41 +164,56 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  const int kv_end = (q0 + BM < S) ? q0 + BM : S;  // keys this tile needs
   const int n_kt = (kv_end + BN - 1) / BN;
+  // Tiles every wave needs: their first key is at most the first row's
+  // position.  At most two more follow, which some waves skip.
+  const int n_all_raw = (P + q0 + 31) / BN + 1;
+  const int n_all = n_all_raw < n_kt ? n_all_raw : n_kt;
 
   // Tile staging.  Each thread moves VPT 16-byte vectors of K and of V per
   // tile, as pairs of adjacent keys (rows 2p and 2p+1) at the same column c,
   // so that the bf16 V^T store can write both keys of a column as one dword.
-  // Tile kt+1 is loaded into registers while tile kt is computed.  Key
-  // indices past the prompt are clamped to its last row (always valid): their
-  // scores are masked, so no load needs a branch.
+  // Tile kt+1 is loaded into registers while tile kt is computed.  Positions
+  // past kv_end are clamped to its last one (always valid): their scores are
+  // masked, so no load needs a branch.  Positions below P come from the
+  // cache, the others from the new rows.
   auto tile_row = [&](int it) { return 2 * (tid / LPR + (it >> 1) * (256 / LPR)) + (it & 1); };
   const int c = tid % LPR;
   u32x4 kreg[VPT], vreg[VPT];
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < VPT; ++it) {
-      const int key = kt * BN + tile_row(it);
-      const size_t off = ((size_t)(key < S ? key : S - 1) * D + c * EV) * EB;
-      kreg[it] = *reinterpret_cast<const u32x4 *>(kbase + off);
-      vreg[it] = *reinterpret_cast<const u32x4 *>(vbase + off);
+      const int key0 = kt * BN + tile_row(it);
+      const int key = key0 < kv_end ? key0 : kv_end - 1;
+      const char *kp, *vp;
+      if (HIST && key < P) {
+        kp = kcache + (size_t)key * RB;
+        vp = vcache + (size_t)key * RB;
+      } else {
+        kp = kin + (size_t)(key - P) * kv_stride;
+        vp = vin + (size_t)(key - P) * kv_stride;
+      }
+      kreg[it] = *reinterpret_cast<const u32x4 *>(kp + c * 16);
+      vreg[it] = *reinterpret_cast<const u32x4 *>(vp + c * 16);
     }
   };
   load_tile(0);
 
   // Stage tile kt in LDS (and in the cache when it is ours to write), then
   // start loading tile kt + 1.
+  // The new rows of this query tile's tokens, positions [P + q0, kv_end),
+  // are this workgroup's to write to the cache (the first query head of a
+  // group writes them).
   auto stage = [&](int kt) {
     const int key0 = kt * BN;
-    const bool store_cache = writer && key0 >= q0;  // this tile's rows are ours to write
+    const bool store_cache = writer && key0 + BN > P + q0;
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int it = 0; it < VPT; ++it) {
       const int row = tile_row(it);
       const int key = key0 + row;
-      if (store_cache && key < S) {
-        const size_t off = ((size_t)key * D + c * EV) * EB;
+      if (store_cache && key >= P + q0 && key < kv_end) {
+        const size_t off = (size_t)key * RB + c * 16;
         *reinterpret_cast<u32x4 *>(kcache + off) = kreg[it];
         *reinterpret_cast<u32x4 *>(vcache + off) = vreg[it];
       }
@@ -235,12 +274,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
       }
     }
 
-    // Causal mask, only on tiles that reach past the wave's first row or the
-    // prompt's end (a wave-uniform branch).  Key key0 + 32 kb + 8 (i/4) + 4 h
-    // + i%4 is visible iff it is <= qrow and < S, i.e. iff the compile-time
-    // offset 32 kb + 8 (i/4) + i%4 is <= lim.
-    if ((key0 + BN - 1 > q0 + wave * 32) || (key0 + BN > S)) {
-      const int lim = (qrow < S - 1 ? qrow : S - 1) - key0 - 4 * h;
+    // Causal mask, only on tiles that reach past the position of the wave's
+    // first row or past kv_end (a wave-uniform branch).  Key key0 + 32 kb +
+    // 8 (i/4) + 4 h + i%4 is visible iff it is <= P + qrow and < kv_end,
+    // i.e. iff the compile-time offset 32 kb + 8 (i/4) + i%4 is <= lim.
+    if ((key0 + BN - 1 > P + q0 + wave * 32) || (key0 + BN > kv_end)) {
+      const int lim = (P + qrow < kv_end - 1 ? P + qrow : kv_end - 1) - key0 - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -317,21 +356,30 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     }
   };
 
-  // Only the last key tile can lie wholly above a wave's rows (its first key
-  // is at most q0 + 64), so every wave computes every earlier tile and the
-  // skip test sits outside the loop.
-  for (int kt = 0; kt < n_kt - 1; ++kt) {
+  // Every wave computes the first n_all tiles; the at most two after them
+  // (first key past the position of the tile's first row, within 96 of it)
+  // are skipped by the waves whose rows all lie before them.  The skip tests
+  // sit outside the loop: inside it the compiler copies the accumulators on
+  // every iteration.
+  for (int kt = 0; kt < n_all; ++kt) {
     stage(kt);
     compute(kt);
   }
-  stage(n_kt - 1);
-  if ((n_kt - 1) * BN <= wave_last) compute(n_kt - 1);
+  if (n_all < n_kt) {
+    stage(n_all);
+    if (n_all * BN <= wave_last) compute(n_all);
+  }
+  if (n_all + 1 < n_kt) {
+    stage(n_all + 1);
+    if ((n_all + 1) * BN <= wave_last) compute(n_all + 1);
+  }
 
   // Normalise and write O[qrow][d] for d = 32 db + 8 g + 4 h + 0..3.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qrow >= S) return;
   const float inv = 1.f / l_tot;
-  char *orow = a.o + ((step_head * a.Hq + hq) * (size_t)S + qrow) * D * EB;
+  char *orow = a.o + ((size_t)l * a.q_sl + (size_t)hq * a.q_sh + a.q_row0[bb]) * RB +
+               (size_t)qrow * q_stride;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -349,28 +397,36 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
 }
 
 // Register budgets: at D = 64, three workgroups per CU for bf16 and two for
-// fp32; D = 128 keeps one, since capping it would spill.
-template <int DT>
+// fp32; D = 128 keeps one, since capping it would spill.  HIST: some
+// sequence has cached positions before its new tokens.
+template <int DT, bool HIST>
 __global__ __launch_bounds__(256, DT == KVC_BF16 ? 3 : 2) void prefill_kernel_d64(PrefillArgs a) {
-  prefill_tile<DT, 64>(a);
+  prefill_tile<DT, 64, HIST>(a);
 }
-template <int DT>
-__global__ __launch_bounds__(256) void prefill_kernel_d128(PrefillArgs a) { prefill_tile<DT, 128>(a); }
+template <int DT, bool HIST>
+__global__ __launch_bounds__(256) void prefill_kernel_d128(PrefillArgs a) {
+  prefill_tile<DT, 128, HIST>(a);
+}
+
+template <int DT, bool HIST>
+void launch_dt(const PrefillArgs &a, int D, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n_layers * a.Hq), (unsigned)(a.q_tiles * a.nb));
+  if (D == 64)
+    hipLaunchKernelGGL((prefill_kernel_d64<DT, HIST>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel_d128<DT, HIST>), grid, dim3(256), 0, s, a);
+}
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, hipStream_t s) {
-  const dim3 grid((unsigned)(a.n_layers * a.B * a.Hq), (unsigned)a.q_tiles);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, hipStream_t s) {
+  if (a.q_tiles <= 0 || a.nb <= 0) return hipSuccess;
   if (dtype == KVC_F32) {
-    if (D == 64)
-      hipLaunchKernelGGL((prefill_kernel_d64<KVC_F32>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel_d128<KVC_F32>), grid, dim3(256), 0, s, a);
+    if (history) launch_dt<KVC_F32, true>(a, D, s);
+    else launch_dt<KVC_F32, false>(a, D, s);
   } else {
-    if (D == 64)
-      hipLaunchKernelGGL((prefill_kernel_d64<KVC_BF16>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel_d128<KVC_BF16>), grid, dim3(256), 0, s, a);
+    if (history) launch_dt<KVC_BF16, true>(a, D, s);
+    else launch_dt<KVC_BF16, false>(a, D, s);
   }
   return hipGetLastError();
 }

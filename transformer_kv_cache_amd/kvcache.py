@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 3  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 4  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -99,6 +99,9 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_combine.restype = i32
         lib.kvc_attn_prefill.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp]
         lib.kvc_attn_prefill.restype = i32
+        lib.kvc_attn_prefill_varlen.argtypes = [cp, i32, i32, vp, vp, vp, i32, ip, ip,
+                                                ctypes.c_float, vp, vp]
+        lib.kvc_attn_prefill_varlen.restype = i32
         pp = ctypes.POINTER(PagedCacheDesc)
         f32 = ctypes.c_float
         lib.kvc_paged_cache_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -350,6 +353,35 @@ def attn_prefill(cache: KVCache, q, k, v, scale: float | None = None, out=None,
     _check(library().kvc_attn_prefill(
         ctypes.byref(d), layer0, n_layers, q.data_ptr(), k.data_ptr(), v.data_ptr(), Hq, S,
         float(scale), out.data_ptr(), _stream(cache.device, stream)))
+    return out
+
+
+def attn_prefill_varlen(cache: KVCache, q, k, v, cu_seqlens, hist_len, scale: float | None = None,
+                        out=None, layer0: int = 0, stream=None):
+    """Packed variable-length prefill with history: q [n_layers,T,Hq,D], k/v
+    [n_layers,T,Hkv,D] token-major; sequence b's new tokens are rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 and go to cache positions hist_len[b]
+    ..; new token i of sequence b attends to positions 0 .. hist_len[b]+i."""
+    n_layers, T, Hq, _ = q.shape
+    _check_tensor("q", q, cache, (n_layers, T, Hq, cache.D))
+    _check_tensor("k", k, cache, (n_layers, T, cache.Hkv, cache.D))
+    _check_tensor("v", v, cache, (n_layers, T, cache.Hkv, cache.D))
+    cu = np.ascontiguousarray(
+        cu_seqlens.cpu().numpy() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens,
+        dtype=np.int32)
+    if cu.shape != (cache.B + 1,) or int(cu[-1]) != T:
+        raise ValueError(f"cu_seqlens must have shape ({cache.B + 1},) and end at T = {T}")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, tuple(q.shape))
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, cache.B)
+    d = cache.desc()
+    _check(library().kvc_attn_prefill_varlen(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), k.data_ptr(), v.data_ptr(), Hq,
+        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), hp, float(scale), out.data_ptr(),
+        _stream(cache.device, stream)))
     return out
 
 

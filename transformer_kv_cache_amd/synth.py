@@ -275,3 +275,57 @@ def paged_batched_decode(seed=0, gqa=False, block_size=16, B=8, L=12) -> PagedWo
                                seed=seed, dtype="bf16", L=L, B=B, Hq=Hq, Hkv=Hkv, D=D,
                                block_size=block_size, max_blocks=1024 // block_size,
                                draw_lengths=(1, 1024))
+
+
+# ---- packed variable-length prefill inputs ---------------------------------
+
+@dataclass
+class VarlenWorkload:
+    """A cache with per-sequence history (as ``Workload``) plus one packed
+    prefill: ``q`` ``[L, T, Hq, D]``, ``k``/``v`` ``[L, T, Hkv, D]``
+    token-major, sequence b's new tokens at rows ``cu_seqlens[b] ..
+    cu_seqlens[b+1]-1``."""
+    name: str
+    dtype: str
+    L: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    Tmax: int
+    hist: np.ndarray
+    cu_seqlens: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+def make_varlen_workload(name, *, seed, dtype, L, B, Hq, Hkv, D, Tmax, hist, lens) -> VarlenWorkload:
+    base = make_workload(name, seed=seed, dtype=dtype, L=L, B=B, Hq=Hq, Hkv=Hkv, D=D, Tmax=Tmax,
+                         hist=hist)
+    rng = np.random.default_rng(seed + 7919)
+    lens = np.asarray(lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = (as_dtype(_normal(rng, (L, T, H, D)), dtype) for H in (Hq, Hkv, Hkv))
+    return VarlenWorkload(name, dtype, L, B, Hq, Hkv, D, Tmax, base.hist, cu, base.k_cache,
+                          base.v_cache, q, k, v)
+
+
+def varlen_prefill_batch(seed=0, dtype="bf16", gqa=False, B=8, L=12) -> VarlenWorkload:
+    """A packed batch of B prompts: prompt lengths U[1, 512] on cached
+    prefixes U[0, 512] (a prefix-cache hit, or an earlier chunk), Tmax=1024;
+    MHA (H=12, D=64) or GQA (32 query heads, 8 KV heads, D=128)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, 513, size=B)
+    hist = rng.integers(0, 513, size=B)
+    Hq, Hkv, D = (32, 8, 128) if gqa else (12, 12, 64)
+    return make_varlen_workload(f"varlen_prefill_{'gqa' if gqa else 'mha'}_{dtype}", seed=seed,
+                                dtype=dtype, L=L, B=B, Hq=Hq, Hkv=Hkv, D=D, Tmax=1024, hist=hist,
+                                lens=lens)
