@@ -302,6 +302,32 @@ def bench_prefill(torch, K, S, dtype, reps, rotate=4):
             "hbm_gbs": hbm_bytes / us / 1e3, "algorithmic_flops": flops}
 
 
+def bench_varlen_prefill(torch, K, w, reps, rotate=4):
+    """Time one packed variable-length prefill (synth.VarlenWorkload)."""
+    from gpu_common import to_dev, torch_dtype
+    dt = torch_dtype(w.dtype)
+    qs, ks, vs = (replicate(torch, to_dev(a), rotate) for a in (w.q, w.k, w.v))
+    caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=kk, v=vv) for kk, vv in
+              zip(replicate(torch, to_dev(w.k_cache), rotate),
+                  replicate(torch, to_dev(w.v_cache), rotate))]
+    outs = [torch.empty_like(qs[0]) for _ in range(rotate)]
+
+    def call(r):
+        K.attn_prefill_varlen(caches[r], qs[r], ks[r], vs[r], w.cu_seqlens, w.hist,
+                              scale=w.scale, out=outs[r])
+
+    for r in range(rotate):
+        call(r)
+    us = GraphTimer(torch, call, rotate).time(reps)
+    lens = np.diff(w.cu_seqlens).astype(np.int64)
+    hist = w.hist.astype(np.int64)
+    # new token i of sequence b attends to P_b + i + 1 positions
+    flops = int(4 * w.D * w.L * w.Hq * np.sum(lens * hist + lens * (lens + 1) // 2))
+    tflops = flops / us / 1e6
+    return {"us": us, "tflops": tflops, "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.dtype],
+            "algorithmic_flops": flops, "lengths": lens.tolist(), "history": hist.tolist()}
+
+
 def cpu_baseline(w, target_s, max_steps=100000):
     """The oracle, as it stands, on a bounded sample of the headline step:
     append + attention for all 12 layers, repeated until ~target_s seconds."""
@@ -427,6 +453,13 @@ def main():
                 pre.append({k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in bench_prefill(torch, K, S, dtype, 40).items()})
         extras["prefill_12layer"] = pre
+        varlen = {}
+        for gqa in (False, True):
+            name = "bf16_" + ("gqa32q8kv_D128" if gqa else "mha12_D64") + "_B8"
+            log(f"varlen prefill {name}")
+            r = bench_varlen_prefill(torch, K, synth.varlen_prefill_batch(seed=5, gqa=gqa), 20)
+            varlen[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        extras["prefill_varlen_12layer"] = varlen
 
     step_us = head["step_us"]
     traffic = read_traffic()

@@ -185,7 +185,6 @@ kvc::PrefillArgs prefill_args(const kvc_cache *cache, int32_t layer0, int32_t n_
 void set_slice(kvc::PrefillArgs *a, int b0, int B) {
   a->b0 = b0;
   a->nb = B - b0 < kvc::kMaxBatchPerLaunch ? B - b0 : kvc::kMaxBatchPerLaunch;
-  a->nb_div = kvc::magic_for(a->nb);
 }
 
 }  // namespace
@@ -366,8 +365,7 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_la
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
   const int64_t tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-  const int64_t slice = cache->B < kvc::kMaxBatchPerLaunch ? cache->B : kvc::kMaxBatchPerLaunch;
-  if (tiles * slice > 65535 || (int64_t)cache->B * Hq * S >= 4294967296LL)
+  if (tiles > 65535 || (int64_t)cache->B * Hq * S >= 4294967296LL)
     return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or rows for one launch", fn);
 
   // Padded layout [n_layers, B, H, S, D]: no history, S new tokens each.
@@ -428,8 +426,7 @@ kvc_status kvc_attn_prefill_varlen(const kvc_cache *cache, int32_t layer0, int32
   int max_len = 0;
   for (int b = 0; b < cache->B; ++b) max_len = lens[b] > max_len ? lens[b] : max_len;
   const int64_t tiles = (max_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-  const int64_t slice = cache->B < kvc::kMaxBatchPerLaunch ? cache->B : kvc::kMaxBatchPerLaunch;
-  if (tiles * slice > 65535 || T * Hq >= 4294967296LL)
+  if (tiles > 65535 || T * Hq >= 4294967296LL)
     return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or tokens for one launch", fn);
 
   // Packed token-major layout [n_layers, T, H, D].

@@ -152,7 +152,6 @@ struct PrefillArgs {
   int32_t layer0, n_layers, group;
   int32_t b0, nb;
   int32_t q_tiles;      // most query tiles of one sequence in the slice
-  uint32_t nb_div;      // div_magic multiplier for nb
   float scale_log2;
   int64_t q_sl, kv_sl;
   int32_t q_sh, q_si, kv_sh, kv_si;

@@ -111,21 +111,36 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   const int h = lane >> 5;     // half-wave
   const int col = lane & 31;   // MFMA column / row within a 32 block
 
-  // Grid: x = (layer, query head); y = (tile rank, sequence in the slice),
-  // sequence fastest, so that every sequence's longest (last) query tiles
-  // come first.
+  // Grid: x = (layer, query head); y = tile rank, so that every sequence's
+  // longest (last) query tiles come first; z = sequence in the slice, read
+  // straight from the grid so that its length and offsets load in the first
+  // scalar round.
   const int head = blockIdx.x;
-  const int hq = head % a.Hq;
-  const int l = head / a.Hq;
-  const int rank = div_magic((int)blockIdx.y, a.nb, a.nb_div);
-  const int bb = (int)blockIdx.y - rank * a.nb;
+  const int rank = blockIdx.y;
+  const int bb = blockIdx.z;
+  // Every kernel argument the prologue needs, fetched in one scalar round
+  // (the empty asm takes them all as operands, so none of their loads is
+  // deferred behind the early exit or the index arithmetic).
   const int S = a.len[bb];   // new tokens of this sequence
   const int P = HIST ? a.hist[bb] : 0;  // positions already cached
+  const uint32_t q_row0 = a.q_row0[bb], kv_row0 = a.kv_row0[bb];
+  const int Hq = a.Hq, group = a.group, Bn = a.B, Hkv = a.Hkv, Tmax = a.Tmax;
+  const int layer0 = a.layer0, b0 = a.b0;
+  const int64_t q_sl = a.q_sl, kv_sl = a.kv_sl;
+  const int q_sh = a.q_sh, q_si = a.q_si, kv_sh = a.kv_sh, kv_si = a.kv_si;
+  const char *qp = a.q, *kp_in = a.k, *vp_in = a.v;
+  char *kcp = a.k_cache, *vcp = a.v_cache;
+  asm volatile("" ::"s"(S), "s"(P), "s"(q_row0), "s"(kv_row0), "s"(Hq), "s"(group), "s"(Bn),
+               "s"(Hkv), "s"(Tmax), "s"(layer0), "s"(b0), "s"(q_sl), "s"(kv_sl), "s"(q_sh),
+               "s"(q_si), "s"(kv_sh), "s"(kv_si), "s"(qp), "s"(kp_in), "s"(vp_in), "s"(kcp),
+               "s"(vcp));
   const int qt = (S + BM - 1) / BM - 1 - rank;
   if (qt < 0) return;
-  const int b = a.b0 + bb;
-  const int hkv = hq / a.group;
-  const bool writer = (hq % a.group) == 0;
+  const int hq = head % Hq;
+  const int l = head / Hq;
+  const int b = b0 + bb;
+  const int hkv = hq / group;
+  const bool writer = (hq % group) == 0;
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + col;            // this lane's new token
   const int wave_last = P + q0 + wave * 32 + 31;    // last position the wave's rows see
@@ -134,28 +149,29 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
 
   // New token i of this sequence: q / o at qbase + i * q_stride, its k / v
   // at kin / vin + i * kv_stride.  Cached position j at kcache / vcache + j * RB.
-  const char *qbase = a.q + ((size_t)l * a.q_sl + (size_t)hq * a.q_sh + a.q_row0[bb]) * RB;
-  const size_t q_stride = (size_t)a.q_si * RB;
-  const size_t kv_in = ((size_t)l * a.kv_sl + (size_t)hkv * a.kv_sh + a.kv_row0[bb]) * RB;
-  const char *kin = a.k + kv_in;
-  const char *vin = a.v + kv_in;
-  const size_t kv_stride = (size_t)a.kv_si * RB;
-  const size_t crow0 = (((size_t)(a.layer0 + l) * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax;
-  char *kcache = a.k_cache + crow0 * RB;
-  char *vcache = a.v_cache + crow0 * RB;
+  const size_t q_off = ((size_t)l * q_sl + (size_t)hq * q_sh + q_row0) * RB;
+  const char *qbase = qp + q_off;
+  const size_t q_stride = (size_t)q_si * RB;
+  const size_t kv_in = ((size_t)l * kv_sl + (size_t)hkv * kv_sh + kv_row0) * RB;
+  const char *kin = kp_in + kv_in;
+  const char *vin = vp_in + kv_in;
+  const size_t kv_stride = (size_t)kv_si * RB;
+  const size_t crow0 = (((size_t)(layer0 + l) * Bn + b) * Hkv + hkv) * (size_t)Tmax;
+  char *kcache = kcp + crow0 * RB;
+  char *vcache = vcp + crow0 * RB;
 
   // Q fragments, resident for the whole kernel.
   //   bf16: qv[ds] = Q[qrow][16 ds + 8 h .. +7]        (B operand of 32x32x16)
   //   fp32: qv[j]  = Q[qrow][8 j + 4 h .. +3]           (4 B operands of 32x32x2)
+  //   Rows past the sequence read its last row (valid, finite); their
+  //   outputs are never written.
   constexpr int QV = (DT == KVC_BF16) ? D / 16 : D / 8;
   u32x4 qv[QV];
+  const char *qrow_p = qbase + (size_t)(qrow < S ? qrow : S - 1) * q_stride;
 #pragma unroll
   for (int j = 0; j < QV; ++j) {
-    qv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (qrow < S) {
-      const int d0 = (DT == KVC_BF16) ? 16 * j + 8 * h : 8 * j + 4 * h;
-      qv[j] = *reinterpret_cast<const u32x4 *>(qbase + (size_t)qrow * q_stride + d0 * EB);
-    }
+    const int d0 = (DT == KVC_BF16) ? 16 * j + 8 * h : 8 * j + 4 * h;
+    qv[j] = *reinterpret_cast<const u32x4 *>(qrow_p + d0 * EB);
   }
 
   f32x16 acc_o[DB];
@@ -180,21 +196,37 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   auto tile_row = [&](int it) { return 2 * (tid / LPR + (it >> 1) * (256 / LPR)) + (it & 1); };
   const int c = tid % LPR;
   u32x4 kreg[VPT], vreg[VPT];
-  auto load_tile = [&](int kt) {
+  // Byte offset of this thread's rows inside a tile of new rows (loop
+  // invariant, so the common tile costs no per-lane multiply).
+  size_t in_off[VPT];
 #pragma unroll
-    for (int it = 0; it < VPT; ++it) {
-      const int key0 = kt * BN + tile_row(it);
-      const int key = key0 < kv_end ? key0 : kv_end - 1;
-      const char *kp, *vp;
-      if (HIST && key < P) {
-        kp = kcache + (size_t)key * RB;
-        vp = vcache + (size_t)key * RB;
-      } else {
-        kp = kin + (size_t)(key - P) * kv_stride;
-        vp = vin + (size_t)(key - P) * kv_stride;
+  for (int it = 0; it < VPT; ++it) in_off[it] = (size_t)tile_row(it) * kv_stride + c * 16;
+  auto load_tile = [&](int kt) {
+    const int tk0 = kt * BN;
+    if (tk0 + BN <= kv_end && (!HIST || tk0 >= P)) {
+      // the whole tile is new rows, none past kv_end
+      const size_t base = (size_t)(tk0 - P) * kv_stride;
+#pragma unroll
+      for (int it = 0; it < VPT; ++it) {
+        kreg[it] = *reinterpret_cast<const u32x4 *>(kin + base + in_off[it]);
+        vreg[it] = *reinterpret_cast<const u32x4 *>(vin + base + in_off[it]);
       }
-      kreg[it] = *reinterpret_cast<const u32x4 *>(kp + c * 16);
-      vreg[it] = *reinterpret_cast<const u32x4 *>(vp + c * 16);
+    } else {
+#pragma unroll
+      for (int it = 0; it < VPT; ++it) {
+        const int key0 = tk0 + tile_row(it);
+        const int key = key0 < kv_end ? key0 : kv_end - 1;
+        const char *kp, *vp;
+        if (HIST && key < P) {
+          kp = kcache + (size_t)key * RB;
+          vp = vcache + (size_t)key * RB;
+        } else {
+          kp = kin + (size_t)(key - P) * kv_stride;
+          vp = vin + (size_t)(key - P) * kv_stride;
+        }
+        kreg[it] = *reinterpret_cast<const u32x4 *>(kp + c * 16);
+        vreg[it] = *reinterpret_cast<const u32x4 *>(vp + c * 16);
+      }
     }
   };
   load_tile(0);
@@ -378,8 +410,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qrow >= S) return;
   const float inv = 1.f / l_tot;
-  char *orow = a.o + ((size_t)l * a.q_sl + (size_t)hq * a.q_sh + a.q_row0[bb]) * RB +
-               (size_t)qrow * q_stride;
+  char *orow = a.o + q_off + (size_t)qrow * q_stride;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -410,7 +441,7 @@ __global__ __launch_bounds__(256) void prefill_kernel_d128(PrefillArgs a) {
 
 template <int DT, bool HIST>
 void launch_dt(const PrefillArgs &a, int D, hipStream_t s) {
-  const dim3 grid((unsigned)(a.n_layers * a.Hq), (unsigned)(a.q_tiles * a.nb));
+  const dim3 grid((unsigned)(a.n_layers * a.Hq), (unsigned)a.q_tiles, (unsigned)a.nb);
   if (D == 64)
     hipLaunchKernelGGL((prefill_kernel_d64<DT, HIST>), grid, dim3(256), 0, s, a);
   else
