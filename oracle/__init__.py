@@ -83,6 +83,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_paged_append.restype = i32
     lib.oracle_paged_attention.argtypes = [vp, vp, vp] + [i32] * 11 + [vp, vp, i32, dbl, vp]
     lib.oracle_paged_attention.restype = i32
+    lib.oracle_paged_prefill_varlen.argtypes = [vp, vp] + [i32] * 8 + [vp, vp, vp, i32, i32, vp,
+                                                                       vp, vp, i32, dbl, vp]
+    lib.oracle_paged_prefill_varlen.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_set_threads.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -243,6 +246,33 @@ def paged_attention(q, k_pool, v_pool, hist_len, block_table, scale, layer0=0, l
                                     layer0, n_layers, Hq, B, N, _ptr(hist), _ptr(bt), bt.shape[1],
                                     float(scale), _ptr(out))
     _check(rc, "oracle_paged_attention")
+    return out
+
+
+def paged_prefill_varlen(k_pool, v_pool, q, k, v, cu_seqlens, hist_len, block_table, scale,
+                         layer0=0, lib=None) -> np.ndarray:
+    """prefill_varlen into a paged cache (pools [L, num_blocks, Hkv,
+    block_size, D], block_table int32 [B, max_blocks])."""
+    lib = lib or load()
+    L, nblk, Hkv, bs, D, bt = _paged_shapes(k_pool, v_pool, block_table, "paged_prefill_varlen")
+    n_layers, T, Hq, D2 = q.shape
+    B = bt.shape[0]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if D2 != D or k.shape != (n_layers, T, Hkv, D) or v.shape != k.shape or cu.shape != (B + 1,):
+        raise ValueError("paged_prefill_varlen: shape mismatch")
+    if int(cu[-1]) != T:
+        raise ValueError("paged_prefill_varlen: cu_seqlens[B] must equal the packed token count")
+    dt = _dtype_code(k_pool)
+    for a in (v_pool, q, k, v):
+        if _dtype_code(a) != dt:
+            raise TypeError("paged_prefill_varlen: dtype mismatch")
+    hist = np.ascontiguousarray(hist_len, dtype=np.int32)
+    out = np.zeros(q.shape, dtype=np.float64)
+    rc = lib.oracle_paged_prefill_varlen(_ptr(k_pool), _ptr(v_pool), L, nblk, Hkv, bs, D, dt,
+                                         layer0, n_layers, _ptr(q), _ptr(k), _ptr(v), Hq, B,
+                                         _ptr(cu), _ptr(hist), _ptr(bt), bt.shape[1], float(scale),
+                                         _ptr(out))
+    _check(rc, "oracle_paged_prefill_varlen")
     return out
 
 

@@ -351,14 +351,17 @@ static size_t paged_row(int l, int blk, int h, int r, int num_blocks, int Hkv,
 static int paged_check(int L, int num_blocks, int Hkv, int block_size, int D,
                        int layer0, int n_layers, int B, int N,
                        const int32_t *hist_len, const int32_t *block_table,
-                       int max_blocks) {
+                       int max_blocks, const int32_t *cu_seqlens) {
   if (L < 0 || num_blocks < 0 || Hkv <= 0 || block_size <= 0 || D <= 0 ||
       B < 0 || N < 0 || max_blocks < 0 || layer0 < 0 || n_layers < 0 ||
       layer0 + n_layers > L)
     return ORACLE_E_ARG;
   for (int b = 0; b < B; ++b) {
     if (hist_len[b] < 0) return ORACLE_E_ARG;
-    const int64_t end = (int64_t)hist_len[b] + N;
+    /* N new rows each, or sequence b's share of a packed batch */
+    const int n_new = cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : N;
+    if (n_new < 0) return ORACLE_E_ARG;
+    const int64_t end = (int64_t)hist_len[b] + n_new;
     if (end > (int64_t)max_blocks * block_size) return ORACLE_E_CAPACITY;
     for (int64_t j = 0; j * block_size < end; ++j) {
       const int32_t blk = block_table[(size_t)b * max_blocks + j];
@@ -382,7 +385,7 @@ int oracle_paged_append(void *k_pool, void *v_pool, int L, int num_blocks,
                         int B, int N, const int32_t *hist_len,
                         const int32_t *block_table, int max_blocks) {
   int rc = paged_check(L, num_blocks, Hkv, block_size, D, layer0, n_layers, B,
-                       N, hist_len, block_table, max_blocks);
+                       N, hist_len, block_table, max_blocks, NULL);
   if (rc != ORACLE_OK) return rc;
   const size_t es = elem_size(dtype);
   for (int l = 0; l < n_layers; ++l)
@@ -415,7 +418,7 @@ int oracle_paged_attention(const void *q, const void *k_pool,
                            const int32_t *hist_len, const int32_t *block_table,
                            int max_blocks, double scale, double *out) {
   int rc = paged_check(L, num_blocks, Hkv, block_size, D, layer0, n_layers, B,
-                       N, hist_len, block_table, max_blocks);
+                       N, hist_len, block_table, max_blocks, NULL);
   if (rc != ORACLE_OK) return rc;
   if (Hq <= 0 || Hq % Hkv != 0) return ORACLE_E_ARG;
   const int Tlog = max_blocks * block_size;
@@ -441,6 +444,65 @@ int oracle_paged_attention(const void *q, const void *k_pool,
         }
   rc = oracle_attention(q, kc, vc, n_layers, B, Hkv, Tlog, D, dtype, 0,
                         n_layers, Hq, N, hist_len, scale, out);
+  free(kc);
+  free(vc);
+  return rc;
+}
+
+/*
+ * Packed variable-length prefill into a paged cache: gather each sequence's
+ * cached positions [0, P_b) in order into a contiguous copy, run
+ * oracle_prefill_varlen on it, and write the new rows, positions [P_b, P_b +
+ * S_b), back to their slots.  Same definition; only where rows live differs.
+ */
+int oracle_paged_prefill_varlen(void *k_pool, void *v_pool, int L,
+                                int num_blocks, int Hkv, int block_size, int D,
+                                int dtype, int layer0, int n_layers,
+                                const void *q, const void *k, const void *v,
+                                int Hq, int B, const int32_t *cu_seqlens,
+                                const int32_t *hist_len,
+                                const int32_t *block_table, int max_blocks,
+                                double scale, double *out) {
+  if (B < 0 || cu_seqlens[0] != 0) return ORACLE_E_ARG;
+  int rc = paged_check(L, num_blocks, Hkv, block_size, D, layer0, n_layers, B,
+                       0, hist_len, block_table, max_blocks, cu_seqlens);
+  if (rc != ORACLE_OK) return rc;
+  const int Tlog = max_blocks * block_size;
+  const size_t es = elem_size(dtype);
+  const size_t n = (size_t)n_layers * B * Hkv * (size_t)Tlog * D;
+  char *kc = (char *)calloc(n > 0 ? n : 1, es);
+  char *vc = (char *)calloc(n > 0 ? n : 1, es);
+  if (!kc || !vc) {
+    free(kc);
+    free(vc);
+    return ORACLE_E_ARG;
+  }
+  for (int l = 0; l < n_layers; ++l)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < Hkv; ++h)
+        for (int cpos = 0; cpos < hist_len[b]; ++cpos) {
+          const int blk = block_table[(size_t)b * max_blocks + cpos / block_size];
+          const size_t src = paged_row(layer0 + l, blk, h, cpos % block_size,
+                                       num_blocks, Hkv, block_size, D);
+          const size_t dst = cache_row(l, b, h, cpos, B, Hkv, Tlog, D);
+          memcpy(kc + dst * es, (const char *)k_pool + src * es, (size_t)D * es);
+          memcpy(vc + dst * es, (const char *)v_pool + src * es, (size_t)D * es);
+        }
+  rc = oracle_prefill_varlen(kc, vc, n_layers, B, Hkv, Tlog, D, dtype, 0,
+                             n_layers, q, k, v, Hq, cu_seqlens, hist_len,
+                             scale, out);
+  if (rc == ORACLE_OK)
+    for (int l = 0; l < n_layers; ++l)
+      for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h)
+          for (int npos = hist_len[b]; npos < hist_len[b] + cu_seqlens[b + 1] - cu_seqlens[b]; ++npos) {
+            const int blk = block_table[(size_t)b * max_blocks + npos / block_size];
+            const size_t dst = paged_row(layer0 + l, blk, h, npos % block_size,
+                                         num_blocks, Hkv, block_size, D);
+            const size_t src = cache_row(l, b, h, npos, B, Hkv, Tlog, D);
+            memcpy((char *)k_pool + dst * es, kc + src * es, (size_t)D * es);
+            memcpy((char *)v_pool + dst * es, vc + src * es, (size_t)D * es);
+          }
   free(kc);
   free(vc);
   return rc;

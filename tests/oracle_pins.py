@@ -613,6 +613,37 @@ def pin_varlen_refusals(lib):
         assert synth.is_canary(kc).all() and synth.is_canary(vc).all()
 
 
+def pin_paged_varlen_equals_contiguous(lib):
+    """The packed prefill into a paged cache (shuffled table) gives the
+    contiguous packed prefill's outputs bit for bit, and leaves the new rows
+    where a following decode step reads them: that step's outputs match too."""
+    rng = _rng(73)
+    L, B, Hkv, G, D, bs, mb = 2, 3, 2, 2, 8, 4, 8
+    nblk = B * mb + 3
+    lens = [6, 0, 9]
+    hist = np.array([5, 12, 0], np.int32)
+    kc, vc = _empty_cache(L, B, Hkv, bs * mb, D)
+    _fill_history(kc, vc, hist, rng)
+    bt = rng.permutation(nblk)[: B * mb].astype(np.int32).reshape(B, mb)
+    kp, vp = _paged_from_history(lib, kc, vc, hist, bt, nblk, bs)
+    T = sum(lens)
+    q = rng.standard_normal((L, T, Hkv * G, D), dtype=np.float32)
+    k = rng.standard_normal((L, T, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((L, T, Hkv, D), dtype=np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ref = oracle.prefill_varlen(kc, vc, q, k, v, cu, hist, 0.4, lib=lib)
+    got = oracle.paged_prefill_varlen(kp, vp, q, k, v, cu, hist, bt, 0.4, lib=lib)
+    assert np.array_equal(got, ref)
+    h2 = hist + np.array(lens, np.int32)
+    q1 = rng.standard_normal((L, B, Hkv * G, 1, D), dtype=np.float32)
+    k1 = rng.standard_normal((L, B, Hkv, 1, D), dtype=np.float32)
+    v1 = rng.standard_normal((L, B, Hkv, 1, D), dtype=np.float32)
+    ref1 = _decode(lib, kc, vc, q1, k1, v1, h2, 0.4)
+    oracle.paged_append(kp, vp, k1, v1, h2, bt, lib=lib)
+    got1 = oracle.paged_attention(q1, kp, vp, h2, bt, 0.4, lib=lib)
+    assert np.array_equal(got1, ref1)
+
+
 ALL_PINS = [
     pin_cache_bytes_golden,
     pin_single_key_exact,
@@ -635,4 +666,5 @@ ALL_PINS = [
     pin_varlen_equals_padded,
     pin_varlen_ragged_equals_per_sequence,
     pin_varlen_refusals,
+    pin_paged_varlen_equals_contiguous,
 ]

@@ -79,6 +79,8 @@ MUTANTS = {
                                 "const size_t qrow = (((size_t)l * Hq + hq) * T + cu_seqlens[b] + i) * (size_t)D;"),
     "varlen_tokens_head_major": ("const size_t src = (((size_t)l * T + cu_seqlens[b] + i) * Hkv + h) * (size_t)D;",
                                  "const size_t src = (((size_t)l * Hkv + h) * T + cu_seqlens[b] + i) * (size_t)D;"),
+    "paged_prefill_writes_history_slots": ("for (int npos = hist_len[b]; npos < hist_len[b] + cu_seqlens[b + 1] - cu_seqlens[b]; ++npos) {",
+                                           "for (int npos = 0; npos < cu_seqlens[b + 1] - cu_seqlens[b]; ++npos) {"),
     # the paged cache: block-table lookup, row inside the block, head, layer
     "paged_append_block_from_offset": ("block_table[(size_t)b * max_blocks + t / block_size]",
                                        "block_table[(size_t)b * max_blocks + t % block_size]"),
