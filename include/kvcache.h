@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef enum {
   KVC_OK = 0,
@@ -323,6 +323,21 @@ kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0,
                                  const int32_t *block_table, int32_t max_blocks,
                                  float scale, void *o, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* kvc_attn_prefill_varlen into a paged cache: cached positions below
+ * hist_len[b] are read through sequence b's block table and the new tokens'
+ * K/V are written to their slots.  B sequences (cu_seqlens [B + 1],
+ * hist_len [B] on the host; block_table [B, max_blocks] on the device);
+ * capacity max_blocks * block_size positions per sequence. */
+kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache,
+                                         int32_t layer0, int32_t n_layers,
+                                         const void *q, const void *k,
+                                         const void *v, int32_t Hq, int32_t B,
+                                         const int32_t *cu_seqlens,
+                                         const int32_t *hist_len,
+                                         const int32_t *block_table,
+                                         int32_t max_blocks, float scale,
+                                         void *o, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvc_last_error(void);

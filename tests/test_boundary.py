@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 4
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 5
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -339,3 +339,35 @@ def test_varlen_prefill_error_paths(lib):
     assert call(c=ctypes.byref(desc(h, D=32))) == E_UNSUPPORTED
     assert call(cu=hist(0, 0, 0), q=None, k=None, v=None, o=None) == OK  # no tokens: no-op
 
+
+
+def test_paged_varlen_prefill_error_paths(lib):
+    h = Host()
+    d = pdesc(h)  # L=2, 8 blocks, Hkv=2, block_size=4, D=64
+    p = h.ptr()
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=p, k=p, v=p, Hq=4, B=2,
+                 cu=hist(0, 3, 7), hist=hist(2, 5), bt=h.ptr(), mb=4, scale=0.125, o=p)
+        a.update(kw)
+        return lib.kvc_paged_attn_prefill_varlen(a["c"], a["layer0"], a["n_layers"], a["q"],
+                                                 a["k"], a["v"], a["Hq"], a["B"], a["cu"],
+                                                 a["hist"], a["bt"], a["mb"], a["scale"], a["o"],
+                                                 None)
+
+    assert call(cu=hist(1, 3, 7)) == E_SHAPE              # does not start at 0
+    assert call(cu=hist(0, 5, 3)) == E_SHAPE              # decreases
+    assert call(cu=None) == E_NULL
+    assert call(hist=hist(2, 13)) == E_CAPACITY           # 13 + 4 > 4 blocks x 4
+    assert "exceeds" in err(lib)
+    assert call(hist=hist(-1, 0)) == E_SHAPE
+    assert call(bt=None) == E_NULL
+    assert call(bt=h.ptr(offset=2)) == E_NULL             # misaligned table
+    assert call(mb=-1) == E_SHAPE
+    assert call(Hq=3) == E_SHAPE
+    assert call(q=None) == E_NULL
+    assert call(layer0=1) == E_SHAPE
+    assert call(scale=float("inf")) == E_SHAPE
+    assert call(c=ctypes.byref(pdesc(h, bs=6))) == E_SHAPE
+    assert call(c=ctypes.byref(pdesc(h, D=32))) == E_UNSUPPORTED
+    assert call(cu=hist(0, 0, 0), q=None, k=None, v=None, o=None) == OK  # no tokens: no-op

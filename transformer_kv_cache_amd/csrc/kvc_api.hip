@@ -187,6 +187,73 @@ void set_slice(kvc::PrefillArgs *a, int b0, int B) {
   a->nb = B - b0 < kvc::kMaxBatchPerLaunch ? B - b0 : kvc::kMaxBatchPerLaunch;
 }
 
+// Shared by kvc_attn_prefill_varlen and kvc_paged_attn_prefill_varlen
+// (pg.block_table set: `cache` is the logical view of the pools).
+kvc_status varlen_impl(const char *fn, const kvc_cache *cache, const kvc::PagedGeom &pg,
+                       int32_t layer0, int32_t n_layers, const void *q, const void *k,
+                       const void *v, int32_t Hq, const int32_t *cu_seqlens,
+                       const int32_t *hist_len, float scale, void *o, void *stream) {
+  kvc_status st = check_cache(cache, layer0, n_layers, fn);
+  if (st != KVC_OK) return st;
+  if (Hq <= 0 || Hq % cache->Hkv != 0)
+    return fail(KVC_E_SHAPE, "%s: Hq = %d is not a positive multiple of Hkv = %d", fn, Hq, cache->Hkv);
+  if (!std::isfinite(scale)) return fail(KVC_E_SHAPE, "%s: scale is not finite", fn);
+  if (!cu_seqlens) return fail(KVC_E_NULL, "%s: cu_seqlens is NULL", fn);
+  if (cu_seqlens[0] != 0) return fail(KVC_E_SHAPE, "%s: cu_seqlens[0] = %d, not 0", fn, cu_seqlens[0]);
+  for (int b = 0; b < cache->B; ++b)
+    if (cu_seqlens[b + 1] < cu_seqlens[b])
+      return fail(KVC_E_SHAPE, "%s: cu_seqlens decreases at %d", fn, b + 1);
+  const int64_t T = cu_seqlens[cache->B];
+  std::vector<int32_t> lens(cache->B);
+  for (int b = 0; b < cache->B; ++b) lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+  // capacity: hist_len[b] + S_b <= Tmax, checked per sequence
+  if (cache->B > 0 && !hist_len) return fail(KVC_E_NULL, "%s: hist_len is NULL", fn);
+  for (int b = 0; b < cache->B; ++b) {
+    if (hist_len[b] < 0) return fail(KVC_E_SHAPE, "%s: hist_len[%d] = %d < 0", fn, b, hist_len[b]);
+    if ((int64_t)hist_len[b] + lens[b] > cache->Tmax)
+      return fail(KVC_E_CAPACITY, "%s: hist_len[%d] + S_%d = %d + %d exceeds Tmax = %d", fn, b, b,
+                  hist_len[b], lens[b], cache->Tmax);
+  }
+  if (T == 0 || n_layers == 0 || cache->B == 0) return ok();
+  if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
+  if (!q || !k || !v || !o) return fail(KVC_E_NULL, "%s: q, k, v or o is NULL", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
+  int max_len = 0;
+  for (int b = 0; b < cache->B; ++b) max_len = lens[b] > max_len ? lens[b] : max_len;
+  const int64_t tiles = (max_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+  if (tiles > 65535 || T * Hq >= 4294967296LL)
+    return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or tokens for one launch", fn);
+
+  // Packed token-major layout [n_layers, T, H, D].
+  kvc::PrefillArgs a = prefill_args(cache, layer0, n_layers, q, k, v, Hq, scale, o);
+  a.pg = pg;
+  a.q_sl = T * Hq;
+  a.q_sh = 1;
+  a.q_si = Hq;
+  a.kv_sl = T * cache->Hkv;
+  a.kv_sh = 1;
+  a.kv_si = cache->Hkv;
+  for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
+    set_slice(&a, b0, cache->B);
+    int slice_len = 0;
+    bool history = false;
+    for (int i = 0; i < a.nb; ++i) {
+      const int b = b0 + i;
+      a.hist[i] = hist_len[b];
+      a.len[i] = lens[b];
+      a.q_row0[i] = (uint32_t)((int64_t)cu_seqlens[b] * Hq);
+      a.kv_row0[i] = (uint32_t)((int64_t)cu_seqlens[b] * cache->Hkv);
+      if (lens[b] > slice_len) slice_len = lens[b];
+      if (hist_len[b] > 0 && lens[b] > 0) history = true;
+    }
+    a.q_tiles = (slice_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, history, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,65 +463,8 @@ kvc_status kvc_attn_prefill_varlen(const kvc_cache *cache, int32_t layer0, int32
                                    const void *q, const void *k, const void *v, int32_t Hq,
                                    const int32_t *cu_seqlens, const int32_t *hist_len, float scale,
                                    void *o, void *stream) {
-  static const char *fn = "kvc_attn_prefill_varlen";
-  kvc_status st = check_cache(cache, layer0, n_layers, fn);
-  if (st != KVC_OK) return st;
-  if (Hq <= 0 || Hq % cache->Hkv != 0)
-    return fail(KVC_E_SHAPE, "%s: Hq = %d is not a positive multiple of Hkv = %d", fn, Hq, cache->Hkv);
-  if (!std::isfinite(scale)) return fail(KVC_E_SHAPE, "%s: scale is not finite", fn);
-  if (!cu_seqlens) return fail(KVC_E_NULL, "%s: cu_seqlens is NULL", fn);
-  if (cu_seqlens[0] != 0) return fail(KVC_E_SHAPE, "%s: cu_seqlens[0] = %d, not 0", fn, cu_seqlens[0]);
-  for (int b = 0; b < cache->B; ++b)
-    if (cu_seqlens[b + 1] < cu_seqlens[b])
-      return fail(KVC_E_SHAPE, "%s: cu_seqlens decreases at %d", fn, b + 1);
-  const int64_t T = cu_seqlens[cache->B];
-  std::vector<int32_t> lens(cache->B);
-  for (int b = 0; b < cache->B; ++b) lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
-  // capacity: hist_len[b] + S_b <= Tmax, checked per sequence
-  if (cache->B > 0 && !hist_len) return fail(KVC_E_NULL, "%s: hist_len is NULL", fn);
-  for (int b = 0; b < cache->B; ++b) {
-    if (hist_len[b] < 0) return fail(KVC_E_SHAPE, "%s: hist_len[%d] = %d < 0", fn, b, hist_len[b]);
-    if ((int64_t)hist_len[b] + lens[b] > cache->Tmax)
-      return fail(KVC_E_CAPACITY, "%s: hist_len[%d] + S_%d = %d + %d exceeds Tmax = %d", fn, b, b,
-                  hist_len[b], lens[b], cache->Tmax);
-  }
-  if (T == 0 || n_layers == 0 || cache->B == 0) return ok();
-  if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
-  if (!q || !k || !v || !o) return fail(KVC_E_NULL, "%s: q, k, v or o is NULL", fn);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
-  int max_len = 0;
-  for (int b = 0; b < cache->B; ++b) max_len = lens[b] > max_len ? lens[b] : max_len;
-  const int64_t tiles = (max_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-  if (tiles > 65535 || T * Hq >= 4294967296LL)
-    return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or tokens for one launch", fn);
-
-  // Packed token-major layout [n_layers, T, H, D].
-  kvc::PrefillArgs a = prefill_args(cache, layer0, n_layers, q, k, v, Hq, scale, o);
-  a.q_sl = T * Hq;
-  a.q_sh = 1;
-  a.q_si = Hq;
-  a.kv_sl = T * cache->Hkv;
-  a.kv_sh = 1;
-  a.kv_si = cache->Hkv;
-  for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
-    set_slice(&a, b0, cache->B);
-    int slice_len = 0;
-    bool history = false;
-    for (int i = 0; i < a.nb; ++i) {
-      const int b = b0 + i;
-      a.hist[i] = hist_len[b];
-      a.len[i] = lens[b];
-      a.q_row0[i] = (uint32_t)((int64_t)cu_seqlens[b] * Hq);
-      a.kv_row0[i] = (uint32_t)((int64_t)cu_seqlens[b] * cache->Hkv);
-      if (lens[b] > slice_len) slice_len = lens[b];
-      if (hist_len[b] > 0 && lens[b] > 0) history = true;
-    }
-    a.q_tiles = (slice_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, history, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, fn);
-  }
-  return ok();
+  return varlen_impl("kvc_attn_prefill_varlen", cache, kvc::PagedGeom{}, layer0, n_layers, q, k, v,
+                     Hq, cu_seqlens, hist_len, scale, o, stream);
 }
 
 }  // extern "C"
@@ -518,6 +528,21 @@ kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0, i
   if (st != KVC_OK) return st;
   return decode_impl(fn, kBoth, &view, pg, layer0, n_layers, q, k_new, v_new, true, Hq, N,
                      hist_len, scale, o, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache, int32_t layer0,
+                                         int32_t n_layers, const void *q, const void *k,
+                                         const void *v, int32_t Hq, int32_t B,
+                                         const int32_t *cu_seqlens, const int32_t *hist_len,
+                                         const int32_t *block_table, int32_t max_blocks,
+                                         float scale, void *o, void *stream) {
+  static const char *fn = "kvc_paged_attn_prefill_varlen";
+  kvc_cache view;
+  kvc::PagedGeom pg;
+  kvc_status st = paged_view(cache, B, block_table, max_blocks, fn, &view, &pg);
+  if (st != KVC_OK) return st;
+  return varlen_impl(fn, &view, pg, layer0, n_layers, q, k, v, Hq, cu_seqlens, hist_len, scale, o,
+                     stream);
 }
 
 }  // extern "C"

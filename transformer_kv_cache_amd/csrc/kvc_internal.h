@@ -159,6 +159,7 @@ struct PrefillArgs {
   int32_t len[kMaxBatchPerLaunch];      // S_b
   uint32_t q_row0[kMaxBatchPerLaunch];  // row0 of q / o
   uint32_t kv_row0[kMaxBatchPerLaunch]; // row0 of k / v
+  PagedGeom pg;         // paged cache, else block_table == nullptr
 };
 
 // Host launchers (one translation unit each).  They assume validated

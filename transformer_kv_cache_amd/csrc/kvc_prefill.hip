@@ -92,7 +92,7 @@ template <int D> struct Smem<KVC_F32, D> {
   alignas(16) float v[BN * kVStride];
 };
 
-template <int DT, int D, bool HIST>
+template <int DT, int D, bool HIST, bool PAGED>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   constexpr int EB = Dtype<DT>::kBytes;
   constexpr int EV = Dtype<DT>::kPer16B;
@@ -201,9 +201,25 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   size_t in_off[VPT];
 #pragma unroll
   for (int it = 0; it < VPT; ++it) in_off[it] = (size_t)tile_row(it) * kv_stride + c * 16;
+  // Cached position `key` of this (layer, sequence, KV head): contiguous
+  // rows, or its slot through the block table.
+  auto cache_ptr = [&](char *contig, char *pool, int key) -> char * {
+    if constexpr (PAGED)
+      return pool + paged_row(a.pg, b, key, layer0 + l, hkv, Hkv) * RB;
+    else
+      return contig + (size_t)key * RB;
+  };
   auto load_tile = [&](int kt) {
     const int tk0 = kt * BN;
-    if (tk0 + BN <= kv_end && (!HIST || tk0 >= P)) {
+    if (HIST && !PAGED && tk0 + BN <= P) {
+      // the whole tile is cached rows of a contiguous cache
+#pragma unroll
+      for (int it = 0; it < VPT; ++it) {
+        const size_t off = (size_t)(tk0 + tile_row(it)) * RB + c * 16;
+        kreg[it] = *reinterpret_cast<const u32x4 *>(kcache + off);
+        vreg[it] = *reinterpret_cast<const u32x4 *>(vcache + off);
+      }
+    } else if (tk0 + BN <= kv_end && (!HIST || tk0 >= P)) {
       // the whole tile is new rows, none past kv_end
       const size_t base = (size_t)(tk0 - P) * kv_stride;
 #pragma unroll
@@ -218,8 +234,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
         const int key = key0 < kv_end ? key0 : kv_end - 1;
         const char *kp, *vp;
         if (HIST && key < P) {
-          kp = kcache + (size_t)key * RB;
-          vp = vcache + (size_t)key * RB;
+          kp = cache_ptr(kcache, kcp, key);
+          vp = cache_ptr(vcache, vcp, key);
         } else {
           kp = kin + (size_t)(key - P) * kv_stride;
           vp = vin + (size_t)(key - P) * kv_stride;
@@ -245,9 +261,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
       const int row = tile_row(it);
       const int key = key0 + row;
       if (store_cache && key >= P + q0 && key < kv_end) {
-        const size_t off = (size_t)key * RB + c * 16;
-        *reinterpret_cast<u32x4 *>(kcache + off) = kreg[it];
-        *reinterpret_cast<u32x4 *>(vcache + off) = vreg[it];
+        *reinterpret_cast<u32x4 *>(cache_ptr(kcache, kcp, key) + c * 16) = kreg[it];
+        *reinterpret_cast<u32x4 *>(cache_ptr(vcache, vcp, key) + c * 16) = vreg[it];
       }
       *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kreg[it];
       if constexpr (DT == KVC_BF16) {
@@ -429,36 +444,44 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
 
 // Register budgets: at D = 64, three workgroups per CU for bf16 and two for
 // fp32; D = 128 keeps one, since capping it would spill.  HIST: some
-// sequence has cached positions before its new tokens.
-template <int DT, bool HIST>
+// sequence has cached positions before its new tokens; PAGED: the cache is
+// a paged pool.
+template <int DT, bool HIST, bool PAGED>
 __global__ __launch_bounds__(256, DT == KVC_BF16 ? 3 : 2) void prefill_kernel_d64(PrefillArgs a) {
-  prefill_tile<DT, 64, HIST>(a);
+  prefill_tile<DT, 64, HIST, PAGED>(a);
 }
-template <int DT, bool HIST>
+template <int DT, bool HIST, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_kernel_d128(PrefillArgs a) {
-  prefill_tile<DT, 128, HIST>(a);
+  prefill_tile<DT, 128, HIST, PAGED>(a);
 }
 
-template <int DT, bool HIST>
+template <int DT, bool HIST, bool PAGED>
 void launch_dt(const PrefillArgs &a, int D, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_layers * a.Hq), (unsigned)a.q_tiles, (unsigned)a.nb);
   if (D == 64)
-    hipLaunchKernelGGL((prefill_kernel_d64<DT, HIST>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel_d64<DT, HIST, PAGED>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel_d128<DT, HIST>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel_d128<DT, HIST, PAGED>), grid, dim3(256), 0, s, a);
+}
+
+template <int DT>
+void launch_flags(const PrefillArgs &a, int D, bool history, hipStream_t s) {
+  const bool paged = a.pg.block_table != nullptr;
+  if (paged) {
+    if (history) launch_dt<DT, true, true>(a, D, s);
+    else launch_dt<DT, false, true>(a, D, s);
+  } else {
+    if (history) launch_dt<DT, true, false>(a, D, s);
+    else launch_dt<DT, false, false>(a, D, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, hipStream_t s) {
   if (a.q_tiles <= 0 || a.nb <= 0) return hipSuccess;
-  if (dtype == KVC_F32) {
-    if (history) launch_dt<KVC_F32, true>(a, D, s);
-    else launch_dt<KVC_F32, false>(a, D, s);
-  } else {
-    if (history) launch_dt<KVC_BF16, true>(a, D, s);
-    else launch_dt<KVC_BF16, false>(a, D, s);
-  }
+  if (dtype == KVC_F32) launch_flags<KVC_F32>(a, D, history, s);
+  else launch_flags<KVC_BF16>(a, D, history, s);
   return hipGetLastError();
 }
 

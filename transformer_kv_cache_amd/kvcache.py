@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 4  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 5  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -116,6 +116,9 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_paged_decode_step.argtypes = [pp, i32, i32, vp, vp, vp, i32, i32, i32, ip, vp, i32,
                                               f32, vp, vp, sz, vp]
         lib.kvc_paged_decode_step.restype = i32
+        lib.kvc_paged_attn_prefill_varlen.argtypes = [pp, i32, i32, vp, vp, vp, i32, i32, ip, ip,
+                                                      vp, i32, f32, vp, vp]
+        lib.kvc_paged_attn_prefill_varlen.restype = i32
         if path is None:
             _lib = lib
     return lib
@@ -511,3 +514,32 @@ def paged_decode_step(cache: PagedKVCache, q, k_new, v_new, hist_len, block_tabl
         raise ValueError("paged_decode_step needs k_new and v_new")
     return _paged_decode("step", cache, q, k_new, v_new, hist_len, block_table, scale, out, layer0,
                          workspace, stream)
+
+
+def paged_attn_prefill_varlen(cache: PagedKVCache, q, k, v, cu_seqlens, hist_len, block_table,
+                              scale: float | None = None, out=None, layer0: int = 0, stream=None):
+    """attn_prefill_varlen into a paged cache: history read and new rows
+    written through block_table (int32 [B, max_blocks] on the device)."""
+    B, mb = _check_table(cache, block_table)
+    n_layers, T, Hq, _ = q.shape
+    _check_tensor("q", q, cache, (n_layers, T, Hq, cache.D))
+    _check_tensor("k", k, cache, (n_layers, T, cache.Hkv, cache.D))
+    _check_tensor("v", v, cache, (n_layers, T, cache.Hkv, cache.D))
+    cu = np.ascontiguousarray(
+        cu_seqlens.cpu().numpy() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens,
+        dtype=np.int32)
+    if cu.shape != (B + 1,) or int(cu[-1]) != T:
+        raise ValueError(f"cu_seqlens must have shape ({B + 1},) and end at T = {T}")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, tuple(q.shape))
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, B)
+    d = cache.desc()
+    _check(library().kvc_paged_attn_prefill_varlen(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), k.data_ptr(), v.data_ptr(), Hq, B,
+        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), hp, block_table.data_ptr(), mb,
+        float(scale), out.data_ptr(), _stream(cache.device, stream)))
+    return out
+

@@ -329,3 +329,30 @@ def varlen_prefill_batch(seed=0, dtype="bf16", gqa=False, B=8, L=12) -> VarlenWo
     return make_varlen_workload(f"varlen_prefill_{'gqa' if gqa else 'mha'}_{dtype}", seed=seed,
                                 dtype=dtype, L=L, B=B, Hq=Hq, Hkv=Hkv, D=D, Tmax=1024, hist=hist,
                                 lens=lens)
+
+
+@dataclass
+class PagedVarlenWorkload:
+    """A paged cache with per-sequence history (as ``PagedWorkload``) plus one
+    packed prefill laid out as in ``VarlenWorkload``."""
+    pool: PagedWorkload
+    cu_seqlens: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+    def __getattr__(self, name):
+        return getattr(self.pool, name)
+
+
+def make_paged_varlen_workload(name, *, seed, dtype, L, B, Hq, Hkv, D, block_size, max_blocks,
+                               hist, lens, shared_prefix_blocks=0) -> PagedVarlenWorkload:
+    pool = make_paged_workload(name, seed=seed, dtype=dtype, L=L, B=B, Hq=Hq, Hkv=Hkv, D=D,
+                               block_size=block_size, max_blocks=max_blocks, hist=hist,
+                               step_lens=(), shared_prefix_blocks=shared_prefix_blocks)
+    rng = np.random.default_rng(seed + 104729)
+    lens = np.asarray(lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = (as_dtype(_normal(rng, (L, T, H, D)), dtype) for H in (Hq, Hkv, Hkv))
+    return PagedVarlenWorkload(pool, cu, q, k, v)
