@@ -302,19 +302,33 @@ def bench_prefill(torch, K, S, dtype, reps, rotate=4):
             "hbm_gbs": hbm_bytes / us / 1e3, "algorithmic_flops": flops}
 
 
-def bench_varlen_prefill(torch, K, w, reps, rotate=4):
-    """Time one packed variable-length prefill (synth.VarlenWorkload)."""
+def bench_varlen_prefill(torch, K, w, reps, rotate=4, block_size=0):
+    """Time one packed variable-length prefill (synth.VarlenWorkload); with
+    block_size > 0 the same rows sit in block pools behind a shuffled table
+    and the paged entry point runs."""
     from gpu_common import to_dev, torch_dtype
+    from transformer_kv_cache_amd import synth
     dt = torch_dtype(w.dtype)
     qs, ks, vs = (replicate(torch, to_dev(a), rotate) for a in (w.q, w.k, w.v))
-    caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=kk, v=vv) for kk, vv in
-              zip(replicate(torch, to_dev(w.k_cache), rotate),
-                  replicate(torch, to_dev(w.v_cache), rotate))]
     outs = [torch.empty_like(qs[0]) for _ in range(rotate)]
+    if block_size:
+        kp, vp, table = synth.paged_from_contiguous(w.k_cache, w.v_cache, block_size, seed=11)
+        bt = torch.from_numpy(table).cuda()
+        caches = [K.PagedKVCache(w.L, kp.shape[1], w.Hkv, block_size, w.D, dt, k=kk, v=vv)
+                  for kk, vv in zip(replicate(torch, to_dev(kp), rotate),
+                                    replicate(torch, to_dev(vp), rotate))]
 
-    def call(r):
-        K.attn_prefill_varlen(caches[r], qs[r], ks[r], vs[r], w.cu_seqlens, w.hist,
-                              scale=w.scale, out=outs[r])
+        def call(r):
+            K.paged_attn_prefill_varlen(caches[r], qs[r], ks[r], vs[r], w.cu_seqlens, w.hist, bt,
+                                        scale=w.scale, out=outs[r])
+    else:
+        caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=kk, v=vv) for kk, vv in
+                  zip(replicate(torch, to_dev(w.k_cache), rotate),
+                      replicate(torch, to_dev(w.v_cache), rotate))]
+
+        def call(r):
+            K.attn_prefill_varlen(caches[r], qs[r], ks[r], vs[r], w.cu_seqlens, w.hist,
+                                  scale=w.scale, out=outs[r])
 
     for r in range(rotate):
         call(r)
@@ -457,8 +471,13 @@ def main():
         for gqa in (False, True):
             name = "bf16_" + ("gqa32q8kv_D128" if gqa else "mha12_D64") + "_B8"
             log(f"varlen prefill {name}")
-            r = bench_varlen_prefill(torch, K, synth.varlen_prefill_batch(seed=5, gqa=gqa), 20)
+            wv = synth.varlen_prefill_batch(seed=5, gqa=gqa)
+            r = bench_varlen_prefill(torch, K, wv, 20)
             varlen[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+            log(f"varlen prefill {name}, paged cache, block size 16")
+            r = bench_varlen_prefill(torch, K, wv, 20, block_size=16)
+            varlen[name + "_paged_bs16"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                            for k, v in r.items()}
         extras["prefill_varlen_12layer"] = varlen
 
     step_us = head["step_us"]

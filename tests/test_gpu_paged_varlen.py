@@ -112,22 +112,13 @@ def test_paged_varlen_equals_contiguous_bitwise():
     from transformer_kv_cache_amd import kvcache as K
     w = synth.make_varlen_workload("contig", seed=66, dtype="bf16", L=2, B=3, Hq=12, Hkv=12,
                                    D=64, Tmax=512, hist=[0, 77, 320], lens=[256, 200, 190])
-    o_c = None
     cc = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, torch.bfloat16, k=to_dev(w.k_cache),
                    v=to_dev(w.v_cache))
     o_c = to_host(K.attn_prefill_varlen(cc, to_dev(w.q), to_dev(w.k), to_dev(w.v),
                                         w.cu_seqlens, w.hist, scale=w.scale))
-    bs, mb = 32, 16
-    nblk = w.B * mb + 3
-    rng = np.random.default_rng(67)
-    table = rng.permutation(nblk)[:w.B * mb].astype(np.int32).reshape(w.B, mb)
-    # pools holding the contiguous cache's rows, block by block
-    kp = synth.canary_cache((w.L, nblk, w.Hkv, bs, w.D), w.dtype)
-    vp = synth.canary_cache((w.L, nblk, w.Hkv, bs, w.D), w.dtype)
-    for b in range(w.B):
-        for j in range(mb):
-            kp[:, table[b, j]] = w.k_cache[:, b, :, j * bs:(j + 1) * bs]
-            vp[:, table[b, j]] = w.v_cache[:, b, :, j * bs:(j + 1) * bs]
+    bs, mb = 32, w.Tmax // 32
+    kp, vp, table = synth.paged_from_contiguous(w.k_cache, w.v_cache, bs, seed=67)
+    nblk = kp.shape[1]
     pc = K.PagedKVCache(w.L, nblk, w.Hkv, bs, w.D, torch.bfloat16, k=to_dev(kp), v=to_dev(vp))
     o_p = to_host(K.paged_attn_prefill_varlen(pc, to_dev(w.q), to_dev(w.k), to_dev(w.v),
                                               w.cu_seqlens, w.hist,

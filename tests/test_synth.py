@@ -42,3 +42,17 @@ def test_generators_are_deterministic_and_shaped():
         assert not synth.is_canary(c.k_cache[:, bb, :, :p]).any()
         assert synth.is_canary(c.k_cache[:, bb, :, p:]).all()
     assert c.steps[0][0].shape == (2, 3, 4, 1, 8) and c.steps[0][1].shape == (2, 3, 2, 1, 8)
+
+
+def test_paged_from_contiguous_round_trip():
+    w = synth.make_workload("rt", seed=3, dtype="bf16", L=2, B=3, Hq=2, Hkv=2, D=64, Tmax=64,
+                            hist=[5, 0, 63])
+    kp, vp, table = synth.paged_from_contiguous(w.k_cache, w.v_cache, 16, seed=1)
+    assert kp.shape == (2, 3 * 4 + 3, 2, 16, 64) and table.shape == (3, 4)
+    assert len(np.unique(table)) == table.size
+    for b in range(3):
+        for t in range(64):
+            assert np.array_equal(kp[:, table[b, t // 16], :, t % 16], w.k_cache[:, b, :, t])
+            assert np.array_equal(vp[:, table[b, t // 16], :, t % 16], w.v_cache[:, b, :, t])
+    spare = np.setdiff1d(np.arange(kp.shape[1]), table)
+    assert synth.is_canary(kp[:, spare]).all() and synth.is_canary(vp[:, spare]).all()

@@ -356,3 +356,24 @@ def make_paged_varlen_workload(name, *, seed, dtype, L, B, Hq, Hkv, D, block_siz
     T = int(cu[-1])
     q, k, v = (as_dtype(_normal(rng, (L, T, H, D)), dtype) for H in (Hq, Hkv, Hkv))
     return PagedVarlenWorkload(pool, cu, q, k, v)
+
+
+def paged_from_contiguous(k_cache, v_cache, block_size, seed=0, spare_blocks=3):
+    """The rows of a contiguous cache ``[L, B, Hkv, Tmax, D]`` laid out in
+    block pools through a shuffled table: returns (k_pool, v_pool,
+    block_table), block ``table[b][j]`` holding positions ``j*block_size ..
+    (j+1)*block_size - 1`` of sequence ``b``; spare blocks hold canaries."""
+    L, B, Hkv, Tmax, D = k_cache.shape
+    if Tmax % block_size:
+        raise ValueError("Tmax must be a multiple of block_size")
+    mb = Tmax // block_size
+    nblk = B * mb + spare_blocks
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(nblk)[:B * mb].astype(np.int32).reshape(B, mb)
+    shape = (L, nblk, Hkv, block_size, D)
+    dtype = "bf16" if k_cache.dtype == np.uint16 else "f32"
+    kp, vp = canary_cache(shape, dtype), canary_cache(shape, dtype)
+    blocks = lambda c: np.transpose(c.reshape(L, B, Hkv, mb, block_size, D), (0, 1, 3, 2, 4, 5))
+    kp[:, table.reshape(-1)] = blocks(k_cache).reshape(L, B * mb, Hkv, block_size, D)
+    vp[:, table.reshape(-1)] = blocks(v_cache).reshape(L, B * mb, Hkv, block_size, D)
+    return kp, vp, table
