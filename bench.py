@@ -96,8 +96,8 @@ def read_traffic():
     if vals.get("decode_source_sha256") != decode_source_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(vals["hbm_bytes_per_launch"].split()[0])
+    except (KeyError, ValueError, IndexError):
         return None
 
 
@@ -383,7 +383,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X)", file=sys.stderr)
+              "(the path is per-GPU: each GPU would run it on its own shard)", file=sys.stderr)
         sys.exit(2)
 
     import torch

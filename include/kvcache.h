@@ -72,7 +72,7 @@ typedef enum {
   KVC_E_DTYPE = -3,       /* unknown element type */
   KVC_E_CAPACITY = -4,    /* hist_len[b] + N (or S) exceeds Tmax */
   KVC_E_WORKSPACE = -5,   /* decode workspace missing or too small */
-  KVC_E_UNSUPPORTED = -6, /* a valid shape this build has no kernel for */
+  KVC_E_UNSUPPORTED = -6, /* a valid shape the library has no kernel for */
   KVC_E_HIP = -7          /* the HIP runtime refused a launch */
 } kvc_status;
 
