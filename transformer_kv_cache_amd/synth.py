@@ -377,3 +377,60 @@ def paged_from_contiguous(k_cache, v_cache, block_size, seed=0, spare_blocks=3):
     kp[:, table.reshape(-1)] = blocks(k_cache).reshape(L, B * mb, Hkv, block_size, D)
     vp[:, table.reshape(-1)] = blocks(v_cache).reshape(L, B * mb, Hkv, block_size, D)
     return kp, vp, table
+
+
+# ---- synthetic GPT-2-shaped weights ------------------------------------------
+
+@dataclass
+class GPT2Weights:
+    """Random weights of a GPT-2-style decoder (the pages run GPT-2 Small:
+    12 layers, width 768, 12 heads, 1024 positions; trained weights are not
+    available, so N(0, 0.02) draws stand in for them).  Per-layer tensors are
+    stacked on a leading layer axis; linear weights are ``[in, out]``."""
+    L: int
+    d: int
+    H: int
+    V: int
+    T: int
+    wte: np.ndarray      # [V, d] token embedding, also the output projection
+    wpe: np.ndarray      # [T, d] position embedding
+    ln1_g: np.ndarray    # [L, d]
+    ln1_b: np.ndarray
+    w_qkv: np.ndarray    # [L, d, 3d]
+    b_qkv: np.ndarray    # [L, 3d]
+    w_o: np.ndarray      # [L, d, d]
+    b_o: np.ndarray      # [L, d]
+    ln2_g: np.ndarray
+    ln2_b: np.ndarray
+    w_fc: np.ndarray     # [L, d, 4d]
+    b_fc: np.ndarray     # [L, 4d]
+    w_pr: np.ndarray     # [L, 4d, d]
+    b_pr: np.ndarray     # [L, d]
+    lnf_g: np.ndarray    # [d]
+    lnf_b: np.ndarray
+
+    @property
+    def D(self) -> int:
+        return self.d // self.H
+
+
+def gpt2_weights(seed=0, L=12, d=768, H=12, V=50257, T=1024) -> GPT2Weights:
+    """fp32 draws in field order: weights N(0, 0.02), biases N(0, 0.02),
+    layer-norm gains 1 + N(0, 0.1) and shifts N(0, 0.02)."""
+    rng = np.random.default_rng(seed)
+    n = lambda *shape, s=0.02: (s * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+    g = lambda *shape: (1.0 + n(*shape, s=0.1)).astype(np.float32)
+    return GPT2Weights(L, d, H, V, T,
+                       wte=n(V, d), wpe=n(T, d),
+                       ln1_g=g(L, d), ln1_b=n(L, d),
+                       w_qkv=n(L, d, 3 * d), b_qkv=n(L, 3 * d),
+                       w_o=n(L, d, d), b_o=n(L, d),
+                       ln2_g=g(L, d), ln2_b=n(L, d),
+                       w_fc=n(L, d, 4 * d), b_fc=n(L, 4 * d),
+                       w_pr=n(L, 4 * d, d), b_pr=n(L, d),
+                       lnf_g=g(d), lnf_b=n(d))
+
+
+def token_ids(seed, n, V) -> np.ndarray:
+    """n token ids uniform in [0, V)."""
+    return np.random.default_rng(seed).integers(0, V, size=n).astype(np.int64)
