@@ -342,6 +342,43 @@ def bench_varlen_prefill(torch, K, w, reps, rotate=4, block_size=0):
             "algorithmic_flops": flops, "lengths": lens.tolist(), "history": hist.tolist()}
 
 
+def bench_gpt2(torch, contexts=(128, 512, 1000), reps=20):
+    """Per-token latency of a GPT-2 Small-shaped decoder (synthetic fp32
+    weights, batch 1) at each context length T: the cached step (token T-1
+    through the decode entry point over T-1 cached positions, every layer,
+    then the output projection of the last position) and the recomputing
+    step (all T tokens through the prefill entry point), each captured in a
+    HIP graph and replayed."""
+    from transformer_kv_cache_amd import synth
+    from transformer_kv_cache_amd.gpt2 import GPT2
+    w = synth.gpt2_weights(seed=0)
+    m = GPT2(w)
+    ids = torch.from_numpy(synth.token_ids(1, max(contexts), w.V)).cuda()
+    cache, scratch = m.new_cache(), m.new_cache()
+    res = {}
+    for T in contexts:
+        m.forward(ids[:T - 1], cache, 0, last_only=True)
+        tok = ids[T - 1:T].clone()
+        full = ids[:T].clone()
+
+        def cached(r):
+            m.forward(tok, cache, T - 1, last_only=True)
+
+        def recompute(r):
+            m.forward(full, scratch, 0, last_only=True)
+
+        cached(0)
+        recompute(0)
+        torch.cuda.synchronize()
+        c_us = GraphTimer(torch, cached, 1).time(reps)
+        r_us = GraphTimer(torch, recompute, 1).time(reps)
+        res[f"T{T}"] = {"cached_ms_per_token": round(c_us / 1e3, 4),
+                        "recompute_ms_per_token": round(r_us / 1e3, 4),
+                        "speedup": round(r_us / c_us, 2)}
+    res["model"] = "12 layers, width 768, 12 heads, vocabulary 50257, fp32, batch 1, synthetic weights"
+    return res
+
+
 def cpu_baseline(w, target_s, max_steps=100000):
     """The oracle, as it stands, on a bounded sample of the headline step:
     append + attention for all 12 layers, repeated until ~target_s seconds."""
@@ -479,6 +516,8 @@ def main():
             varlen[name + "_paged_bs16"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                             for k, v in r.items()}
         extras["prefill_varlen_12layer"] = varlen
+        log("GPT-2 Small-shaped decoder: cached vs recomputed per-token latency")
+        extras["gpt2_small_cached_vs_recompute"] = bench_gpt2(torch)
 
     step_us = head["step_us"]
     traffic = read_traffic()

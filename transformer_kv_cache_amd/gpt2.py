@@ -1,0 +1,119 @@
+"""A GPT-2-style decoder on the GPU around the KV-cache entry points.
+
+[KV-2] openai-hub.com/news/2435, "GPT-2缓存实测：千倍计算只快6倍": GPT-2 Small
+(12 layers, width 768, 12 heads, 1024 positions, FP32, batch 1, greedy
+decoding) generated with a KV cache and by recomputing the whole context
+every step; the table there gives the per-token latency of both at context
+1000.  This module runs both forms on MI355X with synthetic weights
+(trained ones are not available):
+
+  * cached: the prompt goes through ``kvc_attn_prefill`` (which also fills
+    the cache), each new token through ``kvc_decode_step`` (append + split-K
+    attention over the history), one call per layer;
+  * recompute: every step runs the whole context through
+    ``kvc_attn_prefill`` again on a scratch cache.
+
+The block follows the published GPT-2 design: pre-norm residual blocks,
+learned positions, layer-norm eps 1e-5, tanh GELU, final layer norm, token
+embedding reused as the output projection; q/k/v are the three d-wide
+thirds of the QKV product with head h owning columns [h D, (h+1) D).  The
+attention and every cache access run in the library's HIP kernels; the
+dense products are plain library GEMMs (hipBLASLt through torch, fp32 with
+TF32-style reduced precision off) and the layer norms / GELU / residual adds
+are torch elementwise ops: that part of the model is outside the cache path.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from . import kvcache as K
+
+
+class GPT2:
+    """Weights (a ``synth.GPT2Weights``-like object with numpy arrays) on one
+    GPU, fp32."""
+
+    def __init__(self, w, device="cuda"):
+        torch.backends.cuda.matmul.allow_tf32 = False
+        dev = torch.device(device)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        self.L, self.d, self.H, self.V, self.T = w.L, w.d, w.H, w.V, w.T
+        self.D = w.d // w.H
+        self.scale = 1.0 / math.sqrt(self.D)
+        self.device = dev
+        self.wte, self.wpe = t(w.wte), t(w.wpe)
+        self.wte_t = self.wte.t().contiguous()          # [d, V] output projection
+        names = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b",
+                 "w_fc", "b_fc", "w_pr", "b_pr")
+        self.p = {n: t(getattr(w, n)) for n in names}
+        self.lnf_g, self.lnf_b = t(w.lnf_g), t(w.lnf_b)
+        self._ws = {}
+
+    def new_cache(self) -> K.KVCache:
+        """An empty [L, 1, H, T, D] cache (batch 1, as in the pages)."""
+        return K.KVCache(self.L, 1, self.H, self.T, self.D, torch.float32, device=self.device)
+
+    def _workspace(self, cache, n):
+        key = (cache.k.data_ptr(), n)
+        if key not in self._ws:
+            self._ws[key] = K.new_decode_workspace(cache, 1, self.H, n)
+        return self._ws[key]
+
+    def forward(self, ids, cache: K.KVCache, P: int, last_only=False):
+        """Logits of the N tokens ``ids`` (int64 tensor on the device) at
+        positions P .. P+N-1.  P = 0 prefills ``cache`` with them; P > 0
+        appends them to the P cached positions.  ``last_only`` returns the
+        last position's logits only ([1, V])."""
+        N = int(ids.shape[0])
+        if N == 0:
+            return torch.empty((0, self.V), dtype=torch.float32, device=self.device)
+        if P + N > self.T:
+            raise ValueError(f"context {P + N} exceeds {self.T} positions")
+        d, H, D, p = self.d, self.H, self.D, self.p
+        h = self.wte[ids] + self.wpe[P:P + N]
+        for l in range(self.L):
+            a = F.layer_norm(h, (d,), p["ln1_g"][l], p["ln1_b"][l], eps=1e-5)
+            qkv = torch.addmm(p["b_qkv"][l], a, p["w_qkv"][l])                 # [N, 3d]
+            t = qkv.view(N, 3, H, D).permute(1, 2, 0, 3).contiguous()         # [3, H, N, D]
+            q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
+            if P == 0:
+                o = K.attn_prefill(cache, q, k, v, scale=self.scale, layer0=l)
+            else:
+                o = K.decode_step(cache, q, k, v, [P], scale=self.scale, layer0=l,
+                                  workspace=self._workspace(cache, N))
+            o = o.view(H, N, D).permute(1, 0, 2).reshape(N, d)
+            h = h + torch.addmm(p["b_o"][l], o, p["w_o"][l])
+            m = F.layer_norm(h, (d,), p["ln2_g"][l], p["ln2_b"][l], eps=1e-5)
+            f = F.gelu(torch.addmm(p["b_fc"][l], m, p["w_fc"][l]), approximate="tanh")
+            h = h + torch.addmm(p["b_pr"][l], f, p["w_pr"][l])
+        if last_only:
+            h = h[-1:]
+        h = F.layer_norm(h, (d,), self.lnf_g, self.lnf_b, eps=1e-5)
+        return h @ self.wte_t
+
+    def generate(self, prompt, n_new, cached=True):
+        """Greedy decoding of n_new tokens after ``prompt`` (a list of ids).
+        Returns (tokens, last-position logits of every step as a float64
+        numpy array [n_new, V])."""
+        ids = [int(x) for x in prompt]
+        cache = self.new_cache()
+        scratch = None if cached else self.new_cache()
+        out = []
+        P = 0
+        nxt = ids
+        for _ in range(n_new):
+            if cached:
+                z = self.forward(torch.tensor(nxt, device=self.device), cache, P, last_only=True)
+                P += len(nxt)
+            else:
+                z = self.forward(torch.tensor(ids, device=self.device), scratch, 0, last_only=True)
+            zt = z[0].double().cpu().numpy()
+            out.append(zt)
+            tok = int(np.argmax(zt))
+            ids.append(tok)
+            nxt = [tok]
+        return ids[len(prompt):], np.stack(out)
