@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 5
+#define KVC_ABI_VERSION 6
 
 typedef enum {
   KVC_OK = 0,
@@ -338,6 +338,34 @@ kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache,
                                          const int32_t *block_table,
                                          int32_t max_blocks, float scale,
                                          void *o, void *stream);
+
+/* ---- dense layer of a cached decode step ---------------------------------
+ *
+ * [KV-2] openai-hub.com/news/2435, "千倍计算量为何只换来6倍速度": with the cache,
+ * a decode step computes the projections and the MLP of the new tokens only,
+ * so each weight matrix is read once for a handful of rows.  This is that
+ * step of the GPT-2 block the same page measures (pre-norm, GELU, residual):
+ *
+ *   y[m][n] = act( sum_k xh[m][k] w[k][n] + bias[n] ) + res[m][n]
+ *   xh[m] = (x[m] - mean) / sqrt(var + ln_eps) * ln_g + ln_b  when ln_g is
+ *           given (mean and biased variance over the K features of row m),
+ *           else x[m];  act = 0: identity, 1: GELU, tanh form
+ *           0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+ *
+ * All fp32, device pointers, row-major: x [M, K], w [K, N], bias [N] or
+ * NULL, ln_g / ln_b [K] (both or neither), res [M, N] or NULL, y [M, N].
+ * 1 <= M <= 8, M * K <= 12288 (and (M + 2) * K <= 16384 with the layer
+ * norm), K and N multiples of 4; x, w, res, y and ln_g / ln_b 16-byte
+ * aligned.  y may be the same buffer as res (in-place residual update) but
+ * must not overlap x.  The caller owns every buffer; nothing is allocated.
+ * Errors: KVC_E_NULL (x, w or y missing, or only one of ln_g / ln_b),
+ * KVC_E_SHAPE (sizes, alignment, act, ln_eps, y overlapping x),
+ * KVC_E_UNSUPPORTED (more rows or inputs than that: prompt-sized inputs
+ * belong to a GEMM library), KVC_E_HIP (launch failure). */
+kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *w,
+                          int32_t N, const float *bias, const float *ln_g,
+                          const float *ln_b, float ln_eps, int32_t act,
+                          const float *res, float *y, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvc_last_error(void);

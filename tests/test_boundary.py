@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 5
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 6
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -371,3 +371,43 @@ def test_paged_varlen_prefill_error_paths(lib):
     assert call(c=ctypes.byref(pdesc(h, bs=6))) == E_SHAPE
     assert call(c=ctypes.byref(pdesc(h, D=32))) == E_UNSUPPORTED
     assert call(cu=hist(0, 0, 0), q=None, k=None, v=None, o=None) == OK  # no tokens: no-op
+
+
+def test_linear_error_paths(lib):
+    """kvc_linear_f32 rejects bad arguments before any launch (host buffers
+    stand in for device memory: every call below must fail validation)."""
+    h = Host()
+    x, w, y, r = h.ptr(), h.ptr(), h.ptr(), h.ptr()
+    g, b = h.ptr(), h.ptr()
+
+    def call(**kw):
+        a = dict(x=x, M=1, K=8, w=w, N=8, bias=None, g=None, b=None, eps=1e-5, act=0, res=None, y=y)
+        a.update(kw)
+        return lib.kvc_linear_f32(a["x"], a["M"], a["K"], a["w"], a["N"], a["bias"], a["g"], a["b"],
+                                  a["eps"], a["act"], a["res"], a["y"], None)
+
+    assert call(x=None) == E_NULL
+    assert call(w=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(g=g) == E_NULL                     # gain without shift
+    assert call(M=0) == E_SHAPE
+    assert call(K=6) == E_SHAPE                    # not a multiple of 4
+    assert call(N=10) == E_SHAPE
+    assert call(M=9) == E_UNSUPPORTED
+    assert call(M=5, K=3072) == E_UNSUPPORTED      # 15360 inputs > 12288
+    assert "exceed" in err(lib)
+    assert call(act=2) == E_SHAPE
+    assert call(g=g, b=b, eps=float("nan")) == E_SHAPE
+    assert call(x=h.ptr(offset=4)) == E_SHAPE      # misaligned
+    assert call(res=h.ptr(offset=8)) == E_SHAPE
+    assert call(y=x) == E_SHAPE                    # output over the input
+    assert "overlaps" in err(lib)
+
+
+def test_linear_layer_norm_limits(lib):
+    h = Host()
+    x, w, y, g, b = h.ptr(65536), h.ptr(), h.ptr(), h.ptr(65536), h.ptr(65536)
+    call = lambda M, K, gg=g, bb=b: lib.kvc_linear_f32(x, M, K, w, 8, None, gg, bb, 1e-5, 0, None, y, None)
+    assert call(1, 8192) == E_UNSUPPORTED          # (1 + 2) * 8192 > 16384 with the norm
+    assert call(4, 3072) == E_UNSUPPORTED          # (4 + 2) * 3072 > 16384
+    assert call(1, 8, gg=h.ptr(offset=4)) == E_SHAPE   # misaligned gain

@@ -530,6 +530,49 @@ kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0, i
                      hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
+kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *w, int32_t N,
+                          const float *bias, const float *ln_g, const float *ln_b, float ln_eps,
+                          int32_t act, const float *res, float *y, void *stream) {
+  static const char *fn = "kvc_linear_f32";
+  if (!x || !w || !y) return fail(KVC_E_NULL, "%s: x, w or y is NULL", fn);
+  if ((ln_g == nullptr) != (ln_b == nullptr))
+    return fail(KVC_E_NULL, "%s: ln_g and ln_b must both be given or both NULL", fn);
+  if (M < 1 || K < 4 || N < 4 || K % 4 != 0 || N % 4 != 0)
+    return fail(KVC_E_SHAPE, "%s: M = %d, K = %d, N = %d (need M >= 1, K and N positive multiples of 4)",
+                fn, M, K, N);
+  if (M > kvc::kMaxLinearRows || (int64_t)M * K > kvc::kMaxLinearInputs ||
+      (ln_g && (int64_t)(M + 2) * K > kvc::kMaxLinearLds))
+    return fail(KVC_E_UNSUPPORTED,
+                "%s: M = %d rows of K = %d inputs exceed %d rows / %d inputs (%d with the layer norm's "
+                "two parameter rows)", fn, M, K, kvc::kMaxLinearRows, kvc::kMaxLinearInputs,
+                kvc::kMaxLinearLds);
+  if (act != 0 && act != 1) return fail(KVC_E_SHAPE, "%s: act = %d (0 or 1)", fn, act);
+  if (ln_g && !(std::isfinite(ln_eps) && ln_eps >= 0.f))
+    return fail(KVC_E_SHAPE, "%s: ln_eps must be finite and >= 0", fn);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (res && !aligned16(res)) ||
+      (ln_g && (!aligned16(ln_g) || !aligned16(ln_b))))
+    return fail(KVC_E_SHAPE, "%s: x, w, res, y, ln_g and ln_b must be 16-byte aligned", fn);
+  const char *xb = (const char *)x, *xe = xb + (size_t)M * K * sizeof(float);
+  const char *yb = (const char *)y, *ye = yb + (size_t)M * N * sizeof(float);
+  if (yb < xe && xb < ye) return fail(KVC_E_SHAPE, "%s: y overlaps x", fn);
+  kvc::LinearArgs a{};
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.ln_g = ln_g;
+  a.ln_b = ln_b;
+  a.res = res;
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.act = act;
+  a.ln_eps = ln_eps;
+  hipError_t e = kvc::launch_linear(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return ok();
+}
+
 kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache, int32_t layer0,
                                          int32_t n_layers, const void *q, const void *k,
                                          const void *v, int32_t Hq, int32_t B,

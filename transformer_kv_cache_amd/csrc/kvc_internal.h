@@ -162,8 +162,27 @@ struct PrefillArgs {
   PagedGeom pg;         // paged cache, else block_table == nullptr
 };
 
+// Dense layer of a decode step: y = act(LN?(x) W + bias) + res, fp32, for at
+// most kMaxLinearRows rows (kvc_linear_f32).
+constexpr int kMaxLinearRows = 8;
+constexpr int kMaxLinearInputs = 12288;  // M * K floats staged in LDS (48 KiB)
+constexpr int kMaxLinearLds = 16384;     // with the layer norm, (M + 2) * K floats (64 KiB)
+struct LinearArgs {
+  const float *x;      // [M][K]
+  const float *w;      // [K][N]
+  const float *bias;   // [N] or null
+  const float *ln_g;   // [K] or null (no layer norm)
+  const float *ln_b;   // [K] (with ln_g)
+  const float *res;    // [M][N] or null
+  float *y;            // [M][N]
+  int32_t M, K, N;
+  int32_t act;         // 0: none, 1: GELU (tanh form)
+  float ln_eps;
+};
+
 // Host launchers (one translation unit each).  They assume validated
 // arguments and return the launch status.
+hipError_t launch_linear(const LinearArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,

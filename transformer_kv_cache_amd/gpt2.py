@@ -16,11 +16,17 @@ every step; the table there gives the per-token latency of both at context
 The block follows the published GPT-2 design: pre-norm residual blocks,
 learned positions, layer-norm eps 1e-5, tanh GELU, final layer norm, token
 embedding reused as the output projection; q/k/v are the three d-wide
-thirds of the QKV product with head h owning columns [h D, (h+1) D).  The
-attention and every cache access run in the library's HIP kernels; the
-dense products are plain library GEMMs (hipBLASLt through torch, fp32 with
-TF32-style reduced precision off) and the layer norms / GELU / residual adds
-are torch elementwise ops: that part of the model is outside the cache path.
+thirds of the QKV product with head h owning columns [h D, (h+1) D).
+
+Where each step runs:
+  * attention and every cache access: the library's HIP kernels;
+  * the dense layers of a decode step (at most 4 new tokens): the library's
+    fused ``kvc_linear_f32`` (layer norm + matrix-vector product + bias +
+    GELU / residual in one HBM-bound pass over the weights);
+  * the dense layers of a prompt (more tokens): plain library GEMMs
+    (hipBLASLt through torch, fp32, reduced-precision modes off) with torch
+    layer norm / GELU / adds -- compute-bound products, outside the cache
+    path.
 """
 from __future__ import annotations
 
@@ -46,7 +52,9 @@ class GPT2:
         self.scale = 1.0 / math.sqrt(self.D)
         self.device = dev
         self.wte, self.wpe = t(w.wte), t(w.wpe)
-        self.wte_t = self.wte.t().contiguous()          # [d, V] output projection
+        self.Vp = (w.V + 3) // 4 * 4                    # output columns padded to 4
+        self.wte_t = torch.zeros((w.d, self.Vp), dtype=torch.float32, device=dev)
+        self.wte_t[:, :w.V] = self.wte.t()              # [d, Vp] output projection
         names = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b",
                  "w_fc", "b_fc", "w_pr", "b_pr")
         self.p = {n: t(getattr(w, n)) for n in names}
@@ -75,6 +83,8 @@ class GPT2:
             raise ValueError(f"context {P + N} exceeds {self.T} positions")
         d, H, D, p = self.d, self.H, self.D, self.p
         h = self.wte[ids] + self.wpe[P:P + N]
+        if N <= self.DECODE_ROWS:
+            return self._forward_decode(h, cache, P, last_only)
         for l in range(self.L):
             a = F.layer_norm(h, (d,), p["ln1_g"][l], p["ln1_b"][l], eps=1e-5)
             qkv = torch.addmm(p["b_qkv"][l], a, p["w_qkv"][l])                 # [N, 3d]
@@ -93,7 +103,35 @@ class GPT2:
         if last_only:
             h = h[-1:]
         h = F.layer_norm(h, (d,), self.lnf_g, self.lnf_b, eps=1e-5)
-        return h @ self.wte_t
+        return (h @ self.wte_t)[:, :self.V]
+
+    DECODE_ROWS = 4  # rows whose dense layers run in kvc_linear_f32 (4 x 3072 inputs fit)
+
+    def _forward_decode(self, h, cache, P, last_only):
+        """The layers for N <= DECODE_ROWS tokens, every dense layer fused:
+        LN1 + QKV, attention (append + split-K decode, or prefill on an
+        empty cache), output projection + residual, LN2 + FC + GELU,
+        projection + residual, and LN_f + output projection."""
+        N = h.shape[0]
+        d, H, D, p = self.d, self.H, self.D, self.p
+        for l in range(self.L):
+            qkv = K.linear(h, p["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
+            t = qkv.view(N, 3, H, D).permute(1, 2, 0, 3).contiguous()         # [3, H, N, D]
+            q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
+            if P == 0:
+                o = K.attn_prefill(cache, q, k, v, scale=self.scale, layer0=l)
+            else:
+                o = K.decode_step(cache, q, k, v, [P], scale=self.scale, layer0=l,
+                                  workspace=self._workspace(cache, N))
+            o = o.view(H, N, D).permute(1, 0, 2).reshape(N, d).contiguous()
+            K.linear(o, p["w_o"][l], p["b_o"][l], residual=h, out=h)
+            f = K.linear(h, p["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
+                         act="gelu")
+            K.linear(f, p["w_pr"][l], p["b_pr"][l], residual=h, out=h)
+        if last_only:
+            h = h[-1:]
+        z = K.linear(h, self.wte_t, ln=(self.lnf_g, self.lnf_b))
+        return z[:, :self.V]
 
     def generate(self, prompt, n_new, cached=True):
         """Greedy decoding of n_new tokens after ``prompt`` (a list of ids).

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 5  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 6  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -119,6 +119,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_paged_attn_prefill_varlen.argtypes = [pp, i32, i32, vp, vp, vp, i32, i32, ip, ip,
                                                       vp, i32, f32, vp, vp]
         lib.kvc_paged_attn_prefill_varlen.restype = i32
+        lib.kvc_linear_f32.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, f32, i32, vp, vp, vp]
+        lib.kvc_linear_f32.restype = i32
         if path is None:
             _lib = lib
     return lib
@@ -543,3 +545,39 @@ def paged_attn_prefill_varlen(cache: PagedKVCache, q, k, v, cu_seqlens, hist_len
         float(scale), out.data_ptr(), _stream(cache.device, stream)))
     return out
 
+
+def linear(x, w, bias=None, ln=None, act=None, residual=None, out=None, ln_eps=1e-5,
+           stream=None):
+    """y = act(LN(x) w + bias) + residual for the few rows of a decode step
+    (fp32; x [M, K] with M <= 8, w [K, N]).  ``ln`` is (gain, shift) or None;
+    ``act`` is None or "gelu" (tanh form); ``out`` may be ``residual``."""
+    for name, t in (("x", x), ("w", w)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
+                or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D fp32 CUDA tensor")
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError(f"x has {K} features, w has {K2} rows")
+
+    def vec(name, t, n):
+        if t is None:
+            return None
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor of {n} elements")
+        return t
+
+    bias = vec("bias", bias, N)
+    g, b = (None, None) if ln is None else (vec("ln gain", ln[0], K), vec("ln shift", ln[1], K))
+    residual = vec("residual", residual, M * N)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    vec("out", out, M * N)
+    codes = {None: 0, "gelu": 1}
+    if act not in codes:
+        raise ValueError(f"act must be None or 'gelu', got {act!r}")
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(library().kvc_linear_f32(x.data_ptr(), M, K, w.data_ptr(), N, ptr(bias), ptr(g), ptr(b),
+                                    float(ln_eps), codes[act], ptr(residual), out.data_ptr(),
+                                    _stream(x.device, stream)))
+    return out
