@@ -289,3 +289,46 @@ def test_cache_allocation_matches_formula():
         gc.enable()
     assert cache.nbytes == 75_497_472 == grown
     del cache
+
+
+@pytest.mark.parametrize("case", ["mha_fp32", "gqa_bf16_chunked"])
+def test_graph_replays_match_eager(case):
+    """The fused step captured in a HIP graph (as a serving loop or the
+    benchmark runs it): every replay, with unrelated eager work and
+    synchronisations between replays, gives the eager call's output and
+    cache bytes bit for bit."""
+    from transformer_kv_cache_amd import kvcache as K
+    if case == "mha_fp32":
+        w = synth.decode_12layer(1023, seed=8)
+    else:
+        w = synth.make_workload("graph_gqa", seed=9, dtype="bf16", L=2, B=3, Hq=8, Hkv=2, D=128,
+                                Tmax=256, hist=[0, 100, 247], step_lens=(8,))
+    q, k, v = (to_dev(a) for a in w.steps[0])
+    dt = torch_dtype(w.dtype)
+    N = q.shape[3]
+    c_eager = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    ref = to_host(K.decode_step(c_eager, q, k, v, w.hist, scale=w.scale))
+    ref_k, ref_v = to_host(c_eager.k), to_host(c_eager.v)
+    cache = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    ws = K.new_decode_workspace(cache, w.L, w.Hq, N)
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            K.decode_step(cache, q, k, v, w.hist, scale=w.scale, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    other = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    for rep in range(4):
+        print(f"[graph] {case} replay {rep}", flush=True)
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(to_host(out)), bits(ref)), f"replay {rep}"
+        assert np.array_equal(bits(to_host(cache.k)), bits(ref_k))
+        assert np.array_equal(bits(to_host(cache.v)), bits(ref_v))
+        # unrelated eager work on the same workspace and another cache
+        K.decode_step(other, q, k, v, w.hist, scale=w.scale, workspace=ws)
+        ws.fill_(0x7F)
+        torch.cuda.synchronize()
