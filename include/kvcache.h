@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 6
+#define KVC_ABI_VERSION 7
 
 typedef enum {
   KVC_OK = 0,
@@ -169,6 +169,34 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0,
                            const void *v_new, int32_t Hq, int32_t N,
                            const int32_t *hist_len, float scale, void *o,
                            void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* kvc_decode_step with the sequence lengths in device memory, for a step that
+ * is captured once in a HIP graph and replayed every token ([KV-4]
+ * jennyma11.github.io/infra/ch07-01.html, "Decode 阶段": decode steps are
+ * short, fixed-shape kernels whose launch cost graphs remove; [KV-2]
+ * "实验到底测了什么" lists graphs beside paged attention in serving systems);
+ * each replay sees the lengths as they are on the device then.
+ *   hist_len_dev : device, int32 [B], 4-byte aligned; P_b = hist_len_dev[b]
+ *                  is read by the kernels, never by the host.
+ *   hist_max     : bound on every P_b; the launch is sized for it and the
+ *                  kernels clamp P_b into [0, hist_max] (a wrong length gives
+ *                  wrong results, never an access outside the cache).
+ *                  KVC_E_CAPACITY if hist_max + N > Tmax, KVC_E_SHAPE if < 0.
+ * Contiguous cache only; other arguments and errors as kvc_decode_step. */
+kvc_status kvc_decode_step_dl(const kvc_cache *cache, int32_t layer0,
+                              int32_t n_layers, const void *q,
+                              const void *k_new, const void *v_new, int32_t Hq,
+                              int32_t N, const int32_t *hist_len_dev,
+                              int32_t hist_max, float scale, void *o,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* hist_len_dev[b] += n for b < B, enqueued on `stream`: the length update
+ * that follows a captured kvc_decode_step_dl ([KV-4] "Decode 阶段": each step
+ * grows every sequence by its new tokens).  B = 0 or n = 0 is a no-op;
+ * KVC_E_NULL for a NULL array, KVC_E_SHAPE for B < 0 or misalignment. */
+kvc_status kvc_lengths_add(int32_t *hist_len_dev, int32_t B, int32_t n,
                            void *stream);
 
 /*

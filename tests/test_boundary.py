@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 6
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 7
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -411,3 +411,27 @@ def test_linear_layer_norm_limits(lib):
     assert call(1, 8192) == E_UNSUPPORTED          # (1 + 2) * 8192 > 16384 with the norm
     assert call(4, 3072) == E_UNSUPPORTED          # (4 + 2) * 3072 > 16384
     assert call(1, 8, gg=h.ptr(offset=4)) == E_SHAPE   # misaligned gain
+
+
+def test_device_length_step_error_paths(lib):
+    h = Host()
+    d = desc(h)  # L=2, B=2, Hkv=2, Tmax=16, D=64
+    p = h.ptr()
+    need = lib.kvc_decode_workspace_bytes(ctypes.byref(d), 2, 2, 3)
+    ws = h.ptr(need)
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), hd=h.ptr(), hmax=5, N=3, wsb=need)
+        a.update(kw)
+        return lib.kvc_decode_step_dl(a["c"], 0, 2, p, p, p, 2, a["N"], a["hd"], a["hmax"], 0.125, p,
+                                      ws, a["wsb"], None)
+
+    assert call(hd=None) == E_NULL
+    assert call(hmax=14) == E_CAPACITY             # 14 + 3 > 16
+    assert call(hmax=-1) == E_SHAPE
+    assert call(hd=h.ptr(offset=2)) == E_SHAPE     # misaligned lengths
+    assert call(wsb=0) == E_WORKSPACE
+    assert call(N=0, hd=None) == OK                # nothing to do
+    assert lib.kvc_lengths_add(None, 2, 1, None) == E_NULL
+    assert lib.kvc_lengths_add(h.ptr(), -1, 1, None) == E_SHAPE
+    assert lib.kvc_lengths_add(None, 0, 1, None) == OK

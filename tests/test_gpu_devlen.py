@@ -1,0 +1,107 @@
+"""kvc_decode_step_dl (lengths in device memory) and kvc_lengths_add,
+through the C ABI: bit-identical to kvc_decode_step with host lengths, and a
+decode loop captured once in a HIP graph ([decode step, lengths += N]) and
+replayed token after token matches the oracle's append + attention at every
+step, with the growing lengths read on the device."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_kv_cache_amd import synth
+from gpu_common import TOL, bits, to_dev, to_host, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from transformer_kv_cache_amd import kvcache as K
+    K.library()  # fail loudly if the HIP library is missing
+
+
+CASES = {
+    "fp32_12layer_P1000": lambda: synth.decode_12layer(1000, seed=61),
+    "bf16_gqa_batched": lambda: synth.batched_decode(seed=62, gqa=True),
+    "fp32_chunked_N8": lambda: synth.chunked_decode(900, 8, seed=63),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_device_lengths_equal_host_lengths(case):
+    from transformer_kv_cache_amd import kvcache as K
+    w = CASES[case]()
+    q, k, v = (to_dev(a) for a in w.steps[0])
+    N = q.shape[3]
+    dt = torch_dtype(w.dtype)
+    print(f"[devlen] {case} hist={w.hist.tolist()[:8]} N={N}", flush=True)
+    c1 = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    c2 = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    o1 = to_host(K.decode_step(c1, q, k, v, w.hist, scale=w.scale))
+    hd = torch.from_numpy(w.hist.astype(np.int32)).cuda()
+    o2 = to_host(K.decode_step_dl(c2, q, k, v, hd, w.Tmax - N, scale=w.scale))
+    assert np.array_equal(bits(o1), bits(o2))
+    assert np.array_equal(bits(to_host(c1.k)), bits(to_host(c2.k)))
+    assert np.array_equal(bits(to_host(c1.v)), bits(to_host(c2.v)))
+
+
+@pytest.mark.parametrize("gqa", [False, True])
+def test_graph_captured_decode_loop(gqa):
+    """Six tokens through one captured graph: inputs copied in before each
+    replay, lengths advanced on the device by the graph itself."""
+    from transformer_kv_cache_amd import kvcache as K
+    w = synth.make_workload("devlen_loop", seed=64 + gqa, dtype="bf16" if gqa else "f32", L=3, B=3,
+                            Hq=8 if gqa else 4, Hkv=2 if gqa else 4, D=128 if gqa else 64,
+                            Tmax=512, hist=[0, 130, 500], step_lens=(1,) * 6)
+    dt = torch_dtype(w.dtype)
+    cache = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    q, k, v = (to_dev(a) for a in w.steps[0])
+    out = torch.empty_like(q)
+    hd = torch.from_numpy(w.hist.astype(np.int32)).cuda()
+    ws = K.new_decode_workspace(cache, w.L, w.Hq, 1)
+    hist_max = w.Tmax - 1
+    K.decode_step_dl(cache, q, k, v, hd, hist_max, scale=w.scale, out=out, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    cache.k.copy_(to_dev(w.k_cache))
+    cache.v.copy_(to_dev(w.v_cache))
+    hd.copy_(torch.from_numpy(w.hist.astype(np.int32)))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            K.decode_step_dl(cache, q, k, v, hd, hist_max, scale=w.scale, out=out, workspace=ws)
+            K.lengths_add(hd, 1)
+    torch.cuda.current_stream().wait_stream(s)
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    hist = w.hist.copy()
+    for n, (qs, ks, vs) in enumerate(w.steps):
+        print(f"[devlen] loop gqa={gqa} step {n} hist={hist.tolist()}", flush=True)
+        q.copy_(to_dev(qs)); k.copy_(to_dev(ks)); v.copy_(to_dev(vs))
+        g.replay()
+        torch.cuda.synchronize()
+        oracle.append(kc, vc, ks, vs, hist)
+        ref = oracle.attention(qs, kc, vc, hist, w.scale)
+        got = synth.to_float(to_host(out))
+        assert float(np.max(np.abs(got - ref))) <= TOL[w.dtype], n
+        hist = hist + 1
+        assert np.array_equal(to_host(hd), hist)
+    assert np.array_equal(bits(to_host(cache.k)), bits(kc))
+    assert np.array_equal(bits(to_host(cache.v)), bits(vc))
+
+
+def test_lengths_past_the_bound_are_clamped():
+    """A device length above hist_max reads as hist_max (no access past the
+    bound): same output as the call with the length at the bound."""
+    from transformer_kv_cache_amd import kvcache as K
+    w = synth.make_workload("devlen_clamp", seed=66, dtype="f32", L=1, B=2, Hq=4, Hkv=4, D=64,
+                            Tmax=256, hist=[200, 200], step_lens=(1,))
+    q, k, v = (to_dev(a) for a in w.steps[0])
+    outs = []
+    for lens in ([200, 200], [200, 250]):
+        c = K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+        hd = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        outs.append(to_host(K.decode_step_dl(c, q, k, v, hd, 200, scale=w.scale)))
+    assert np.array_equal(bits(outs[0]), bits(outs[1]))

@@ -294,14 +294,27 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
                        const kvc::PagedGeom &pg, int32_t layer0, int32_t n_layers, const void *q,
                        const void *k_new, const void *v_new, bool fused, int32_t Hq, int32_t N,
                        const int32_t *hist_len, float scale, void *o, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+                       size_t workspace_bytes, void *stream, bool device_lengths = false,
+                       const int32_t *hist_dev = nullptr, int32_t hist_max = 0) {
   kvc_status st = check_cache(cache, layer0, n_layers, fn);
   if (st != KVC_OK) return st;
   if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
   if (Hq <= 0 || Hq % cache->Hkv != 0)
     return fail(KVC_E_SHAPE, "%s: Hq = %d is not a positive multiple of Hkv = %d", fn, Hq, cache->Hkv);
   if (!std::isfinite(scale)) return fail(KVC_E_SHAPE, "%s: scale is not finite", fn);
-  if ((st = check_hist(cache, hist_len, N, fn)) != KVC_OK) return st;
+  if (device_lengths) {
+    // lengths stay on the device: only their bound is checked here
+    if (!hist_dev && N > 0 && n_layers > 0 && cache->B > 0)
+      return fail(KVC_E_NULL, "%s: hist_len is NULL", fn);
+    if (((uintptr_t)hist_dev & 3u) != 0)
+      return fail(KVC_E_SHAPE, "%s: hist_len must be 4-byte aligned", fn);
+    if (hist_max < 0) return fail(KVC_E_SHAPE, "%s: hist_max = %d < 0", fn, hist_max);
+    if ((int64_t)hist_max + N > cache->Tmax)
+      return fail(KVC_E_CAPACITY, "%s: hist_max + N = %d + %d exceeds Tmax = %d", fn, hist_max, N,
+                  cache->Tmax);
+  } else if ((st = check_hist(cache, hist_len, N, fn)) != KVC_OK) {
+    return st;
+  }
   if (N == 0 || n_layers == 0 || cache->B == 0) return ok();
   if ((st = check_cache_pointers(cache, fn)) != KVC_OK) return st;
   if (!q || !o) return fail(KVC_E_NULL, "%s: q or o is NULL", fn);
@@ -351,14 +364,21 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   // the cache, else from the cache), so both forms do the same arithmetic.
   a.tail = g.mfma ? 0 : 1;
   a.pg = pg;
+  a.hist_dev = hist_dev;
+  a.hist_max = hist_max;
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
     a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
     int max_keys = 0;  // keys the split pass covers, longest sequence
-    for (int i = 0; i < a.nb; ++i) {
-      a.hist[i] = hist_len[b0 + i];
-      const int keys = hist_len[b0 + i] + (a.tail ? 0 : N);
-      if (keys > max_keys) max_keys = keys;
+    if (hist_dev) {
+      // sized for the bound; workgroups past a sequence's own length exit
+      max_keys = hist_max + (a.tail ? 0 : N);
+    } else {
+      for (int i = 0; i < a.nb; ++i) {
+        a.hist[i] = hist_len[b0 + i];
+        const int keys = hist_len[b0 + i] + (a.tail ? 0 : N);
+        if (keys > max_keys) max_keys = keys;
+      }
     }
     const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
     hipError_t e = hipSuccess;
@@ -390,6 +410,26 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0, int32_t n_lay
                            size_t workspace_bytes, void *stream) {
   return decode_impl("kvc_decode_step", kBoth, cache, kvc::PagedGeom{}, layer0, n_layers, q, k_new, v_new, true, Hq,
                      N, hist_len, scale, o, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_decode_step_dl(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                              const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                              int32_t N, const int32_t *hist_len_dev, int32_t hist_max, float scale,
+                              void *o, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl("kvc_decode_step_dl", kBoth, cache, kvc::PagedGeom{}, layer0, n_layers, q,
+                     k_new, v_new, true, Hq, N, nullptr, scale, o, workspace, workspace_bytes,
+                     stream, true, hist_len_dev, hist_max);
+}
+
+kvc_status kvc_lengths_add(int32_t *hist_len_dev, int32_t B, int32_t n, void *stream) {
+  if (B < 0) return fail(KVC_E_SHAPE, "kvc_lengths_add: B = %d < 0", B);
+  if (B == 0 || n == 0) return ok();
+  if (!hist_len_dev) return fail(KVC_E_NULL, "kvc_lengths_add: hist_len is NULL");
+  if (((uintptr_t)hist_len_dev & 3u) != 0)
+    return fail(KVC_E_SHAPE, "kvc_lengths_add: hist_len must be 4-byte aligned");
+  hipError_t e = kvc::launch_lengths_add(hist_len_dev, B, n, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "kvc_lengths_add");
+  return ok();
 }
 
 kvc_status kvc_decode_split(const kvc_cache *cache, int32_t layer0, int32_t n_layers, const void *q,

@@ -52,4 +52,16 @@ hipError_t launch_append(const AppendArgs &a, int /*dtype*/, int /*D*/, hipStrea
   return hipGetLastError();
 }
 
+// hist[b] += n for b < B: the device-side length update of a captured
+// decode step (kvc_lengths_add).
+__global__ __launch_bounds__(64) void lengths_add_kernel(int32_t *hist, int B, int n) {
+  const int b = (int)(blockIdx.x * 64 + threadIdx.x);
+  if (b < B) hist[b] += n;
+}
+
+hipError_t launch_lengths_add(int32_t *hist, int B, int n, hipStream_t s) {
+  hipLaunchKernelGGL(lengths_add_kernel, dim3((unsigned)((B + 63) / 64)), dim3(64), 0, s, hist, B, n);
+  return hipGetLastError();
+}
+
 }  // namespace kvc

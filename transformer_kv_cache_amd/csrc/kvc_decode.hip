@@ -117,7 +117,7 @@ __device__ __forceinline__ float rescale(float m, float M) {
   return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
-template <int DT, int D, int KPL, bool PAGED>
+template <int DT, int D, int KPL, bool PAGED, bool DEVLEN>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
   constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // Every kernel argument the prologue needs, fetched in one scalar round:
   // the empty asm takes them all as operands, so none of their loads can be
   // deferred behind the early exit or the index arithmetic.
-  const int P = a.hist[bb];
+  const int P = seq_hist<DEVLEN>(a, bb);
   const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0, tail = a.tail;
   const uint32_t hkv_div = a.hkv_div;
   const char *k_cache = a.k_cache, *v_cache = a.v_cache, *qp = a.q;
@@ -325,7 +325,7 @@ template <> struct Elem<KVC_BF16> {
 // In the fused step k_P, v_P come from k_new / v_new and this pass then
 // writes them to cache slot P (read by no kernel of the step, so the write
 // is race-free); otherwise they are read from slot P.
-template <int DT, int D>
+template <int DT, int D, bool DEVLEN>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int EPL = D / 64;  // elements per lane
   typedef typename Elem<DT>::bits bits;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int l = blockIdx.y;
   // Every kernel argument, fetched in one scalar round (the empty asm takes
   // them all as operands, so no load is deferred behind a branch).
-  const int P = a.hist[bb];
+  const int P = seq_hist<DEVLEN>(a, bb);
   const int Hq = a.Hq, N = a.N, tail = a.tail, split_keys = a.split_keys, B = a.B, Hkv = a.Hkv;
   const int Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0, max_splits = a.max_splits;
   const uint32_t split_div = a.split_div;
@@ -463,9 +463,11 @@ template <int DT, int D>
 hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
   if (a.pg.block_table)
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true, false>), grid, dim3(256), 0, s, a);
+  else if (a.hist_dev)
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -481,12 +483,22 @@ int decode_split_keys(int dtype, int D) {
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) {
   const int rows = a.Hq * a.N;  // per (layer, sequence); one wave each
   const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)a.n_layers, (unsigned)a.nb);
+  if (a.hist_dev) {
+    if (dtype == KVC_F32) {
+      if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_F32, 64, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<KVC_F32, 128, true>), grid, dim3(256), 0, s, a);
+    } else {
+      if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_BF16, 64, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<KVC_BF16, 128, true>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (dtype == KVC_F32) {
-    if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_F32, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<KVC_F32, 128>), grid, dim3(256), 0, s, a);
+    if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_F32, 64, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<KVC_F32, 128, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_BF16, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<KVC_BF16, 128>), grid, dim3(256), 0, s, a);
+    if (D == 64) hipLaunchKernelGGL((combine_kernel<KVC_BF16, 64, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<KVC_BF16, 128, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

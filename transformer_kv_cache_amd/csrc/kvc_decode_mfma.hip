@@ -65,7 +65,7 @@ __device__ __forceinline__ int vec_index(int j, int g) {
 }
 
 // KPW keys per wave (a multiple of 16), RM = 16 query rows per workgroup.
-template <int DT, int D, int KPW, bool FUSED, bool PAGED>
+template <int DT, int D, int KPW, bool FUSED, bool PAGED, bool DEVLEN>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int EB = Dtype<DT>::kBytes;
   constexpr int EV = Dtype<DT>::kPer16B;   // elements per 16-byte vector
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   const int split = blockIdx.x;
   const int bb = blockIdx.z;
-  const int P = a.hist[bb];
+  const int P = seq_hist<DEVLEN>(a, bb);
   const int rt = blockIdx.y % a.row_tiles;
   const int lh = blockIdx.y / a.row_tiles;
   const int l = div_magic(lh, a.Hkv, a.hkv_div);
@@ -292,14 +292,18 @@ template <int DT, int D, int KPW>
 hipError_t launch_kpw(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv * a.row_tiles), (unsigned)a.nb);
   const bool paged = a.pg.block_table != nullptr;
-  if (fused && paged)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, true>), grid, dim3(256), 0, s, a);
+  if (a.hist_dev) {
+    // device lengths: the fused step on a contiguous cache only
+    if (!fused || paged) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, false, true>), grid, dim3(256), 0, s, a);
+  } else if (fused && paged)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, true, false>), grid, dim3(256), 0, s, a);
   else if (fused)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, false, false>), grid, dim3(256), 0, s, a);
   else if (paged)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false, true, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, false, false, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

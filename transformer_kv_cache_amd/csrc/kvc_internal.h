@@ -120,8 +120,25 @@ struct DecodeArgs {
   int32_t tail;        // 1 (vector kernel): the split states cover keys
                        // [0, P) and the combine adds key P
   PagedGeom pg;        // paged cache, else block_table == nullptr
+  // Device lengths (kvc_decode_step_dl): hist_dev[b0 + bb] clamped into
+  // [0, hist_max] replaces hist[bb]; null for host lengths.
+  const int32_t *hist_dev;
+  int32_t hist_max;
   int32_t hist[kMaxBatchPerLaunch];
 };
+
+// Cached positions of sequence bb of the launch slice: the host value from
+// the kernel arguments, or with DEVLEN the device array, clamped so that a
+// wrong value can give wrong results but no access outside the cache.
+template <bool DEVLEN>
+__device__ __forceinline__ int seq_hist(const DecodeArgs &a, int bb) {
+  if constexpr (DEVLEN) {
+    const int v = a.hist_dev[a.b0 + bb];
+    return v < 0 ? 0 : (v > a.hist_max ? a.hist_max : v);
+  } else {
+    return a.hist[bb];
+  }
+}
 
 // floor(2^32 / d) capped at 2^32 - 1: the multiplier div_magic uses for d.
 inline uint32_t magic_for(int d) {
@@ -183,6 +200,7 @@ struct LinearArgs {
 // Host launchers (one translation unit each).  They assume validated
 // arguments and return the launch status.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t s);
+hipError_t launch_lengths_add(int32_t *hist, int B, int n, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
