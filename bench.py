@@ -375,6 +375,13 @@ def bench_gpt2(torch, contexts=(128, 512, 1000), reps=20):
         res[f"T{T}"] = {"cached_ms_per_token": round(c_us / 1e3, 4),
                         "recompute_ms_per_token": round(r_us / 1e3, 4),
                         "speedup": round(r_us / c_us, 2)}
+    # the pages' second measurement: a 1016-token greedy generation, here with
+    # the whole token step captured once (device lengths) and replayed
+    prompt = synth.token_ids(2, 8, w.V).tolist()
+    toks, ms = m.generate_graph(prompt, 1016)
+    res["generate_1016_tokens_cached_graph"] = {"prompt": len(prompt), "tokens": len(toks),
+                                                "ms_per_token": round(ms, 4),
+                                                "seconds": round(ms * (len(toks) - 1) / 1e3, 3)}
     res["model"] = "12 layers, width 768, 12 heads, vocabulary 50257, fp32, batch 1, synthetic weights"
     return res
 

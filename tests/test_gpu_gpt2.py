@@ -88,3 +88,16 @@ def test_gpt2_small_shape_matches_oracle():
         z = m.forward(torch.from_numpy(ids[P:P + 1]).cuda(), cache, P, last_only=True)
         rz = G.forward(w, ids[P:P + 1], oc)[-1]
         assert np.max(np.abs(z[0].double().cpu().numpy() - rz)) <= TOL
+
+
+def test_graph_generation_loop_matches_oracle():
+    """The whole token step captured once (device lengths) and replayed:
+    the greedy tokens equal the oracle's cached generation."""
+    from transformer_kv_cache_amd.gpt2 import GPT2
+    w = synth.gpt2_weights(**SMALL)
+    prompt = synth.token_ids(26, 7, w.V).tolist()
+    print("[gpt2] graph generation loop", flush=True)
+    toks, ms = GPT2(w).generate_graph(prompt, 20)
+    rt, _ = G.generate(w, prompt, 20, cached=True)
+    assert toks == rt
+    assert ms > 0

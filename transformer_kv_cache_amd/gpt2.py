@@ -133,6 +133,71 @@ class GPT2:
         z = K.linear(h, self.wte_t, ln=(self.lnf_g, self.lnf_b))
         return z[:, :self.V]
 
+    def _decode_token_dl(self, tok, hd, cache):
+        """One cached decode step for the token ids ``tok`` (int64 [1] on the
+        device) at the device position ``hd`` (int32 [1]); every shape and
+        argument is fixed, so the step can be captured once and replayed."""
+        d, H, D, p = self.d, self.H, self.D, self.p
+        h = self.wte[tok] + self.wpe[hd.long()]
+        for l in range(self.L):
+            qkv = K.linear(h, p["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
+            q, k, v = (qkv[:, j * d:(j + 1) * d].view(1, 1, H, 1, D) for j in range(3))
+            o = K.decode_step_dl(cache, q, k, v, hd, self.T - 1, scale=self.scale, layer0=l,
+                                 workspace=self._workspace(cache, 1))
+            K.linear(o.view(1, d), p["w_o"][l], p["b_o"][l], residual=h, out=h)
+            f = K.linear(h, p["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
+                         act="gelu")
+            K.linear(f, p["w_pr"][l], p["b_pr"][l], residual=h, out=h)
+        z = K.linear(h, self.wte_t, ln=(self.lnf_g, self.lnf_b))
+        return z[:, :self.V]
+
+    def generate_graph(self, prompt, n_new):
+        """Greedy decoding with the whole token step -- every layer, the
+        output projection, the argmax and the length update -- captured in
+        one HIP graph after the prompt's prefill and replayed n_new - 1 times.
+        Returns (tokens, the replay time per token in ms)."""
+        if n_new <= 0:
+            return [], 0.0
+        cache = self.new_cache()
+        ids = torch.tensor([int(x) for x in prompt], device=self.device)
+        z = self.forward(ids, cache, 0, last_only=True)
+        toks = torch.empty(n_new, dtype=torch.int64, device=self.device)
+        tok = torch.argmax(z[0]).view(1)
+        toks[0] = tok[0]
+        hd = torch.tensor([len(prompt)], dtype=torch.int32, device=self.device)
+        step = torch.zeros(1, dtype=torch.int64, device=self.device)
+        one = torch.ones(1, dtype=torch.int64, device=self.device)
+
+        def body():
+            zz = self._decode_token_dl(tok, hd, cache)
+            tok.copy_(torch.argmax(zz[0]).view(1))
+            step.add_(one)
+            toks.index_copy_(0, step, tok)
+            K.lengths_add(hd, 1)
+
+        if n_new == 1:
+            return toks.tolist(), 0.0
+        # warm up the workspace and the GEMM handles on a scratch copy of the state
+        saved = (cache.k.clone(), cache.v.clone(), hd.clone(), tok.clone(), step.clone())
+        body()
+        cache.k.copy_(saved[0]); cache.v.copy_(saved[1]); hd.copy_(saved[2])
+        tok.copy_(saved[3]); step.copy_(saved[4])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                body()
+        torch.cuda.current_stream().wait_stream(s)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n_new - 1):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return toks.tolist(), t0.elapsed_time(t1) / (n_new - 1)
+
     def generate(self, prompt, n_new, cached=True):
         """Greedy decoding of n_new tokens after ``prompt`` (a list of ids).
         Returns (tokens, last-position logits of every step as a float64
