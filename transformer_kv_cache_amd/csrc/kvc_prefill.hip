@@ -136,6 +136,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
                "s"(vcp));
   const int qt = (S + BM - 1) / BM - 1 - rank;
   if (qt < 0) return;
+  // Issue priority: a query tile with at most half the key tiles of the
+  // sequence's last one outranks the longer ones it shares a CU with.  The
+  // arbiter otherwise favours the oldest waves, so all workgroups resident
+  // on a CU finish together and the short tiles still queued run last, a few
+  // per CU; with the short ones first, their slots turn over early.  Short
+  // sequences (under four query tiles) gain nothing and keep the default.
+  // Measured: causal bf16 S=1024 45.5 -> 43 us.
+  if (S > 3 * BM && 2 * ((P + qt * BM + BM + BN - 1) / BN) <= (P + S + BN - 1) / BN)
+    __builtin_amdgcn_s_setprio(2);
   const int hq = head % Hq;
   const int l = head / Hq;
   const int b = b0 + bb;
