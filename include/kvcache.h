@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 7
+#define KVC_ABI_VERSION 8
 
 typedef enum {
   KVC_OK = 0,
@@ -351,6 +351,20 @@ kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0,
                                  const int32_t *block_table, int32_t max_blocks,
                                  float scale, void *o, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* kvc_paged_decode_step with the lengths in device memory: hist_len_dev and
+ * hist_max as for kvc_decode_step_dl (capacity: hist_max + N within
+ * max_blocks * block_size), so that a captured graph of the paged step stays
+ * valid as the sequences grow; the block table is read on the device as
+ * before, so its entries may change between replays too. */
+kvc_status kvc_paged_decode_step_dl(const kvc_paged_cache *cache, int32_t layer0,
+                                    int32_t n_layers, const void *q,
+                                    const void *k_new, const void *v_new,
+                                    int32_t Hq, int32_t B, int32_t N,
+                                    const int32_t *hist_len_dev, int32_t hist_max,
+                                    const int32_t *block_table, int32_t max_blocks,
+                                    float scale, void *o, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /* kvc_attn_prefill_varlen into a paged cache: cached positions below
  * hist_len[b] are read through sequence b's block table and the new tokens'

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 7
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 8
 
 
 def test_cache_bytes_against_the_page_table(lib):

@@ -556,6 +556,22 @@ kvc_status kvc_paged_attn_decode(const kvc_paged_cache *cache, int32_t layer0, i
                      hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
+kvc_status kvc_paged_decode_step_dl(const kvc_paged_cache *cache, int32_t layer0,
+                                    int32_t n_layers, const void *q, const void *k_new,
+                                    const void *v_new, int32_t Hq, int32_t B, int32_t N,
+                                    const int32_t *hist_len_dev, int32_t hist_max,
+                                    const int32_t *block_table, int32_t max_blocks, float scale,
+                                    void *o, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  static const char *fn = "kvc_paged_decode_step_dl";
+  kvc_cache view;
+  kvc::PagedGeom pg;
+  kvc_status st = paged_view(cache, B, block_table, max_blocks, fn, &view, &pg);
+  if (st != KVC_OK) return st;
+  return decode_impl(fn, kBoth, &view, pg, layer0, n_layers, q, k_new, v_new, true, Hq, N, nullptr,
+                     scale, o, workspace, workspace_bytes, stream, true, hist_len_dev, hist_max);
+}
+
 kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0, int32_t n_layers,
                                  const void *q, const void *k_new, const void *v_new, int32_t Hq,
                                  int32_t B, int32_t N, const int32_t *hist_len,

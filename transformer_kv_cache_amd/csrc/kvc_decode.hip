@@ -462,7 +462,9 @@ constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
 template <int DT, int D>
 hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
-  if (a.pg.block_table)
+  if (a.pg.block_table && a.hist_dev)
+    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true, true>), grid, dim3(256), 0, s, a);
+  else if (a.pg.block_table)
     hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true, false>), grid, dim3(256), 0, s, a);
   else if (a.hist_dev)
     hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false, true>), grid, dim3(256), 0, s, a);

@@ -293,9 +293,12 @@ hipError_t launch_kpw(const DecodeArgs &a, int splits, bool fused, hipStream_t s
   const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv * a.row_tiles), (unsigned)a.nb);
   const bool paged = a.pg.block_table != nullptr;
   if (a.hist_dev) {
-    // device lengths: the fused step on a contiguous cache only
-    if (!fused || paged) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, false, true>), grid, dim3(256), 0, s, a);
+    // device lengths: the fused step only
+    if (!fused) return hipErrorInvalidValue;
+    if (paged)
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, true, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, false, true>), grid, dim3(256), 0, s, a);
   } else if (fused && paged)
     hipLaunchKernelGGL((decode_mfma_kernel<DT, D, KPW, true, true, false>), grid, dim3(256), 0, s, a);
   else if (fused)

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 7  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 8  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -122,6 +122,9 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_step_dl.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, vp, i32,
                                            ctypes.c_float, vp, vp, sz, vp]
         lib.kvc_decode_step_dl.restype = i32
+        lib.kvc_paged_decode_step_dl.argtypes = [pp, i32, i32, vp, vp, vp, i32, i32, i32, vp, i32,
+                                                 vp, i32, f32, vp, vp, sz, vp]
+        lib.kvc_paged_decode_step_dl.restype = i32
         lib.kvc_lengths_add.argtypes = [vp, i32, i32, vp]
         lib.kvc_lengths_add.restype = i32
         lib.kvc_linear_f32.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, f32, i32, vp, vp, vp]
@@ -547,6 +550,43 @@ def _paged_decode(fn_name, cache, q, k_new, v_new, hist_len, block_table, scale,
                                            block_table.data_ptr(), mb, float(scale),
                                            out.data_ptr(), workspace.data_ptr(), wsb, st)
     _check(status)
+    return out
+
+
+def paged_decode_step_dl(cache: PagedKVCache, q, k_new, v_new, hist_len_dev, hist_max: int,
+                         block_table, scale: float | None = None, out=None, layer0: int = 0,
+                         workspace=None, stream=None):
+    """paged_decode_step with the lengths in ``hist_len_dev`` (int32 CUDA
+    tensor [B], read on the device; ``hist_max`` bounds them), for steps
+    captured once in a HIP graph."""
+    B, mb = _check_table(cache, block_table)
+    n_layers, _, Hq, N, _ = q.shape
+    shape = (n_layers, B, Hq, N, cache.D)
+    _check_tensor("q", q, cache, shape)
+    kshape = (n_layers, B, cache.Hkv, N, cache.D)
+    _check_tensor("k_new", k_new, cache, kshape)
+    _check_tensor("v_new", v_new, cache, kshape)
+    if (not isinstance(hist_len_dev, torch.Tensor) or hist_len_dev.dtype != torch.int32
+            or not hist_len_dev.is_cuda or hist_len_dev.device != cache.device
+            or not hist_len_dev.is_contiguous() or hist_len_dev.numel() != B):
+        raise ValueError(f"hist_len_dev must be a contiguous int32 CUDA tensor of {B} elements "
+                         "on the cache's device")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, cache, shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    if workspace is None:
+        need = paged_decode_workspace_bytes(cache, n_layers, B, Hq, N, mb)
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream, need=need)
+    if workspace.device != cache.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the cache's device")
+    d = cache.desc()
+    _check(library().kvc_paged_decode_step_dl(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), Hq, B,
+        N, hist_len_dev.data_ptr(), int(hist_max), block_table.data_ptr(), mb, float(scale),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(cache.device, stream)))
     return out
 
 
