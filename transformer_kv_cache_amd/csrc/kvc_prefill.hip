@@ -26,10 +26,12 @@
 //   max / sum need a single exchange between the two half-waves
 //   O^T += V^T . P^T     (P^T is taken straight from the S^T accumulators)
 // Computing the transposed products keeps the softmax probabilities in the
-// registers that feed the second MFMA: the key order inside each 16-key MFMA
-// step is permuted to match the accumulator layout, and the V tile is stored
-// to LDS in that permuted order (bf16) so each operand fetch is one 16-byte
-// LDS read.
+// registers that feed the second MFMA.  Their key order inside a 16-key MFMA
+// step follows the accumulator layout ({0-3, 8-11} in the low half-wave,
+// {4-7, 12-15} in the high); the bf16 V tile stays in LDS as loaded (keys x
+// D) and the gfx950 transpose load (ds_read_b64_tr_b16) hands each lane one
+// d of four keys, two loads giving exactly that order -- no transposition
+// work in the staging.
 //   bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV product,
 //         fp32 accumulation.
 //   fp32: v_mfma_f32_32x32x2_f32, everything in fp32 (no reduced precision).
@@ -47,21 +49,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128;  // query rows per workgroup (32 per wave)
 constexpr int BN = 64;   // keys per tile
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Position of key k (0..15) of a 16-key group in the permuted V^T rows: bits
-// 2 and 3 swapped, so a half-wave's eight probabilities of one MFMA step
-// ({0-3, 8-11} for the low half, {4-7, 12-15} for the high half) are
-// contiguous.
-__device__ __forceinline__ int perm16(int k) {
-  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -75,15 +70,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int DT, int D> struct Smem;
 template <int D> struct Smem<KVC_BF16, D> {
   static constexpr int kKStride = D + 8;    // bf16 elements per K row (16-B multiple)
-  static constexpr int kVtStride = BN + 8;  // bf16 elements per V^T row
-  // V^T row d starts at element vt_row(d): rows are kVtStride apart, plus 32
-  // bytes after every 16 rows.  Without that gap the staging writes, which put
-  // one key pair of eight rows 8 apart into the same LDS bank (8 rows span a
-  // multiple of 32 dwords), serialise eight ways; with it they are at most
-  // two-way, and the 16-byte operand reads stay conflict-free.
-  static __device__ __forceinline__ int vt_row(int d) { return d * kVtStride + (d >> 4) * 16; }
+  // V rows as loaded (keys x D).  The PV operand is read through the gfx950
+  // transpose load (ds_read_b64_tr_b16): a 16-lane group reads four rows of
+  // 32 bytes and each lane receives one d of the four keys.  A row stride of
+  // D + 16 elements puts the four rows 8 banks apart, so a group's read is
+  // conflict-free.
+  static constexpr int kVStride = D + 16;
   alignas(16) uint16_t k[BN * kKStride];
-  alignas(16) uint16_t vt[D * kVtStride + (D / 16) * 16];
+  alignas(16) uint16_t v[BN * kVStride];
 };
 template <int D> struct Smem<KVC_F32, D> {
   static constexpr int kKStride = D + 4;
@@ -110,6 +104,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int h = lane >> 5;     // half-wave
   const int col = lane & 31;   // MFMA column / row within a 32 block
+  // Transpose-load address of this lane (bf16 V operand): in its 16-lane
+  // group, lane 4 j + p names row 4 h + j, elements 4 p .. 4 p + 3 of the
+  // group's 16 d (16 for the second group of a half-wave).
+  const int v_tr_off = (4 * h + ((lane & 15) >> 2)) * ((DT == KVC_BF16) ? D + 16 : 0) +
+                       (lane & 16) + 4 * (lane & 3);
 
   // Grid: x = (layer, query head); y = tile rank, so that every sequence's
   // longest (last) query tiles come first; z = sequence in the slice, read
@@ -196,8 +195,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   const int n_all = n_all_raw < n_kt ? n_all_raw : n_kt;
 
   // Tile staging.  Each thread moves VPT 16-byte vectors of K and of V per
-  // tile, as pairs of adjacent keys (rows 2p and 2p+1) at the same column c,
-  // so that the bf16 V^T store can write both keys of a column as one dword.
+  // tile, from pairs of adjacent keys (rows 2p and 2p+1) at the same column
+  // c; K and V land in LDS row-major, one 16-byte store per vector.
   // Tile kt+1 is loaded into registers while tile kt is computed.  Positions
   // past kv_end are clamped to its last one (always valid): their scores are
   // masked, so no load needs a branch.  Positions below P come from the
@@ -274,22 +273,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
         *reinterpret_cast<u32x4 *>(cache_ptr(vcache, vcp, key) + c * 16) = vreg[it];
       }
       *reinterpret_cast<u32x4 *>(&sm.k[row * Smem<DT, D>::kKStride + c * EV]) = kreg[it];
-      if constexpr (DT == KVC_BF16) {
-        if (it & 1) {
-          // rows row-1 (even) and row: perm16 keeps bits 0-1, so they stay adjacent
-          const int pos = ((row - 1) & ~15) | perm16((row - 1) & 15);
-          const u32x4 lo = vreg[it - 1], hi = vreg[it];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t e0 = (lo[j] & 0xFFFFu) | (hi[j] << 16);          // element 2j
-            const uint32_t e1 = (lo[j] >> 16) | (hi[j] & 0xFFFF0000u);      // element 2j+1
-            *reinterpret_cast<uint32_t *>(&sm.vt[Smem<DT, D>::vt_row(c * EV + 2 * j) + pos]) = e0;
-            *reinterpret_cast<uint32_t *>(&sm.vt[Smem<DT, D>::vt_row(c * EV + 2 * j + 1) + pos]) = e1;
-          }
-        }
-      } else {
-        *reinterpret_cast<u32x4 *>(&sm.v[row * Smem<DT, D>::kVStride + c * EV]) = vreg[it];
-      }
+      *reinterpret_cast<u32x4 *>(&sm.v[row * Smem<DT, D>::kVStride + c * EV]) = vreg[it];
     }
     __syncthreads();
     if (kt + 1 < n_kt) load_tile(kt + 1);
@@ -392,8 +376,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
             pw[j] = pack_bf16x2(acc_s[kb][8 * t + 2 * j], acc_s[kb][8 * t + 2 * j + 1]);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const u32x4 vf = *reinterpret_cast<const u32x4 *>(
-                &sm.vt[Smem<DT, D>::vt_row(32 * db + col) + 32 * kb + 16 * t + 8 * h]);
+            // keys 32 kb + 16 t + {0-3, 8-11} (low half-wave) or {4-7, 12-15}
+            // (high), the order of pw; this lane's d = 32 db + col
+            const uint16_t *vb = &sm.v[(32 * kb + 16 * t) * Smem<DT, D>::kVStride + 32 * db + v_tr_off];
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)vb);
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(vb + 8 * Smem<DT, D>::kVStride));
+            const v8i16 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pw), acc_o[db], 0, 0, 0);
           }
