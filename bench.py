@@ -202,8 +202,8 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     res["step_bytes"] = decode_bytes(w, N) + new_rows_bytes(w, N)
     # split kernel alone.  One query row per KV head (vector kernel): K/V of
     # the cached keys [0, P) and q read; the combine pass adds key P from
-    # k_new/v_new and appends it.  Several rows per KV head (matrix-core
-    # kernel): K/V of all keys (new rows from k_new/v_new) and q read, new
+    # k_new/v_new and appends it.  Several rows per KV head (multi-row
+    # kernels): K/V of all keys (new rows from k_new/v_new) and q read, new
     # rows written.
     if (w.Hq // w.Hkv) * N == 1:
         res["split_bytes"] = kv_read_bytes(w, 0) + q_bytes(w, N)

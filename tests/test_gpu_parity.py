@@ -93,6 +93,29 @@ def test_decode_rows_and_groups(N, G, dtype):
                               Hq=2 * G, Hkv=2, D=64, Tmax=Tmax, hist=hist, step_lens=(N,)))
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("G,N", [(2, 1), (4, 1), (1, 2), (1, 3), (2, 2), (4, 2)])
+def test_decode_rows_bf16_d128(G, N, fused):
+    """A few query rows per KV head with 256-byte bf16 rows (D = 128): GQA
+    groups and short chunks, histories on both sides of the 64-key split
+    edges, new rows straddling a split edge, an empty history."""
+    Tmax = 260
+    hist = [0, 63, 64 - N // 2, 127, Tmax - N]
+    check(synth.make_workload(f"rows_bf16_G{G}_N{N}", seed=100 + 10 * G + N, dtype="bf16", L=2,
+                              B=5, Hq=2 * G, Hkv=2, D=128, Tmax=Tmax, hist=hist, step_lens=(N,)),
+          fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("N", [2, 4, 6, 7, 8])
+def test_decode_rows_f32_split_edges(N, fused):
+    """fp32 D = 64 chunks of 2-8 rows around the 64-key split edges."""
+    Tmax = 200
+    hist = [0, 1, 63 - N, 64, 65, 128 - N // 2, Tmax - N]
+    check(synth.make_workload(f"rows_f32_N{N}", seed=200 + N, dtype="f32", L=3, B=7, Hq=3, Hkv=3,
+                              D=64, Tmax=Tmax, hist=hist, step_lens=(N,)), fused=fused)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_d128(dtype):
     check(synth.make_workload("decode_d128", seed=11, dtype=dtype, L=2, B=3, Hq=8, Hkv=2, D=128,

@@ -74,8 +74,19 @@ kvc_status hip_status(hipError_t e, const char *fn) {
   return ok();
 }
 
+// Split kernel of a decode call: one query row per KV head (vector kernel),
+// a few rows with 256-byte key rows (multi-row vector kernel), else the
+// matrix-core kernel in tiles of 16 rows.
+enum class DecodeKernel { kVector, kRows, kMfma };
+
+// Build-time switch: 0 sends every multi-row call to the matrix-core kernel.
+#ifndef KVC_DECODE_ROWS
+#define KVC_DECODE_ROWS 1
+#endif
+
 struct DecodeGeometry {
-  bool mfma;  // several query rows per KV head: matrix-core kernel
+  DecodeKernel kernel;
+  bool mfma;  // several query rows per KV head (rows or matrix-core kernel)
   int rows, row_tile, row_tiles, split_keys, max_splits;
   size_t ws_o_bytes, ws_ml_bytes, total;
 };
@@ -87,10 +98,16 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
   const int G = Hq / c->Hkv;
   g.rows = G * N;
   g.mfma = g.rows > 1;
-  g.row_tile = g.mfma ? kvc::kMfmaRowTile : kvc::decode_row_tile(g.rows);
+  g.kernel = !g.mfma ? DecodeKernel::kVector
+             : (KVC_DECODE_ROWS && kvc::decode_rows_fits(c->dtype, c->D, g.rows)) ? DecodeKernel::kRows
+                                                                                  : DecodeKernel::kMfma;
+  g.row_tile = g.kernel == DecodeKernel::kVector ? kvc::decode_row_tile(g.rows)
+               : g.kernel == DecodeKernel::kRows ? g.rows
+                                                 : kvc::kMfmaRowTile;
   g.row_tiles = (g.rows + g.row_tile - 1) / g.row_tile;
-  g.split_keys = g.mfma ? kvc::decode_mfma_split_keys(c->dtype, c->D)
-                        : kvc::decode_split_keys(c->dtype, c->D);
+  g.split_keys = g.kernel == DecodeKernel::kVector ? kvc::decode_split_keys(c->dtype, c->D)
+                 : g.kernel == DecodeKernel::kRows ? kvc::decode_rows_split_keys()
+                                                   : kvc::decode_mfma_split_keys(c->dtype, c->D);
   g.max_splits = (c->Tmax + g.split_keys - 1) / g.split_keys;
   if (g.max_splits < 1) g.max_splits = 1;
   const size_t qrows = (size_t)n_layers * c->B * Hq * N;
@@ -355,6 +372,7 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   a.rows = g.rows;
   a.row_tiles = g.row_tiles;
   a.max_splits = g.max_splits;
+  a.ws_rows = (int64_t)n_layers * cache->B * Hq * N;
   a.split_keys = g.split_keys;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.hkv_div = kvc::magic_for(cache->Hkv);
@@ -383,9 +401,11 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
     const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
     hipError_t e = hipSuccess;
     if ((phases & kSplit) && splits > 0)
-      e = g.mfma ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused,
-                                           (hipStream_t)stream)
-                 : kvc::launch_decode(a, cache->dtype, cache->D, splits, (hipStream_t)stream);
+      e = g.kernel == DecodeKernel::kRows
+              ? kvc::launch_decode_rows(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream)
+          : g.kernel == DecodeKernel::kMfma
+              ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream)
+              : kvc::launch_decode(a, cache->dtype, cache->D, splits, (hipStream_t)stream);
     if (e == hipSuccess && (phases & kCombine) && (a.tail || splits > 1))
       e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);

@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const float val = o / L;
       store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
     } else {
-      const size_t ws = (size_t)row * a.max_splits + split;
+      const size_t ws = ws_slot(a, row, split);
       a.ws_o[ws * D + d] = o;
       if (d == 0) {
         a.ws_ml[ws * 2] = M;
@@ -338,13 +338,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   // them all as operands, so no load is deferred behind a branch).
   const int P = seq_hist<DEVLEN>(a, bb);
   const int Hq = a.Hq, N = a.N, tail = a.tail, split_keys = a.split_keys, B = a.B, Hkv = a.Hkv;
-  const int Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0, max_splits = a.max_splits;
+  const int Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0;
   const uint32_t split_div = a.split_div;
   const char *qp = a.q, *knp = a.k_new, *vnp = a.v_new;
   char *kcp = a.k_cache, *vcp = a.v_cache;
   const float *ws_o = a.ws_o, *ws_ml = a.ws_ml;
   asm volatile("" ::"s"(P), "s"(Hq), "s"(N), "s"(tail), "s"(split_keys), "s"(B), "s"(Hkv),
-               "s"(Tmax), "s"(layer0), "s"(b0), "s"(max_splits), "s"(split_div), "s"(qp),
+               "s"(Tmax), "s"(layer0), "s"(b0), "s"(split_div), "s"(qp),
                "s"(knp), "s"(vnp), "s"(kcp), "s"(vcp), "s"(ws_o), "s"(ws_ml));
   if (rloc >= Hq * N) return;
   const int nk = tail ? P : P + N;  // keys covered by split states
@@ -352,7 +352,6 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (!tail && nsplit <= 1) return;  // written by the split kernel
   const int b = b0 + bb;
   const long long row = ((long long)l * B + b) * (Hq * N) + rloc;
-  const size_t ws0 = (size_t)row * max_splits;
 
   // Cache slot P of this row's (layer, sequence, KV head); rows are
   // (l, b, hkv) in tail mode (G = N = 1), so q, k_new and v_new share the
@@ -371,10 +370,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
       const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
-      mv[t] = ws_ml[(ws0 + sp) * 2];
-      lv[t] = ws_ml[(ws0 + sp) * 2 + 1];
+      const size_t ws = ws_slot(a, row, sp);
+      mv[t] = ws_ml[ws * 2];
+      lv[t] = ws_ml[ws * 2 + 1];
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) ov[t][j] = ws_o[(ws0 + sp) * D + lane + 64 * j];
+      for (int j = 0; j < EPL; ++j) ov[t][j] = ws_o[ws * D + lane + 64 * j];
     }
   };
   // Key P's rows (loaded unconditionally, from q itself when unused, so that

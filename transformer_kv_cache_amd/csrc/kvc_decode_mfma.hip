@@ -20,7 +20,9 @@
 // waves) covers 16 query rows and a split of 4 x KPW keys; the per-row softmax
 // states of the waves merge in LDS and then follow the same path as the
 // vector kernel: the output directly, or (max, sum, partial output) into the
-// workspace for the split-combine kernel.  In the fused step keys [P, P+N)
+// workspace for the split-combine kernel.  Calls with 2-8 fp32 rows of
+// D = 64 or 2-4 bf16 rows of D = 128 run on the multi-row vector kernel
+// (kvc_decode_rows.hip) instead, which streams faster.  In the fused step keys [P, P+N)
 // are read straight from k_new / v_new, and the workgroups of row tile 0 that
 // hold them write them to their cache slots (no workgroup reads those slots
 // during the call).
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       const float val = o / L;
       store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
     } else {
-      const size_t ws = (size_t)row * a.max_splits + split;
+      const size_t ws = ws_slot(a, row, split);
       a.ws_o[ws * D + d] = o;
       if (d == 0) {
         a.ws_ml[ws * 2] = M;

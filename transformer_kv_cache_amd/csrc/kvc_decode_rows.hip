@@ -1,0 +1,444 @@
+// kvc_decode_rows.hip -- split-K decode for a few query rows per KV head on
+// the vector ALUs, streaming K/V in the access pattern of the single-row
+// kernel.
+//
+// Same computation as kvc_decode.hip and kvc_decode_mfma.hip ([KV-4]
+// jennyma11.github.io/infra/ch07-01.html, "Decode 阶段", listing 1-2; [KV-2]
+// openai-hub.com/news/2435, "一个很容易漏掉的错误": row i of N new rows sees keys
+// 0 .. P+i), for a KV head that serves R = G * N query rows with 256-byte
+// key rows: 2 <= R <= 8 in fp32 (D = 64), 2 <= R <= 4 in bf16 (D = 128) --
+// GQA groups and short chunks.
+//
+// Streaming.  A workgroup (256 lanes) owns one (layer, sequence, KV head,
+// split of 16 * KPL consecutive keys).  A key row is one 16-lane DPP row
+// wide; a workgroup-wide load covers 16 consecutive rows (4 KB), so every
+// wave instruction reads 1 KB of contiguous memory, and each lane issues its
+// KPL K loads and KPL V loads before any arithmetic, as the single-row
+// kernel does.
+//
+// Scores.  Each lane forms its 16-byte slice of the dot product with each of
+// the RP (R padded to a power of two) query rows, then the RP partial sums
+// are reduced over the 16 lanes of the key by a butterfly reduce-scatter:
+// at each of the first log2(RP) steps a lane keeps half of its values and
+// adds the partner's other half, the remaining steps add single values.  The
+// partner pairs are DPP lane swaps inside the row (xor 8 = rotate by 8,
+// xor 7 = half-row mirror, xor 2 and xor 1 = quad permutes).  Register j of
+// lane c holds the partial of query row j ^ f(c), with f linear and chosen
+// so that the half the partner gives away always holds the rows the lane
+// keeps: no selects, RP - 1 + (4 - log2 RP) adds per key instead of 4 RP.
+// Lane c ends with the score of row f(c).
+// Softmax.  Per row over the wave: a row's scores sit in its lanes' KPL
+// registers and in the wave's four DPP rows (xor 16 / 32 permlane swaps).
+// P.V.  The weights are gathered back over the 16 lanes (the reverse
+// butterfly, RP - 1 moves), so every lane holds all rows' weights of its key
+// and accumulates RP rows of its 16-byte slice of V, in its permuted row
+// order; the wave's four DPP rows (four keys per load) are then summed by a
+// reduce-scatter with the gfx950 permlane32 / permlane16 swaps, each row
+// keeping a quarter of the accumulators.  With 8 fp32 rows the product runs
+// on the matrix cores instead: the contiguous V slices are already the A
+// operand of v_mfma_f32_16x16x4f32 with the four keys of a load as the
+// contraction, and each lane's own weight is its B element, so neither the
+// gather nor the cross-row sum is needed.
+// Merge.  The four waves through LDS, then as in the other split kernels:
+// the output directly for a single split, else (max, sum, partial output)
+// per row into the workspace for the combine.
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a softmax state with max m when merged under a common max M.
+__device__ __forceinline__ float rescale(float m, float M) {
+  return m == kNegInf ? 0.f : fast_exp2(m - M);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Partner of butterfly step S inside a 16-lane row: lane c ^ 8, c ^ 7, c ^ 2,
+// c ^ 1 (DPP row_ror:8, row_half_mirror, quad_perm [2,3,0,1], [1,0,3,2]).
+constexpr int kStepCtrl[4] = {0x128, 0x141, 0x4E, 0xB1};
+template <int S>
+__device__ __forceinline__ float step_partner(float x) {
+  return dpp_mov<kStepCtrl[S]>(x);
+}
+
+// Row order of lane c: register j holds query row j ^ row_perm<RP>(c).
+// Writing c in the basis {8, 7, 2, 1} of the step masks, c = a0*8 ^ a1*7 ^
+// a2*2 ^ a3*1 with a0 = c3, a1 = c2, a2 = c1 ^ c2, a3 = c0 ^ c2, and
+// f(c) = sum over halving steps S < log2(RP) of a_S * (RP >> (S + 1)).  Then
+// f(c ^ mask_S) = f(c) ^ (RP >> (S + 1)) for a halving step (the partner's
+// upper half holds this lane's lower-half rows) and f(c ^ mask_S) = f(c) for
+// the steps after them (partners hold the same row).
+template <int RP>
+__device__ __forceinline__ int row_perm(int c) {
+  const int c3 = (c >> 3) & 1, c2 = (c >> 2) & 1, c1 = (c >> 1) & 1, c0 = c & 1;
+  const int a[4] = {c3, c2, c1 ^ c2, c0 ^ c2};
+  int f = 0;
+#pragma unroll
+  for (int s = 0; (RP >> (s + 1)) > 0; ++s) f |= a[s] * (RP >> (s + 1));
+  return f;
+}
+
+// Butterfly reduce-scatter of v[0 .. RP) over the 16 lanes of a DPP row;
+// returns the full sum of row f(c).
+template <int RP, int S = 0>
+__device__ __forceinline__ float reduce_rows(float *v) {
+  if constexpr (S == 4) {
+    return v[0];
+  } else {
+    constexpr int n = RP >> S;
+    if constexpr (n >= 2) {
+#pragma unroll
+      for (int j = 0; j < n / 2; ++j) v[j] += step_partner<S>(v[j + n / 2]);
+    } else {
+      v[0] += step_partner<S>(v[0]);
+    }
+    return reduce_rows<RP, S + 1>(v);
+  }
+}
+
+// Reverse butterfly: from u[0] = value of row f(c), fill u[0 .. RP) with the
+// values of rows j ^ f(c) held by the other lanes of the DPP row.
+template <int RP, int S>
+__device__ __forceinline__ void gather_rows(float *u) {
+  if constexpr (S >= 0) {
+    constexpr int n = RP >> (S + 1);
+#pragma unroll
+    for (int j = 0; j < n; ++j) u[j + n] = step_partner<S>(u[j]);
+    gather_rows<RP, S - 1>(u);
+  }
+}
+
+template <int RP>
+constexpr int log2_of() {
+  return RP == 2 ? 1 : RP == 4 ? 2 : RP == 8 ? 3 : 4;
+}
+
+// x combined (sum, or max with MAX) with the value 16 or 32 lanes away,
+// every lane getting the result (gfx950 permlane swap of x with itself).
+template <int OFF, bool MAX = false>
+__device__ __forceinline__ float xor_combine(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = (OFF == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y0 = __uint_as_float(r[0]), y1 = __uint_as_float(r[1]);
+  return MAX ? fmaxf(y0, y1) : y0 + y1;
+}
+
+// Sum of a and b's partners in the paired DPP rows: permlane32 pairs lanes
+// l and l + 32 (rows 0-2, 1-3), permlane16 rows 0-1 and 2-3.  Swapping the
+// upper half of a with the lower half of b and adding gives, in the lower
+// half, a summed over the pair, and in the upper half, b summed over it.
+template <int OFF>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  const auto r = (OFF == 32)
+                     ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                     : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// K/V rows are read once per call: non-temporal loads, as in the single-row
+// kernel.
+__device__ __forceinline__ u32x4 stream_load(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+template <int DT, int RP, int KPL, bool MPV, bool FUSED, bool PAGED, bool DEVLEN>
+__global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
+  constexpr int EV = Dtype<DT>::kPer16B;  // elements per 16-byte vector
+  constexpr int D = 16 * EV;              // 256-byte rows
+  constexpr int SPLIT = 16 * KPL;         // keys per workgroup
+  constexpr int NV = RP * EV;             // accumulators per lane
+  static_assert(RP >= 2 && RP <= 16 && (RP & (RP - 1)) == 0, "rows");
+  static_assert(!MPV || (DT == KVC_F32 && RP == 8), "matrix-core P.V: fp32, 8 rows");
+
+  __shared__ float sh_o[4][RP * D];
+  __shared__ float sh_m[4][RP], sh_l[4][RP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane & 15;   // 16-byte slice of the key row
+  const int kg = lane >> 4;  // DPP row of the wave
+  const int rg = tid >> 4;   // key row within a workgroup load (0 .. 15)
+
+  const int split = blockIdx.x;
+  const int bb = blockIdx.z;
+  const int lh = blockIdx.y;
+  const int P = seq_hist<DEVLEN>(a, bb);
+  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, N = a.N, rows = a.rows;
+  const int Hq = a.Hq;
+  const uint32_t hkv_div = a.hkv_div;
+  asm volatile("" ::"s"(P), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(N), "s"(rows), "s"(Hq),
+               "s"(hkv_div));
+  const int nkeys = P + N;
+  const int nsplit = (nkeys + SPLIT - 1) / SPLIT;
+  if (split >= nsplit) return;
+  const int l = div_magic(lh, Hkv, hkv_div);
+  const int hkv = lh - l * Hkv;
+  const int b = a.b0 + bb;
+
+  const size_t crow0 = (((size_t)(layer0 + l) * B + b) * Hkv + hkv) * (size_t)Tmax;
+  const char *kc = a.k_cache + crow0 * 256;
+  const char *vc = a.v_cache + crow0 * 256;
+  const size_t nrow0 = (((size_t)l * B + b) * Hkv + hkv) * (size_t)N;
+  // Query rows of this (layer, sequence, KV head): rr = g * N + i, contiguous.
+  const long long qrow0 = (((long long)l * B + b) * Hq + (long long)hkv * a.group) * N;
+
+  // This lane's row order, and the last key its own row f(c) may see (-1 for
+  // padding rows: nothing visible).
+  const int f = row_perm<RP>(c);
+  const int lim = f < rows ? P + f % N : -1;
+
+  // 1. Query slices (row j ^ f; padding rows read the last real row), then
+  //    every K and V load of the split.
+  u32x4 qw[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j) {
+    const int rr = j ^ f;
+    qw[j] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + (rr < rows ? rr : rows - 1)) * 16 + c];
+  }
+  const int key0 = split * SPLIT;
+  u32x4 kw[KPL], vw[KPL];
+  size_t prow[KPL];
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    const int key = key0 + kk * 16 + rg;
+    const int kidx = key < nkeys ? key : nkeys - 1;
+    if constexpr (PAGED) prow[kk] = paged_row(a.pg, b, kidx, layer0 + l, hkv, Hkv);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    const int key = key0 + kk * 16 + rg;
+    const int kidx = key < nkeys ? key : nkeys - 1;
+    const u32x4 *kp, *vp;
+    if (FUSED && kidx >= P) {
+      kp = reinterpret_cast<const u32x4 *>(a.k_new) + (nrow0 + (kidx - P)) * 16 + c;
+      vp = reinterpret_cast<const u32x4 *>(a.v_new) + (nrow0 + (kidx - P)) * 16 + c;
+    } else if constexpr (PAGED) {
+      kp = reinterpret_cast<const u32x4 *>(a.k_cache) + prow[kk] * 16 + c;
+      vp = reinterpret_cast<const u32x4 *>(a.v_cache) + prow[kk] * 16 + c;
+    } else {
+      const uint32_t off = (uint32_t)(kidx * 16 + c) * 16u;
+      kp = reinterpret_cast<const u32x4 *>(kc + off);
+      vp = reinterpret_cast<const u32x4 *>(vc + off);
+    }
+    kw[kk] = stream_load(kp);
+    vw[kk] = stream_load(vp);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Fused step: the workgroup holding keys [P, P + N) writes them to their
+  // cache slots (no workgroup reads those slots during the call).
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      const int key = key0 + kk * 16 + rg;
+      if (key >= P && key < nkeys) {
+        u32x4 *kd, *vd;
+        if constexpr (PAGED) {
+          kd = reinterpret_cast<u32x4 *>(a.k_cache) + prow[kk] * 16 + c;
+          vd = reinterpret_cast<u32x4 *>(a.v_cache) + prow[kk] * 16 + c;
+        } else {
+          kd = reinterpret_cast<u32x4 *>(a.k_cache) + (crow0 + key) * 16 + c;
+          vd = reinterpret_cast<u32x4 *>(a.v_cache) + (crow0 + key) * 16 + c;
+        }
+        *kd = kw[kk];
+        *vd = vw[kk];
+      }
+    }
+  }
+
+  // 2. Scores of row f in the log2 domain, one per key load.
+  float s[KPL];
+  {
+    float qf[RP][EV];
+#pragma unroll
+    for (int j = 0; j < RP; ++j) unpack16<DT>(qw[j], qf[j]);
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      float kf[EV];
+      unpack16<DT>(kw[kk], kf);
+      float part[RP];
+#pragma unroll
+      for (int j = 0; j < RP; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) d = fmaf(qf[j][e], kf[e], d);
+        part[j] = d;
+      }
+      const float dot = reduce_rows<RP>(part);
+      s[kk] = (key0 + kk * 16 + rg <= lim) ? dot * a.scale_log2 : kNegInf;
+    }
+  }
+
+  // 3. Row max over the wave, weights, row sums.
+  float m = s[0];
+#pragma unroll
+  for (int kk = 1; kk < KPL; ++kk) m = fmaxf(m, s[kk]);
+  m = xor_combine<16, true>(m);
+  m = xor_combine<32, true>(m);
+  float lsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    s[kk] = (m == kNegInf) ? 0.f : fast_exp2(s[kk] - m);
+    lsum += s[kk];
+  }
+  lsum = xor_combine<16>(lsum);
+  lsum = xor_combine<32>(lsum);
+
+  // 4. P.V summed over the wave, into this wave's LDS slice.
+  if constexpr (MPV) {
+    // On the matrix cores: per key load, O^T[d][col] += sum over the load's
+    // four keys k of V[k][d] P[row f(col)][k], v_mfma_f32_16x16x4f32 with
+    // A[i][k] = V[key k][4 i + t] (lane (i, k) = (c, kg): element t of its
+    // own V slice) and B[k][col] = the weight lane (col, k) holds.  Lane
+    // (c, kg) ends with row f(c), elements d = 16 kg + 4 r + t.
+    f32x4 acc4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      float vf[EV];
+      unpack16<DT>(vw[kk], vf);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[t], s[kk], acc4[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<f32x4 *>(&sh_o[wave][f * D + 16 * kg + 4 * r]) =
+          f32x4{acc4[0][r], acc4[1][r], acc4[2][r], acc4[3][r]};
+  } else {
+    // On the vector ALUs: weights gathered over the DPP row, acc[j][e] =
+    // row j ^ f, element c * EV + e; then summed over the wave's four DPP
+    // rows, lane (c, kg) keeping accumulators [kg * NV / 4, (kg + 1) * NV / 4).
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      float u[RP];
+      u[0] = s[kk];
+      gather_rows<RP, log2_of<RP>() - 1>(u);
+      float vf[EV];
+      unpack16<DT>(vw[kk], vf);
+#pragma unroll
+      for (int j = 0; j < RP; ++j)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[j * EV + e] = fmaf(u[j], vf[e], acc[j * EV + e]);
+    }
+    float half[NV / 2];
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) half[i] = swap_add<32>(acc[i], acc[i + NV / 2]);
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i) {
+      const int idx = kg * (NV / 4) + i;
+      const int j = idx / EV, e = idx % EV;
+      sh_o[wave][(j ^ f) * D + c * EV + e] = swap_add<16>(half[i], half[i + NV / 4]);
+    }
+  }
+
+  // 5. Merge the four waves; write the output or the split state.
+  if (kg == 0) {
+    sh_m[wave][f] = m;
+    sh_l[wave][f] = lsum;
+  }
+  __syncthreads();
+
+  for (int t = tid; t < rows * D; t += 256) {
+    const int r = t / D;
+    const int d = t % D;
+    float M = sh_m[0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh_m[w][r]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float fw = rescale(sh_m[w][r], M);
+      o = fmaf(fw, sh_o[w][r * D + d], o);
+      L = fmaf(fw, sh_l[w][r], L);
+    }
+    const long long row = qrow0 + r;
+    if (nsplit == 1) {
+      const float val = o / L;
+      store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
+    } else {
+      const size_t ws = ws_slot(a, row, split);
+      a.ws_o[ws * D + d] = o;
+      if (d == 0) {
+        a.ws_ml[ws * 2] = M;
+        a.ws_ml[ws * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Keys each lane group loads per split (a split covers 16 times as many).
+// Build-time tuning constant; 8 measured best for the chunked fp32 and the
+// bf16 GQA decode workloads (4 and 2 were slower).
+#ifndef KVC_ROWS_KEYS_PER_LANE
+#define KVC_ROWS_KEYS_PER_LANE 8
+#endif
+constexpr int kRowsKpl = KVC_ROWS_KEYS_PER_LANE;
+// P.V of 8 fp32 rows on the matrix cores (1) or the vector ALUs (0).
+#ifndef KVC_ROWS_MFMA_PV
+#define KVC_ROWS_MFMA_PV 1
+#endif
+
+template <int DT, int RP>
+hipError_t launch_rp(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
+  constexpr bool MPV = KVC_ROWS_MFMA_PV && DT == KVC_F32 && RP == 8;
+  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
+  const bool paged = a.pg.block_table != nullptr;
+  if (a.hist_dev) {
+    if (!fused) return hipErrorInvalidValue;  // device lengths: the fused step only
+    if (paged)
+      hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, true, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, false, true>), grid, dim3(256), 0, s, a);
+  } else if (fused && paged)
+    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, true, false>), grid, dim3(256), 0, s, a);
+  else if (fused)
+    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, false, false>), grid, dim3(256), 0, s, a);
+  else if (paged)
+    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, false, true, false>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, false, false, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
+  if (a.rows <= 2) return launch_rp<DT, 2>(a, splits, fused, s);
+  if (a.rows <= 4) return launch_rp<DT, 4>(a, splits, fused, s);
+  if constexpr (DT == KVC_F32) return launch_rp<DT, 8>(a, splits, fused, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_rows_fits(int dtype, int D, int rows) {
+  if (rows < 2) return false;
+  if (dtype == KVC_F32) return D == 64 && rows <= 8;
+  return D == 128 && rows <= 4;
+}
+
+int decode_rows_split_keys() { return 16 * kRowsKpl; }
+
+hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits, bool fused,
+                              hipStream_t s) {
+  if (!decode_rows_fits(dtype, D, a.rows) || a.row_tiles != 1) return hipErrorInvalidValue;
+  return dtype == KVC_F32 ? launch_dt<KVC_F32>(a, splits, fused, s)
+                          : launch_dt<KVC_BF16>(a, splits, fused, s);
+}
+
+}  // namespace kvc

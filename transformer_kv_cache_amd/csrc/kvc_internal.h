@@ -104,8 +104,9 @@ struct DecodeArgs {
   const char *k_new, *v_new;  // fused step: the N new rows, [n_layers,B,Hkv,N,D]
   const char *q;
   char *o;
-  float *ws_o;       // [rows][max_splits][D] unnormalised partial outputs
-  float *ws_ml;      // [rows][max_splits][2] partial (max, sum), log2 domain
+  float *ws_o;       // [max_splits][ws_rows][D] unnormalised partial outputs
+  float *ws_ml;      // [max_splits][ws_rows][2] partial (max, sum), log2 domain
+  int64_t ws_rows;   // query rows of the call: n_layers * B * Hq * N
   int32_t B, Hkv, Hq, Tmax, N;
   int32_t layer0, n_layers;
   int32_t group;       // Hq / Hkv
@@ -126,6 +127,14 @@ struct DecodeArgs {
   int32_t hist_max;
   int32_t hist[kMaxBatchPerLaunch];
 };
+
+// Workspace slot of query row `row` (index into the call's
+// [n_layers, B, Hq, N] rows) and split `split`, split-major: the rows a
+// workgroup writes for one split are contiguous, and so are those of its
+// neighbours in the grid, which run on the same XCD and share its L2.
+__device__ __forceinline__ size_t ws_slot(const DecodeArgs &a, long long row, int split) {
+  return (size_t)split * (size_t)a.ws_rows + (size_t)row;
+}
 
 // Cached positions of sequence bb of the launch slice: the host value from
 // the kernel arguments, or with DEVLEN the device array, clamped so that a
@@ -205,15 +214,22 @@ hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
+hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits,
+                              bool fused_append, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, hipStream_t s);
 
 // Geometry shared by kvc_decode_workspace_bytes and the decode launchers.
-// One query row per KV head runs on the vector kernel; more rows (GQA groups,
-// chunked decode) run on the matrix-core kernel in tiles of 16 rows.
+// One query row per KV head runs on the vector kernel; a few rows with
+// 256-byte key rows (GQA groups, short chunks) on the multi-row vector
+// kernel; other multi-row calls on the matrix-core kernel in tiles of 16 rows.
 int decode_row_tile(int rows);
 int decode_split_keys(int dtype, int D);
 int decode_mfma_split_keys(int dtype, int D);
+// Multi-row vector kernel: 2 <= rows with 256-byte key rows, up to 8 rows in
+// fp32 (D = 64) and 4 in bf16 (D = 128); all rows in one tile.
+bool decode_rows_fits(int dtype, int D, int rows);
+int decode_rows_split_keys();
 constexpr int kMfmaRowTile = 16;
 
 }  // namespace kvc
