@@ -407,8 +407,32 @@ def cpu_baseline(w, target_s, max_steps=100000):
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
-    return {"seconds": dt, "steps": n, "threads": oracle.max_threads(), "us_per_step": dt / n * 1e6,
-            "out": out}
+    res = {"seconds": dt, "steps": n, "threads": oracle.max_threads(), "us_per_step": dt / n * 1e6,
+           "out": out}
+    # the same steps on one thread, over a fifth of the time
+    oracle.set_threads(1)
+    n1 = 0
+    t0 = time.perf_counter()
+    while n1 < max_steps:
+        oracle.append(kc, vc, k, v, w.hist)
+        oracle.attention(q, kc, vc, w.hist, w.scale)
+        n1 += 1
+        if time.perf_counter() - t0 >= target_s / 5:
+            break
+    res["one_thread_us_per_step"] = (time.perf_counter() - t0) / n1 * 1e6
+    oracle.set_threads(threads)
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -421,6 +445,10 @@ def main():
                     help="length of the oracle's timed CPU sample")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the sweep, chunked/batched decode and prefill extras")
+    ap.add_argument("--only", choices=["prefill", "multirow"], default=None,
+                    help="time only the causal prefill workloads, or only the multi-row decode "
+                         "workloads (chunked, batched MHA / GQA), print them and exit (used for "
+                         "rocprofv3 counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (used to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -450,6 +478,26 @@ def main():
     K.library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.only == "prefill":
+        pre = []
+        for S in (256, 1024):
+            for dtype in ("f32", "bf16"):
+                log(f"prefill S={S} {dtype}")
+                pre.append({"S": S, "dtype": dtype, **bench_prefill(torch, K, S, dtype, 40)})
+        print(json.dumps({"prefill_12layer": pre}), flush=True)
+        return
+    if args.only == "multirow":
+        res = {}
+        for name, wm in (("chunked_decode_P1000_N8", synth.chunked_decode(1000, 8, seed=1)),
+                         ("batched_decode_bf16_mha12_D64", synth.batched_decode(seed=3, gqa=False)),
+                         ("batched_decode_bf16_gqa32q8kv_D128", synth.batched_decode(seed=3, gqa=True))):
+            log(name)
+            r = bench_decode(torch, K, wm, args.steps, args.warmup, 4)
+            r.pop("_out0")
+            res[name] = r
+        print(json.dumps(res), flush=True)
+        return
 
     log("headline: 12-layer fp32 decode at T=1024")
     w = synth.decode_12layer(1023, seed=0)
@@ -562,7 +610,9 @@ def main():
                          "cores": cpu["threads"], "kind": "oracle",
                          "sample": f"{cpu['steps']} full decode steps (append + attention, all 12 "
                                    f"layers) of the same workload, {cpu['seconds']:.1f} s",
-                         "us_per_step": round(cpu["us_per_step"], 1)},
+                         "us_per_step": round(cpu["us_per_step"], 1),
+                         "one_thread_us_per_step": round(cpu["one_thread_us_per_step"], 1),
+                         "cpu_model": cpu_model()},
         "parity_max_abs_err": max_err,
         "modes": {"graph_fused12_step_us": round(step_us, 3),
                   "graph_two_call_step_us": round(head["two_call_step_us"], 3),

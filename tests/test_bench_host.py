@@ -30,3 +30,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_baseline_times_the_oracle_on_all_and_one_thread():
+    """The CPU leg runs the oracle's append + attention on the headline
+    step's inputs, on the affinity's threads and then on one thread, and
+    returns the oracle's own output for the parity check."""
+    import numpy as np
+    import oracle
+    from transformer_kv_cache_amd import synth
+    w = synth.make_workload("cpu_leg", seed=1, dtype="f32", L=2, B=1, Hq=2, Hkv=2, D=64, Tmax=40,
+                            hist=[20], step_lens=(1,))
+    r = bench.cpu_baseline(w, 0.2)
+    assert r["steps"] >= 1 and r["us_per_step"] > 0 and r["one_thread_us_per_step"] > 0
+    assert r["threads"] >= 1
+    q, k, v = w.steps[0]
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    oracle.append(kc, vc, k, v, w.hist)
+    assert np.array_equal(r["out"], oracle.attention(q, kc, vc, w.hist, w.scale))
+    m = bench.cpu_model()
+    assert m is None or isinstance(m, str)
