@@ -38,7 +38,7 @@ MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix-core peaks
 METRIC = "decode attention µs/step + achieved HBM GB/s at T=1024; prefill TFLOP/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")  # split kernel
 DECODE_SOURCES = [os.path.join(ROOT, "transformer_kv_cache_amd", "csrc", f)
-                  for f in ("kvc_decode.hip", "kvc_internal.h")]
+                  for f in ("kvc_decode.hip", "kvc_device.h", "kvc_internal.h")]
 
 
 def log(msg):

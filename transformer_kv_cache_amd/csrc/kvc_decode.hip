@@ -39,49 +39,12 @@
 // last-workgroup ticket: the ticket needs a device-scope release fence in
 // every workgroup, which on gfx950 is an L2 write-back (buffer_wbl2), and
 // that measured about ten times slower than the extra launch.
+#include "kvc_device.h"
 #include "kvc_internal.h"
 
 namespace kvc {
 
 namespace {
-
-constexpr float kNegInf = -__builtin_huge_valf();
-
-// DPP controls (GFX9 encoding).
-constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-constexpr int kDppRowRor8 = 0x128;   // rotate by 8 inside each 16-lane row
-
-// x combined (sum, or max with MAX) with the value OFF lanes away, OFF in
-// {8, 16, 32}, every lane getting the result.  OFF = 8 is a DPP rotate inside
-// the 16-lane row; OFF = 16 and 32 use the gfx950 permlane swaps, which trade
-// rows (or half-waves) between two registers: swapping x with itself leaves
-// the two partners' values in the two results, so combining them gives the
-// pair's total in every lane, in VALU latency rather than an LDS round trip.
-template <int OFF, bool MAX = false>
-__device__ __forceinline__ float xor_combine(float x) {
-  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "partner distance");
-  float y0, y1;
-  if constexpr (OFF == 8) {
-    y0 = x;
-    y1 = dpp_mov<kDppRowRor8>(x);
-  } else {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = (OFF == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
-                               : __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    y0 = __uint_as_float(r[0]);
-    y1 = __uint_as_float(r[1]);
-  }
-  return MAX ? fmaxf(y0, y1) : y0 + y1;
-}
 
 // Sum over the LPR lanes that hold one key row; every lane gets the total.
 // Lane groups are aligned blocks of LPR lanes.  After the two quad steps a
@@ -97,8 +60,6 @@ __device__ __forceinline__ float row_allreduce(float x) {
   return x;
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // K/V rows are read exactly once per call: non-temporal loads keep them from
 // displacing reusable lines in the caches.
 #ifndef KVC_DECODE_NONTEMPORAL
@@ -110,11 +71,6 @@ __device__ __forceinline__ u32x4 stream_load(const u32x4 *p) {
 #else
   return *p;
 #endif
-}
-
-// Weight of a softmax state with max m when merged under a common max M.
-__device__ __forceinline__ float rescale(float m, float M) {
-  return m == kNegInf ? 0.f : fast_exp2(m - M);
 }
 
 template <int DT, int D, int KPL, bool PAGED, bool DEVLEN>

@@ -26,6 +26,7 @@
 // are read straight from k_new / v_new, and the workgroups of row tile 0 that
 // hold them write them to their cache slots (no workgroup reads those slots
 // during the call).
+#include "kvc_device.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -34,14 +35,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ float rescale(float m, float M) {
-  return m == kNegInf ? 0.f : fast_exp2(m - M);
-}
 
 #ifndef KVC_MFMA_NONTEMPORAL
 #define KVC_MFMA_NONTEMPORAL 0

@@ -42,6 +42,7 @@
 // Merge.  The four waves through LDS, then as in the other split kernels:
 // the output directly for a single split, else (max, sum, partial output)
 // per row into the workspace for the combine.
+#include "kvc_device.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -50,23 +51,9 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Weight of a softmax state with max m when merged under a common max M.
-__device__ __forceinline__ float rescale(float m, float M) {
-  return m == kNegInf ? 0.f : fast_exp2(m - M);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
 // Partner of butterfly step S inside a 16-lane row: lane c ^ 8, c ^ 7, c ^ 2,
 // c ^ 1 (DPP row_ror:8, row_half_mirror, quad_perm [2,3,0,1], [1,0,3,2]).
-constexpr int kStepCtrl[4] = {0x128, 0x141, 0x4E, 0xB1};
+constexpr int kStepCtrl[4] = {kDppRowRor8, kDppHalfMirror, kDppQuadXor2, kDppQuadXor1};
 template <int S>
 __device__ __forceinline__ float step_partner(float x) {
   return dpp_mov<kStepCtrl[S]>(x);
@@ -122,17 +109,6 @@ __device__ __forceinline__ void gather_rows(float *u) {
 template <int RP>
 constexpr int log2_of() {
   return RP == 2 ? 1 : RP == 4 ? 2 : RP == 8 ? 3 : 4;
-}
-
-// x combined (sum, or max with MAX) with the value 16 or 32 lanes away,
-// every lane getting the result (gfx950 permlane swap of x with itself).
-template <int OFF, bool MAX = false>
-__device__ __forceinline__ float xor_combine(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto r = (OFF == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
-                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float y0 = __uint_as_float(r[0]), y1 = __uint_as_float(r[1]);
-  return MAX ? fmaxf(y0, y1) : y0 + y1;
 }
 
 // Sum of a and b's partners in the paired DPP rows: permlane32 pairs lanes

@@ -39,6 +39,7 @@
 // entirely above its own 32 rows.  Grid order puts the longest (last) query
 // tiles of every sequence first, and with a (layer, head) count that is a
 // multiple of 8 all tiles of one head land on the same XCD and share its L2.
+#include "kvc_device.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -54,9 +55,6 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128;  // query rows per workgroup (32 per wave)
 constexpr int BN = 64;   // keys per tile
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
