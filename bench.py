@@ -302,6 +302,37 @@ def bench_prefill(torch, K, S, dtype, reps, rotate=4):
             "hbm_gbs": hbm_bytes / us / 1e3, "algorithmic_flops": flops}
 
 
+def bench_generation_c1(torch, K, reps=200):
+    """The single-layer generation (prompt of 16 prefilled, then four
+    single-token fused decode steps, one layer, Tmax=32): the whole sequence
+    captured in one graph per replica, timed per sequence."""
+    from gpu_common import to_dev
+    from transformer_kv_cache_amd import synth
+    w = synth.single_layer_generation(seed=0)
+    rotate = 2
+    caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, torch.float32) for _ in range(rotate)]
+    pre = [tuple(to_dev(a) for a in w.prefill) for _ in range(rotate)]
+    steps = [[tuple(to_dev(a) for a in st) for st in w.steps] for _ in range(rotate)]
+    wss = [K.new_decode_workspace(caches[0], w.L, w.Hq, 1) for _ in range(rotate)]
+    outs = [torch.empty_like(pre[0][0]) for _ in range(rotate)]
+    step_outs = [torch.empty_like(steps[0][0][0]) for _ in range(rotate)]
+    S = w.prefill[0].shape[3]
+
+    def sequence(r):
+        q, k, v = pre[r]
+        K.attn_prefill(caches[r], q, k, v, scale=w.scale, out=outs[r])
+        hist = np.full(w.B, S, dtype=np.int32)
+        for (qs, ks, vs) in steps[r]:
+            K.decode_step(caches[r], qs, ks, vs, hist, scale=w.scale, out=step_outs[r],
+                          workspace=wss[r])
+            hist += 1
+
+    for r in range(rotate):
+        sequence(r)
+    us = GraphTimer(torch, sequence, rotate).time(reps)
+    return {"sequence_us": us, "prefill_len": S, "decode_steps": len(w.steps)}
+
+
 def bench_varlen_prefill(torch, K, w, reps, rotate=4, block_size=0):
     """Time one packed variable-length prefill (synth.VarlenWorkload); with
     block_size > 0 the same rows sit in block pools behind a shuffled table
@@ -559,6 +590,9 @@ def main():
                 pre.append({k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in bench_prefill(torch, K, S, dtype, 40).items()})
         extras["prefill_12layer"] = pre
+        log("single-layer generation (prompt 16 + 4 decode steps)")
+        extras["single_layer_generation"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                             for k, v in bench_generation_c1(torch, K).items()}
         varlen = {}
         for gqa in (False, True):
             name = "bf16_" + ("gqa32q8kv_D128" if gqa else "mha12_D64") + "_B8"
@@ -612,6 +646,7 @@ def main():
                                    f"layers) of the same workload, {cpu['seconds']:.1f} s",
                          "us_per_step": round(cpu["us_per_step"], 1),
                          "one_thread_us_per_step": round(cpu["one_thread_us_per_step"], 1),
+                         "gpu_speedup": round(cpu["us_per_step"] / step_us, 1),
                          "cpu_model": cpu_model()},
         "parity_max_abs_err": max_err,
         "modes": {"graph_fused12_step_us": round(step_us, 3),
