@@ -163,6 +163,13 @@ def test_decode_error_paths(lib):
     need_big = lib.kvc_decode_workspace_bytes(ctypes.byref(big), 2, 40000, 1)
     assert call(c=ctypes.byref(big), Hq=40000, N=1, hist=hist(2), ws=h.ptr(256), wsb=need_big) == E_UNSUPPORTED
     assert "exceed one launch" in err(lib)
+    # two query rows per KV head with 256-byte rows: the splits of a context
+    # longer than 65535 splits of 128 keys do not fit one launch's grid
+    long = desc(h, L=1, B=1, Hkv=1, Tmax=65536 * 128)
+    need_long = lib.kvc_decode_workspace_bytes(ctypes.byref(long), 1, 2, 1)
+    assert call(c=ctypes.byref(long), n_layers=1, Hq=2, N=1, hist=hist(0), ws=h.ptr(256),
+                wsb=need_long) == E_UNSUPPORTED
+    assert "key splits" in err(lib)
 
 
 def test_decode_step_error_paths(lib):

@@ -346,6 +346,10 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   if ((long long)n_layers * cache->Hkv * g.row_tiles > 65535)
     return fail(KVC_E_UNSUPPORTED, "%s: %d layers x %d KV heads x %d row tiles exceed one launch", fn,
                 n_layers, cache->Hkv, g.row_tiles);
+  // the multi-row vector kernel puts the splits on the grid's y axis
+  if (g.kernel == DecodeKernel::kRows && g.max_splits > 65535)
+    return fail(KVC_E_UNSUPPORTED, "%s: Tmax = %d gives %d key splits, more than one launch holds", fn,
+                cache->Tmax, g.max_splits);
   if (!workspace) return fail(KVC_E_WORKSPACE, "%s: workspace is NULL", fn);
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(KVC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);

@@ -146,9 +146,14 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   const int kg = lane >> 4;  // DPP row of the wave
   const int rg = tid >> 4;   // key row within a workgroup load (0 .. 15)
 
-  const int split = blockIdx.x;
+  // Grid: x = (layer, KV head), y = split, z = sequence in the batch slice.
+  // With the head count a multiple of 8 every split of one head runs on the
+  // same XCD (workgroups are dealt round-robin to the 8 XCDs), and the
+  // workgroups past a short sequence's last split sit together at the end
+  // of its slice (batched GQA decode 36.0 -> 35.2 us against split-major).
+  const int lh = blockIdx.x;
+  const int split = blockIdx.y;
   const int bb = blockIdx.z;
-  const int lh = blockIdx.y;
   const int P = seq_hist<DEVLEN>(a, bb);
   const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, N = a.N, rows = a.rows;
   const int Hq = a.Hq;
@@ -373,7 +378,7 @@ constexpr int kRowsKpl = KVC_ROWS_KEYS_PER_LANE;
 template <int DT, int RP>
 hipError_t launch_rp(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
   constexpr bool MPV = KVC_ROWS_MFMA_PV && DT == KVC_F32 && RP == 8;
-  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
+  const dim3 grid((unsigned)(a.n_layers * a.Hkv), (unsigned)splits, (unsigned)a.nb);
   const bool paged = a.pg.block_table != nullptr;
   if (a.hist_dev) {
     if (!fused) return hipErrorInvalidValue;  // device lengths: the fused step only

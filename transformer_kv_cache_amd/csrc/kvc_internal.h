@@ -130,8 +130,8 @@ struct DecodeArgs {
 
 // Workspace slot of query row `row` (index into the call's
 // [n_layers, B, Hq, N] rows) and split `split`, split-major: the rows a
-// workgroup writes for one split are contiguous, and so are those of its
-// neighbours in the grid, which run on the same XCD and share its L2.
+// workgroup writes for one split are contiguous, and the next (layer, head)
+// unit's rows for the same split follow them.
 __device__ __forceinline__ size_t ws_slot(const DecodeArgs &a, long long row, int split) {
   return (size_t)split * (size_t)a.ws_rows + (size_t)row;
 }
