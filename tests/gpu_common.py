@@ -86,3 +86,40 @@ def assert_matches(w: synth.Workload, gpu, ref, tol=None):
         assert err <= tol, f"{w.name} phase {n}: max abs error {err:.3e} > {tol:.1e}"
     assert np.array_equal(bits(g_k), bits(r_k)), f"{w.name}: K cache bytes differ"
     assert np.array_equal(bits(g_v), bits(r_v)), f"{w.name}: V cache bytes differ"
+
+
+def run_paged(w, fused, layer0=0, n_layers=None):
+    """Every step of `w` through the paged entry points.  Returns (outputs,
+    final K pool, final V pool) as numpy."""
+    from transformer_kv_cache_amd import kvcache as K
+    cache = K.PagedKVCache(w.L, w.num_blocks, w.Hkv, w.block_size, w.D, torch_dtype(w.dtype),
+                           k=to_dev(w.k_pool), v=to_dev(w.v_pool))
+    bt = torch.from_numpy(w.block_table).cuda()
+    hist = w.hist.copy()
+    outs = []
+    for (q, k, v) in w.steps:
+        nl = n_layers or q.shape[0]
+        qd, kd, vd = (to_dev(np.ascontiguousarray(a[:nl])) for a in (q, k, v))
+        if fused:
+            outs.append(K.paged_decode_step(cache, qd, kd, vd, hist, bt, scale=w.scale,
+                                            layer0=layer0))
+        else:
+            K.paged_append(cache, kd, vd, hist, bt, layer0=layer0)
+            outs.append(K.paged_attn_decode(cache, qd, hist, bt, scale=w.scale, layer0=layer0))
+        hist += q.shape[3]
+    torch.cuda.synchronize()
+    return [to_host(o) for o in outs], to_host(cache.k), to_host(cache.v)
+
+
+def run_paged_oracle(w, layer0=0, n_layers=None):
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    hist = w.hist.copy()
+    outs = []
+    for (q, k, v) in w.steps:
+        nl = n_layers or q.shape[0]
+        q, k, v = (np.ascontiguousarray(a[:nl]) for a in (q, k, v))
+        oracle.paged_append(kp, vp, k, v, hist, w.block_table, layer0=layer0)
+        outs.append(oracle.paged_attention(q, kp, vp, hist, w.block_table, w.scale,
+                                           layer0=layer0))
+        hist += q.shape[3]
+    return outs, kp, vp
