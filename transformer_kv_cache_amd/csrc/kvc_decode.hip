@@ -60,6 +60,9 @@ __device__ __forceinline__ float row_allreduce(float x) {
   return x;
 }
 
+template <int NRG>
+constexpr int kLog2Nrg = NRG == 8 ? 3 : NRG == 16 ? 4 : NRG == 32 ? 5 : 6;
+
 // K/V rows are read exactly once per call: non-temporal loads keep them from
 // displacing reusable lines in the caches.
 #ifndef KVC_DECODE_NONTEMPORAL
@@ -127,16 +130,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // 1. Issue the query load and every K and V load of this split up front.
   //    Keys past the last visible one are clamped to it (a valid, written
   //    slot) so that no load sits behind a branch; their scores are masked.
-  //    A paged cache first looks up each key's block (one load per key, all
+  //    A paged cache first looks up the blocks (for blocks of at least NRG
+  //    positions one scalar load per key load, else one load per key, all
   //    issued together), then streams the rows from their blocks.
   const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
   u32x4 kw[KPL], vw[KPL];
   if constexpr (PAGED) {
     size_t prow[KPL];
+    if (a.pg.bs_log2 >= kLog2Nrg<NRG>) {
+      // blocks of at least NRG positions: one scalar id lookup per load
+      paged_rows_grouped<KPL, NRG>(a.pg, b, key0, key0 + last, rg, layer0 + l, hkv, Hkv, prow);
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < KPL; ++kk) {
-      const int kr = kk * NRG + rg;
-      prow[kk] = paged_row(a.pg, b, key0 + (kr < last ? kr : last), layer0 + l, hkv, Hkv);
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int kr = kk * NRG + rg;
+        prow[kk] = paged_row(a.pg, b, key0 + (kr < last ? kr : last), layer0 + l, hkv, Hkv);
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < KPL; ++kk) {

@@ -190,11 +190,17 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   const int key0 = split * SPLIT;
   u32x4 kw[KPL], vw[KPL];
   size_t prow[KPL];
+  if constexpr (PAGED) {
+    if (a.pg.bs_log2 >= 4) {
+      // blocks of at least 16 positions: one scalar id lookup per load
+      paged_rows_grouped<KPL, 16>(a.pg, b, key0, nkeys - 1, rg, layer0 + l, hkv, Hkv, prow);
+    } else {
 #pragma unroll
-  for (int kk = 0; kk < KPL; ++kk) {
-    const int key = key0 + kk * 16 + rg;
-    const int kidx = key < nkeys ? key : nkeys - 1;
-    if constexpr (PAGED) prow[kk] = paged_row(a.pg, b, kidx, layer0 + l, hkv, Hkv);
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int key = key0 + kk * 16 + rg;
+        prow[kk] = paged_row(a.pg, b, key < nkeys ? key : nkeys - 1, layer0 + l, hkv, Hkv);
+      }
+    }
   }
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {

@@ -88,6 +88,41 @@ __device__ __forceinline__ size_t paged_row(const PagedGeom &p, int b, int t, in
          (size_t)(t & ((1 << p.bs_log2) - 1));
 }
 
+// A load whose address is the same in every lane, through the constant
+// address space so that it becomes a scalar load.
+__device__ __forceinline__ int uniform_load(const int32_t *p) {
+  return *(const __attribute__((address_space(4))) int32_t *)(p);
+}
+
+// Pool rows of KPL groups of NRG consecutive positions of sequence b: group
+// kk holds positions first + kk * NRG + lane_off for lane_off in [0, NRG),
+// clamped to last_pos.  Call only when the block size is at least NRG and
+// `first` is a multiple of NRG: then every group lies in one block, so its
+// id is the same in all lanes and the KPL ids are fetched as scalar loads,
+// all in flight together, instead of one vector load per lane and key.
+// Block ids are clamped into the pool as in paged_row.
+template <int KPL, int NRG>
+__device__ __forceinline__ void paged_rows_grouped(const PagedGeom &p, int b, int first, int last_pos,
+                                                   int lane_off, int layer, int h, int Hkv,
+                                                   size_t (&prow)[KPL]) {
+  const int32_t *tbl = p.block_table + (size_t)b * p.max_blocks;
+  int blk[KPL];
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    const int g0 = first + kk * NRG;
+    blk[kk] = uniform_load(tbl + ((g0 < last_pos ? g0 : last_pos) >> p.bs_log2));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < KPL; ++kk) {
+    const int pos0 = first + kk * NRG + lane_off;
+    const int pos = pos0 < last_pos ? pos0 : last_pos;
+    const int bk = blk[kk] < 0 ? 0 : (blk[kk] >= p.num_blocks ? p.num_blocks - 1 : blk[kk]);
+    prow[kk] = ((((size_t)layer * p.num_blocks + bk) * Hkv + h) << p.bs_log2) +
+               (size_t)(pos & ((1 << p.bs_log2) - 1));
+  }
+}
+
 struct AppendArgs {
   char *k_cache, *v_cache;
   const char *k_new, *v_new;
