@@ -200,6 +200,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   // masked, so no load needs a branch.  Positions below P come from the
   // cache, the others from the new rows.
   auto tile_row = [&](int it) { return 2 * (tid / LPR + (it >> 1) * (256 / LPR)) + (it & 1); };
+  // Rows of one wave for one pair of vectors (it = 2 g, 2 g + 1): a
+  // kGroup-aligned run of kGroup = 128 / LPR consecutive rows.
+  constexpr int kGroup = 128 / LPR;
+  constexpr int kGroupLog2 = kGroup == 4 ? 2 : kGroup == 8 ? 3 : 4;
+  static_assert(VPT % 2 == 0 && (kGroup == 4 || kGroup == 8 || kGroup == 16), "row groups");
   const int c = tid % LPR;
   u32x4 kreg[VPT], vreg[VPT];
   // Byte offset of this thread's rows inside a tile of new rows (loop
@@ -224,6 +229,29 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
         const size_t off = (size_t)(tk0 + tile_row(it)) * RB + c * 16;
         kreg[it] = *reinterpret_cast<const u32x4 *>(kcache + off);
         vreg[it] = *reinterpret_cast<const u32x4 *>(vcache + off);
+      }
+    } else if (HIST && PAGED && tk0 + BN <= P && a.pg.bs_log2 >= kGroupLog2) {
+      // The whole tile is cached rows of a paged pool whose blocks hold at
+      // least G = 128 / LPR positions: the G rows a wave loads with each
+      // pair of vectors are G-aligned, so they lie in one block and its id
+      // is the same in all the wave's lanes -- one scalar load per pair.
+      const int32_t *tbl = a.pg.block_table + (size_t)b * a.pg.max_blocks;
+      int blk[VPT / 2];
+#pragma unroll
+      for (int g = 0; g < VPT / 2; ++g) {
+        const int r0 = __builtin_amdgcn_readfirstlane(tile_row(2 * g) & ~(kGroup - 1));
+        blk[g] = uniform_load(tbl + ((tk0 + r0) >> a.pg.bs_log2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int nb = a.pg.num_blocks, bmask = (1 << a.pg.bs_log2) - 1;
+#pragma unroll
+      for (int it = 0; it < VPT; ++it) {
+        const int key = tk0 + tile_row(it);
+        const int bk = blk[it >> 1] < 0 ? 0 : (blk[it >> 1] >= nb ? nb - 1 : blk[it >> 1]);
+        const size_t prow = ((((size_t)(layer0 + l) * nb + bk) * Hkv + hkv) << a.pg.bs_log2) +
+                            (size_t)(key & bmask);
+        kreg[it] = *reinterpret_cast<const u32x4 *>(kcp + prow * RB + c * 16);
+        vreg[it] = *reinterpret_cast<const u32x4 *>(vcp + prow * RB + c * 16);
       }
     } else if (tk0 + BN <= kv_end && (!HIST || tk0 >= P)) {
       // the whole tile is new rows, none past kv_end
