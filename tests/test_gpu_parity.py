@@ -116,6 +116,20 @@ def test_decode_rows_f32_split_edges(N, fused):
                               D=64, Tmax=Tmax, hist=hist, step_lens=(N,)), fused=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("dtype,D,G,N", [("f32", 64, 1, 1), ("bf16", 64, 1, 1), ("f32", 64, 1, 8),
+                                         ("bf16", 128, 4, 1), ("bf16", 128, 2, 3), ("f32", 128, 4, 4)])
+def test_long_context_many_splits(dtype, D, G, N, fused):
+    """Contexts of several thousand keys: 30-260 split states per query row,
+    so the combine merges them over many chunks (every shorter workload fits
+    in one), for each split kernel."""
+    Tmax = 8192
+    hist = [Tmax - N, 4097, 1000]
+    check(synth.make_workload(f"long_{dtype}_D{D}_G{G}_N{N}", seed=300 + D + 10 * G + N, dtype=dtype,
+                              L=1, B=3, Hq=2 * G, Hkv=2, D=D, Tmax=Tmax, hist=hist,
+                              step_lens=(N,)), fused=fused)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_d128(dtype):
     check(synth.make_workload("decode_d128", seed=11, dtype=dtype, L=2, B=3, Hq=8, Hkv=2, D=128,
