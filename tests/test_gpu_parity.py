@@ -75,6 +75,15 @@ def test_prefill_ragged(S, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
+def test_prefill_long_prompt(dtype, D):
+    """A 3000-token prompt (47 key tiles for the last query tile, a ragged
+    last tile) with GQA, then two decode steps on top of it."""
+    check(synth.make_workload(f"prefill_long_D{D}", seed=400 + D, dtype=dtype, L=1, B=1, Hq=4,
+                              Hkv=2, D=D, Tmax=3008, prefill_len=3000, step_lens=(1, 3)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
 def test_prefill_gqa_and_d128(dtype, D):
     check(synth.make_workload(f"prefill_gqa_D{D}", seed=D, dtype=dtype, L=1, B=2, Hq=8, Hkv=2,
                               D=D, Tmax=200, prefill_len=150, step_lens=(1, 3)))
