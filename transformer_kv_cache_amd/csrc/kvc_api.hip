@@ -106,7 +106,7 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
                                                  : kvc::kMfmaRowTile;
   g.row_tiles = (g.rows + g.row_tile - 1) / g.row_tile;
   g.split_keys = g.kernel == DecodeKernel::kVector ? kvc::decode_split_keys(c->dtype, c->D)
-                 : g.kernel == DecodeKernel::kRows ? kvc::decode_rows_split_keys()
+                 : g.kernel == DecodeKernel::kRows ? kvc::decode_rows_split_keys(c->dtype, c->D)
                                                    : kvc::decode_mfma_split_keys(c->dtype, c->D);
   g.max_splits = (c->Tmax + g.split_keys - 1) / g.split_keys;
   if (g.max_splits < 1) g.max_splits = 1;

@@ -5,20 +5,21 @@
 // Same computation as kvc_decode.hip and kvc_decode_mfma.hip ([KV-4]
 // jennyma11.github.io/infra/ch07-01.html, "Decode 阶段", listing 1-2; [KV-2]
 // openai-hub.com/news/2435, "一个很容易漏掉的错误": row i of N new rows sees keys
-// 0 .. P+i), for a KV head that serves R = G * N query rows with 256-byte
-// key rows: 2 <= R <= 8 in fp32 (D = 64), 2 <= R <= 4 in bf16 (D = 128) --
-// GQA groups and short chunks.
+// 0 .. P+i), for a KV head that serves R = G * N query rows -- GQA groups
+// and short chunks: 2 <= R <= 8 in fp32 with D = 64, 2 <= R <= 4 in bf16
+// with D = 128 or 64.
 //
 // Streaming.  A workgroup (256 lanes) owns one (layer, sequence, KV head,
-// split of 16 * KPL consecutive keys).  A key row is one 16-lane DPP row
-// wide; a workgroup-wide load covers 16 consecutive rows (4 KB), so every
+// split of 256 / LPR * KPL consecutive keys).  A key row is LPR lanes wide
+// (16 for 256-byte rows: one DPP row; 8 for 128-byte rows: half of one); a
+// workgroup-wide load covers 256 / LPR consecutive rows (4 KB), so every
 // wave instruction reads 1 KB of contiguous memory, and each lane issues its
 // KPL K loads and KPL V loads before any arithmetic, as the single-row
 // kernel does.
 //
 // Scores.  Each lane forms its 16-byte slice of the dot product with each of
 // the RP (R padded to a power of two) query rows, then the RP partial sums
-// are reduced over the 16 lanes of the key by a butterfly reduce-scatter:
+// are reduced over the LPR lanes of the key by a butterfly reduce-scatter:
 // at each of the first log2(RP) steps a lane keeps half of its values and
 // adds the partner's other half, the remaining steps add single values.  The
 // partner pairs are DPP lane swaps inside the row (xor 8 = rotate by 8,
@@ -53,56 +54,68 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Partner of butterfly step S inside a 16-lane row: lane c ^ 8, c ^ 7, c ^ 2,
 // c ^ 1 (DPP row_ror:8, row_half_mirror, quad_perm [2,3,0,1], [1,0,3,2]).
+// A key row of 16 lanes takes steps 0-3; one of 8 lanes (128-byte rows)
+// takes steps 1-3, all of which stay inside its 8 lanes.
 constexpr int kStepCtrl[4] = {kDppRowRor8, kDppHalfMirror, kDppQuadXor2, kDppQuadXor1};
 template <int S>
 __device__ __forceinline__ float step_partner(float x) {
   return dpp_mov<kStepCtrl[S]>(x);
 }
 
-// Row order of lane c: register j holds query row j ^ row_perm<RP>(c).
+// First butterfly step for key rows of LPR lanes.
+template <int LPR>
+constexpr int first_step() {
+  return LPR == 16 ? 0 : 1;
+}
+
+// Row order of lane c: register j holds query row j ^ row_perm<RP, LPR>(c).
 // Writing c in the basis {8, 7, 2, 1} of the step masks, c = a0*8 ^ a1*7 ^
 // a2*2 ^ a3*1 with a0 = c3, a1 = c2, a2 = c1 ^ c2, a3 = c0 ^ c2, and
-// f(c) = sum over halving steps S < log2(RP) of a_S * (RP >> (S + 1)).  Then
-// f(c ^ mask_S) = f(c) ^ (RP >> (S + 1)) for a halving step (the partner's
-// upper half holds this lane's lower-half rows) and f(c ^ mask_S) = f(c) for
-// the steps after them (partners hold the same row).
-template <int RP>
+// f(c) = sum over the halving steps S (the first log2(RP) steps from
+// first_step) of a_S * (RP >> (S - first + 1)).  Then f(c ^ mask_S) =
+// f(c) ^ (RP >> (S - first + 1)) for a halving step (the partner's upper
+// half holds this lane's lower-half rows) and f(c ^ mask_S) = f(c) for the
+// steps after them (partners hold the same row).  With 8-lane rows c < 8,
+// so a0 = 0 and step 0 is not taken.
+template <int RP, int LPR>
 __device__ __forceinline__ int row_perm(int c) {
+  constexpr int F = first_step<LPR>();
   const int c3 = (c >> 3) & 1, c2 = (c >> 2) & 1, c1 = (c >> 1) & 1, c0 = c & 1;
   const int a[4] = {c3, c2, c1 ^ c2, c0 ^ c2};
   int f = 0;
 #pragma unroll
-  for (int s = 0; (RP >> (s + 1)) > 0; ++s) f |= a[s] * (RP >> (s + 1));
+  for (int s = F; (RP >> (s - F + 1)) > 0; ++s) f |= a[s] * (RP >> (s - F + 1));
   return f;
 }
 
-// Butterfly reduce-scatter of v[0 .. RP) over the 16 lanes of a DPP row;
-// returns the full sum of row f(c).
-template <int RP, int S = 0>
+// Butterfly reduce-scatter of v[0 .. RP) over the LPR lanes of a key row,
+// steps F .. 3; returns the full sum of row f(c).
+template <int RP, int F, int S = F>
 __device__ __forceinline__ float reduce_rows(float *v) {
   if constexpr (S == 4) {
     return v[0];
   } else {
-    constexpr int n = RP >> S;
+    constexpr int n = RP >> (S - F);
     if constexpr (n >= 2) {
 #pragma unroll
       for (int j = 0; j < n / 2; ++j) v[j] += step_partner<S>(v[j + n / 2]);
     } else {
       v[0] += step_partner<S>(v[0]);
     }
-    return reduce_rows<RP, S + 1>(v);
+    return reduce_rows<RP, F, S + 1>(v);
   }
 }
 
 // Reverse butterfly: from u[0] = value of row f(c), fill u[0 .. RP) with the
-// values of rows j ^ f(c) held by the other lanes of the DPP row.
-template <int RP, int S>
+// values of rows j ^ f(c) held by the other lanes of the key row (steps
+// S down to F).
+template <int RP, int F, int S>
 __device__ __forceinline__ void gather_rows(float *u) {
-  if constexpr (S >= 0) {
-    constexpr int n = RP >> (S + 1);
+  if constexpr (S >= F) {
+    constexpr int n = RP >> (S - F + 1);
 #pragma unroll
     for (int j = 0; j < n; ++j) u[j + n] = step_partner<S>(u[j]);
-    gather_rows<RP, S - 1>(u);
+    gather_rows<RP, F, S - 1>(u);
   }
 }
 
@@ -127,14 +140,17 @@ __device__ __forceinline__ float swap_add(float a, float b) {
 // kernel.
 __device__ __forceinline__ u32x4 stream_load(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 
-template <int DT, int RP, int KPL, bool MPV, bool FUSED, bool PAGED, bool DEVLEN>
+template <int DT, int LPR, int RP, int KPL, bool MPV, bool FUSED, bool PAGED, bool DEVLEN>
 __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;  // elements per 16-byte vector
-  constexpr int D = 16 * EV;              // 256-byte rows
-  constexpr int SPLIT = 16 * KPL;         // keys per workgroup
+  constexpr int D = LPR * EV;             // LPR * 16-byte rows
+  constexpr int F = first_step<LPR>();    // first butterfly step
+  constexpr int NRG = 256 / LPR;          // key rows per workgroup load
+  constexpr int SPLIT = NRG * KPL;        // keys per workgroup
   constexpr int NV = RP * EV;             // accumulators per lane
+  static_assert(LPR == 8 || LPR == 16, "key row width");
   static_assert(RP >= 2 && RP <= 16 && (RP & (RP - 1)) == 0, "rows");
-  static_assert(!MPV || (DT == KVC_F32 && RP == 8), "matrix-core P.V: fp32, 8 rows");
+  static_assert(!MPV || (DT == KVC_F32 && RP == 8 && LPR == 16), "matrix-core P.V: fp32, 8 rows");
 
   __shared__ float sh_o[4][RP * D];
   __shared__ float sh_m[4][RP], sh_l[4][RP];
@@ -142,9 +158,9 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = lane & 15;   // 16-byte slice of the key row
-  const int kg = lane >> 4;  // DPP row of the wave
-  const int rg = tid >> 4;   // key row within a workgroup load (0 .. 15)
+  const int c = lane & (LPR - 1);  // 16-byte slice of the key row
+  const int kg = lane / LPR;       // key row within the wave load
+  const int rg = tid / LPR;        // key row within a workgroup load
 
   // Grid: x = (layer, KV head), y = split, z = sequence in the batch slice.
   // With the head count a multiple of 8 every split of one head runs on the
@@ -168,15 +184,15 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   const int b = a.b0 + bb;
 
   const size_t crow0 = (((size_t)(layer0 + l) * B + b) * Hkv + hkv) * (size_t)Tmax;
-  const char *kc = a.k_cache + crow0 * 256;
-  const char *vc = a.v_cache + crow0 * 256;
+  const char *kc = a.k_cache + crow0 * (LPR * 16);
+  const char *vc = a.v_cache + crow0 * (LPR * 16);
   const size_t nrow0 = (((size_t)l * B + b) * Hkv + hkv) * (size_t)N;
   // Query rows of this (layer, sequence, KV head): rr = g * N + i, contiguous.
   const long long qrow0 = (((long long)l * B + b) * Hq + (long long)hkv * a.group) * N;
 
   // This lane's row order, and the last key its own row f(c) may see (-1 for
   // padding rows: nothing visible).
-  const int f = row_perm<RP>(c);
+  const int f = row_perm<RP, LPR>(c);
   const int lim = f < rows ? P + f % N : -1;
 
   // 1. Query slices (row j ^ f; padding rows read the last real row), then
@@ -185,36 +201,36 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < RP; ++j) {
     const int rr = j ^ f;
-    qw[j] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + (rr < rows ? rr : rows - 1)) * 16 + c];
+    qw[j] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + (rr < rows ? rr : rows - 1)) * LPR + c];
   }
   const int key0 = split * SPLIT;
   u32x4 kw[KPL], vw[KPL];
   size_t prow[KPL];
   if constexpr (PAGED) {
-    if (a.pg.bs_log2 >= 4) {
-      // blocks of at least 16 positions: one scalar id lookup per load
-      paged_rows_grouped<KPL, 16>(a.pg, b, key0, nkeys - 1, rg, layer0 + l, hkv, Hkv, prow);
+    if (a.pg.bs_log2 >= (LPR == 16 ? 4 : 5)) {
+      // blocks of at least NRG positions: one scalar id lookup per load
+      paged_rows_grouped<KPL, NRG>(a.pg, b, key0, nkeys - 1, rg, layer0 + l, hkv, Hkv, prow);
     } else {
 #pragma unroll
       for (int kk = 0; kk < KPL; ++kk) {
-        const int key = key0 + kk * 16 + rg;
+        const int key = key0 + kk * NRG + rg;
         prow[kk] = paged_row(a.pg, b, key < nkeys ? key : nkeys - 1, layer0 + l, hkv, Hkv);
       }
     }
   }
 #pragma unroll
   for (int kk = 0; kk < KPL; ++kk) {
-    const int key = key0 + kk * 16 + rg;
+    const int key = key0 + kk * NRG + rg;
     const int kidx = key < nkeys ? key : nkeys - 1;
     const u32x4 *kp, *vp;
     if (FUSED && kidx >= P) {
-      kp = reinterpret_cast<const u32x4 *>(a.k_new) + (nrow0 + (kidx - P)) * 16 + c;
-      vp = reinterpret_cast<const u32x4 *>(a.v_new) + (nrow0 + (kidx - P)) * 16 + c;
+      kp = reinterpret_cast<const u32x4 *>(a.k_new) + (nrow0 + (kidx - P)) * LPR + c;
+      vp = reinterpret_cast<const u32x4 *>(a.v_new) + (nrow0 + (kidx - P)) * LPR + c;
     } else if constexpr (PAGED) {
-      kp = reinterpret_cast<const u32x4 *>(a.k_cache) + prow[kk] * 16 + c;
-      vp = reinterpret_cast<const u32x4 *>(a.v_cache) + prow[kk] * 16 + c;
+      kp = reinterpret_cast<const u32x4 *>(a.k_cache) + prow[kk] * LPR + c;
+      vp = reinterpret_cast<const u32x4 *>(a.v_cache) + prow[kk] * LPR + c;
     } else {
-      const uint32_t off = (uint32_t)(kidx * 16 + c) * 16u;
+      const uint32_t off = (uint32_t)(kidx * LPR + c) * 16u;
       kp = reinterpret_cast<const u32x4 *>(kc + off);
       vp = reinterpret_cast<const u32x4 *>(vc + off);
     }
@@ -228,15 +244,15 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   if constexpr (FUSED) {
 #pragma unroll
     for (int kk = 0; kk < KPL; ++kk) {
-      const int key = key0 + kk * 16 + rg;
+      const int key = key0 + kk * NRG + rg;
       if (key >= P && key < nkeys) {
         u32x4 *kd, *vd;
         if constexpr (PAGED) {
-          kd = reinterpret_cast<u32x4 *>(a.k_cache) + prow[kk] * 16 + c;
-          vd = reinterpret_cast<u32x4 *>(a.v_cache) + prow[kk] * 16 + c;
+          kd = reinterpret_cast<u32x4 *>(a.k_cache) + prow[kk] * LPR + c;
+          vd = reinterpret_cast<u32x4 *>(a.v_cache) + prow[kk] * LPR + c;
         } else {
-          kd = reinterpret_cast<u32x4 *>(a.k_cache) + (crow0 + key) * 16 + c;
-          vd = reinterpret_cast<u32x4 *>(a.v_cache) + (crow0 + key) * 16 + c;
+          kd = reinterpret_cast<u32x4 *>(a.k_cache) + (crow0 + key) * LPR + c;
+          vd = reinterpret_cast<u32x4 *>(a.v_cache) + (crow0 + key) * LPR + c;
         }
         *kd = kw[kk];
         *vd = vw[kk];
@@ -262,8 +278,8 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
         for (int e = 0; e < EV; ++e) d = fmaf(qf[j][e], kf[e], d);
         part[j] = d;
       }
-      const float dot = reduce_rows<RP>(part);
-      s[kk] = (key0 + kk * 16 + rg <= lim) ? dot * a.scale_log2 : kNegInf;
+      const float dot = reduce_rows<RP, F>(part);
+      s[kk] = (key0 + kk * NRG + rg <= lim) ? dot * a.scale_log2 : kNegInf;
     }
   }
 
@@ -271,6 +287,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   float m = s[0];
 #pragma unroll
   for (int kk = 1; kk < KPL; ++kk) m = fmaxf(m, s[kk]);
+  if constexpr (LPR == 8) m = xor_combine<8, true>(m);
   m = xor_combine<16, true>(m);
   m = xor_combine<32, true>(m);
   float lsum = 0.f;
@@ -279,6 +296,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
     s[kk] = (m == kNegInf) ? 0.f : fast_exp2(s[kk] - m);
     lsum += s[kk];
   }
+  if constexpr (LPR == 8) lsum = xor_combine<8>(lsum);
   lsum = xor_combine<16>(lsum);
   lsum = xor_combine<32>(lsum);
 
@@ -305,9 +323,11 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
       *reinterpret_cast<f32x4 *>(&sh_o[wave][f * D + 16 * kg + 4 * r]) =
           f32x4{acc4[0][r], acc4[1][r], acc4[2][r], acc4[3][r]};
   } else {
-    // On the vector ALUs: weights gathered over the DPP row, acc[j][e] =
-    // row j ^ f, element c * EV + e; then summed over the wave's four DPP
-    // rows, lane (c, kg) keeping accumulators [kg * NV / 4, (kg + 1) * NV / 4).
+    // On the vector ALUs: weights gathered over the key row, acc[j][e] =
+    // row j ^ f, element c * EV + e; then summed over the wave's key rows --
+    // for 8-lane rows first the two halves of each DPP row (all values),
+    // then over the four DPP rows, lane (c, kg) of DPP row q = kg * LPR / 16
+    // keeping accumulators [q * NV / 4, (q + 1) * NV / 4).
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
@@ -315,7 +335,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
     for (int kk = 0; kk < KPL; ++kk) {
       float u[RP];
       u[0] = s[kk];
-      gather_rows<RP, log2_of<RP>() - 1>(u);
+      gather_rows<RP, F, F + log2_of<RP>() - 1>(u);
       float vf[EV];
       unpack16<DT>(vw[kk], vf);
 #pragma unroll
@@ -323,14 +343,21 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EV; ++e) acc[j * EV + e] = fmaf(u[j], vf[e], acc[j * EV + e]);
     }
+    if constexpr (LPR == 8) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = xor_combine<8>(acc[i]);
+    }
     float half[NV / 2];
 #pragma unroll
     for (int i = 0; i < NV / 2; ++i) half[i] = swap_add<32>(acc[i], acc[i + NV / 2]);
+    const int q = lane >> 4;  // DPP row
 #pragma unroll
     for (int i = 0; i < NV / 4; ++i) {
-      const int idx = kg * (NV / 4) + i;
+      const int idx = q * (NV / 4) + i;
       const int j = idx / EV, e = idx % EV;
-      sh_o[wave][(j ^ f) * D + c * EV + e] = swap_add<16>(half[i], half[i + NV / 4]);
+      const float v = swap_add<16>(half[i], half[i + NV / 4]);
+      // both 8-lane halves of a DPP row hold the same sums: one writes
+      if (LPR == 16 || (kg & 1) == 0) sh_o[wave][(j ^ f) * D + c * EV + e] = v;
     }
   }
 
@@ -373,9 +400,10 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   }
 }
 
-// Keys each lane group loads per split (a split covers 16 times as many).
-// Build-time tuning constant; 8 measured best for the chunked fp32 and the
-// bf16 GQA decode workloads (4 and 2 were slower).
+// Keys each lane group loads per split (a split covers 256 / LPR times as
+// many).  Build-time tuning constant; 8 measured best for the chunked fp32
+// and the bf16 GQA decode workloads (2, 4, 6, 12 and 16 were slower or
+// equal).
 #ifndef KVC_ROWS_KEYS_PER_LANE
 #define KVC_ROWS_KEYS_PER_LANE 8
 #endif
@@ -385,33 +413,33 @@ constexpr int kRowsKpl = KVC_ROWS_KEYS_PER_LANE;
 #define KVC_ROWS_MFMA_PV 1
 #endif
 
-template <int DT, int RP>
+template <int DT, int LPR, int RP>
 hipError_t launch_rp(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
-  constexpr bool MPV = KVC_ROWS_MFMA_PV && DT == KVC_F32 && RP == 8;
+  constexpr bool MPV = KVC_ROWS_MFMA_PV && DT == KVC_F32 && RP == 8 && LPR == 16;
   const dim3 grid((unsigned)(a.n_layers * a.Hkv), (unsigned)splits, (unsigned)a.nb);
   const bool paged = a.pg.block_table != nullptr;
   if (a.hist_dev) {
     if (!fused) return hipErrorInvalidValue;  // device lengths: the fused step only
     if (paged)
-      hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, true, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_rows_kernel<DT, LPR, RP, kRowsKpl, MPV, true, true, true>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, false, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_rows_kernel<DT, LPR, RP, kRowsKpl, MPV, true, false, true>), grid, dim3(256), 0, s, a);
   } else if (fused && paged)
-    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_rows_kernel<DT, LPR, RP, kRowsKpl, MPV, true, true, false>), grid, dim3(256), 0, s, a);
   else if (fused)
-    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, true, false, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_rows_kernel<DT, LPR, RP, kRowsKpl, MPV, true, false, false>), grid, dim3(256), 0, s, a);
   else if (paged)
-    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, false, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_rows_kernel<DT, LPR, RP, kRowsKpl, MPV, false, true, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_rows_kernel<DT, RP, kRowsKpl, MPV, false, false, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_rows_kernel<DT, LPR, RP, kRowsKpl, MPV, false, false, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, int LPR>
 hipError_t launch_dt(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
-  if (a.rows <= 2) return launch_rp<DT, 2>(a, splits, fused, s);
-  if (a.rows <= 4) return launch_rp<DT, 4>(a, splits, fused, s);
-  if constexpr (DT == KVC_F32) return launch_rp<DT, 8>(a, splits, fused, s);
+  if (a.rows <= 2) return launch_rp<DT, LPR, 2>(a, splits, fused, s);
+  if (a.rows <= 4) return launch_rp<DT, LPR, 4>(a, splits, fused, s);
+  if constexpr (DT == KVC_F32 && LPR == 16) return launch_rp<DT, LPR, 8>(a, splits, fused, s);
   return hipErrorInvalidValue;
 }
 
@@ -420,16 +448,20 @@ hipError_t launch_dt(const DecodeArgs &a, int splits, bool fused, hipStream_t s)
 bool decode_rows_fits(int dtype, int D, int rows) {
   if (rows < 2) return false;
   if (dtype == KVC_F32) return D == 64 && rows <= 8;
-  return D == 128 && rows <= 4;
+  return (D == 128 || D == 64) && rows <= 4;
 }
 
-int decode_rows_split_keys() { return 16 * kRowsKpl; }
+int decode_rows_split_keys(int dtype, int D) {
+  const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;
+  return (256 / lpr) * kRowsKpl;
+}
 
 hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits, bool fused,
                               hipStream_t s) {
   if (!decode_rows_fits(dtype, D, a.rows) || a.row_tiles != 1) return hipErrorInvalidValue;
-  return dtype == KVC_F32 ? launch_dt<KVC_F32>(a, splits, fused, s)
-                          : launch_dt<KVC_BF16>(a, splits, fused, s);
+  if (dtype == KVC_F32) return launch_dt<KVC_F32, 16>(a, splits, fused, s);
+  return D == 128 ? launch_dt<KVC_BF16, 16>(a, splits, fused, s)
+                  : launch_dt<KVC_BF16, 8>(a, splits, fused, s);
 }
 
 }  // namespace kvc
