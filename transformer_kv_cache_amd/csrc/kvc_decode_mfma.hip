@@ -21,7 +21,7 @@
 // states of the waves merge in LDS and then follow the same path as the
 // vector kernel: the output directly, or (max, sum, partial output) into the
 // workspace for the split-combine kernel.  Calls with 2-8 fp32 rows of
-// D = 64 or 2-4 bf16 rows of D = 128 or 64 run on the multi-row vector kernel
+// D = 64 or 2-8 bf16 rows of D = 128 or 64 run on the multi-row vector kernel
 // (kvc_decode_rows.hip) instead, which streams faster.  In the fused step keys [P, P+N)
 // are read straight from k_new / v_new, and the workgroups of row tile 0 that
 // hold them write them to their cache slots (no workgroup reads those slots

@@ -6,8 +6,7 @@
 // jennyma11.github.io/infra/ch07-01.html, "Decode 阶段", listing 1-2; [KV-2]
 // openai-hub.com/news/2435, "一个很容易漏掉的错误": row i of N new rows sees keys
 // 0 .. P+i), for a KV head that serves R = G * N query rows -- GQA groups
-// and short chunks: 2 <= R <= 8 in fp32 with D = 64, 2 <= R <= 4 in bf16
-// with D = 128 or 64.
+// and short chunks: 2 <= R <= 8, fp32 with D = 64 or bf16 with D = 128 or 64.
 //
 // Streaming.  A workgroup (256 lanes) owns one (layer, sequence, KV head,
 // split of 256 / LPR * KPL consecutive keys).  A key row is LPR lanes wide
@@ -439,7 +438,7 @@ template <int DT, int LPR>
 hipError_t launch_dt(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
   if (a.rows <= 2) return launch_rp<DT, LPR, 2>(a, splits, fused, s);
   if (a.rows <= 4) return launch_rp<DT, LPR, 4>(a, splits, fused, s);
-  if constexpr (DT == KVC_F32 && LPR == 16) return launch_rp<DT, LPR, 8>(a, splits, fused, s);
+  if constexpr (DT == KVC_BF16 || LPR == 16) return launch_rp<DT, LPR, 8>(a, splits, fused, s);
   return hipErrorInvalidValue;
 }
 
@@ -448,7 +447,7 @@ hipError_t launch_dt(const DecodeArgs &a, int splits, bool fused, hipStream_t s)
 bool decode_rows_fits(int dtype, int D, int rows) {
   if (rows < 2) return false;
   if (dtype == KVC_F32) return D == 64 && rows <= 8;
-  return (D == 128 || D == 64) && rows <= 4;
+  return (D == 128 || D == 64) && rows <= 8;
 }
 
 int decode_rows_split_keys(int dtype, int D) {

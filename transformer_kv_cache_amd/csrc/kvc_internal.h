@@ -261,9 +261,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, 
 int decode_row_tile(int rows);
 int decode_split_keys(int dtype, int D);
 int decode_mfma_split_keys(int dtype, int D);
-// Multi-row vector kernel: 2 <= rows, up to 8 rows in fp32 (D = 64, 256-byte
-// key rows) and 4 in bf16 (D = 128 or 64: 256- or 128-byte rows); all rows
-// in one tile.
+// Multi-row vector kernel: 2 <= rows <= 8, fp32 with D = 64 (256-byte key
+// rows) or bf16 with D = 128 or 64 (256- or 128-byte rows); all rows in one
+// tile.
 bool decode_rows_fits(int dtype, int D, int rows);
 int decode_rows_split_keys(int dtype, int D);
 constexpr int kMfmaRowTile = 16;
