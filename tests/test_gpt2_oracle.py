@@ -1,8 +1,11 @@
 """Pins of the GPT-2-style oracle (oracle/gpt2.py) against facts that do not
-come from the oracle itself: the pages' cached-versus-recompute identity
-([KV-2] "正确性先于性能", tests 2-4), closed forms of layer norm and GELU, the
-pinned C attention oracle, causality, and a closed form of the whole model
-when every block is switched off."""
+come from the oracle itself: an independent GPT-2 implementation (the
+Hugging Face ``transformers`` GPT2LMHeadModel, loaded with the same weights),
+which is the pages' first correctness test ([KV-2] "正确性先于性能", test 1:
+the no-cache model's full logits against the reference implementation); the
+pages' cached-versus-recompute identity (tests 2-4); closed forms of layer
+norm and GELU; the pinned C attention oracle; causality; and a closed form of
+the whole model when every block is switched off."""
 import math
 
 import numpy as np
@@ -132,6 +135,60 @@ def test_blocks_switched_off_reduce_to_embeddings():
     assert np.max(np.abs(G.forward(w, ids) - want)) <= 1e-12
 
 
+def _hf_logits(w, ids):
+    """Full-sequence logits of ``ids`` from the Hugging Face GPT-2 model
+    built in float64 with the weights of ``w`` (dropout off, layer-norm eps
+    1e-5, tanh GELU, output projection tied to the token embedding).  Its
+    Conv1D layers store [in, out] matrices, the layout of w_qkv, w_o, w_fc
+    and w_pr; its attention splits the QKV product into q, k, v thirds and
+    each third into heads by its own code, not the oracle's."""
+    transformers = pytest.importorskip("transformers")
+    import torch
+    cfg = transformers.GPT2Config(
+        n_layer=w.L, n_embd=w.d, n_head=w.H, vocab_size=w.V, n_positions=w.T,
+        layer_norm_epsilon=1e-5, activation_function="gelu_new", resid_pdrop=0.0,
+        embd_pdrop=0.0, attn_pdrop=0.0, tie_word_embeddings=True,
+        bos_token_id=0, eos_token_id=0)
+    model = transformers.GPT2LMHeadModel(cfg).double().eval()
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    sd = {"transformer.wte.weight": t(w.wte), "transformer.wpe.weight": t(w.wpe),
+          "transformer.ln_f.weight": t(w.lnf_g), "transformer.ln_f.bias": t(w.lnf_b),
+          "lm_head.weight": t(w.wte)}
+    for l in range(w.L):
+        p = f"transformer.h.{l}."
+        sd.update({p + "ln_1.weight": t(w.ln1_g[l]), p + "ln_1.bias": t(w.ln1_b[l]),
+                   p + "attn.c_attn.weight": t(w.w_qkv[l]), p + "attn.c_attn.bias": t(w.b_qkv[l]),
+                   p + "attn.c_proj.weight": t(w.w_o[l]), p + "attn.c_proj.bias": t(w.b_o[l]),
+                   p + "ln_2.weight": t(w.ln2_g[l]), p + "ln_2.bias": t(w.ln2_b[l]),
+                   p + "mlp.c_fc.weight": t(w.w_fc[l]), p + "mlp.c_fc.bias": t(w.b_fc[l]),
+                   p + "mlp.c_proj.weight": t(w.w_pr[l]), p + "mlp.c_proj.bias": t(w.b_pr[l])})
+    missing, unexpected = model.load_state_dict(sd, strict=False)
+    assert not unexpected and all("attn.bias" in k or "masked_bias" in k for k in missing), \
+        (missing, unexpected)
+    with torch.no_grad():
+        out = model(torch.from_numpy(np.asarray(ids, dtype=np.int64))[None], use_cache=False)
+    return out.logits[0].numpy()
+
+
+def test_logits_match_reference_implementation():
+    """[KV-2] "正确性先于性能", test 1: the no-cache model's full logits
+    against an independent GPT-2 implementation on the same weights, every
+    position of a 20-token sequence (both float64: agreement to rounding)."""
+    ids = synth.token_ids(12, 20, W.V)
+    ref = _hf_logits(W, ids)
+    assert np.max(np.abs(G.forward(W, ids) - ref)) <= 1e-12
+
+
+def test_logits_match_reference_implementation_gpt2_small_width():
+    """The same at GPT-2 Small's sizes (12 layers, width 768, 12 heads,
+    vocabulary 50257, 1024 positions) on a short sequence placed at the
+    start of the position table."""
+    w = synth.gpt2_weights(seed=4)
+    ids = synth.token_ids(13, 5, w.V)
+    ref = _hf_logits(w, ids)
+    assert np.max(np.abs(G.forward(w, ids) - ref)) <= 1e-12
+
+
 # ---- plausible mistakes the pins must catch ----------------------------------
 
 MUTANTS = {
@@ -144,9 +201,15 @@ MUTANTS = {
     "no_final_norm": ("return layer_norm(h, _f(w.lnf_g), _f(w.lnf_b)) @", "return h @"),
     "cache_rows_not_written": ("cache.k[l, :, P:P + N] = k", "cache.k[l, :, P:P + N] = 0 * k"),
     "softmax_without_max": ("s = s - s.max(axis=-1, keepdims=True)", "s = s - 0.0"),
+    "qkv_thirds_swapped": ("q, k, v = (qkv[:, j * d:", "k, q, v = (qkv[:, j * d:"),
+    "heads_interleaved": (".reshape(N, H, D).transpose(1, 0, 2) for j",
+                          ".reshape(N, D, H).transpose(2, 0, 1) for j"),
+    "layer_norm_gain_and_shift_swapped": ("a = layer_norm(h, _f(w.ln1_g[l]), _f(w.ln1_b[l]))",
+                                          "a = layer_norm(h, _f(w.ln1_b[l]), _f(w.ln1_g[l]))"),
+    "mlp_without_gelu": ("h = h + gelu(m @ _f(w.w_fc[l])", "h = h + (m @ _f(w.w_fc[l])"),
 }
 
-PINS = [test_cached_decode_equals_recompute_every_step, test_context_limit, test_layer_norm_closed_form,
+PINS = [test_logits_match_reference_implementation, test_cached_decode_equals_recompute_every_step, test_context_limit, test_layer_norm_closed_form,
         test_gelu_closed_forms, test_attention_matches_pinned_c_oracle, test_attention_large_scores,
         test_causal,
         test_blocks_switched_off_reduce_to_embeddings,
