@@ -2,13 +2,16 @@
 
 One step = the whole decode hot path for GPT-2 Small at context 1024: the new
 token's K/V rows written into all 12 layers' caches and the attention of the
-new query rows against the 1024 cached keys, issued as one kvc_decode_step
-(split-K kernel that also writes the new rows, then the split-combine kernel).
+new query rows against the 1024 cached keys, issued as one kvc_decode_step:
+one kernel, the split-K pass over the cached keys whose last split workgroup
+of each row merges the row's splits with the new key and appends its row.
 Inputs: fp32, B=1, 12 layers x 12 heads, D=64, history P=1023, N(0,1) from a
 fixed seed.
 
 Timing: steps are captured in a HIP graph (torch.cuda.CUDAGraph) and replayed;
-HIP events on the capture/replay stream bracket exactly --steps steps.  Eight
+HIP events on the capture/replay stream bracket exactly --steps steps, five
+times after a warm-up, and every figure is the median of the five samples
+(min and max reported for the headline).  Eight
 cache replicas (604 MB in total, more than twice the 256 MB Infinity Cache)
 rotate step by step, so every step streams its K/V from HBM rather than from
 a cache level.  The oracle (CPU, double precision) is timed beside it on a
@@ -34,11 +37,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
+# A plain streaming read of the step's 75.5 MB (2,304 workgroups, each 32 KB
+# of 16-byte loads issued at once, cold, back-to-back launches) measured on
+# the box at 12.37 us: the most this step's bytes can move at, as a fraction
+# of HBM_PEAK_GBS.
+PLAIN_READ_FRAC = 0.763
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix-core peaks
 METRIC = "decode attention µs/step + achieved HBM GB/s at T=1024; prefill TFLOP/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")  # split kernel
 DECODE_SOURCES = [os.path.join(ROOT, "transformer_kv_cache_amd", "csrc", f)
-                  for f in ("kvc_decode.hip", "kvc_device.h", "kvc_internal.h")]
+                  for f in ("kvc_decode.hip", "kvc_device.h", "kvc_internal.h", "kvc_api.hip")]
 
 
 def log(msg):
@@ -101,15 +109,21 @@ def read_traffic():
         return None
 
 
+SAMPLES = 5  # timed samples per figure; the figure is their median
+
+
 class GraphTimer:
     """Capture `fn(r)` for r in a rotation into HIP graphs and time exactly
-    `count` calls with events on the replay stream."""
+    `count` calls with events on the replay stream, SAMPLES times; `time`
+    returns the median (microseconds per call) and leaves every sample in
+    `samples`."""
 
     def __init__(self, torch, fn, rotate):
         self.torch = torch
         self.rotate = rotate
         self.fn = fn
         self.graphs = {}
+        self.samples = []
 
     def _graph(self, n):
         if n not in self.graphs:
@@ -133,16 +147,19 @@ class GraphTimer:
         for _ in range(warm):
             g_full.replay()
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(full):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) * 1e3 / count  # microseconds per call
+        self.samples = []
+        for _ in range(SAMPLES):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(full):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            end.record()
+            torch.cuda.synchronize()
+            self.samples.append(start.elapsed_time(end) * 1e3 / count)  # microseconds per call
+        return float(np.median(self.samples))
 
 
 def replicate(torch, arr_dev, n):
@@ -152,7 +169,7 @@ def replicate(torch, arr_dev, n):
 def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=False):
     """Time the decode step (append + attention) of workload `w` (one step
     of N rows).  Returns a dict of timings and the device state of replica 0."""
-    from gpu_common import to_dev, torch_dtype
+    from transformer_kv_cache_amd.hostio import to_dev, torch_dtype
     q_np, k_np, v_np = w.steps[0]
     N = q_np.shape[3]
     base_k, base_v = to_dev(w.k_cache), to_dev(w.v_cache)
@@ -192,7 +209,9 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
         step(i % rotate)
     torch.cuda.synchronize()
     res = {}
-    res["step_us"] = GraphTimer(torch, step, rotate).time(steps)
+    t_step = GraphTimer(torch, step, rotate)
+    res["step_us"] = t_step.time(steps)
+    res["step_us_min"], res["step_us_max"] = min(t_step.samples), max(t_step.samples)
     res["split_us"] = GraphTimer(torch, split_only, rotate).time(steps)
     res["combine_us"] = GraphTimer(torch, combine_only, rotate).time(steps)
     res["two_call_step_us"] = GraphTimer(torch, step_two_calls, rotate).time(steps)
@@ -200,11 +219,11 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     res["append_us"] = GraphTimer(torch, append_only, rotate).time(steps)
     # the fused step reads the new rows from k_new/v_new and writes them once
     res["step_bytes"] = decode_bytes(w, N) + new_rows_bytes(w, N)
-    # split kernel alone.  One query row per KV head (vector kernel): K/V of
-    # the cached keys [0, P) and q read; the combine pass adds key P from
-    # k_new/v_new and appends it.  Several rows per KV head (multi-row
-    # kernels): K/V of all keys (new rows from k_new/v_new) and q read, new
-    # rows written.
+    # split pass alone (kvc_decode_split: the same kernel without the merge).
+    # One query row per KV head: K/V of the cached keys [0, P) and q read;
+    # the merge adds key P from k_new/v_new and appends it.  Several rows per
+    # KV head (multi-row kernels): K/V of all keys (new rows from
+    # k_new/v_new) and q read, new rows written.
     if (w.Hq // w.Hkv) * N == 1:
         res["split_bytes"] = kv_read_bytes(w, 0) + q_bytes(w, N)
     else:
@@ -242,7 +261,7 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
 def bench_paged_decode(torch, K, w, steps, warmup, rotate):
     """Time the paged decode step of paged workload `w` (one step of N rows),
     pools and inputs rotated over `rotate` replicas like bench_decode."""
-    from gpu_common import to_dev, torch_dtype
+    from transformer_kv_cache_amd.hostio import to_dev, torch_dtype
     q_np, k_np, v_np = w.steps[0]
     N = q_np.shape[3]
     dt = torch_dtype(w.dtype)
@@ -277,11 +296,15 @@ def bench_paged_decode(torch, K, w, steps, warmup, rotate):
     return res
 
 
-def bench_prefill(torch, K, S, dtype, reps, rotate=4):
-    from gpu_common import to_dev, torch_dtype
+def bench_prefill(torch, K, S, dtype, reps):
+    from transformer_kv_cache_amd.hostio import to_dev, torch_dtype
     from transformer_kv_cache_amd import synth
     w = synth.causal_prefill(S, dtype, seed=7)
     dt = torch_dtype(dtype)
+    # replicas so that at least 512 MB of inputs, outputs and cache rows are
+    # touched between two uses of one, twice the 256 MB Infinity Cache
+    touched = 6 * w.L * w.Hq * S * w.D * elem_bytes(dtype)
+    rotate = max(4, -(-512_000_000 // touched))
     q0, k0, v0 = (to_dev(a) for a in w.prefill)
     qs, ks, vs = (replicate(torch, t, rotate) for t in (q0, k0, v0))
     caches = [K.KVCache(w.L, w.B, w.Hkv, w.Tmax, w.D, dt) for _ in range(rotate)]
@@ -306,7 +329,7 @@ def bench_generation_c1(torch, K, reps=200):
     """The single-layer generation (prompt of 16 prefilled, then four
     single-token fused decode steps, one layer, Tmax=32): the whole sequence
     captured in one graph per replica, timed per sequence."""
-    from gpu_common import to_dev
+    from transformer_kv_cache_amd.hostio import to_dev
     from transformer_kv_cache_amd import synth
     w = synth.single_layer_generation(seed=0)
     rotate = 2
@@ -337,7 +360,7 @@ def bench_varlen_prefill(torch, K, w, reps, rotate=4, block_size=0):
     """Time one packed variable-length prefill (synth.VarlenWorkload); with
     block_size > 0 the same rows sit in block pools behind a shuffled table
     and the paged entry point runs."""
-    from gpu_common import to_dev, torch_dtype
+    from transformer_kv_cache_amd.hostio import to_dev, torch_dtype
     from transformer_kv_cache_amd import synth
     dt = torch_dtype(w.dtype)
     qs, ks, vs = (replicate(torch, to_dev(a), rotate) for a in (w.q, w.k, w.v))
@@ -499,9 +522,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "copies": 4}), flush=True)
         return
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     from transformer_kv_cache_amd import kvcache as K, synth
-    from gpu_common import to_host
+    from transformer_kv_cache_amd.hostio import to_host
 
     if not os.path.exists(K.LIB_PATH):
         from transformer_kv_cache_amd import build
@@ -626,20 +648,27 @@ def main():
         "config": {"workload": "GPT-2 Small KV-cache decode step, 12 layers, fp32, B=1, H=12, "
                                "D=64, Tmax=1024, history 1023 + 1 new token (T=1024)",
                    "layers": 12, "batch": 1, "heads": 12, "head_dim": 64, "context": 1024,
-                   "step": "kvc_decode_step: split-K kernel over the cached keys + combine kernel (adds the new key, appends its row)",
+                   "step": "kvc_decode_step: one kernel -- split-K pass over the cached keys, "
+                           "the last split workgroup of each row merges the row's splits with "
+                           "the new key and appends its row",
                    "rotating_cache_replicas": args.rotate},
         "decode_us_per_step": round(step_us, 3),
+        "decode_us_per_step_min": round(head["step_us_min"], 3),
+        "decode_us_per_step_max": round(head["step_us_max"], 3),
         "step_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(head["split_gbs"], 1),
+        # the step is one kernel launch: its algorithmic bytes over its time
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / step_us / 1e3, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
+                     "frac": round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_kernel<f32,D64,KPL4> (split-K pass over the cached keys, "
-                               "kvc_decode_split)",
-                     "launch_us": round(head["split_us"], 3),
-                     "algorithmic_bytes": head["split_bytes"],
-                     "combine_kernel_us": round(head["combine_us"], 3),
-                     "step_frac": round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4)},
+                     "kernel": "decode_kernel<f32,D64,KPL8,merge> (the whole step in one launch: "
+                               "split-K over keys [0,1023), the last split of each row merges "
+                               "and adds key 1023, appending its row)",
+                     "launch_us": round(step_us, 3),
+                     "algorithmic_bytes": step_bytes,
+                     "split_pass_only_us": round(head["split_us"], 3),
+                     "split_pass_only_frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
+                     "plain_read_ceiling_frac": PLAIN_READ_FRAC},
         "cpu_baseline": {"value": round(step_bytes / cpu["us_per_step"] / 1e3, 3), "unit": "GB/s",
                          "cores": cpu["threads"], "kind": "oracle",
                          "sample": f"{cpu['steps']} full decode steps (append + attention, all 12 "

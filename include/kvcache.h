@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 8
+#define KVC_ABI_VERSION 9
 
 typedef enum {
   KVC_OK = 0,
@@ -116,9 +116,11 @@ kvc_status kvc_append(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
 /*
  * Workspace bytes kvc_attn_decode needs for this geometry: the partial
  * softmax states (max, sum and unnormalised output row) of the split-K
- * passes.  It depends only on the cache geometry, n_layers, Hq and N, never
- * on the lengths, so one workspace serves every step.  Returns 0 on invalid
- * sizes.
+ * passes and, for one query row per KV head, one 8-byte arrival counter per
+ * query row (the last split of a row to finish merges the row inside the
+ * same launch).  It depends only on the cache geometry, n_layers, Hq and N,
+ * never on the lengths, so one workspace serves every step.  Returns 0 on
+ * invalid sizes.
  */
 size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers,
                                   int32_t Hq, int32_t N);
@@ -135,13 +137,22 @@ size_t kvc_decode_workspace_bytes(const kvc_cache *cache, int32_t n_layers,
  * there).  The K/V rows of the N new tokens must already be in the cache at
  * positions [P, P+N) (call kvc_append first with the same hist_len).
  *   q, o       : device, [n_layers, B, Hq, N, D], cache dtype
- *   scale      : finite score scale, normally 1/sqrt(D)
+ *   scale      : finite score scale, normally 1/sqrt(D); any finite value
+ *                is accepted (0 gives equal weights over the visible keys, a
+ *                negative one the scores' negation).  Every decode and
+ *                prefill entry point takes it the same way; an infinite or
+ *                NaN scale is KVC_E_SHAPE.
  *   workspace  : device, >= kvc_decode_workspace_bytes(...) bytes, 256-byte
- *                aligned, caller-owned scratch.  Its contents need no
- *                initialisation and are meaningless after the call; calls
- *                enqueued one after another on a stream may share one.  Two
- *                calls in flight at the same time must not share a
- *                workspace.
+ *                aligned, caller-owned.  Zero-fill it once before its first
+ *                use: with one query row per KV head its first bytes are
+ *                arrival counters that must be zero when a call starts, and
+ *                every call that returns KVC_OK leaves them zero again when
+ *                its kernels end; the rest is scratch.  A call of another
+ *                geometry (cache shape, n_layers, B, Hq or N) may use those
+ *                bytes as scratch, so give each geometry its own workspace
+ *                (or zero-fill it again when switching).  Calls enqueued one
+ *                after another on a stream may share one.  Two calls in
+ *                flight at the same time must not share a workspace.
  */
 kvc_status kvc_attn_decode(const kvc_cache *cache, int32_t layer0,
                            int32_t n_layers, const void *q, int32_t Hq,

@@ -8,25 +8,9 @@ import torch
 
 import oracle
 from transformer_kv_cache_amd import synth
+from transformer_kv_cache_amd.hostio import to_dev, to_host, torch_dtype  # noqa: F401 (re-exported)
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}  # max abs error against the oracle
-
-
-def to_dev(a: np.ndarray) -> torch.Tensor:
-    if a.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-
-def to_host(t: torch.Tensor) -> np.ndarray:
-    t = t.detach().cpu().contiguous()
-    if t.dtype == torch.bfloat16:
-        return t.view(torch.int16).numpy().view(np.uint16).copy()
-    return t.numpy().copy()
-
-
-def torch_dtype(dtype: str):
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
 
 
 def bits(a: np.ndarray) -> np.ndarray:

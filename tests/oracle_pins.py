@@ -162,6 +162,36 @@ def pin_two_keys_sigmoid(lib):
         assert abs(out[0, 0, 0, 1, 0] - expect1) < 1e-14, (out[0, 0, 0, 1, 0], expect1)
 
 
+def pin_zero_and_negative_scale(lib):
+    """Any finite scale: with scale 0 every visible key scores 0, so each row
+    is the plain mean of its visible V rows (closed form); a negative scale
+    is the positive one applied to -q (IEEE negation is exact, so bit for
+    bit); and the two-key logistic form holds with a negative scale."""
+    L, B, H, T, D, N, P = 1, 2, 2, 16, 8, 3, 6
+    rng = _rng(21)
+    kc, vc = _empty_cache(L, B, H, T, D)
+    hist = np.full(B, P, np.int32)
+    _fill_history(kc, vc, hist, rng)
+    q, k, v = (rng.standard_normal((L, B, H, N, D), dtype=np.float32) for _ in range(3))
+    out0 = _decode(lib, kc.copy(), vc.copy(), q, k, v, hist, 0.0)
+    kk, vv = kc.copy(), vc.copy()
+    oracle.append(kk, vv, k, v, hist, lib=lib)
+    for i in range(N):
+        mean = vv[:, :, :, : P + i + 1].astype(np.float64).mean(axis=3)
+        assert np.allclose(out0[:, :, :, i], mean, rtol=0, atol=1e-12)
+    neg = _decode(lib, kc.copy(), vc.copy(), q, k, v, hist, -0.35)
+    pos = _decode(lib, kc.copy(), vc.copy(), -q, k, v, hist, 0.35)
+    assert np.array_equal(neg, pos)
+    assert not np.allclose(neg, _decode(lib, kc.copy(), vc.copy(), q, k, v, hist, 0.35))
+    kc1, vc1 = _empty_cache(1, 1, 1, 3, 1)
+    q1 = np.array([0.8, 0.8], np.float32).reshape(1, 1, 1, 2, 1)
+    k1 = np.array([-0.5, 1.25], np.float32).reshape(1, 1, 1, 2, 1)
+    v1 = np.array([3.0, -1.0], np.float32).reshape(1, 1, 1, 2, 1)
+    out1 = _decode(lib, kc1, vc1, q1, k1, v1, np.zeros(1, np.int32), -0.5)
+    z = -0.5 * float(np.float32(0.8)) * (1.25 - -0.5)
+    assert abs(out1[0, 0, 0, 1, 0] - (3.0 + (-1.0 - 3.0) / (1.0 + math.exp(-z)))) < 1e-14
+
+
 # ------------------------------------------------------------ library routine
 
 def sdpa_reference(q, kc, vc, hist, scale, N):
@@ -651,6 +681,7 @@ ALL_PINS = [
     pin_uniform_keys_give_mean,
     pin_one_hot_selects_value,
     pin_two_keys_sigmoid,
+    pin_zero_and_negative_scale,
     pin_matches_torch_sdpa,
     pin_cached_equals_recompute,
     pin_chunk_invariance,

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 8
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 9
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -147,6 +147,8 @@ def test_decode_error_paths(lib):
     assert call(N=-2) == E_SHAPE
     assert call(scale=float("nan")) == E_SHAPE
     assert call(scale=float("inf")) == E_SHAPE
+    for sc in (0.0, -0.0, -0.125, -3.5):
+        assert call(N=0, scale=sc) == OK
     assert call(hist=hist(2, 14)) == E_CAPACITY
     assert call(hist=None) == E_NULL
     assert call(q=None) == E_NULL
@@ -241,8 +243,13 @@ def test_prefill_error_paths(lib):
     assert call(k=None) == E_NULL
     assert call(o=None) == E_NULL
     assert call(scale=float("nan")) == E_SHAPE
+    assert call(scale=float("-inf")) == E_SHAPE
     assert call(v=h.ptr(offset=2)) == E_SHAPE
     assert call(c=ctypes.byref(desc(h, D=32))) == E_UNSUPPORTED
+    # any finite scale is accepted, zero and negative ones included (the
+    # empty prompt returns before anything is enqueued)
+    for sc in (0.0, -0.0, -0.125, -3.5, 1e-30):
+        assert call(S=0, scale=sc) == OK
 
 
 def test_workspace_size_is_length_independent(lib):

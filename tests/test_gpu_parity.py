@@ -89,6 +89,22 @@ def test_prefill_gqa_and_d128(dtype, D):
                               D=D, Tmax=200, prefill_len=150, step_lens=(1, 3)))
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("scale", [0.0, -0.125, -0.3])
+@pytest.mark.parametrize("G", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_and_negative_scale(dtype, G, scale, fused):
+    """Any finite scale: a 200-token prompt (two query tiles, a diagonal
+    crossing each) and decode steps of 1 and 3 rows on top, with a zero or a
+    negative score scale, through every kernel family (prefill, single-row
+    and multi-row decode)."""
+    w = synth.make_workload(f"scale_{scale}_G{G}", seed=int(50 + 100 * abs(scale)) + G,
+                            dtype=dtype, L=2, B=2, Hq=2 * G, Hkv=2, D=64, Tmax=256,
+                            prefill_len=200, step_lens=(1, 3))
+    w.scale_value = scale
+    check(w, fused=fused)
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 9, 17])
 @pytest.mark.parametrize("G", [1, 4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -290,21 +306,36 @@ def test_split_then_combine_equals_one_call(case):
     assert np.max(np.abs(synth.to_float(outs["one_call"][0]) - ref_out)) <= TOL[w.dtype]
 
 
-def test_repeated_calls_reuse_workspace_bitwise():
-    """Repeated calls on one workspace, including after a call of another
-    geometry scribbled over it, give bit-identical outputs."""
+@pytest.mark.parametrize("n_layers", [12, 1])
+def test_repeated_calls_reuse_workspace_bitwise(n_layers):
+    """Repeated calls on one workspace give bit-identical outputs, whatever
+    the scratch part holds (NaN bit patterns), and leave its arrival
+    counters (the first 8 bytes per query row, rounded up to 256) zero after
+    every call, the in-launch merge and the two-launch form alike."""
     from transformer_kv_cache_amd import kvcache as K
     w = synth.decode_12layer(1000, seed=4)
     q, k, v = w.steps[0]
     cache = K.KVCache(12, 1, 12, 1024, 64, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
     K.append(cache, to_dev(k), to_dev(v), w.hist)
-    ws = K.new_decode_workspace(cache, 12, 12, 1)
-    qd = to_dev(q)
-    outs = [to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)) for _ in range(3)]
-    ws.fill_(0xFF)  # NaN bit patterns everywhere in the scratch
-    outs += [to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)) for _ in range(2)]
+    ws = K.new_decode_workspace(cache, n_layers, 12, 1)
+    ctr = (8 * n_layers * 12 + 255) // 256 * 256
+    qd = to_dev(np.ascontiguousarray(q[:n_layers]))
+    outs = []
+    for scribble in (False, True):
+        if scribble:
+            ws[ctr:].fill_(0xFF)  # NaN bit patterns everywhere in the scratch
+        for _ in range(3):
+            outs.append(to_host(K.attn_decode(cache, qd, w.hist, workspace=ws)))
+            torch.cuda.synchronize()
+            assert not ws[:ctr].any(), "arrival counters not back at zero"
+        o = K.decode_split(cache, qd, w.hist, workspace=ws)
+        K.decode_combine(cache, qd, w.hist, out=o, workspace=ws)
+        outs.append(to_host(o))
+        torch.cuda.synchronize()
+        assert not ws[:ctr].any()
     for o in outs[1:]:
         assert np.array_equal(bits(o), bits(outs[0]))
+    assert np.max(np.abs(outs[0] - run_oracle(w)[0][0][:n_layers])) <= TOL["f32"]
 
 
 def test_capacity_error_leaves_cache_untouched():
@@ -374,7 +405,9 @@ def test_graph_replays_match_eager(case):
         assert np.array_equal(bits(to_host(out)), bits(ref)), f"replay {rep}"
         assert np.array_equal(bits(to_host(cache.k)), bits(ref_k))
         assert np.array_equal(bits(to_host(cache.v)), bits(ref_v))
-        # unrelated eager work on the same workspace and another cache
+        # unrelated eager work on the same workspace and another cache, and
+        # garbage in its scratch part (its arrival counters, the first 8
+        # bytes per query row rounded up to 256, must stay zero)
         K.decode_step(other, q, k, v, w.hist, scale=w.scale, workspace=ws)
-        ws.fill_(0x7F)
+        ws[(8 * w.L * w.B * w.Hq * N + 255) // 256 * 256:].fill_(0x7F)
         torch.cuda.synchronize()

@@ -48,6 +48,10 @@ kvc_status check_cache(const kvc_cache *c, int32_t layer0, int32_t n_layers, con
   if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > c->L)
     return fail(KVC_E_SHAPE, "%s: layers [%d, %d+%d) outside [0, %d)", fn, layer0, layer0, n_layers,
                 c->L);
+  // the decode kernels address a head's rows with 32-bit byte offsets
+  if ((int64_t)c->Tmax * c->D * elem_bytes(c->dtype) >= (int64_t)1 << 32)
+    return fail(KVC_E_UNSUPPORTED, "%s: Tmax = %d rows of %d bytes exceed 4 GiB per head", fn, c->Tmax,
+                c->D * elem_bytes(c->dtype));
   return KVC_OK;
 }
 
@@ -79,16 +83,13 @@ kvc_status hip_status(hipError_t e, const char *fn) {
 // matrix-core kernel in tiles of 16 rows.
 enum class DecodeKernel { kVector, kRows, kMfma };
 
-// Build-time switch: 0 sends every multi-row call to the matrix-core kernel.
-#ifndef KVC_DECODE_ROWS
-#define KVC_DECODE_ROWS 1
-#endif
-
 struct DecodeGeometry {
   DecodeKernel kernel;
   bool mfma;  // several query rows per KV head (rows or matrix-core kernel)
-  int rows, row_tile, row_tiles, split_keys, max_splits;
-  size_t ws_o_bytes, ws_ml_bytes, total;
+  int rows, row_tile, row_tiles;
+  int split_keys;  // keys per split (single-row kernel: its smallest split)
+  int max_splits;  // workspace stride in splits (for the smallest split)
+  size_t ws_o_bytes, ws_ml_bytes, ctr_bytes, total;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -99,13 +100,14 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
   g.rows = G * N;
   g.mfma = g.rows > 1;
   g.kernel = !g.mfma ? DecodeKernel::kVector
-             : (KVC_DECODE_ROWS && kvc::decode_rows_fits(c->dtype, c->D, g.rows)) ? DecodeKernel::kRows
-                                                                                  : DecodeKernel::kMfma;
-  g.row_tile = g.kernel == DecodeKernel::kVector ? kvc::decode_row_tile(g.rows)
+             : kvc::decode_rows_fits(c->dtype, c->D, g.rows) ? DecodeKernel::kRows
+                                                              : DecodeKernel::kMfma;
+  g.row_tile = g.kernel == DecodeKernel::kVector ? 1
                : g.kernel == DecodeKernel::kRows ? g.rows
                                                  : kvc::kMfmaRowTile;
   g.row_tiles = (g.rows + g.row_tile - 1) / g.row_tile;
-  g.split_keys = g.kernel == DecodeKernel::kVector ? kvc::decode_split_keys(c->dtype, c->D)
+  // (the single-row kernel's splits hold at least 4 keys per lane group)
+  g.split_keys = g.kernel == DecodeKernel::kVector ? kvc::decode_rows_per_load(c->dtype, c->D) * 4
                  : g.kernel == DecodeKernel::kRows ? kvc::decode_rows_split_keys(c->dtype, c->D)
                                                    : kvc::decode_mfma_split_keys(c->dtype, c->D);
   g.max_splits = (c->Tmax + g.split_keys - 1) / g.split_keys;
@@ -113,8 +115,50 @@ DecodeGeometry decode_geometry(const kvc_cache *c, int32_t n_layers, int32_t Hq,
   const size_t qrows = (size_t)n_layers * c->B * Hq * N;
   g.ws_o_bytes = round_up(qrows * g.max_splits * c->D * sizeof(float), 256);
   g.ws_ml_bytes = round_up(qrows * g.max_splits * 2 * sizeof(float), 256);
-  g.total = g.ws_o_bytes + g.ws_ml_bytes;
+  // arrival counters of the single-row kernel's in-launch merge
+  g.ctr_bytes = g.kernel == DecodeKernel::kVector ? round_up(qrows * sizeof(uint64_t), 256) : 0;
+  g.total = g.ws_o_bytes + g.ws_ml_bytes + g.ctr_bytes;
   return g;
+}
+
+// Single-row kernel: keys per lane group (kpl; a split holds rows_per_load
+// * kpl keys) and whether the merge runs inside the launch.  Measured
+// (12-layer fp32 step at T=1024, and the same as 12 one-layer calls):
+// in-launch merge with kpl 8 -- 16.2 us and 74 us per step -- beats kpl 4
+// (17.1 / 78) and smaller splits by far (kpl 1: 43 / 185 us: every split
+// of a row counts itself on one counter, so many splits serialise there),
+// and the two-launch form at any kpl (best: kpl 4, 16.5 / 78 us).  The
+// in-launch merge holds every split workgroup until the L2 has taken its
+// state, which is hidden only while all of them are resident at once (about
+// six per CU at kpl 8); larger grids merge in a second launch, with kpl 4.
+constexpr long long kMaxMergeWorkgroups = 1280;
+
+struct VectorPlan {
+  int kpl;
+  bool merge_in_launch;
+};
+
+VectorPlan plan_vector(int units, int max_keys, int rows_per_load, bool merge_supported) {
+  const long long split8 = (long long)rows_per_load * 8;
+  const long long splits8 = (max_keys + split8 - 1) / split8;
+  const long long grid8 = 8LL * ((units + 7) / 8) * (splits8 > 0 ? splits8 : 1);
+  if (merge_supported && grid8 <= kMaxMergeWorkgroups) return {8, true};
+  return {4, false};
+}
+
+// XCDs of the current device (the attribute is read once per device): the
+// in-launch merge needs every split of a row on one XCD, which the
+// round-robin dispatch gives when the count divides 8.
+bool merge_in_launch_supported() {
+  static int cache[64];  // 0 unknown, 1 supported, 2 not
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  if (dev < 64 && cache[dev]) return cache[dev] == 1;
+  int n = 0;
+  const bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess &&
+                  n >= 1 && n <= 8 && (8 % n) == 0;
+  if (dev < 64) cache[dev] = ok ? 1 : 2;
+  return ok;
 }
 
 // Shared by kvc_append and kvc_paged_append (pg.block_table set: `cache` is
@@ -195,7 +239,11 @@ kvc::PrefillArgs prefill_args(const kvc_cache *cache, int32_t layer0, int32_t n_
   a.layer0 = layer0;
   a.n_layers = n_layers;
   a.group = Hq / cache->Hkv;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // The prefill kernel needs a positive exponent factor (see PrefillArgs):
+  // a negative scale flips the sign of q, a zero one zeroes q.
+  a.scale_log2 = (scale == 0.f ? 1.f : std::fabs(scale)) * 1.4426950408889634f;
+  a.q_keep = scale == 0.f ? 0u : 0xFFFFFFFFu;
+  a.q_flip = scale < 0.f ? (cache->dtype == KVC_BF16 ? 0x80008000u : 0x80000000u) : 0u;
   return a;
 }
 
@@ -346,6 +394,12 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   if ((long long)n_layers * cache->Hkv * g.row_tiles > 65535)
     return fail(KVC_E_UNSUPPORTED, "%s: %d layers x %d KV heads x %d row tiles exceed one launch", fn,
                 n_layers, cache->Hkv, g.row_tiles);
+  // the single-row kernel's one-dimensional grid
+  if (g.kernel == DecodeKernel::kVector &&
+      8LL * ((n_layers * (long long)(cache->B < kvc::kMaxBatchPerLaunch ? cache->B : kvc::kMaxBatchPerLaunch) *
+              cache->Hkv + 7) / 8) * g.max_splits > 2147483647LL)
+    return fail(KVC_E_UNSUPPORTED, "%s: %d layers x %d KV heads x %d key splits exceed one launch", fn,
+                n_layers, cache->Hkv, g.max_splits);
   // the multi-row vector kernel puts the splits on the grid's y axis
   if (g.kernel == DecodeKernel::kRows && g.max_splits > 65535)
     return fail(KVC_E_UNSUPPORTED, "%s: Tmax = %d gives %d key splits, more than one launch holds", fn,
@@ -363,8 +417,9 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   a.v_new = (const char *)v_new;
   a.q = (const char *)q;
   a.o = (char *)o;
-  a.ws_o = (float *)workspace;
-  a.ws_ml = (float *)((char *)workspace + g.ws_o_bytes);
+  // [arrival counters][partial outputs][partial (max, sum)]
+  a.ws_o = (float *)((char *)workspace + g.ctr_bytes);
+  a.ws_ml = (float *)((char *)workspace + g.ctr_bytes + g.ws_o_bytes);
   a.B = cache->B;
   a.Hkv = cache->Hkv;
   a.Hq = Hq;
@@ -377,7 +432,7 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   a.row_tiles = g.row_tiles;
   a.max_splits = g.max_splits;
   a.ws_rows = (int64_t)n_layers * cache->B * Hq * N;
-  a.split_keys = g.split_keys;
+  a.split_keys = g.split_keys;  // the single-row kernel picks its own per launch
   a.scale_log2 = scale * 1.4426950408889634f;
   a.hkv_div = kvc::magic_for(cache->Hkv);
   a.split_div = kvc::magic_for(g.split_keys);
@@ -388,6 +443,9 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   a.pg = pg;
   a.hist_dev = hist_dev;
   a.hist_max = hist_max;
+  a.counters = g.ctr_bytes ? (uint64_t *)workspace : nullptr;
+  a.nl_div = kvc::magic_for(n_layers);
+  const bool vec = g.kernel == DecodeKernel::kVector;
   for (int b0 = 0; b0 < cache->B; b0 += kvc::kMaxBatchPerLaunch) {
     a.b0 = b0;
     a.nb = cache->B - b0 < kvc::kMaxBatchPerLaunch ? cache->B - b0 : kvc::kMaxBatchPerLaunch;
@@ -402,16 +460,40 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
         if (keys > max_keys) max_keys = keys;
       }
     }
-    const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
     hipError_t e = hipSuccess;
-    if ((phases & kSplit) && splits > 0)
-      e = g.kernel == DecodeKernel::kRows
-              ? kvc::launch_decode_rows(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream)
-          : g.kernel == DecodeKernel::kMfma
-              ? kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream)
-              : kvc::launch_decode(a, cache->dtype, cache->D, splits, (hipStream_t)stream);
-    if (e == hipSuccess && (phases & kCombine) && (a.tail || splits > 1))
-      e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
+    if (vec) {
+      // Single-row kernel: split size for this call, then one launch with
+      // the merge inside it, or the split pass and the combine pass.
+      a.units = n_layers * a.nb * cache->Hkv;
+      const int rpl = kvc::decode_rows_per_load(cache->dtype, cache->D);
+      // the same plan for the one-call and the two-phase entry points, so
+      // that their outputs are bit-identical
+      const VectorPlan plan = plan_vector(a.units, max_keys, rpl, merge_in_launch_supported());
+      const int kpl = plan.kpl;
+      a.split_keys = rpl * kpl;
+      a.split_div = kvc::magic_for(a.split_keys);
+      const int splits = (max_keys + a.split_keys - 1) / a.split_keys;
+      // a launch always covers every row: with no cached key (P = 0) the
+      // merge alone gives the output (v_P)
+      a.grid_splits = splits > 0 ? splits : 1;
+      a.grid_splits_div = kvc::magic_for(a.grid_splits);
+      if (phases == kBoth && plan.merge_in_launch) {
+        e = kvc::launch_decode(a, cache->dtype, cache->D, kpl, true, (hipStream_t)stream);
+      } else {
+        if ((phases & kSplit) && splits > 0)
+          e = kvc::launch_decode(a, cache->dtype, cache->D, kpl, false, (hipStream_t)stream);
+        if (e == hipSuccess && (phases & kCombine))
+          e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
+      }
+    } else {
+      const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
+      if ((phases & kSplit) && splits > 0)
+        e = g.kernel == DecodeKernel::kRows
+                ? kvc::launch_decode_rows(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream)
+                : kvc::launch_decode_mfma(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream);
+      if (e == hipSuccess && (phases & kCombine) && splits > 1)
+        e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();

@@ -1,19 +1,17 @@
-// kvc_decode.hip -- split-K ("flash-decode") attention of N new query rows
-// against the KV cache.
+// kvc_decode.hip -- split-K ("flash-decode") attention of one new query row
+// per KV head against the KV cache, with the merge of the splits done inside
+// the same launch.
 //
 // What it computes ([KV-4] jennyma11.github.io/infra/ch07-01.html, "Decode
 // 阶段", listing 1-2; [KV-2] openai-hub.com/news/2435, "一个很容易漏掉的错误"):
-// for each (layer, sequence b, query head, new row i) the softmax of
-// scale * q . K_j over keys j = 0 .. P_b + i, applied to V.  Decode reads every
-// cached K/V byte once and does ~1 flop per byte, so it is bound by HBM
-// bandwidth ([KV-2] "千倍计算量为何只换来6倍速度").
+// for each (layer, sequence b, KV head) the softmax of scale * q . K_j over
+// keys j = 0 .. P_b, applied to V.  Decode reads every cached K/V byte once
+// and does ~1 flop per byte, so it is bound by HBM bandwidth ([KV-2]
+// "千倍计算量为何只换来6倍速度").  Several query rows per KV head (GQA groups,
+// chunked decode) go to kvc_decode_rows.hip / kvc_decode_mfma.hip.
 //
-// Work split.  This vector kernel serves the case of one query row per KV
-// head (plain multi-head single-token decode); several rows per KV head (GQA
-// groups, chunked decode) go to the matrix-core kernel in kvc_decode_mfma.hip.
-// A workgroup (256 lanes, 4 waves) owns one (layer, sequence, KV head, split
-// of SPLIT consecutive keys) and the head's single query row.  Inside the
-// workgroup:
+// Work split.  A workgroup (256 lanes, 4 waves) owns one (layer, sequence,
+// KV head, split of SPLIT consecutive keys of [0, P)).  Inside it:
 //   * a key row of D elements is LPR = D*elem/16 lanes wide; each lane loads
 //     one 16-byte vector of it (global_load_dwordx4).  Consecutive lane groups
 //     take consecutive rows, so one wave-wide load covers 64*16 contiguous
@@ -26,19 +24,33 @@
 //     over its keys; the states are merged across the wave with cross-lane
 //     exchanges and across the 4 waves through LDS, rescaling by exp2 of
 //     the max difference (log2(e) is folded into the scale).
-// Combine.  Each workgroup writes its (max, sum, P.V) state to the
-// workspace and a second, small kernel merges the states of every query row
-// (rescaling by exp2 of the max difference) and writes the output.  The
-// split kernel covers keys [0, P); the combine kernel adds the last key P as
-// one more state, read from the new K/V row in the fused step (kvc_decode_step,
-// which also writes that row to its cache slot there) and from the cache
-// otherwise, so the fused and the two-call forms do the same arithmetic.
-// Every split workgroup thus runs one uniform code path: none waits on the
-// new row or on a store before its arithmetic, which would lengthen the
-// slowest workgroup.  The merge is a separate launch rather than a
-// last-workgroup ticket: the ticket needs a device-scope release fence in
-// every workgroup, which on gfx950 is an L2 write-back (buffer_wbl2), and
-// that measured about ten times slower than the extra launch.
+// The last key, P, is not in any split: it is merged as one more state
+// (scale log2(e) q.k_P, 1, v_P), read from the new K/V row in the fused step
+// (kvc_decode_step, which also writes that row to its cache slot) and from
+// the cache otherwise, so the fused and the two-call forms do the same
+// arithmetic.
+//
+// Merge inside the launch.  Each split workgroup writes its (max, sum, P.V)
+// state to the workspace and counts itself on an arrival counter of its
+// query row; the workgroup that arrives last merges every state of the row
+// with key P's and writes the output (and resets the counter, so the
+// workspace's counters are zero again when the kernel ends).  A device-scope
+// release fence per workgroup would make this an L2 write-back on gfx950;
+// instead all workgroups of a row run on one XCD and exchange the states
+// through that XCD's L2: workgroups are dispatched to the XCDs round-robin
+// by linear id, so the grid is one-dimensional with the row's XCD fixed by
+// its position (id % 8).  A writer waits until the L2 has acknowledged its
+// state stores before it counts itself, and the last one reads the states
+// with L1-bypassing loads, which the L2 serves.  Each workgroup also reads
+// its XCD id from the hardware and adds it to the counter; the merging
+// workgroup checks that every writer of the row ran on its own XCD and
+// writes NaN for the row otherwise, so a placement other than the documented
+// one can only fail loudly.  The wait
+// for the acknowledgement costs a round trip per workgroup, hidden while
+// every workgroup is resident at once and exposed when they queue for CU
+// slots, so the host takes this path only when the grid fits the chip in
+// one round; otherwise (and when the XCD count does not divide 8) the merge
+// is a second kernel, combine_kernel, which runs the same merge code.
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -65,207 +77,7 @@ constexpr int kLog2Nrg = NRG == 8 ? 3 : NRG == 16 ? 4 : NRG == 32 ? 5 : 6;
 
 // K/V rows are read exactly once per call: non-temporal loads keep them from
 // displacing reusable lines in the caches.
-#ifndef KVC_DECODE_NONTEMPORAL
-#define KVC_DECODE_NONTEMPORAL 1
-#endif
-__device__ __forceinline__ u32x4 stream_load(const u32x4 *p) {
-#if KVC_DECODE_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-
-template <int DT, int D, int KPL, bool PAGED, bool DEVLEN>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
-  constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
-  constexpr int NRG = 256 / LPR;                 // key rows per wave-group load
-  constexpr int SPLIT = NRG * KPL;               // keys per workgroup
-  static_assert(LPR * EV == D, "row layout");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rg = tid / LPR;
-  const int c = tid % LPR;
-
-  // Grid: x = split, y = (layer, KV head), z = sequence in the batch slice.
-  // The sequence comes straight from blockIdx.z so its length can be fetched
-  // while the other indices are still being computed.  One query row per KV
-  // head (G = N = 1), so the query row index equals the KV head index.
-  const int split = blockIdx.x;
-  const int bb = blockIdx.z;
-  const int lh = blockIdx.y;
-  // Every kernel argument the prologue needs, fetched in one scalar round:
-  // the empty asm takes them all as operands, so none of their loads can be
-  // deferred behind the early exit or the index arithmetic.
-  const int P = seq_hist<DEVLEN>(a, bb);
-  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0, tail = a.tail;
-  const uint32_t hkv_div = a.hkv_div;
-  const char *k_cache = a.k_cache, *v_cache = a.v_cache, *qp = a.q;
-  asm volatile("" ::"s"(P), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(b0), "s"(tail),
-               "s"(hkv_div), "s"(k_cache), "s"(v_cache), "s"(qp));
-  // Keys of this pass: 0 .. P-1 when the combine pass adds key P (always,
-  // as launched), else 0 .. P.
-  const int nk = P + 1 - tail;
-  const int nsplit = (nk + SPLIT - 1) / SPLIT;
-  if (split >= nsplit) return;
-  const int l = div_magic(lh, Hkv, hkv_div);
-  const int hkv = lh - l * Hkv;
-  const int b = b0 + bb;
-  // (layer, sequence, KV head) indices fit in 32 bits; only the row offsets
-  // need 64.
-  const uint32_t head = (uint32_t)(((layer0 + l) * B + b) * Hkv + hkv);
-  const size_t crow0 = (size_t)head * (uint32_t)Tmax;
-  const uint32_t row = (uint32_t)((l * B + b) * Hkv + hkv);  // (l, b, hq, i = 0), Hq = Hkv
-
-  const int key0 = split * SPLIT;
-  const int last = nk - 1 - key0;  // offset of the last visible key in this split
-  // Uniform bases plus 32-bit per-lane byte offsets: global loads with an SGPR
-  // base take one VGPR per address.
-  const char *kc = k_cache + crow0 * (LPR * 16);
-  const char *vc = v_cache + crow0 * (LPR * 16);
-
-  // 1. Issue the query load and every K and V load of this split up front.
-  //    Keys past the last visible one are clamped to it (a valid, written
-  //    slot) so that no load sits behind a branch; their scores are masked.
-  //    A paged cache first looks up the blocks (for blocks of at least NRG
-  //    positions one scalar load per key load, else one load per key, all
-  //    issued together), then streams the rows from their blocks.
-  const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
-  u32x4 kw[KPL], vw[KPL];
-  if constexpr (PAGED) {
-    size_t prow[KPL];
-    if (a.pg.bs_log2 >= kLog2Nrg<NRG>) {
-      // blocks of at least NRG positions: one scalar id lookup per load
-      paged_rows_grouped<KPL, NRG>(a.pg, b, key0, key0 + last, rg, layer0 + l, hkv, Hkv, prow);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KPL; ++kk) {
-        const int kr = kk * NRG + rg;
-        prow[kk] = paged_row(a.pg, b, key0 + (kr < last ? kr : last), layer0 + l, hkv, Hkv);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < KPL; ++kk) {
-      kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(k_cache) + prow[kk] * LPR + c);
-      vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(v_cache) + prow[kk] * LPR + c);
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KPL; ++kk) {
-      const int kr = kk * NRG + rg;  // key offset within the split
-      const uint32_t off = (uint32_t)((key0 + (kr < last ? kr : last)) * LPR + c) * 16u;
-      kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(kc + off));
-      vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off));
-    }
-  }
-  // Keep the scheduler from interleaving arithmetic (and its waits) into the
-  // load burst: all loads of the split are in flight before the first wait.
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. Scores in the log2 domain; key key0 + kk*NRG + rg is visible iff its
-  //    offset is at most `last`, a compare of rg against a uniform bound.
-  float qf[EV];
-  unpack16<DT>(qw, qf);
-  float s[KPL];
-#pragma unroll
-  for (int kk = 0; kk < KPL; ++kk) {
-    float kf[EV];
-    unpack16<DT>(kw[kk], kf);
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) dot = fmaf(qf[e], kf[e], dot);
-    dot = row_allreduce<LPR>(dot);
-    s[kk] = (rg <= last - kk * NRG) ? dot * a.scale_log2 : kNegInf;
-  }
-
-  // 3. Per-row-group softmax state over its KPL keys.  Row group 0 always
-  //    holds key key0, which is visible, so in the merged state the max is
-  //    finite.
-  float m = s[0];
-#pragma unroll
-  for (int kk = 1; kk < KPL; ++kk) m = fmaxf(m, s[kk]);
-  float lsum = 0.f, acc[EV];
-#pragma unroll
-  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < KPL; ++kk) {
-    float vf[EV];
-    unpack16<DT>(vw[kk], vf);
-    const float p = (m == kNegInf) ? 0.f : fast_exp2(s[kk] - m);
-    lsum += p;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-  }
-
-  // 4. Merge the row groups of this wave (lanes with the same c).
-  {
-    float M = m;
-    if constexpr (LPR <= 8) M = xor_combine<8, true>(M);
-    if constexpr (LPR <= 16) M = xor_combine<16, true>(M);
-    M = xor_combine<32, true>(M);
-    const float f = rescale(m, M);
-    lsum *= f;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] *= f;
-    if constexpr (LPR <= 8) {
-      lsum = xor_combine<8>(lsum);
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<8>(acc[e]);
-    }
-    if constexpr (LPR <= 16) {
-      lsum = xor_combine<16>(lsum);
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<16>(acc[e]);
-    }
-    lsum = xor_combine<32>(lsum);
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] = xor_combine<32>(acc[e]);
-    m = M;
-  }
-
-  // 5. Merge the four waves through LDS; write this split's state (or the
-  //    output, for a single split with no key left to the combine pass).
-  __shared__ float sh_o[4][D];
-  __shared__ float sh_m[4];
-  __shared__ float sh_l[4];
-  if (lane < LPR) {
-#pragma unroll
-    for (int e = 0; e < EV; ++e) sh_o[wave][c * EV + e] = acc[e];
-    if (c == 0) {
-      sh_m[wave] = m;
-      sh_l[wave] = lsum;
-    }
-  }
-  __syncthreads();
-
-  if (tid < D) {
-    const int d = tid;
-    float M = sh_m[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh_m[w]);
-    float o = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = rescale(sh_m[w], M);
-      o = fmaf(f, sh_o[w][d], o);
-      L = fmaf(f, sh_l[w], L);
-    }
-    if (!tail && nsplit == 1) {
-      const float val = o / L;
-      store_elems<DT>(a.o, (size_t)row * D + d, &val, 1);
-    } else {
-      const size_t ws = ws_slot(a, row, split);
-      a.ws_o[ws * D + d] = o;
-      if (d == 0) {
-        a.ws_ml[ws * 2] = M;
-        a.ws_ml[ws * 2 + 1] = L;
-      }
-    }
-  }
-}
+__device__ __forceinline__ u32x4 stream_load(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 
 // One element of a row in the cache dtype: raw bits, and widened to fp32.
 template <int DT> struct Elem;
@@ -278,18 +90,364 @@ template <> struct Elem<KVC_BF16> {
   static __device__ __forceinline__ float widen(bits u) { return __uint_as_float((uint32_t)u << 16); }
 };
 
-// Merge of the split-K states of query rows: o = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s with M = max_s m_s.  One wave per row, lane j holding
-// elements j, j + 64, ... of it.  Grid: x = blocks of 4 rows over the Hq * N
-// rows of one (layer, sequence), y = layer, z = sequence in the batch slice,
-// so that a row's index needs no division.
-//   Without `tail` only rows whose sequence needed more than one split are
-// merged (the split kernel wrote the others).  With `tail` (one query row per
-// KV head) the split states cover keys [0, P) and this pass adds key P: its
-// state is (m, l, o) = (scale log2(e) q.k_P, 1, v_P), merged like any split.
-// In the fused step k_P, v_P come from k_new / v_new and this pass then
-// writes them to cache slot P (read by no kernel of the step, so the write
-// is race-free); otherwise they are read from slot P.
+// Loads of split states written by other workgroups of this launch: they
+// bypass the CU's L1 (which may hold a stale copy of a line shared with
+// another row's states) and are served by the L2 the writers stored to.
+__device__ __forceinline__ float state_load(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void state_load_ml(const float *p, float &m, float &l) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  m = __uint_as_float((uint32_t)u);
+  l = __uint_as_float((uint32_t)(u >> 32));
+}
+
+// Key P's score in the log2 domain, scale log2(e) q.k_P, from one wave whose
+// lane j holds elements j, j + 64, ... of q and k_P.
+template <int DT, int EPL>
+__device__ __forceinline__ float key_score(const typename Elem<DT>::bits (&qn)[EPL],
+                                           const typename Elem<DT>::bits (&kn)[EPL], float scale_log2) {
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) dot = fmaf(Elem<DT>::widen(qn[j]), Elem<DT>::widen(kn[j]), dot);
+  dot = row_allreduce<16>(dot);
+  dot = xor_combine<16>(dot);
+  dot = xor_combine<32>(dot);
+  return dot * scale_log2;
+}
+
+// Merge of a query row's split states into the running state (M, L, o) of
+// one wave (lane j holds output elements j, j + 64, ...):
+//   o = sum_s 2^(m_s - M') o_s + 2^(M - M') o,  L likewise,  M' = max(M, m_s)
+// over splits 0 .. nsplit-1, in chunks of CH whose loads are all issued
+// before any is used.  The fused kernel's last workgroup and combine_kernel
+// both run exactly this, so their outputs are bit-identical.
+template <int D>
+__device__ __forceinline__ void merge_states(const float *ws_o, const float *ws_ml, int64_t ws_rows,
+                                             int64_t row, int nsplit, int lane, float &M, float &L,
+                                             float (&o)[D / 64]) {
+  constexpr int EPL = D / 64;
+  constexpr int CH = 16;
+  for (int s0 = 0; s0 < nsplit; s0 += CH) {
+    float mv[CH], lv[CH], ov[CH][EPL];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
+      const size_t ws = (size_t)sp * (size_t)ws_rows + (size_t)row;
+      state_load_ml(ws_ml + ws * 2, mv[t], lv[t]);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ov[t][j] = state_load(ws_o + ws * D + lane + 64 * j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float Mc = M;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      if (s0 + t >= nsplit) mv[t] = kNegInf;
+      Mc = fmaxf(Mc, mv[t]);
+    }
+    const float fr = rescale(M, Mc);
+    L *= fr;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) o[j] *= fr;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const float f = rescale(mv[t], Mc);
+      L = fmaf(f, lv[t], L);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) o[j] = fmaf(f, ov[t][j], o[j]);
+    }
+    M = Mc;
+  }
+}
+
+// Cache row index (in rows of D elements) of position P of this (layer,
+// sequence, KV head): contiguous, or through the block table.
+template <bool PAGED>
+__device__ __forceinline__ size_t slot_row(const DecodeArgs &a, int b, int P, int layer, int hkv) {
+  if constexpr (PAGED) return paged_row(a.pg, b, P, layer, hkv, a.Hkv);
+  else return (((size_t)layer * a.B + b) * a.Hkv + hkv) * (size_t)a.Tmax + P;
+}
+
+// The split kernel.  Grid: one dimension of 8 * ceil(units / 8) * grid_splits
+// workgroups.  Workgroup w runs on XCD w % 8 (round-robin dispatch); with
+// j = w / 8 it takes split j % grid_splits of unit (j / grid_splits) * 8 +
+// w % 8, so all splits of a unit share an XCD.  A unit is one (sequence,
+// layer, KV head) = one query row (G = N = 1): u = (bb * n_layers + l) * Hkv
+// + hkv.  MERGE: the last-arriving split workgroup merges (see above);
+// otherwise every split only writes its state for combine_kernel.
+template <int DT, int D, int KPL, bool PAGED, bool DEVLEN, bool MERGE>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  constexpr int EV = Dtype<DT>::kPer16B;        // elements per 16-byte vector
+  constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per key row
+  constexpr int NRG = 256 / LPR;                 // key rows per wave-group load
+  constexpr int SPLIT = NRG * KPL;               // keys per workgroup
+  constexpr int EPL = D / 64;                    // output elements per lane of one wave
+  typedef typename Elem<DT>::bits bits;
+  static_assert(LPR * EV == D, "row layout");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = tid / LPR;
+  const int c = tid % LPR;
+
+  const int wg = blockIdx.x;
+  // Every kernel argument the prologue needs, fetched in one scalar round:
+  // the empty asm takes them all as operands, so none of their loads can be
+  // deferred behind the early exits or the index arithmetic.
+  const int units = a.units, grid_splits = a.grid_splits, n_layers = a.n_layers;
+  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, b0 = a.b0;
+  const uint32_t gs_div = a.grid_splits_div, hkv_div = a.hkv_div, nl_div = a.nl_div;
+  const char *k_cache = a.k_cache, *v_cache = a.v_cache, *qp = a.q;
+  asm volatile("" ::"s"(units), "s"(grid_splits), "s"(n_layers), "s"(Hkv), "s"(B), "s"(Tmax),
+               "s"(layer0), "s"(b0), "s"(gs_div), "s"(hkv_div), "s"(nl_div), "s"(k_cache),
+               "s"(v_cache), "s"(qp));
+  const int lj = wg >> 3;
+  const int lu = div_magic(lj, grid_splits, gs_div);
+  const int split = lj - lu * grid_splits;
+  const int u = lu * 8 + (wg & 7);
+  if (u >= units) return;
+  const int t = div_magic(u, Hkv, hkv_div);
+  const int hkv = u - t * Hkv;
+  const int bb = div_magic(t, n_layers, nl_div);
+  const int l = t - bb * n_layers;
+  const int P = seq_hist<DEVLEN>(a, bb);
+  // Split states cover keys [0, P); key P is merged by the last workgroup.
+  const int nsplit = (P + SPLIT - 1) / SPLIT;
+  if (split >= (nsplit > 0 ? nsplit : 1)) return;
+  if (!MERGE && nsplit == 0) return;
+  const int b = b0 + bb;
+  // (layer, sequence, KV head) indices fit in 32 bits; only the row offsets
+  // need 64.
+  const uint32_t head = (uint32_t)(((layer0 + l) * B + b) * Hkv + hkv);
+  const size_t crow0 = (size_t)head * (uint32_t)Tmax;
+  const uint32_t row = (uint32_t)((l * B + b) * Hkv + hkv);  // (l, b, hq, i = 0), Hq = Hkv
+
+  // Key P's rows for the merge (wave 0; lane j holds elements j + 64 e), in
+  // the same burst as the split's loads: q, and k_P / v_P from the new rows
+  // (fused step) or from cache slot P.
+  bits qn[EPL], kn[EPL], vn[EPL];
+  size_t slot = 0;
+  if (MERGE && wave == 0) {
+    slot = slot_row<PAGED>(a, b, P, layer0 + l, hkv) * D;
+    const bits *qb = reinterpret_cast<const bits *>(qp) + (size_t)row * D;
+    const bits *kb = a.k_new ? reinterpret_cast<const bits *>(a.k_new) + (size_t)row * D
+                             : reinterpret_cast<const bits *>(k_cache) + slot;
+    const bits *vb = a.v_new ? reinterpret_cast<const bits *>(a.v_new) + (size_t)row * D
+                             : reinterpret_cast<const bits *>(v_cache) + slot;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      qn[j] = qb[lane + 64 * j];
+      kn[j] = kb[lane + 64 * j];
+      vn[j] = vb[lane + 64 * j];
+    }
+  }
+
+  float Mw = kNegInf, Lw = 0.f, ow[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) ow[j] = 0.f;
+  if (nsplit > 0) {
+    const int key0 = split * SPLIT;
+    const int last = P - 1 - key0;  // offset of the last key of this split
+    // Uniform bases plus 32-bit per-lane byte offsets (the host bounds a
+    // head's rows below 4 GiB): global loads with an SGPR base take one VGPR
+    // per address.
+    const char *kc = k_cache + crow0 * (LPR * 16);
+    const char *vc = v_cache + crow0 * (LPR * 16);
+
+    // 1. Issue the query load and every K and V load of this split up front.
+    //    Keys past the last one are clamped to it (a valid, written slot) so
+    //    that no load sits behind a branch; their scores are masked.  A paged
+    //    cache first looks up the blocks (for blocks of at least NRG
+    //    positions one scalar load per key load, else one load per key, all
+    //    issued together), then streams the rows from their blocks.
+    const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
+    u32x4 kw[KPL], vw[KPL];
+    if constexpr (PAGED) {
+      size_t prow[KPL];
+      if (a.pg.bs_log2 >= kLog2Nrg<NRG>) {
+        // blocks of at least NRG positions: one scalar id lookup per load
+        paged_rows_grouped<KPL, NRG>(a.pg, b, key0, key0 + last, rg, layer0 + l, hkv, Hkv, prow);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KPL; ++kk) {
+          const int kr = kk * NRG + rg;
+          prow[kk] = paged_row(a.pg, b, key0 + (kr < last ? kr : last), layer0 + l, hkv, Hkv);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(k_cache) + prow[kk] * LPR + c);
+        vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(v_cache) + prow[kk] * LPR + c);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int kr = kk * NRG + rg;  // key offset within the split
+        const uint32_t off = (uint32_t)((key0 + (kr < last ? kr : last)) * LPR + c) * 16u;
+        kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(kc + off));
+        vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off));
+      }
+    }
+    // Keep the scheduler from interleaving arithmetic (and its waits) into
+    // the load burst: all loads of the split are in flight before the first
+    // wait.
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. Scores in the log2 domain; key key0 + kk*NRG + rg is visible iff its
+    //    offset is at most `last`, a compare of rg against a uniform bound.
+    float qf[EV];
+    unpack16<DT>(qw, qf);
+    float s[KPL];
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      float kf[EV];
+      unpack16<DT>(kw[kk], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) dot = fmaf(qf[e], kf[e], dot);
+      dot = row_allreduce<LPR>(dot);
+      s[kk] = (rg <= last - kk * NRG) ? dot * a.scale_log2 : kNegInf;
+    }
+
+    // 3. Per-row-group softmax state over its KPL keys.  Row group 0 always
+    //    holds key key0, which is visible, so in the merged state the max is
+    //    finite.
+    float m = s[0];
+#pragma unroll
+    for (int kk = 1; kk < KPL; ++kk) m = fmaxf(m, s[kk]);
+    float lsum = 0.f, acc[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      float vf[EV];
+      unpack16<DT>(vw[kk], vf);
+      const float p = (m == kNegInf) ? 0.f : fast_exp2(s[kk] - m);
+      lsum += p;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+
+    // 4. Merge the row groups of this wave (lanes with the same c).
+    {
+      float M = m;
+      if constexpr (LPR <= 8) M = xor_combine<8, true>(M);
+      if constexpr (LPR <= 16) M = xor_combine<16, true>(M);
+      M = xor_combine<32, true>(M);
+      const float f = rescale(m, M);
+      lsum *= f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] *= f;
+      if constexpr (LPR <= 8) {
+        lsum = xor_combine<8>(lsum);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[e] = xor_combine<8>(acc[e]);
+      }
+      if constexpr (LPR <= 16) {
+        lsum = xor_combine<16>(lsum);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[e] = xor_combine<16>(acc[e]);
+      }
+      lsum = xor_combine<32>(lsum);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<32>(acc[e]);
+      m = M;
+    }
+
+    // 5. Merge the four waves through LDS into wave 0 (lane j: elements
+    //    j + 64 e) and write this split's state.
+    __shared__ float sh_o[4][D];
+    __shared__ float sh_m[4];
+    __shared__ float sh_l[4];
+    if (lane < LPR) {
+#pragma unroll
+      for (int e = 0; e < EV; ++e) sh_o[wave][c * EV + e] = acc[e];
+      if (c == 0) {
+        sh_m[wave] = m;
+        sh_l[wave] = lsum;
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    Mw = sh_m[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) Mw = fmaxf(Mw, sh_m[w]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = rescale(sh_m[w], Mw);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ow[j] = fmaf(f, sh_o[w][lane + 64 * j], ow[j]);
+      Lw = fmaf(f, sh_l[w], Lw);
+    }
+    const size_t ws = (size_t)split * (size_t)a.ws_rows + row;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) a.ws_o[ws * D + lane + 64 * j] = ow[j];
+    if (lane == 0)
+      *reinterpret_cast<uint64_t *>(a.ws_ml + ws * 2) =
+          (uint64_t)__float_as_uint(Mw) | ((uint64_t)__float_as_uint(Lw) << 32);
+  }
+  if constexpr (MERGE) {
+    if (wave != 0) return;
+    bool misplaced = false;
+    if (nsplit > 1) {
+      // Count this split once the L2 holds its state; the last to arrive
+      // merges.  The 64-bit count also sums each writer's XCD id x and x^2:
+      // with n writers, sum x = n y and sum x^2 = n y^2 hold for the merging
+      // workgroup's id y only if every x equals y (their variance about y is
+      // zero), i.e. only if every state went through this L2.
+      uint32_t xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      xcc &= 0xFu;
+      const uint64_t mark = 1ull | ((uint64_t)xcc << 16) | ((uint64_t)(xcc * xcc) << 36);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint64_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(a.counters + row, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(prev >> 32)) << 32) |
+             __builtin_amdgcn_readfirstlane((uint32_t)prev);
+      const uint64_t n = prev & 0xFFFFu;
+      if (n != (uint64_t)(nsplit - 1)) return;
+      asm volatile("" ::: "memory");
+      misplaced = ((prev >> 16) & 0xFFFFFu) != n * xcc || (prev >> 36) != n * xcc * xcc;
+    }
+    // The merge: key P's state first, then every split's (this one's
+    // included, read back), then the normalisation.
+    float M = key_score<DT, EPL>(qn, kn, a.scale_log2);
+    float L = 1.f, o[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) o[j] = Elem<DT>::widen(vn[j]);
+    merge_states<D>(a.ws_o, a.ws_ml, a.ws_rows, row, nsplit, lane, M, L, o);
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const float val = misplaced ? __builtin_nanf("") : o[j] * inv;
+      store_elems<DT>(a.o, (size_t)row * D + lane + 64 * j, &val, 1);
+    }
+    if (a.k_new) {
+      // the append of the new row (no workgroup of this launch reads slot P)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        reinterpret_cast<bits *>(a.k_cache)[slot + lane + 64 * j] = kn[j];
+        reinterpret_cast<bits *>(a.v_cache)[slot + lane + 64 * j] = vn[j];
+      }
+    }
+    if (nsplit > 1 && lane == 0)
+      __hip_atomic_store(a.counters + row, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Merge of the split-K states of query rows as a second launch.  One wave
+// per row, lane j holding elements j, j + 64, ... of it.  Grid: x = blocks
+// of 4 rows over the Hq * N rows of one (layer, sequence), y = layer, z =
+// sequence in the batch slice, so that a row's index needs no division.
+//   Without `tail` (several rows per KV head) only rows whose sequence needed
+// more than one split are merged (the split kernel wrote the others).  With
+// `tail` (one query row per KV head) the split states cover keys [0, P) and
+// this pass adds key P first, as the fused kernel's merge does: from k_new /
+// v_new in the fused step, which it then writes to cache slot P (read by no
+// kernel of the step, so the write is race-free), else from the cache.
 template <int DT, int D, bool DEVLEN>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int EPL = D / 64;  // elements per lane
@@ -325,23 +483,6 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
                                          : (((size_t)(layer0 + l) * B + b) * Hkv + rloc) * Tmax + P) *
                       D;
   const bool fused = knp != nullptr;
-
-  // Splits in chunks of CH, every load of a chunk issued before any is used
-  // (indices clamped, extra splits masked), merged online across chunks.  The
-  // key-P rows and the first chunk are loaded together.
-  constexpr int CH = 16;
-  float mv[CH], lv[CH], ov[CH][EPL];
-  auto load_chunk = [&](int s0) {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
-      const size_t ws = ws_slot(a, row, sp);
-      mv[t] = ws_ml[ws * 2];
-      lv[t] = ws_ml[ws * 2 + 1];
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) ov[t][j] = ws_o[ws * D + lane + 64 * j];
-    }
-  };
   // Key P's rows (loaded unconditionally, from q itself when unused, so that
   // no load sits behind a branch the compiler could fill with their use).
   const bits *qb = reinterpret_cast<const bits *>(qp) + (size_t)row * D;
@@ -358,56 +499,24 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     kn[j] = kb[lane + 64 * j];
     vn[j] = vb[lane + 64 * j];
   }
-  if (nsplit > 0) load_chunk(0);
-  __builtin_amdgcn_sched_barrier(0);
   if (tail && fused) {
-    // the append of the new row, issued before the merge arithmetic
+    // the append of the new row
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       reinterpret_cast<bits *>(kcp)[slot + lane + 64 * j] = kn[j];
       reinterpret_cast<bits *>(vcp)[slot + lane + 64 * j] = vn[j];
     }
   }
-
   float M = kNegInf, L = 0.f, o[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) o[j] = 0.f;
   if (tail) {
-    float dot = 0.f;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) dot = fmaf(Elem<DT>::widen(qn[j]), Elem<DT>::widen(kn[j]), dot);
-    dot = row_allreduce<16>(dot);
-    dot = xor_combine<16>(dot);
-    dot = xor_combine<32>(dot);
-    M = dot * a.scale_log2;
+    M = key_score<DT, EPL>(qn, kn, a.scale_log2);
     L = 1.f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) o[j] = Elem<DT>::widen(vn[j]);
   }
-  for (int s0 = 0; s0 < nsplit; s0 += CH) {
-    if (s0 > 0) {
-      load_chunk(s0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    float Mc = M;
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      if (s0 + t >= nsplit) mv[t] = kNegInf;
-      Mc = fmaxf(Mc, mv[t]);
-    }
-    const float fr = rescale(M, Mc);
-    L *= fr;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) o[j] *= fr;
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const float f = rescale(mv[t], Mc);
-      L = fmaf(f, lv[t], L);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) o[j] = fmaf(f, ov[t][j], o[j]);
-    }
-    M = Mc;
-  }
+  merge_states<D>(ws_o, ws_ml, a.ws_rows, row, nsplit, lane, M, L, o);
   const float inv = 1.f / L;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
@@ -416,35 +525,33 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   }
 }
 
-// Keys each lane group loads per split: a split covers 256 / LPR * this many
-// keys (64 for fp32 D=64).  Build-time tuning constant; 4 measured best
-// across the fp32, bf16 and GQA decode workloads.
-#ifndef KVC_DECODE_KEYS_PER_LANE
-#define KVC_DECODE_KEYS_PER_LANE 4
-#endif
-constexpr int kKeysPerLane = KVC_DECODE_KEYS_PER_LANE;
-
-template <int DT, int D>
-hipError_t launch_one(const DecodeArgs &a, int splits, hipStream_t s) {
-  const dim3 grid((unsigned)splits, (unsigned)(a.n_layers * a.Hkv), (unsigned)a.nb);
+template <int DT, int D, int KPL, bool MERGE>
+hipError_t launch_kpl(const DecodeArgs &a, unsigned grid, hipStream_t s) {
   if (a.pg.block_table && a.hist_dev)
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, KPL, true, true, MERGE>), dim3(grid), dim3(256), 0, s, a);
   else if (a.pg.block_table)
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, KPL, true, false, MERGE>), dim3(grid), dim3(256), 0, s, a);
   else if (a.hist_dev)
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, KPL, false, true, MERGE>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<DT, D, kKeysPerLane, false, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, KPL, false, false, MERGE>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int DT, int D, bool MERGE>
+hipError_t launch_dt(const DecodeArgs &a, int kpl, unsigned grid, hipStream_t s) {
+  switch (kpl) {
+    case 4: return launch_kpl<DT, D, 4, MERGE>(a, grid, s);
+    case 8: return launch_kpl<DT, D, 8, MERGE>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-int decode_row_tile(int /*rows*/) { return 1; }
-
-int decode_split_keys(int dtype, int D) {
+int decode_rows_per_load(int dtype, int D) {
   const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;
-  return (256 / lpr) * kKeysPerLane;
+  return 256 / lpr;
 }
 
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) {
@@ -470,15 +577,20 @@ hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool merge, hipStream_t s) {
   // The vector kernel serves one query row per KV head (G = N = 1) only.
-  if (a.rows != 1 || a.N != 1 || a.group != 1) return hipErrorInvalidValue;
+  if (a.rows != 1 || a.N != 1 || a.group != 1 || a.grid_splits < 1) return hipErrorInvalidValue;
+  const unsigned grid = 8u * (unsigned)((a.units + 7) / 8) * (unsigned)a.grid_splits;
   if (dtype == KVC_F32) {
-    if (D == 64) return launch_one<KVC_F32, 64>(a, splits, s);
-    return launch_one<KVC_F32, 128>(a, splits, s);
+    if (D == 64) return merge ? launch_dt<KVC_F32, 64, true>(a, kpl, grid, s)
+                              : launch_dt<KVC_F32, 64, false>(a, kpl, grid, s);
+    return merge ? launch_dt<KVC_F32, 128, true>(a, kpl, grid, s)
+                 : launch_dt<KVC_F32, 128, false>(a, kpl, grid, s);
   }
-  if (D == 64) return launch_one<KVC_BF16, 64>(a, splits, s);
-  return launch_one<KVC_BF16, 128>(a, splits, s);
+  if (D == 64) return merge ? launch_dt<KVC_BF16, 64, true>(a, kpl, grid, s)
+                            : launch_dt<KVC_BF16, 64, false>(a, kpl, grid, s);
+  return merge ? launch_dt<KVC_BF16, 128, true>(a, kpl, grid, s)
+               : launch_dt<KVC_BF16, 128, false>(a, kpl, grid, s);
 }
 
 }  // namespace kvc

@@ -155,6 +155,13 @@ struct DecodeArgs {
   uint32_t split_div;  // div_magic multiplier for split_keys
   int32_t tail;        // 1 (vector kernel): the split states cover keys
                        // [0, P) and the combine adds key P
+  // Vector kernel: one-dimensional grid of 8 * ceil(units / 8) * grid_splits
+  // workgroups (units = n_layers * nb * Hkv query rows), and the per-row
+  // arrival counters of the in-launch merge (zero before and after a call).
+  uint64_t *counters;
+  int32_t units, grid_splits;
+  uint32_t grid_splits_div;  // div_magic multiplier for grid_splits
+  uint32_t nl_div;           // div_magic multiplier for n_layers
   PagedGeom pg;        // paged cache, else block_table == nullptr
   // Device lengths (kvc_decode_step_dl): hist_dev[b0 + bb] clamped into
   // [0, hist_max] replaces hist[bb]; null for host lengths.
@@ -213,7 +220,13 @@ struct PrefillArgs {
   int32_t layer0, n_layers, group;
   int32_t b0, nb;
   int32_t q_tiles;      // most query tiles of one sequence in the slice
+  // |scale| * log2(e) (log2(e) when scale is 0).  The kernel takes the max of
+  // the raw scores and folds this positive factor into the exponent; the
+  // sign of the scale is moved onto q instead: each 32-bit word of q is
+  // replaced by (word & q_keep) ^ q_flip -- the sign bits flipped for a
+  // negative scale, q zeroed for a zero one (exact in both cases).
   float scale_log2;
+  uint32_t q_keep, q_flip;
   int64_t q_sl, kv_sl;
   int32_t q_sh, q_si, kv_sh, kv_si;
   int32_t hist[kMaxBatchPerLaunch];     // P_b
@@ -246,7 +259,7 @@ struct LinearArgs {
 hipError_t launch_linear(const LinearArgs &a, hipStream_t s);
 hipError_t launch_lengths_add(int32_t *hist, int B, int n, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int splits, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool merge, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
 hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits,
@@ -258,8 +271,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, 
 // One query row per KV head runs on the vector kernel; a few rows with
 // 256-byte key rows (GQA groups, short chunks) on the multi-row vector
 // kernel; other multi-row calls on the matrix-core kernel in tiles of 16 rows.
-int decode_row_tile(int rows);
-int decode_split_keys(int dtype, int D);
+// Single-row kernel: a split covers decode_rows_per_load * kpl keys, kpl 4
+// or 8 chosen per call.
+int decode_rows_per_load(int dtype, int D);
 int decode_mfma_split_keys(int dtype, int D);
 // Multi-row vector kernel: 2 <= rows <= 8, fp32 with D = 64 (256-byte key
 // rows) or bf16 with D = 128 or 64 (256- or 128-byte rows); all rows in one

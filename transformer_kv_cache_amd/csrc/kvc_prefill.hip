@@ -174,10 +174,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   constexpr int QV = (DT == KVC_BF16) ? D / 16 : D / 8;
   u32x4 qv[QV];
   const char *qrow_p = qbase + (size_t)(qrow < S ? qrow : S - 1) * q_stride;
+  const uint32_t q_keep = a.q_keep, q_flip = a.q_flip;
 #pragma unroll
   for (int j = 0; j < QV; ++j) {
     const int d0 = (DT == KVC_BF16) ? 16 * j + 8 * h : 8 * j + 4 * h;
-    qv[j] = *reinterpret_cast<const u32x4 *>(qrow_p + d0 * EB);
+    // the sign of the score scale (a zero scale zeroes q)
+    qv[j] = (*reinterpret_cast<const u32x4 *>(qrow_p + d0 * EB) & q_keep) ^ q_flip;
   }
 
   f32x16 acc_o[DB];
@@ -355,9 +357,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
       }
     }
     // Online softmax for this lane's query, in log2 units: the raw scores are
-    // maximised first (the scale is positive, so scaling commutes with max)
-    // and the scale is folded into the exponent, p = 2^(s sc - m), one FMA per
-    // score.
+    // maximised first (sc is positive -- the scale's sign sits on q -- so
+    // scaling commutes with max and a masked -inf stays -inf) and the scale
+    // is folded into the exponent, p = 2^(s sc - m), one FMA per score.
     const float sc = a.scale_log2;
     float mt = kNegInf;
 #pragma unroll

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 8  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 9  # KVC_ABI_VERSION of the header these signatures follow
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -172,6 +172,9 @@ class KVCache:
     def nbytes(self) -> int:
         return cache_bytes(self.L, self.B, self.Hkv, self.Tmax, self.D, self.dtype)
 
+    def geometry(self) -> tuple:
+        return (self.L, self.B, self.Hkv, self.Tmax, self.D, self.dtype)
+
 
 def _hist(hist_len, B):
     h = np.ascontiguousarray(
@@ -217,12 +220,10 @@ def decode_workspace_bytes(cache: KVCache, n_layers: int, Hq: int, N: int) -> in
 
 
 def new_decode_workspace(cache: KVCache, n_layers: int, Hq: int, N: int) -> torch.Tensor:
-    """A 256-byte aligned workspace for kvc_attn_decode with this geometry
-    (scratch: no initialisation needed)."""
-    n = max(decode_workspace_bytes(cache, n_layers, Hq, N), 256)
-    ws = torch.empty(n + 256, dtype=torch.uint8, device=cache.device)
-    off = (-ws.data_ptr()) % 256
-    return ws[off:off + n]
+    """A 256-byte aligned workspace for kvc_attn_decode with this geometry,
+    zero-filled: its arrival counters must start at zero, and every call
+    leaves them at zero again."""
+    return _aligned_workspace(decode_workspace_bytes(cache, n_layers, Hq, N), cache.device)
 
 
 _ws_cache: dict = {}
@@ -230,20 +231,29 @@ _ws_cache: dict = {}
 
 def _aligned_workspace(nbytes, device):
     n = max(int(nbytes), 256)
-    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    ws = torch.zeros(n + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]
 
 
-def _default_workspace(cache, n_layers, Hq, N, stream, need=None):
-    """One growing scratch workspace per (device, stream): calls on one
-    stream run one after another, so they can share it."""
+def _default_workspace(cache, n_layers, Hq, N, stream, need=None, B=None):
+    """One zero-filled workspace per (device, stream, call geometry): calls
+    on one stream run one after another, so calls of one geometry share it
+    (each leaves its arrival counters zero; another geometry could use those
+    bytes as scratch, hence one per geometry).  It is allocated on that
+    stream, and never during graph capture: a captured call must be given
+    its own workspace."""
     if need is None:
         need = decode_workspace_bytes(cache, n_layers, Hq, N)
-    key = (cache.device, int(_stream(cache.device, stream).value or 0))
+    s = stream if stream is not None else torch.cuda.current_stream(cache.device)
+    key = (cache.device, int(s.cuda_stream), type(cache).__name__, cache.geometry(),
+           n_layers, Hq, N, B, need)
     ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < need:
-        ws = _aligned_workspace(need, cache.device)
+    if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("pass an explicit workspace to decode calls captured in a graph")
+        with torch.cuda.stream(s):
+            ws = _aligned_workspace(need, cache.device)
         _ws_cache[key] = ws
     return ws
 
@@ -478,6 +488,9 @@ class PagedKVCache:
         return PagedCacheDesc(self.k.data_ptr(), self.v.data_ptr(), self.L, self.num_blocks,
                               self.Hkv, self.block_size, self.D, _DTYPE_CODE[self.dtype])
 
+    def geometry(self) -> tuple:
+        return (self.L, self.num_blocks, self.Hkv, self.block_size, self.D, self.dtype)
+
 
 def _check_table(cache, block_table):
     if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32
@@ -533,7 +546,7 @@ def _paged_decode(fn_name, cache, q, k_new, v_new, hist_len, block_table, scale,
     _, hp = _hist(hist_len, B)
     if workspace is None:
         need = paged_decode_workspace_bytes(cache, n_layers, B, Hq, N, mb)
-        workspace = _default_workspace(cache, n_layers, Hq, N, stream, need=need)
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream, need=need, B=(B, mb))
     if workspace.device != cache.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the cache's device")
     d = cache.desc()
@@ -578,7 +591,7 @@ def paged_decode_step_dl(cache: PagedKVCache, q, k_new, v_new, hist_len_dev, his
         scale = 1.0 / math.sqrt(cache.D)
     if workspace is None:
         need = paged_decode_workspace_bytes(cache, n_layers, B, Hq, N, mb)
-        workspace = _default_workspace(cache, n_layers, Hq, N, stream, need=need)
+        workspace = _default_workspace(cache, n_layers, Hq, N, stream, need=need, B=(B, mb))
     if workspace.device != cache.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the cache's device")
     d = cache.desc()

@@ -105,10 +105,12 @@ class Workload:
     v_cache: np.ndarray
     prefill: tuple | None = None
     steps: list = field(default_factory=list)
+    # score scale of every call; None means the usual 1/sqrt(D)
+    scale_value: float | None = None
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.D)
+        return 1.0 / math.sqrt(self.D) if self.scale_value is None else self.scale_value
 
 
 def _normal(rng, shape):
@@ -218,10 +220,12 @@ class PagedWorkload:
     k_pool: np.ndarray
     v_pool: np.ndarray
     steps: list = field(default_factory=list)
+    # score scale of every call; None means the usual 1/sqrt(D)
+    scale_value: float | None = None
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.D)
+        return 1.0 / math.sqrt(self.D) if self.scale_value is None else self.scale_value
 
 
 def make_paged_workload(name, *, seed, dtype, L, B, Hq, Hkv, D, block_size, max_blocks,
