@@ -182,6 +182,26 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0,
                            void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/*
+ * kvc_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split states and arrival counters
+ * live in a 16 MiB scratch array inside the library, one per GPU, held from
+ * library load until the process ends; the call itself allocates nothing.
+ * Calls whose states need more than that scratch (the decode workspace of
+ * kvc_decode_workspace_bytes beyond 16 MiB - 64 KiB of states, or more than
+ * 8192 query rows) return KVC_E_WORKSPACE before enqueuing anything.  Every
+ * call on a GPU shares its scratch: calls that may overlap on one GPU (other
+ * streams, or graphs replayed concurrently) race and must not use this entry
+ * point.  Arguments, results and other errors as kvc_decode_step.
+ */
+kvc_status kvc_decode_step_noalloc(const kvc_cache *cache, int32_t layer0,
+                                   int32_t n_layers, const void *q,
+                                   const void *k_new, const void *v_new,
+                                   int32_t Hq, int32_t N,
+                                   const int32_t *hist_len, float scale,
+                                   void *o, void *stream);
+
 /* kvc_decode_step with the sequence lengths in device memory, for a step that
  * is captured once in a HIP graph and replayed every token ([KV-4]
  * jennyma11.github.io/infra/ch07-01.html, "Decode 阶段": decode steps are

@@ -225,6 +225,35 @@ def test_split_and_combine_error_paths(lib):
     assert comb(*args(N=0, q=None, o=None, ws=None, wsb=0)) == OK
 
 
+def test_noalloc_decode_error_paths(lib):
+    """The allocation-free decode step validates everything before it looks
+    up its scratch (so none of this touches the HIP runtime), and refuses a
+    call whose states exceed the scratch."""
+    h = Host()
+    d = desc(h)
+    q, k, v, o = h.ptr(), h.ptr(), h.ptr(), h.ptr()
+
+    def call(**kw):
+        a = dict(c=ctypes.byref(d), layer0=0, n_layers=2, q=q, k=k, v=v, Hq=4, N=1,
+                 hist=hist(2, 5), scale=0.125, o=o, s=None)
+        a.update(kw)
+        return lib.kvc_decode_step_noalloc(a["c"], a["layer0"], a["n_layers"], a["q"], a["k"],
+                                           a["v"], a["Hq"], a["N"], a["hist"], a["scale"], a["o"],
+                                           a["s"])
+
+    assert call(N=0) == OK
+    assert call(Hq=3) == E_SHAPE
+    assert call(scale=float("nan")) == E_SHAPE
+    assert call(hist=hist(2, 16)) == E_CAPACITY
+    assert call(k=None) == E_NULL
+    assert call(o=h.ptr(offset=4)) == E_SHAPE
+    # 12 layers x 64 sequences x 32 KV heads x 8192 positions of D = 128:
+    # far more split states than the 16 MiB scratch
+    big = desc(h, L=12, B=64, Hkv=32, Tmax=8192, D=128)
+    assert call(c=ctypes.byref(big), n_layers=12, Hq=32, hist=hist(*([5] * 64))) == E_WORKSPACE
+    assert "scratch" in err(lib)
+
+
 def test_prefill_error_paths(lib):
     h = Host()
     d = desc(h)

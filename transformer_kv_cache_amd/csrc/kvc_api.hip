@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kvc_internal.h"
@@ -353,6 +354,41 @@ namespace {
 
 enum Phases { kSplit = 1, kCombine = 2, kBoth = 3 };
 
+// Scratch of kvc_decode_step_noalloc: 16 MiB per device (the split states of
+// the 12-layer batched decode workloads fit), held from library load until
+// the process ends.  The first 64 KiB are arrival counters (one per query
+// row, 8192 rows), zero at load and left zero by every call; the states
+// follow.  Host code uses the address hipGetSymbolAddress gives for the
+// current device, never the array's name.
+constexpr size_t kScratchCounterBytes = 64 * 1024;
+constexpr size_t kScratchStateBytes = 16 * 1024 * 1024 - kScratchCounterBytes;
+static __device__ __align__(256) unsigned char scratch[kScratchCounterBytes + kScratchStateBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+// This device's copy of `scratch`, looked up on the first call per device
+// (with that device current).
+kvc_status scratch_for_current_device(const char *fn, void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVC_E_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(KVC_E_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", fn, dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVC_E_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
 // Shared by kvc_attn_decode, kvc_decode_step (fused: k_new / v_new given),
 // kvc_decode_split and kvc_decode_combine.
 kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
@@ -360,7 +396,8 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
                        const void *k_new, const void *v_new, bool fused, int32_t Hq, int32_t N,
                        const int32_t *hist_len, float scale, void *o, void *workspace,
                        size_t workspace_bytes, void *stream, bool device_lengths = false,
-                       const int32_t *hist_dev = nullptr, int32_t hist_max = 0) {
+                       const int32_t *hist_dev = nullptr, int32_t hist_max = 0,
+                       bool in_scratch = false) {
   kvc_status st = check_cache(cache, layer0, n_layers, fn);
   if (st != KVC_OK) return st;
   if (N < 0) return fail(KVC_E_SHAPE, "%s: N = %d < 0", fn, N);
@@ -404,11 +441,27 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   if (g.kernel == DecodeKernel::kRows && g.max_splits > 65535)
     return fail(KVC_E_UNSUPPORTED, "%s: Tmax = %d gives %d key splits, more than one launch holds", fn,
                 cache->Tmax, g.max_splits);
-  if (!workspace) return fail(KVC_E_WORKSPACE, "%s: workspace is NULL", fn);
-  if (((uintptr_t)workspace & 255u) != 0)
-    return fail(KVC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
-  if (workspace_bytes < g.total)
-    return fail(KVC_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, g.total);
+  // Workspace layout: [arrival counters][partial outputs][partial (max,
+  // sum)].  The allocation-free entry point keeps its counters in a fixed
+  // region of the library's scratch that no call writes states into, so
+  // calls of any geometry leave them zero for the next one.
+  size_t state_off = g.ctr_bytes;
+  if (in_scratch) {
+    if (g.ctr_bytes > kScratchCounterBytes || g.ws_o_bytes + g.ws_ml_bytes > kScratchStateBytes)
+      return fail(KVC_E_WORKSPACE, "%s: this call needs %zu bytes of scratch (%zu of counters), more "
+                  "than the %zu (%zu) the allocation-free entry point holds; use kvc_decode_step "
+                  "with a workspace", fn, g.ws_o_bytes + g.ws_ml_bytes, g.ctr_bytes,
+                  (size_t)kScratchStateBytes, (size_t)kScratchCounterBytes);
+    state_off = kScratchCounterBytes;
+    // every check has passed: only now touch the runtime
+    if ((st = scratch_for_current_device(fn, &workspace)) != KVC_OK) return st;
+  } else {
+    if (!workspace) return fail(KVC_E_WORKSPACE, "%s: workspace is NULL", fn);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(KVC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    if (workspace_bytes < g.total)
+      return fail(KVC_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, g.total);
+  }
 
   kvc::DecodeArgs a{};
   a.k_cache = (char *)cache->k;
@@ -417,9 +470,8 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
   a.v_new = (const char *)v_new;
   a.q = (const char *)q;
   a.o = (char *)o;
-  // [arrival counters][partial outputs][partial (max, sum)]
-  a.ws_o = (float *)((char *)workspace + g.ctr_bytes);
-  a.ws_ml = (float *)((char *)workspace + g.ctr_bytes + g.ws_o_bytes);
+  a.ws_o = (float *)((char *)workspace + state_off);
+  a.ws_ml = (float *)((char *)workspace + state_off + g.ws_o_bytes);
   a.B = cache->B;
   a.Hkv = cache->Hkv;
   a.Hq = Hq;
@@ -516,6 +568,15 @@ kvc_status kvc_decode_step(const kvc_cache *cache, int32_t layer0, int32_t n_lay
                            size_t workspace_bytes, void *stream) {
   return decode_impl("kvc_decode_step", kBoth, cache, kvc::PagedGeom{}, layer0, n_layers, q, k_new, v_new, true, Hq,
                      N, hist_len, scale, o, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_decode_step_noalloc(const kvc_cache *cache, int32_t layer0, int32_t n_layers,
+                                   const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                                   int32_t N, const int32_t *hist_len, float scale, void *o,
+                                   void *stream) {
+  return decode_impl("kvc_decode_step_noalloc", kBoth, cache, kvc::PagedGeom{}, layer0, n_layers,
+                     q, k_new, v_new, true, Hq, N, hist_len, scale, o, nullptr, 0, stream, false,
+                     nullptr, 0, true);
 }
 
 kvc_status kvc_decode_step_dl(const kvc_cache *cache, int32_t layer0, int32_t n_layers,

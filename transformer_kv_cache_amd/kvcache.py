@@ -122,6 +122,9 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_decode_step_dl.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, vp, i32,
                                            ctypes.c_float, vp, vp, sz, vp]
         lib.kvc_decode_step_dl.restype = i32
+        lib.kvc_decode_step_noalloc.argtypes = [cp, i32, i32, vp, vp, vp, i32, i32, ip,
+                                                ctypes.c_float, vp, vp]
+        lib.kvc_decode_step_noalloc.restype = i32
         lib.kvc_paged_decode_step_dl.argtypes = [pp, i32, i32, vp, vp, vp, i32, i32, i32, vp, i32,
                                                  vp, i32, f32, vp, vp, sz, vp]
         lib.kvc_paged_decode_step_dl.restype = i32
@@ -310,6 +313,28 @@ def decode_step(cache: KVCache, q, k_new, v_new, hist_len, scale: float | None =
         ctypes.byref(d), layer0, n_layers, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), Hq, N,
         hp, float(scale), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(cache.device, stream)))
+    return out
+
+
+def decode_step_noalloc(cache: KVCache, q, k_new, v_new, hist_len, out,
+                        scale: float | None = None, layer0: int = 0, stream=None):
+    """decode_step with no workspace: the library's per-GPU scratch holds
+    the split states, so the call allocates nothing (``out`` must be given).
+    Calls that may overlap on one GPU must not use it."""
+    n_layers, _, Hq, N, _ = q.shape
+    shape = (n_layers, cache.B, Hq, N, cache.D)
+    _check_tensor("q", q, cache, shape)
+    kshape = (n_layers, cache.B, cache.Hkv, N, cache.D)
+    _check_tensor("k_new", k_new, cache, kshape)
+    _check_tensor("v_new", v_new, cache, kshape)
+    _check_tensor("out", out, cache, shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cache.D)
+    _, hp = _hist(hist_len, cache.B)
+    d = cache.desc()
+    _check(library().kvc_decode_step_noalloc(
+        ctypes.byref(d), layer0, n_layers, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), Hq, N,
+        hp, float(scale), out.data_ptr(), _stream(cache.device, stream)))
     return out
 
 
