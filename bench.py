@@ -499,10 +499,10 @@ def main():
                     help="length of the oracle's timed CPU sample")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the sweep, chunked/batched decode and prefill extras")
-    ap.add_argument("--only", choices=["prefill", "multirow"], default=None,
-                    help="time only the causal prefill workloads, or only the multi-row decode "
-                         "workloads (chunked, batched MHA / GQA), print them and exit (used for "
-                         "rocprofv3 counter runs)")
+    ap.add_argument("--only", choices=["prefill", "multirow", "gpt2"], default=None,
+                    help="time only the causal prefill workloads, the multi-row decode "
+                         "workloads (chunked, batched MHA / GQA) or the GPT-2 decoder, print them "
+                         "and exit (used for rocprofv3 counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (used to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -539,6 +539,10 @@ def main():
                 log(f"prefill S={S} {dtype}")
                 pre.append({"S": S, "dtype": dtype, **bench_prefill(torch, K, S, dtype, 40)})
         print(json.dumps({"prefill_12layer": pre}), flush=True)
+        return
+    if args.only == "gpt2":
+        log("GPT-2 Small-shaped decoder: cached vs recomputed per-token latency")
+        print(json.dumps({"gpt2_small_cached_vs_recompute": bench_gpt2(torch)}), flush=True)
         return
     if args.only == "multirow":
         res = {}

@@ -419,26 +419,66 @@ kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache,
  * so each weight matrix is read once for a handful of rows.  This is that
  * step of the GPT-2 block the same page measures (pre-norm, GELU, residual):
  *
- *   y[m][n] = act( sum_k xh[m][k] w[k][n] + bias[n] ) + res[m][n]
+ *   y[m][n] = act( sum_k xh[m][k] wt[n][k] + bias[n] ) + res[m][n]
  *   xh[m] = (x[m] - mean) / sqrt(var + ln_eps) * ln_g + ln_b  when ln_g is
  *           given (mean and biased variance over the K features of row m),
  *           else x[m];  act = 0: identity, 1: GELU, tanh form
  *           0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
  *
- * All fp32, device pointers, row-major: x [M, K], w [K, N], bias [N] or
- * NULL, ln_g / ln_b [K] (both or neither), res [M, N] or NULL, y [M, N].
- * 1 <= M <= 8, M * K <= 12288 (and (M + 2) * K <= 16384 with the layer
- * norm), K and N multiples of 4; x, w, res, y and ln_g / ln_b 16-byte
- * aligned.  y may be the same buffer as res (in-place residual update) but
- * must not overlap x.  The caller owns every buffer; nothing is allocated.
- * Errors: KVC_E_NULL (x, w or y missing, or only one of ln_g / ln_b),
- * KVC_E_SHAPE (sizes, alignment, act, ln_eps, y overlapping x),
- * KVC_E_UNSUPPORTED (more rows or inputs than that: prompt-sized inputs
- * belong to a GEMM library), KVC_E_HIP (launch failure). */
-kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *w,
+ * All fp32, device pointers: x [M, K] row-major; wt [N, K], the weight
+ * transposed (output feature n's K input weights contiguous, packed once per
+ * model, as kvc_gemm_f32 takes it); bias [N] or NULL; ln_g / ln_b [K] (both
+ * or neither); res [M, N] or NULL; y [M, N].  1 <= M <= 8, M * K <= 12288,
+ * K a multiple of 4; x, wt, res and y 16-byte aligned.  y may be the same
+ * buffer as res (in-place residual update) but must not overlap x.  The
+ * caller owns every buffer; nothing is allocated.
+ * Errors: KVC_E_NULL (x, wt or y missing, or only one of ln_g / ln_b),
+ * KVC_E_SHAPE (sizes, alignment, act, ln_eps, overlaps), KVC_E_UNSUPPORTED
+ * (more rows or inputs than that: prompt-sized inputs go to kvc_gemm_f32),
+ * KVC_E_HIP (launch failure). */
+kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *wt,
                           int32_t N, const float *bias, const float *ln_g,
                           const float *ln_b, float ln_eps, int32_t act,
                           const float *res, float *y, void *stream);
+
+/* ---- dense layers of a prompt ---------------------------------------------
+ *
+ * [KV-2] openai-hub.com/news/2435, "千倍计算量为何只换来6倍速度": without the
+ * cache every step runs the projections and the MLP for every position of
+ * the context again (products of the context length by the model width, on
+ * the matrix cores here); with it only a prompt's first pass does.  The
+ * GPT-2 block of that section: pre-norm, GELU, residual.
+ *
+ * gemm_f32: y[m][n] = act( sum_k a[m][k] wt[n][k] + bias[n] ) + res[m][n],
+ * fp32 throughout (matrix-core fp32 products, no reduced precision),
+ * act = 0: identity, 1: GELU, tanh form (as kvc_linear_f32).
+ *   a  : device [M, K] row-major, or with a_heads = H > 0 head-major
+ *        [H, M, K/H] (the attention output as the prefill writes it); K/H
+ *        a multiple of 64.
+ *   wt : device [N, K]: the weight transposed (output feature n's K input
+ *        weights contiguous, a linear layer's usual layout), packed once
+ *        per model.  bias [N] or NULL.  res [M, N] row-major or NULL; it
+ *        may be y itself (in-place residual update).
+ *   y  : device [M, N] row-major, or with y_qkv_heads = H > 0 the attention
+ *        layout [3, H, M, N/(3H)] (q, k, v for kvc_attn_prefill /
+ *        kvc_decode_step without a permute); N/(3H) a multiple of 4, and no
+ *        res then.
+ *   K a positive multiple of 64, N >= 1, M >= 0 (0: no-op); a, wt, res, y
+ *   16-byte aligned, y not overlapping a.  Errors: KVC_E_NULL, KVC_E_SHAPE
+ *   (sizes, layouts, alignment, overlap), KVC_E_UNSUPPORTED (too large for
+ *   one launch, a residual with the attention layout), KVC_E_HIP. */
+kvc_status kvc_gemm_f32(const float *a, int32_t a_heads, int32_t M, int32_t K,
+                        const float *wt, int32_t N, const float *bias,
+                        int32_t act, const float *res, float *y,
+                        int32_t y_qkv_heads, void *stream);
+
+/* layernorm_f32: y[m] = (x[m] - mean) / sqrt(var + eps) * g + b over the K
+ * features of each row (biased variance), the GPT-2 block's pre-norm.
+ * x, y device [M, K] (y may be x), g, b [K]; K a multiple of 4 up to 4096;
+ * all 16-byte aligned; eps finite and >= 0.  Errors as kvc_gemm_f32. */
+kvc_status kvc_layernorm_f32(const float *x, int32_t M, int32_t K,
+                             const float *g, const float *b, float eps,
+                             float *y, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvc_last_error(void);

@@ -435,7 +435,7 @@ def test_linear_error_paths(lib):
     assert call(g=g) == E_NULL                     # gain without shift
     assert call(M=0) == E_SHAPE
     assert call(K=6) == E_SHAPE                    # not a multiple of 4
-    assert call(N=10) == E_SHAPE
+    assert call(N=0) == E_SHAPE
     assert call(M=9) == E_UNSUPPORTED
     assert call(M=5, K=3072) == E_UNSUPPORTED      # 15360 inputs > 12288
     assert "exceed" in err(lib)
@@ -451,9 +451,29 @@ def test_linear_layer_norm_limits(lib):
     h = Host()
     x, w, y, g, b = h.ptr(65536), h.ptr(), h.ptr(), h.ptr(65536), h.ptr(65536)
     call = lambda M, K, gg=g, bb=b: lib.kvc_linear_f32(x, M, K, w, 8, None, gg, bb, 1e-5, 0, None, y, None)
-    assert call(1, 8192) == E_UNSUPPORTED          # (1 + 2) * 8192 > 16384 with the norm
-    assert call(4, 3072) == E_UNSUPPORTED          # (4 + 2) * 3072 > 16384
-    assert call(1, 8, gg=h.ptr(offset=4)) == E_SHAPE   # misaligned gain
+    assert call(1, 12292) == E_UNSUPPORTED         # more than 12288 inputs with the norm too
+    assert call(5, 3072) == E_UNSUPPORTED          # 15360 inputs
+    assert call(1, 8, gg=h.ptr(offset=2)) == E_SHAPE   # gain not 4-byte aligned
+    # the gemm's limits
+    gemm = lambda **kw: lib.kvc_gemm_f32(*[{**dict(a=x, ah=0, M=4, K=64, wt=w, N=8, bias=None, act=0,
+                                                  res=None, y=y, qh=0, s=None), **kw}[k]
+                                           for k in ("a", "ah", "M", "K", "wt", "N", "bias", "act",
+                                                     "res", "y", "qh", "s")])
+    assert gemm(M=0) == OK
+    assert gemm(K=96) == E_SHAPE                   # not a multiple of 64
+    assert gemm(N=0) == E_SHAPE
+    assert gemm(ah=2) == E_SHAPE                   # 32 features per head
+    assert gemm(qh=2, N=12) == E_SHAPE             # 2 per q / k / v head
+    assert gemm(qh=1, N=12, res=y) == E_UNSUPPORTED
+    assert gemm(wt=None) == E_NULL
+    assert gemm(y=x) == E_SHAPE                    # output over the input
+    ln = lambda **kw: lib.kvc_layernorm_f32(*[{**dict(x=x, M=2, K=64, g=g, b=b, eps=1e-5, y=y, s=None),
+                                               **kw}[k] for k in ("x", "M", "K", "g", "b", "eps", "y", "s")])
+    assert ln(M=0) == OK
+    assert ln(K=6) == E_SHAPE
+    assert ln(K=4100) == E_SHAPE
+    assert ln(eps=-1.0) == E_SHAPE
+    assert ln(g=None) == E_NULL
 
 
 def test_device_length_step_error_paths(lib):

@@ -43,7 +43,7 @@ def run_case(M, K, N, ln, act, res, seed, inplace=False):
     rt = d(r)
     out = rt if inplace else None
     print(f"[linear] M={M} K={K} N={N} ln={ln} act={act} res={res} inplace={inplace}", flush=True)
-    y = Kc.linear(d(x), d(w), bias=d(b), ln=(d(g), d(s)) if ln else None,
+    y = Kc.linear(d(x), d(np.ascontiguousarray(w.T)), bias=d(b), ln=(d(g), d(s)) if ln else None,
                   act="gelu" if act else None, residual=rt if res else None, out=out)
     torch.cuda.synchronize()
     got = y.cpu().numpy().astype(np.float64)
@@ -51,8 +51,9 @@ def run_case(M, K, N, ln, act, res, seed, inplace=False):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 768, 2304), (1, 768, 768), (1, 768, 3072), (1, 3072, 768),
-                                   (1, 768, 50260), (3, 768, 2304), (8, 768, 3072), (4, 3072, 768),
-                                   (1, 4, 4), (2, 12, 20), (8, 1536, 36)])
+                                   (1, 768, 50257), (3, 768, 2304), (8, 768, 3072), (4, 3072, 768),
+                                   (1, 4, 4), (2, 12, 20), (8, 1536, 36), (1, 12288, 5),
+                                   (2, 1540, 7), (5, 260, 9)])
 def test_shapes_plain(M, K, N):
     run_case(M, K, N, ln=False, act=False, res=False, seed=M * 7 + K + N)
 
@@ -68,3 +69,90 @@ def test_fused_epilogues(ln, act, res, M):
 def test_inplace_residual(M):
     """y written over res (h += x W + b, the residual update of a block)."""
     run_case(M, 768, 768, ln=False, act=False, res=True, seed=41 + M, inplace=True)
+
+
+# ---- the prompt-sized product kvc_gemm_f32 and kvc_layernorm_f32 ---------------
+
+def run_gemm(M, K, N, act, res, seed, a_heads=0, qkv_heads=0, inplace=False, bias=True):
+    """kvc_gemm_f32 against a float64 product of the same fp32 inputs, with
+    the oracle's GELU; a given head-major or the output in the attention
+    layout, converted on the host for the reference.  Bound as for the
+    decode-time kernel: 4 K u sum_k |a_k w_kn| + 1e-5 |y| + 1e-6."""
+    from transformer_kv_cache_amd import kvcache as Kc
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal((M, K)) * 1.5 + 0.2).astype(np.float32)
+    w = (0.05 * rng.standard_normal((K, N))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    r = rng.standard_normal((M, N)).astype(np.float32)
+    ref = a.astype(np.float64) @ w.astype(np.float64) + (b if bias else 0.0)
+    if act:
+        ref = G.gelu(ref)
+    if res:
+        ref = ref + r
+    bound = 4 * K * 2.0 ** -24 * (np.abs(a.astype(np.float64)) @ np.abs(w.astype(np.float64))) \
+        + 1e-5 * np.abs(ref) + 1e-6
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    a_dev = d(a.reshape(M, a_heads, K // a_heads).transpose(1, 0, 2)) if a_heads else d(a)
+    rt = d(r)
+    print(f"[gemm] M={M} K={K} N={N} act={act} res={res} a_heads={a_heads} qkv_heads={qkv_heads}",
+          flush=True)
+    y = Kc.gemm(a_dev, d(w.T), bias=d(b) if bias else None, act="gelu" if act else None,
+                residual=rt if res else None, out=rt if inplace else None, a_heads=a_heads,
+                qkv_heads=qkv_heads)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    if qkv_heads:
+        dh = N // (3 * qkv_heads)
+        assert got.shape == (3, qkv_heads, M, dh)
+        got = got.transpose(2, 0, 1, 3).reshape(M, N)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+
+
+@pytest.mark.parametrize("M,K,N", [(1000, 768, 2304), (1000, 768, 768), (1000, 768, 3072),
+                                   (1000, 3072, 768), (64, 768, 768), (1, 64, 4), (65, 128, 100),
+                                   (130, 192, 68), (9, 768, 50257), (3, 64, 6), (200, 320, 36)])
+def test_gemm_shapes(M, K, N):
+    """GPT-2 Small's prompt products at context 1000, tile edges and ragged
+    rows / columns (M and N not multiples of 64), the output projection's
+    vocabulary width (an odd N), a K of 5 tiles."""
+    run_gemm(M, K, N, act=False, res=False, seed=M + K + N)
+
+
+@pytest.mark.parametrize("act,res,bias", [(True, False, True), (False, True, True), (True, True, True),
+                                          (False, False, False)])
+def test_gemm_epilogues(act, res, bias):
+    run_gemm(200, 768, 3072 if act else 768, act=act, res=res, seed=11 + act + 2 * res, bias=bias)
+
+
+def test_gemm_inplace_residual():
+    """y written over res (h += a W + b)."""
+    run_gemm(300, 3072, 768, act=False, res=True, seed=13, inplace=True)
+
+
+@pytest.mark.parametrize("M", [1, 100, 1000])
+def test_gemm_attention_layouts(M):
+    """QKV product written as [3, H, M, D] (q, k, v for the attention calls)
+    and the output projection reading the attention output [H, M, D]."""
+    run_gemm(M, 768, 2304, act=False, res=False, seed=17 + M, qkv_heads=12)
+    run_gemm(M, 768, 768, act=False, res=True, seed=19 + M, a_heads=12)
+
+
+@pytest.mark.parametrize("M,K", [(1, 768), (1000, 768), (7, 128), (5, 3072), (3, 4), (2, 4096)])
+def test_layernorm(M, K):
+    """kvc_layernorm_f32 against the oracle's float64 layer norm of the same
+    fp32 rows: within 1e-5 |y| + 1e-5 (the fp32 mean, variance and rsqrt)."""
+    from transformer_kv_cache_amd import kvcache as Kc
+    rng = np.random.default_rng(M * 31 + K)
+    x = (rng.standard_normal((M, K)) * 3 + 1.5).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(K)).astype(np.float32)
+    ref = G.layer_norm(x.astype(np.float64), g, b)
+    d = lambda a: torch.from_numpy(a).cuda()
+    print(f"[layernorm] M={M} K={K}", flush=True)
+    xd = d(x)
+    y = Kc.layer_norm(xd, d(g), d(b))
+    Kc.layer_norm(xd, d(g), d(b), out=xd)  # in place
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-5), float(np.max(np.abs(got - ref)))
+    assert np.array_equal(xd.cpu().numpy(), y.cpu().numpy())

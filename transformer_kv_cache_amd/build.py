@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvcache.so")
 SOURCES = ["kvc_api.hip", "kvc_append.hip", "kvc_decode.hip", "kvc_decode_mfma.hip",
-           "kvc_decode_rows.hip", "kvc_prefill.hip", "kvc_dense.hip"]
+           "kvc_decode_rows.hip", "kvc_prefill.hip", "kvc_dense.hip", "kvc_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -753,34 +753,37 @@ kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0, i
                      hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
-kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *w, int32_t N,
+kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *wt, int32_t N,
                           const float *bias, const float *ln_g, const float *ln_b, float ln_eps,
                           int32_t act, const float *res, float *y, void *stream) {
   static const char *fn = "kvc_linear_f32";
-  if (!x || !w || !y) return fail(KVC_E_NULL, "%s: x, w or y is NULL", fn);
+  if (!x || !wt || !y) return fail(KVC_E_NULL, "%s: x, wt or y is NULL", fn);
   if ((ln_g == nullptr) != (ln_b == nullptr))
     return fail(KVC_E_NULL, "%s: ln_g and ln_b must both be given or both NULL", fn);
-  if (M < 1 || K < 4 || N < 4 || K % 4 != 0 || N % 4 != 0)
-    return fail(KVC_E_SHAPE, "%s: M = %d, K = %d, N = %d (need M >= 1, K and N positive multiples of 4)",
-                fn, M, K, N);
-  if (M > kvc::kMaxLinearRows || (int64_t)M * K > kvc::kMaxLinearInputs ||
-      (ln_g && (int64_t)(M + 2) * K > kvc::kMaxLinearLds))
-    return fail(KVC_E_UNSUPPORTED,
-                "%s: M = %d rows of K = %d inputs exceed %d rows / %d inputs (%d with the layer norm's "
-                "two parameter rows)", fn, M, K, kvc::kMaxLinearRows, kvc::kMaxLinearInputs,
-                kvc::kMaxLinearLds);
+  if (M < 1 || K < 4 || N < 1 || K % 4 != 0)
+    return fail(KVC_E_SHAPE, "%s: M = %d, K = %d, N = %d (need M >= 1, K a positive multiple of 4, "
+                "N >= 1)", fn, M, K, N);
+  if (M > kvc::kMaxLinearRows || (int64_t)M * K > kvc::kMaxLinearInputs)
+    return fail(KVC_E_UNSUPPORTED, "%s: M = %d rows of K = %d inputs exceed %d rows / %d inputs", fn, M,
+                K, kvc::kMaxLinearRows, kvc::kMaxLinearInputs);
+  if ((int64_t)N * K >= ((int64_t)1 << 31) || N > 65535 * 16)
+    return fail(KVC_E_UNSUPPORTED, "%s: N = %d, K = %d too large for one launch", fn, N, K);
   if (act != 0 && act != 1) return fail(KVC_E_SHAPE, "%s: act = %d (0 or 1)", fn, act);
   if (ln_g && !(std::isfinite(ln_eps) && ln_eps >= 0.f))
     return fail(KVC_E_SHAPE, "%s: ln_eps must be finite and >= 0", fn);
-  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (res && !aligned16(res)) ||
-      (ln_g && (!aligned16(ln_g) || !aligned16(ln_b))))
-    return fail(KVC_E_SHAPE, "%s: x, w, res, y, ln_g and ln_b must be 16-byte aligned", fn);
+  if (!aligned16(x) || !aligned16(wt) || !aligned16(y) || (res && !aligned16(res)) ||
+      (ln_g && (((uintptr_t)ln_g & 3u) || ((uintptr_t)ln_b & 3u))))
+    return fail(KVC_E_SHAPE, "%s: x, wt, res and y must be 16-byte aligned", fn);
   const char *xb = (const char *)x, *xe = xb + (size_t)M * K * sizeof(float);
   const char *yb = (const char *)y, *ye = yb + (size_t)M * N * sizeof(float);
   if (yb < xe && xb < ye) return fail(KVC_E_SHAPE, "%s: y overlaps x", fn);
+  if (res && res != y) {
+    const char *rb = (const char *)res, *re = rb + (size_t)M * N * sizeof(float);
+    if (yb < re && rb < ye) return fail(KVC_E_SHAPE, "%s: y overlaps res without being it", fn);
+  }
   kvc::LinearArgs a{};
   a.x = x;
-  a.w = w;
+  a.wt = wt;
   a.bias = bias;
   a.ln_g = ln_g;
   a.ln_b = ln_b;
@@ -792,6 +795,79 @@ kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *w, 
   a.act = act;
   a.ln_eps = ln_eps;
   hipError_t e = kvc::launch_linear(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return ok();
+}
+
+kvc_status kvc_gemm_f32(const float *a, int32_t a_heads, int32_t M, int32_t K, const float *wt,
+                        int32_t N, const float *bias, int32_t act, const float *res, float *y,
+                        int32_t y_qkv_heads, void *stream) {
+  static const char *fn = "kvc_gemm_f32";
+  if (M < 0 || K < 64 || N < 1 || K % 64 != 0)
+    return fail(KVC_E_SHAPE, "%s: M = %d, K = %d, N = %d (need M >= 0, K a positive multiple of 64, "
+                "N >= 1)", fn, M, K, N);
+  if (act != 0 && act != 1) return fail(KVC_E_SHAPE, "%s: act = %d (0 or 1)", fn, act);
+  if (a_heads < 0 || (a_heads > 0 && (K % a_heads != 0 || (K / a_heads) % 64 != 0)))
+    return fail(KVC_E_SHAPE, "%s: a_heads = %d must split K = %d into parts of a multiple of 64", fn,
+                a_heads, K);
+  if (y_qkv_heads < 0 ||
+      (y_qkv_heads > 0 && (N % (3 * y_qkv_heads) != 0 || (N / (3 * y_qkv_heads)) % 4 != 0)))
+    return fail(KVC_E_SHAPE, "%s: y_qkv_heads = %d must split N = %d into 3 x heads parts of a "
+                "multiple of 4", fn, y_qkv_heads, N);
+  if (y_qkv_heads > 0 && res)
+    return fail(KVC_E_UNSUPPORTED, "%s: a residual needs the row-major output", fn);
+  if ((int64_t)M * N >= ((int64_t)1 << 31) || (int64_t)M * K >= ((int64_t)1 << 31) ||
+      (int64_t)K * N >= ((int64_t)1 << 31) || (M + 63) / 64 > 65535)
+    return fail(KVC_E_UNSUPPORTED, "%s: M = %d, K = %d, N = %d too large for one launch", fn, M, K, N);
+  if (M == 0) return ok();
+  if (!a || !wt || !y) return fail(KVC_E_NULL, "%s: a, wt or y is NULL", fn);
+  if (!aligned16(a) || !aligned16(wt) || !aligned16(y) || (res && !aligned16(res)) ||
+      (bias && ((uintptr_t)bias & 3u)))
+    return fail(KVC_E_SHAPE, "%s: a, wt, res and y must be 16-byte aligned", fn);
+  const char *ab = (const char *)a, *ae = ab + (size_t)M * K * sizeof(float);
+  const char *yb = (const char *)y, *ye = yb + (size_t)M * N * sizeof(float);
+  if (yb < ae && ab < ye) return fail(KVC_E_SHAPE, "%s: y overlaps a", fn);
+  if (res && res != y) {
+    const char *rb = (const char *)res, *re = rb + (size_t)M * N * sizeof(float);
+    if (yb < re && rb < ye) return fail(KVC_E_SHAPE, "%s: y overlaps res without being it", fn);
+  }
+  kvc::GemmArgs g{};
+  g.a = a;
+  g.wt = wt;
+  g.bias = bias;
+  g.res = res;
+  g.y = y;
+  g.M = M;
+  g.K = K;
+  g.N = N;
+  g.act = act;
+  g.a_heads = a_heads;
+  g.y_qkv_heads = y_qkv_heads;
+  hipError_t e = kvc::launch_gemm(g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return ok();
+}
+
+kvc_status kvc_layernorm_f32(const float *x, int32_t M, int32_t K, const float *g, const float *b,
+                             float eps, float *y, void *stream) {
+  static const char *fn = "kvc_layernorm_f32";
+  if (M < 0 || K < 4 || K % 4 != 0 || K > 4096)
+    return fail(KVC_E_SHAPE, "%s: M = %d, K = %d (need M >= 0, K a positive multiple of 4 up to 4096)",
+                fn, M, K);
+  if (!(std::isfinite(eps) && eps >= 0.f)) return fail(KVC_E_SHAPE, "%s: eps must be finite and >= 0", fn);
+  if (M == 0) return ok();
+  if (!x || !g || !b || !y) return fail(KVC_E_NULL, "%s: x, g, b or y is NULL", fn);
+  if (!aligned16(x) || !aligned16(g) || !aligned16(b) || !aligned16(y))
+    return fail(KVC_E_SHAPE, "%s: x, g, b and y must be 16-byte aligned", fn);
+  kvc::LayerNormArgs p{};
+  p.x = x;
+  p.g = g;
+  p.b = b;
+  p.y = y;
+  p.M = M;
+  p.K = K;
+  p.eps = eps;
+  hipError_t e = kvc::launch_layernorm(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   return ok();
 }

@@ -411,6 +411,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (n != (uint64_t)(nsplit - 1)) return;
       asm volatile("" ::: "memory");
       misplaced = ((prev >> 16) & 0xFFFFFu) != n * xcc || (prev >> 36) != n * xcc * xcc;
+    } else if (nsplit == 1) {
+      // the merge reads back this workgroup's own state: wait until the L2
+      // holds it, or the read may return the previous call's
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     // The merge: key P's state first, then every split's (this one's
     // included, read back), then the normalisation.

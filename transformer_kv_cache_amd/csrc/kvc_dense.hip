@@ -1,7 +1,7 @@
 // kvc_dense.hip -- the dense layers of a decoder block for the few rows a
 // cached decode step carries, fused with their neighbours:
 //
-//   y[m][n] = act( sum_k xh[m][k] W[k][n] + bias[n] ) + res[m][n]
+//   y[m][n] = act( sum_k xh[m][k] wt[n][k] + bias[n] ) + res[m][n]
 //   xh = LN(x) (optional, over each row of x) or x,  act = GELU (tanh) or none
 //
 // [KV-2] openai-hub.com/news/2435, "千倍计算量为何只换来6倍速度": with the cache a
@@ -11,22 +11,22 @@
 // structure (pre-norm, GELU, residual) is the GPT-2 block the same section
 // measures.
 //
-// Layout: W row-major [K][N] (input feature k, output feature n), x / y / res
-// row-major [M][N or K], M <= 8 rows, K and N multiples of 4.
+// Layout: the weight transposed, wt [N][K] (output feature n's K input
+// weights contiguous, packed once per model, the layout kvc_gemm_f32 takes
+// too); x / y / res row-major [M][K or N], M <= 8 rows, K a multiple of 4.
 //
-// Work split: a workgroup owns CPW output columns and all K inputs.  Its NT
-// threads are CT = CPW/4 column threads (4 columns = one 16-byte load of a W
-// row) times KG = NT/CT k-groups; k-group g takes rows g, g+KG, ...  A wave
-// instruction therefore reads 64/CT consecutive W rows, CPW*4 contiguous
-// bytes of each.  x (after the layer norm) sits in LDS and is read as a
-// broadcast.  Partial sums are combined across the k-groups of a wave with
-// lane exchanges and across the waves in LDS; the owning thread adds
-// the bias, applies the activation and the residual and stores.  One pass,
-// no atomics, a fixed summation order.  A single-row call uses 1024-thread
-// workgroups: with only N / CPW workgroups (48 for a 768-wide layer), each
-// must keep many W rows in flight to stream at HBM rate.
+// Work split: one wave per RPW output features, four waves per workgroup.
+// A wave reads its RPW rows of wt whole -- each lane 16-byte pieces j,
+// j + 64, ... -- so a 768-wide row is three wave-wide 1 KB loads, and every
+// load of the call is issued before anything waits: the whole matrix is in
+// flight at once across the launch.  Meanwhile the workgroup stages x in
+// LDS and, with the layer norm, normalises it there (mean, then the
+// variance about it).  Each lane then dots its pieces with the same pieces
+// of every x row, the wave sums the partials with lane exchanges, and the
+// owning lane adds bias, GELU and residual and stores: one pass over the
+// weight, no atomics, a fixed summation order.
 //
-// Roofline: HBM, K*N*4 bytes of W per call (plus M*(K+N)*4 for x, y, res).
+// Roofline: HBM, K*N*4 bytes of wt per call (plus M*(K+N)*4 for x, y, res).
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -41,222 +41,171 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return 0.5f * v * (1.f + tanhf(c * (v + 0.044715f * v * v * v)));
 }
 
-// MR: rows the registers are sized for (1, or kMaxLinearRows); NT threads.
-template <int CPW, int MR, int NT>
-__global__ __launch_bounds__(NT) void linear_kernel(LinearArgs a) {
-  constexpr int CT = CPW / 4;    // column threads
-  constexpr int KG = NT / CT;    // k-groups
-  constexpr int NW = NT / 64;    // waves
-  extern __shared__ float xs[];  // [M][K] inputs (normalised) + LN params, then [NW][M][CPW] partials
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// MR: rows the registers are sized for (1, or kMaxLinearRows); RPW output
+// features per wave; PPR 16-byte pieces of a row per lane and chunk (a row
+// of K floats takes ceil(K / 256) pieces per lane, in chunks of PPR).
+template <int MR, int RPW, int PPR>
+__global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
+  extern __shared__ float xs[];  // [M][K] inputs, normalised in place
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int ct = tid % CT;
-  const int kg = tid / CT;
   const int M = a.M, K = a.K, N = a.N;
-  constexpr int U = 4;                        // W rows in flight per thread per batch
-  constexpr int EP = (MR * CPW + NT - 1) / NT;  // epilogue outputs per thread
+  const int k4 = K / 4;
+  const int pieces = (k4 + 63) / 64;  // per lane and row
+  const int nb = (blockIdx.x * 4 + wave) * RPW;  // this wave's first output
 
-  // 0. Every load that does not depend on another is issued first, so the
-  //    call pays one memory round trip before its arithmetic: this thread's
-  //    first U rows of W, its epilogue's bias and residual, x and the
-  //    layer-norm parameters.
-  const int n0 = blockIdx.x * CPW + ct * 4;
-  const bool col_ok = n0 < N;
-  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.w) + (col_ok ? n0 / 4 : 0);
-  const int n4 = N / 4;  // 16-byte vectors per W row
-  f32x4 wv[U];
+  // 0. Every independent load first: the wave's rows of wt (first chunk),
+  //    its bias and residual, x into LDS.
+  const f32x4 *wrow[RPW];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int k = kg + u * KG;
-    wv[u] = (col_ok && k < K) ? w4[(size_t)k * n4] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RPW; ++r) {
+    const int n = nb + r < N ? nb + r : N - 1;
+    wrow[r] = reinterpret_cast<const f32x4 *>(a.wt) + (size_t)n * k4;
   }
-  float e_add[EP];
+  f32x4 wv[RPW][PPR];
+  auto load_chunk = [&](int p0) {
 #pragma unroll
-  for (int e = 0; e < EP; ++e) {
-    const int t = tid + e * NT;
-    const int m = t / CPW, n = blockIdx.x * CPW + t % CPW;
-    float v = 0.f;
-    if (m < M && n < N) {
-      if (a.bias) v += a.bias[n];
-      if (a.res && a.act == 0) v += a.res[(size_t)m * N + n];
+    for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+      for (int i = 0; i < PPR; ++i) {
+        const int q = lane + 64 * (p0 + i);
+        wv[r][i] = q < k4 ? wrow[r][q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    e_add[e] = v;
-  }
-  float e_res[EP];
+  };
+  load_chunk(0);
+  float b_add[RPW], r_add[RPW][MR];
 #pragma unroll
-  for (int e = 0; e < EP; ++e) {
-    const int t = tid + e * NT;
-    const int m = t / CPW, n = blockIdx.x * CPW + t % CPW;
-    e_res[e] = (a.res && a.act != 0 && m < M && n < N) ? a.res[(size_t)m * N + n] : 0.f;
+  for (int r = 0; r < RPW; ++r) {
+    const int n = nb + r;
+    b_add[r] = (a.bias && n < N) ? a.bias[n] : 0.f;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      r_add[r][m] = (a.res && m < M && n < N) ? a.res[(size_t)m * N + n] : 0.f;
   }
   const f32x4 *x4 = reinterpret_cast<const f32x4 *>(a.x);
   f32x4 *xs4 = reinterpret_cast<f32x4 *>(xs);
-  float *lng = xs + (size_t)M * K, *lnb = lng + K;  // layer-norm parameters after x
-  const bool ln = a.ln_g != nullptr;
-  for (int i = tid; i < M * K / 4; i += NT) xs4[i] = x4[i];
-  if (ln) {
-    for (int i = tid; i < K / 4; i += NT) {
-      reinterpret_cast<f32x4 *>(lng)[i] = reinterpret_cast<const f32x4 *>(a.ln_g)[i];
-      reinterpret_cast<f32x4 *>(lnb)[i] = reinterpret_cast<const f32x4 *>(a.ln_b)[i];
-    }
-  }
+  for (int i = tid; i < M * k4; i += 256) xs4[i] = x4[i];
   __syncthreads();
 
-  // 1. Layer-norm statistics of each row in one pass over it, shifted by its
-  //    first element against cancellation: with y = x - x[0],
-  //    mean = x[0] + E[y] and var = E[y^2] - E[y]^2 (biased).  All threads
-  //    share the work; the waves' partial sums meet in LDS.
-  __shared__ float red[2][NW][kMaxLinearRows];
-  float mean[MR], rstd[MR];
-  if (ln) {
+  // 1. Layer norm of each x row in LDS: the mean, then the biased variance
+  //    about it, each summed by all threads and across the waves in LDS.
+  if (a.ln_g) {
+    __shared__ float red[4][kMaxLinearRows];
+    __shared__ float stat[2][kMaxLinearRows];
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      if (m < M) {
-        const float *row = xs + (size_t)m * K;
-        const float x0 = row[0];
-        float s1 = 0.f, s2 = 0.f;
-        for (int k = tid; k < K; k += NT) {
-          const float y = row[k] - x0;
-          s1 += y;
-          s2 += y * y;
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          s1 += __shfl_xor(s1, o);
-          s2 += __shfl_xor(s2, o);
-        }
-        if (lane == 0) {
-          red[0][wave][m] = s1;
-          red[1][wave][m] = s2;
+      for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+          const float *row = xs + (size_t)m * K;
+          float s = 0.f;
+          if (pass == 0) {
+            for (int k = tid; k < K; k += 256) s += row[k];
+          } else {
+            const float mu = stat[0][m];
+            for (int k = tid; k < K; k += 256) {
+              const float d = row[k] - mu;
+              s = fmaf(d, d, s);
+            }
+          }
+          s = wave_sum(s);
+          if (lane == 0) red[wave][m] = s;
         }
       }
+      __syncthreads();
+      if (tid < M) {
+        const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+        stat[pass][tid] = pass == 0 ? s / (float)K : 1.f / sqrtf(s / (float)K + a.ln_eps);
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < M * K; i += 256) {
+      const int m = i / K, k = i - m * K;
+      xs[i] = (xs[i] - stat[0][m]) * stat[1][m] * a.ln_g[k] + a.ln_b[k];
     }
     __syncthreads();
+  }
+
+  // 2. Dot products of this lane's pieces, chunk by chunk (one chunk for
+  //    K <= 256 PPR).
+  float acc[RPW][MR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+  for (int p0 = 0; p0 < pieces; p0 += PPR) {
+    if (p0 > 0) load_chunk(p0);
+#pragma unroll
+    for (int i = 0; i < PPR; ++i) {
+      const int q = lane + 64 * (p0 + i);
+      if (q < k4) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          if (m < M) {
+            const f32x4 xv = xs4[(size_t)m * k4 + q];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+              float t = acc[r][m];
+              t = fmaf(xv[0], wv[r][i][0], t);
+              t = fmaf(xv[1], wv[r][i][1], t);
+              t = fmaf(xv[2], wv[r][i][2], t);
+              t = fmaf(xv[3], wv[r][i][3], t);
+              acc[r][m] = t;
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // 3. Sum over the wave; lane r * MR + m stores output (m, nb + r).
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = nb + r;
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       if (m < M) {
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          s1 += red[0][w][m];
-          s2 += red[1][w][m];
+        const float v = wave_sum(acc[r][m]);
+        if (lane == r * MR + m && n < N) {
+          float y = v + b_add[r];
+          if (a.act == 1) y = gelu_tanh(y);
+          a.y[(size_t)m * N + n] = y + r_add[r][m];
         }
-        const float ey = s1 / (float)K;
-        const float var = fmaxf(s2 / (float)K - ey * ey, 0.f);
-        mean[m] = xs[(size_t)m * K] + ey;
-        rstd[m] = 1.f / sqrtf(var + a.ln_eps);
       }
     }
-  }
-  // Input feature k of row m as the product sees it.
-  auto xin = [&](int m, int k) -> float {
-    const float v = xs[(size_t)m * K + k];
-    return ln ? (v - mean[m]) * rstd[m] * lng[k] + lnb[k] : v;
-  };
-
-  // 2. Partial sums over this k-group's rows, U rows per batch, the next
-  //    batch's loads issued before this batch's arithmetic.
-  f32x4 acc[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = kg;; k += U * KG) {
-    f32x4 nx[U];
-    const bool more = k + U * KG < K;
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k + (U + u) * KG;
-        nx[u] = (col_ok && kk < K) ? w4[(size_t)kk * n4] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k + u * KG;
-      if (kk < K) {
-#pragma unroll
-        for (int m = 0; m < MR; ++m)
-          if (m < M) acc[m] += xin(m, kk) * wv[u];
-      }
-    }
-    if (!more) break;
-#pragma unroll
-    for (int u = 0; u < U; ++u) wv[u] = nx[u];
-  }
-
-  // 3. Sum over the k-groups of the wave (lanes ct, ct + CT, ...), then over
-  //    the waves in LDS (the x rows are no longer read).
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (m < M) {
-#pragma unroll
-      for (int o = CT; o < 64; o <<= 1) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[m][c] += __shfl_xor(acc[m][c], o);
-      }
-    }
-  }
-  __syncthreads();
-  float *part = xs;  // [NW][M][CPW]
-  if (lane < CT) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-      if (m < M)
-        *reinterpret_cast<f32x4 *>(part + ((size_t)wave * M + m) * CPW + ct * 4) = acc[m];
-  }
-  __syncthreads();
-
-  // 4. Epilogue: bias, activation, residual (operands already in registers).
-#pragma unroll
-  for (int e = 0; e < EP; ++e) {
-    const int t = tid + e * NT;
-    const int m = t / CPW;
-    const int c = t % CPW;
-    const int n = blockIdx.x * CPW + c;
-    if (m >= M || n >= N) continue;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) v += part[((size_t)w * M + m) * CPW + c];
-    v += e_add[e];
-    if (a.act == 1) v = gelu_tanh(v);
-    a.y[(size_t)m * N + n] = v + e_res[e];
   }
 }
 
-// Columns per workgroup: wide enough to stream whole cache lines of each W
-// row, narrow enough to give the launch at least 64 workgroups.
-int linear_columns_per_workgroup(int N) {
-  if (N / 64 >= 128) return 64;
-  if (N / 32 >= 64) return 32;
-  return 16;
+template <int MR, int RPW, int PPR>
+void launch_shape(const LinearArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.N + 4 * RPW - 1) / (4 * RPW)));
+  const size_t lds = (size_t)a.M * a.K * sizeof(float);
+  hipLaunchKernelGGL((linear_kernel<MR, RPW, PPR>), grid, dim3(256), lds, s, a);
 }
 
-size_t linear_lds_bytes(int M, int K, bool ln, int cpw, int waves) {
-  const size_t xb = ((size_t)M * K + (ln ? 2 * (size_t)K : 0)) * sizeof(float);
-  const size_t pb = (size_t)waves * M * cpw * sizeof(float);
-  return xb > pb ? xb : pb;
-}
-
-template <int MR, int NT>
+template <int MR>
 void launch_rows(const LinearArgs &a, hipStream_t s) {
-  const int cpw = linear_columns_per_workgroup(a.N);
-  const dim3 grid((unsigned)((a.N + cpw - 1) / cpw));
-  const size_t lds = linear_lds_bytes(a.M, a.K, a.ln_g != nullptr, cpw, NT / 64);
-  if (cpw == 64)
-    hipLaunchKernelGGL((linear_kernel<64, MR, NT>), grid, dim3(NT), lds, s, a);
-  else if (cpw == 32)
-    hipLaunchKernelGGL((linear_kernel<32, MR, NT>), grid, dim3(NT), lds, s, a);
-  else
-    hipLaunchKernelGGL((linear_kernel<16, MR, NT>), grid, dim3(NT), lds, s, a);
+  // outputs per wave so that a lane holds at most 12 pieces of wt
+  const int pieces = (a.K / 4 + 63) / 64;
+  if (pieces <= 3) launch_shape<MR, 4, 3>(a, s);
+  else if (pieces <= 6) launch_shape<MR, 2, 6>(a, s);
+  else launch_shape<MR, 1, 12>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_linear(const LinearArgs &a, hipStream_t s) {
   if (a.M == 1)
-    launch_rows<1, 1024>(a, s);
+    launch_rows<1>(a, s);
   else
-    launch_rows<kMaxLinearRows, 256>(a, s);
+    launch_rows<kMaxLinearRows>(a, s);
   return hipGetLastError();
 }
 

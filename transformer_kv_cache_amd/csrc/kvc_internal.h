@@ -240,10 +240,9 @@ struct PrefillArgs {
 // most kMaxLinearRows rows (kvc_linear_f32).
 constexpr int kMaxLinearRows = 8;
 constexpr int kMaxLinearInputs = 12288;  // M * K floats staged in LDS (48 KiB)
-constexpr int kMaxLinearLds = 16384;     // with the layer norm, (M + 2) * K floats (64 KiB)
 struct LinearArgs {
   const float *x;      // [M][K]
-  const float *w;      // [K][N]
+  const float *wt;     // [N][K]
   const float *bias;   // [N] or null
   const float *ln_g;   // [K] or null (no layer norm)
   const float *ln_b;   // [K] (with ln_g)
@@ -254,9 +253,34 @@ struct LinearArgs {
   float ln_eps;
 };
 
+// Dense layer of a prompt on the matrix cores (kvc_gemm_f32):
+// y = act(a wt^T + bias) + res.  a is [M][K] row-major, or head-major
+// [a_heads][M][K / a_heads]; wt is [N][K]; y is [M][N] row-major, or with
+// y_qkv_heads = H the attention layout [3][H][M][N / (3 H)].  res is
+// [M][N] row-major.
+struct GemmArgs {
+  const float *a, *wt, *bias, *res;
+  float *y;
+  int32_t M, K, N;
+  int32_t act;          // 0: none, 1: GELU (tanh form)
+  int32_t a_heads;      // 0: row-major a
+  int32_t y_qkv_heads;  // 0: row-major y
+};
+
+// Row-wise layer norm (kvc_layernorm_f32): y = (x - mean) / sqrt(var + eps)
+// * g + b over the K features of each of M rows.
+struct LayerNormArgs {
+  const float *x, *g, *b;
+  float *y;
+  int32_t M, K;
+  float eps;
+};
+
 // Host launchers (one translation unit each).  They assume validated
 // arguments and return the launch status.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+hipError_t launch_layernorm(const LayerNormArgs &p, hipStream_t s);
 hipError_t launch_lengths_add(int32_t *hist, int B, int n, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool merge, hipStream_t s);

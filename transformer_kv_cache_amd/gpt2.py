@@ -23,10 +23,11 @@ Where each step runs:
   * the dense layers of a decode step (at most 4 new tokens): the library's
     fused ``kvc_linear_f32`` (layer norm + matrix-vector product + bias +
     GELU / residual in one HBM-bound pass over the weights);
-  * the dense layers of a prompt (more tokens): plain library GEMMs
-    (hipBLASLt through torch, fp32, reduced-precision modes off) with torch
-    layer norm / GELU / adds -- compute-bound products, outside the cache
-    path.
+  * the dense layers of a prompt (more tokens): the library's fp32
+    matrix-core product ``kvc_gemm_f32`` (bias, GELU and residual fused into
+    its store; the QKV product written straight into the attention layout,
+    the output projection reading the attention output as the prefill
+    writes it) and its row-wise ``kvc_layernorm_f32``.
 """
 from __future__ import annotations
 
@@ -34,7 +35,6 @@ import math
 
 import numpy as np
 import torch
-import torch.nn.functional as F
 
 from . import kvcache as K
 
@@ -52,12 +52,13 @@ class GPT2:
         self.scale = 1.0 / math.sqrt(self.D)
         self.device = dev
         self.wte, self.wpe = t(w.wte), t(w.wpe)
-        self.Vp = (w.V + 3) // 4 * 4                    # output columns padded to 4
-        self.wte_t = torch.zeros((w.d, self.Vp), dtype=torch.float32, device=dev)
-        self.wte_t[:, :w.V] = self.wte.t()              # [d, Vp] output projection
         names = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b",
                  "w_fc", "b_fc", "w_pr", "b_pr")
         self.p = {n: t(getattr(w, n)) for n in names}
+        # the dense kernels take each weight transposed ([out, in]), packed
+        # once here; the token embedding [V, d] already is the output
+        # projection's transposed weight
+        self.pt = {n: self.p[n].transpose(1, 2).contiguous() for n in ("w_qkv", "w_o", "w_fc", "w_pr")}
         self.lnf_g, self.lnf_b = t(w.lnf_g), t(w.lnf_b)
         self._ws = {}
 
@@ -85,25 +86,29 @@ class GPT2:
         h = self.wte[ids] + self.wpe[P:P + N]
         if N <= self.DECODE_ROWS:
             return self._forward_decode(h, cache, P, last_only)
+        a = torch.empty_like(h)
+        pt = self.pt
         for l in range(self.L):
-            a = F.layer_norm(h, (d,), p["ln1_g"][l], p["ln1_b"][l], eps=1e-5)
-            qkv = torch.addmm(p["b_qkv"][l], a, p["w_qkv"][l])                 # [N, 3d]
-            t = qkv.view(N, 3, H, D).permute(1, 2, 0, 3).contiguous()         # [3, H, N, D]
+            K.layer_norm(h, p["ln1_g"][l], p["ln1_b"][l], out=a)
+            t = K.gemm(a, pt["w_qkv"][l], p["b_qkv"][l], qkv_heads=H)         # [3, H, N, D]
             q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
             if P == 0:
                 o = K.attn_prefill(cache, q, k, v, scale=self.scale, layer0=l)
             else:
                 o = K.decode_step(cache, q, k, v, [P], scale=self.scale, layer0=l,
                                   workspace=self._workspace(cache, N))
-            o = o.view(H, N, D).permute(1, 0, 2).reshape(N, d)
-            h = h + torch.addmm(p["b_o"][l], o, p["w_o"][l])
-            m = F.layer_norm(h, (d,), p["ln2_g"][l], p["ln2_b"][l], eps=1e-5)
-            f = F.gelu(torch.addmm(p["b_fc"][l], m, p["w_fc"][l]), approximate="tanh")
-            h = h + torch.addmm(p["b_pr"][l], f, p["w_pr"][l])
+            K.gemm(o.view(H, N, D), pt["w_o"][l], p["b_o"][l], residual=h, out=h, a_heads=H)
+            K.layer_norm(h, p["ln2_g"][l], p["ln2_b"][l], out=a)
+            f = K.gemm(a, pt["w_fc"][l], p["b_fc"][l], act="gelu")
+            K.gemm(f, pt["w_pr"][l], p["b_pr"][l], residual=h, out=h)
         if last_only:
             h = h[-1:]
-        h = F.layer_norm(h, (d,), self.lnf_g, self.lnf_b, eps=1e-5)
-        return (h @ self.wte_t)[:, :self.V]
+        if h.shape[0] <= K.MAX_LINEAR_ROWS:
+            z = K.linear(h, self.wte, ln=(self.lnf_g, self.lnf_b))
+        else:
+            # the token embedding [V, d] is already the transposed output weight
+            z = K.gemm(K.layer_norm(h, self.lnf_g, self.lnf_b), self.wte)
+        return z[:, :self.V]
 
     DECODE_ROWS = 4  # rows whose dense layers run in kvc_linear_f32 (4 x 3072 inputs fit)
 
@@ -113,42 +118,46 @@ class GPT2:
         empty cache), output projection + residual, LN2 + FC + GELU,
         projection + residual, and LN_f + output projection."""
         N = h.shape[0]
-        d, H, D, p = self.d, self.H, self.D, self.p
+        d, H, D, p, pt = self.d, self.H, self.D, self.p, self.pt
         for l in range(self.L):
-            qkv = K.linear(h, p["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
-            t = qkv.view(N, 3, H, D).permute(1, 2, 0, 3).contiguous()         # [3, H, N, D]
-            q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
+            qkv = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
+            if N == 1:
+                # one row: q, k, v are already [H, 1, D] slices of the product
+                q, k, v = (qkv[:, j * d:(j + 1) * d].view(1, 1, H, 1, D) for j in range(3))
+            else:
+                t = qkv.view(N, 3, H, D).permute(1, 2, 0, 3).contiguous()     # [3, H, N, D]
+                q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
             if P == 0:
                 o = K.attn_prefill(cache, q, k, v, scale=self.scale, layer0=l)
             else:
                 o = K.decode_step(cache, q, k, v, [P], scale=self.scale, layer0=l,
                                   workspace=self._workspace(cache, N))
-            o = o.view(H, N, D).permute(1, 0, 2).reshape(N, d).contiguous()
-            K.linear(o, p["w_o"][l], p["b_o"][l], residual=h, out=h)
-            f = K.linear(h, p["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
+            o = o.view(1, d) if N == 1 else o.view(H, N, D).permute(1, 0, 2).reshape(N, d).contiguous()
+            K.linear(o, pt["w_o"][l], p["b_o"][l], residual=h, out=h)
+            f = K.linear(h, pt["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
                          act="gelu")
-            K.linear(f, p["w_pr"][l], p["b_pr"][l], residual=h, out=h)
+            K.linear(f, pt["w_pr"][l], p["b_pr"][l], residual=h, out=h)
         if last_only:
             h = h[-1:]
-        z = K.linear(h, self.wte_t, ln=(self.lnf_g, self.lnf_b))
+        z = K.linear(h, self.wte, ln=(self.lnf_g, self.lnf_b))
         return z[:, :self.V]
 
     def _decode_token_dl(self, tok, hd, cache):
         """One cached decode step for the token ids ``tok`` (int64 [1] on the
         device) at the device position ``hd`` (int32 [1]); every shape and
         argument is fixed, so the step can be captured once and replayed."""
-        d, H, D, p = self.d, self.H, self.D, self.p
+        d, H, D, p, pt = self.d, self.H, self.D, self.p, self.pt
         h = self.wte[tok] + self.wpe[hd.long()]
         for l in range(self.L):
-            qkv = K.linear(h, p["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
+            qkv = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
             q, k, v = (qkv[:, j * d:(j + 1) * d].view(1, 1, H, 1, D) for j in range(3))
             o = K.decode_step_dl(cache, q, k, v, hd, self.T - 1, scale=self.scale, layer0=l,
                                  workspace=self._workspace(cache, 1))
-            K.linear(o.view(1, d), p["w_o"][l], p["b_o"][l], residual=h, out=h)
-            f = K.linear(h, p["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
+            K.linear(o.view(1, d), pt["w_o"][l], p["b_o"][l], residual=h, out=h)
+            f = K.linear(h, pt["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
                          act="gelu")
-            K.linear(f, p["w_pr"][l], p["b_pr"][l], residual=h, out=h)
-        z = K.linear(h, self.wte_t, ln=(self.lnf_g, self.lnf_b))
+            K.linear(f, pt["w_pr"][l], p["b_pr"][l], residual=h, out=h)
+        z = K.linear(h, self.wte, ln=(self.lnf_g, self.lnf_b))
         return z[:, :self.V]
 
     def generate_graph(self, prompt, n_new):

@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
 ABI_VERSION = 9  # KVC_ABI_VERSION of the header these signatures follow
+MAX_LINEAR_ROWS = 8  # rows kvc_linear_f32 takes (kMaxLinearRows)
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
            -5: "E_WORKSPACE", -6: "E_UNSUPPORTED", -7: "E_HIP"}
@@ -132,6 +133,10 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_lengths_add.restype = i32
         lib.kvc_linear_f32.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, f32, i32, vp, vp, vp]
         lib.kvc_linear_f32.restype = i32
+        lib.kvc_gemm_f32.argtypes = [vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]
+        lib.kvc_gemm_f32.restype = i32
+        lib.kvc_layernorm_f32.argtypes = [vp, i32, i32, vp, vp, f32, vp, vp]
+        lib.kvc_layernorm_f32.restype = i32
         if path is None:
             _lib = lib
     return lib
@@ -673,19 +678,20 @@ def paged_attn_prefill_varlen(cache: PagedKVCache, q, k, v, cu_seqlens, hist_len
     return out
 
 
-def linear(x, w, bias=None, ln=None, act=None, residual=None, out=None, ln_eps=1e-5,
+def linear(x, wt, bias=None, ln=None, act=None, residual=None, out=None, ln_eps=1e-5,
            stream=None):
-    """y = act(LN(x) w + bias) + residual for the few rows of a decode step
-    (fp32; x [M, K] with M <= 8, w [K, N]).  ``ln`` is (gain, shift) or None;
-    ``act`` is None or "gelu" (tanh form); ``out`` may be ``residual``."""
-    for name, t in (("x", x), ("w", w)):
+    """y = act(LN(x) wt^T + bias) + residual for the few rows of a decode step
+    (fp32; x [M, K] with M <= 8, wt [N, K]: the weight transposed).  ``ln``
+    is (gain, shift) or None; ``act`` is None or "gelu" (tanh form); ``out``
+    may be ``residual``."""
+    for name, t in (("x", x), ("wt", wt)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
                 or not t.is_contiguous() or t.dim() != 2:
             raise ValueError(f"{name} must be a contiguous 2-D fp32 CUDA tensor")
     M, K = x.shape
-    K2, N = w.shape
+    N, K2 = wt.shape
     if K2 != K:
-        raise ValueError(f"x has {K} features, w has {K2} rows")
+        raise ValueError(f"x has {K} features, wt has {K2} columns")
 
     def vec(name, t, n):
         if t is None:
@@ -704,7 +710,71 @@ def linear(x, w, bias=None, ln=None, act=None, residual=None, out=None, ln_eps=1
     if act not in codes:
         raise ValueError(f"act must be None or 'gelu', got {act!r}")
     ptr = lambda t: None if t is None else t.data_ptr()
-    _check(library().kvc_linear_f32(x.data_ptr(), M, K, w.data_ptr(), N, ptr(bias), ptr(g), ptr(b),
+    _check(library().kvc_linear_f32(x.data_ptr(), M, K, wt.data_ptr(), N, ptr(bias), ptr(g), ptr(b),
                                     float(ln_eps), codes[act], ptr(residual), out.data_ptr(),
                                     _stream(x.device, stream)))
+    return out
+
+
+def _f32_matrix(name, t):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor")
+    return t
+
+
+def gemm(a, wt, bias=None, act=None, residual=None, out=None, a_heads: int = 0,
+         qkv_heads: int = 0, stream=None):
+    """y = act(a wt^T + bias) + residual on the matrix cores (fp32), for
+    prompt-sized inputs.  a is [M, K], or [H, M, K/H] head-major with
+    ``a_heads`` = H; wt is the weight transposed, [N, K].  With ``qkv_heads``
+    = H the result is laid out [3, H, M, N/(3H)] (q, k, v for the attention
+    calls).  ``out`` may be ``residual``."""
+    _f32_matrix("a", a)
+    _f32_matrix("wt", wt)
+    if wt.dim() != 2:
+        raise ValueError("wt must be [N, K]")
+    N, K = wt.shape
+    if a_heads:
+        if a.dim() != 3 or a.shape[0] != a_heads or a.shape[0] * a.shape[2] != K:
+            raise ValueError(f"a must be [{a_heads}, M, {K // max(a_heads, 1)}]")
+        M = a.shape[1]
+    else:
+        if a.dim() != 2 or a.shape[1] != K:
+            raise ValueError(f"a must be [M, {K}]")
+        M = a.shape[0]
+    shape = (3, qkv_heads, M, N // (3 * qkv_heads)) if qkv_heads else (M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=a.device)
+    _f32_matrix("out", out)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {shape}")
+    for name, t, n in (("bias", bias, N), ("residual", residual, M * N)):
+        if t is not None and (_f32_matrix(name, t).numel() != n):
+            raise ValueError(f"{name} must have {n} elements")
+    codes = {None: 0, "gelu": 1}
+    if act not in codes:
+        raise ValueError(f"act must be None or 'gelu', got {act!r}")
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(library().kvc_gemm_f32(a.data_ptr(), a_heads, M, K, wt.data_ptr(), N, ptr(bias),
+                                  codes[act], ptr(residual), out.data_ptr(), qkv_heads,
+                                  _stream(a.device, stream)))
+    return out
+
+
+def layer_norm(x, g, b, eps: float = 1e-5, out=None, stream=None):
+    """Row-wise layer norm of x [M, K] (fp32) with gain g and shift b [K];
+    ``out`` may be ``x``."""
+    _f32_matrix("x", x)
+    M, K = x.shape
+    for name, t in (("g", g), ("b", b)):
+        if _f32_matrix(name, t).numel() != K:
+            raise ValueError(f"{name} must have {K} elements")
+    if out is None:
+        out = torch.empty_like(x)
+    _f32_matrix("out", out)
+    if tuple(out.shape) != (M, K):
+        raise ValueError(f"out must have shape {(M, K)}")
+    _check(library().kvc_layernorm_f32(x.data_ptr(), M, K, g.data_ptr(), b.data_ptr(), float(eps),
+                                       out.data_ptr(), _stream(x.device, stream)))
     return out
