@@ -43,25 +43,39 @@ def test_single_layer_generation(seed):
     assert not synth.is_canary(k[:, :, :, :20]).any() and synth.is_canary(k[:, :, :, 20:]).all()
 
 
+SEEDS = [0, 1, 2]
+
+
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("P", [128, 512, 1000, 1023])
-def test_decode_12layer(P):
-    check(synth.decode_12layer(P, seed=P))
+def test_decode_12layer(P, seed):
+    check(synth.decode_12layer(P, seed=seed))
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_chunked_decode(seed):
-    check(synth.chunked_decode(1000, 8, seed=seed))
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_chunked_decode(seed, fused):
+    check(synth.chunked_decode(1000, 8, seed=seed), fused=fused)
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("S", [256, 1024])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_causal_prefill(S, dtype):
-    check(synth.causal_prefill(S, dtype, seed=S + (dtype == "bf16")))
+def test_causal_prefill(S, dtype, seed):
+    check(synth.causal_prefill(S, dtype, seed=seed))
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("gqa", [False, True])
-def test_batched_decode(gqa):
-    check(synth.batched_decode(seed=5, gqa=gqa))
+def test_batched_decode(gqa, seed):
+    check(synth.batched_decode(seed=seed, gqa=gqa))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_decode_12layer_fused_step(seed):
+    """The headline step as the benchmark runs it (kvc_decode_step: one
+    launch, in-launch merge) at T = 1024."""
+    check(synth.decode_12layer(1023, seed=seed), fused=True)
 
 
 # ------------------------------------------------------------- edge cases

@@ -224,46 +224,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const size_t crow0 = (size_t)head * (uint32_t)Tmax;
   const uint32_t row = (uint32_t)((l * B + b) * Hkv + hkv);  // (l, b, hq, i = 0), Hq = Hkv
 
-  // Key P's rows for the merge (wave 0; lane j holds elements j + 64 e), in
-  // the same burst as the split's loads: q, and k_P / v_P from the new rows
-  // (fused step) or from cache slot P.
-  bits qn[EPL], kn[EPL], vn[EPL];
-  size_t slot = 0;
-  if (MERGE && wave == 0) {
-    slot = slot_row<PAGED>(a, b, P, layer0 + l, hkv) * D;
-    const bits *qb = reinterpret_cast<const bits *>(qp) + (size_t)row * D;
-    const bits *kb = a.k_new ? reinterpret_cast<const bits *>(a.k_new) + (size_t)row * D
-                             : reinterpret_cast<const bits *>(k_cache) + slot;
-    const bits *vb = a.v_new ? reinterpret_cast<const bits *>(a.v_new) + (size_t)row * D
-                             : reinterpret_cast<const bits *>(v_cache) + slot;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      qn[j] = qb[lane + 64 * j];
-      kn[j] = kb[lane + 64 * j];
-      vn[j] = vb[lane + 64 * j];
-    }
-  }
-
   float Mw = kNegInf, Lw = 0.f, ow[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) ow[j] = 0.f;
+  const int key0 = split * SPLIT;
+  const int last = P - 1 - key0;  // offset of the last key of this split
+  // 1. Issue the query load and every K and V load of this split up front.
+  //    Keys past the last one are clamped to it (a valid, written slot) so
+  //    that no load sits behind a branch; their scores are masked.  A paged
+  //    cache first looks up the blocks (for blocks of at least NRG positions
+  //    one scalar load per key load, else one load per key, all issued
+  //    together), then streams the rows from their blocks.
+  u32x4 qw, kw[KPL], vw[KPL];
   if (nsplit > 0) {
-    const int key0 = split * SPLIT;
-    const int last = P - 1 - key0;  // offset of the last key of this split
     // Uniform bases plus 32-bit per-lane byte offsets (the host bounds a
     // head's rows below 4 GiB): global loads with an SGPR base take one VGPR
     // per address.
     const char *kc = k_cache + crow0 * (LPR * 16);
     const char *vc = v_cache + crow0 * (LPR * 16);
-
-    // 1. Issue the query load and every K and V load of this split up front.
-    //    Keys past the last one are clamped to it (a valid, written slot) so
-    //    that no load sits behind a branch; their scores are masked.  A paged
-    //    cache first looks up the blocks (for blocks of at least NRG
-    //    positions one scalar load per key load, else one load per key, all
-    //    issued together), then streams the rows from their blocks.
-    const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
-    u32x4 kw[KPL], vw[KPL];
+    qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
     if constexpr (PAGED) {
       size_t prow[KPL];
       if (a.pg.bs_log2 >= kLog2Nrg<NRG>) {
@@ -290,10 +269,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off));
       }
     }
-    // Keep the scheduler from interleaving arithmetic (and its waits) into
-    // the load burst: all loads of the split are in flight before the first
-    // wait.
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Key P's rows for the merge (lane j holds elements j + 64 e), behind the
+  // burst in every wave (no branch, so nothing waits for them before the
+  // merge): q, and k_P / v_P from the new rows (fused step) or from cache
+  // slot P.
+  bits qn[EPL], kn[EPL], vn[EPL];
+  size_t slot = 0;
+  if constexpr (MERGE) {
+    slot = slot_row<PAGED>(a, b, P, layer0 + l, hkv) * D;
+    const bits *qb = reinterpret_cast<const bits *>(qp) + (size_t)row * D;
+    const bits *kb = a.k_new ? reinterpret_cast<const bits *>(a.k_new) + (size_t)row * D
+                             : reinterpret_cast<const bits *>(k_cache) + slot;
+    const bits *vb = a.v_new ? reinterpret_cast<const bits *>(a.v_new) + (size_t)row * D
+                             : reinterpret_cast<const bits *>(v_cache) + slot;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      qn[j] = qb[lane + 64 * j];
+      kn[j] = kb[lane + 64 * j];
+      vn[j] = vb[lane + 64 * j];
+    }
+  }
+  // Keep the scheduler from interleaving arithmetic (and its waits) into the
+  // load burst: all loads of the split are in flight before the first wait.
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (nsplit > 0) {
 
     // 2. Scores in the log2 domain; key key0 + kk*NRG + rg is visible iff its
     //    offset is at most `last`, a compare of rg against a uniform bound.

@@ -36,27 +36,16 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef KVC_MFMA_NONTEMPORAL
-#define KVC_MFMA_NONTEMPORAL 0
-#endif
-__device__ __forceinline__ u32x4 stream_load(const u32x4 *p) {
-#if KVC_MFMA_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
+// K/V loads: plain (non-temporal loads measured no faster here).
+__device__ __forceinline__ u32x4 stream_load(const u32x4 *p) { return *p; }
 
 // Which 16-byte vector of a key row lane group g loads as its j-th: the
 // contraction over d may run in any order as long as the K and Q operands
-// agree.  0: vector 4 j + g (a wave instruction covers the same quarter of
-// 16 rows); 1: vector g J + j (each lane reads one contiguous run).
-#ifndef KVC_MFMA_VEC_ORDER
-#define KVC_MFMA_VEC_ORDER 0
-#endif
+// agree; vector 4 j + g, so a wave instruction covers the same quarter of 16
+// rows (each lane reading one contiguous run instead measured no faster).
 template <int J>
 __device__ __forceinline__ int vec_index(int j, int g) {
-  return KVC_MFMA_VEC_ORDER ? g * J + j : 4 * j + g;
+  return 4 * j + g;
 }
 
 // KPW keys per wave (a multiple of 16), RM = 16 query rows per workgroup.
@@ -307,13 +296,11 @@ hipError_t launch_kpw(const DecodeArgs &a, int splits, bool fused, hipStream_t s
 
 }  // namespace
 
-// Keys per wave: KVC_MFMA_KPW for 256-byte rows (fp32 D = 64, bf16 D = 128),
-// twice that for 128-byte rows and half for 512-byte rows, so that a
-// workgroup always streams the same bytes.  Build-time tuning constant.
-#ifndef KVC_MFMA_KPW
-#define KVC_MFMA_KPW 32
-#endif
-constexpr int kKpw = KVC_MFMA_KPW;
+// Keys per wave: 32 for 256-byte rows (fp32 D = 64, bf16 D = 128), twice
+// that for 128-byte rows and half for 512-byte rows, so that a workgroup
+// always streams the same bytes (16 and 64 keys per wave measured worse for
+// the GQA workload).
+constexpr int kKpw = 32;
 constexpr int kKpwSmall = kKpw >= 32 ? kKpw / 2 : 16;
 
 int decode_mfma_split_keys(int dtype, int D) {

@@ -400,21 +400,14 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
 }
 
 // Keys each lane group loads per split (a split covers 256 / LPR times as
-// many).  Build-time tuning constant; 8 measured best for the chunked fp32
-// and the bf16 GQA decode workloads (2, 4, 6, 12 and 16 were slower or
-// equal).
-#ifndef KVC_ROWS_KEYS_PER_LANE
-#define KVC_ROWS_KEYS_PER_LANE 8
-#endif
-constexpr int kRowsKpl = KVC_ROWS_KEYS_PER_LANE;
-// P.V of 8 fp32 rows on the matrix cores (1) or the vector ALUs (0).
-#ifndef KVC_ROWS_MFMA_PV
-#define KVC_ROWS_MFMA_PV 1
-#endif
+// many): 8 measured best for the chunked fp32 and the bf16 GQA decode
+// workloads (2, 4, 6, 12 and 16 were slower or equal).
+constexpr int kRowsKpl = 8;
 
 template <int DT, int LPR, int RP>
 hipError_t launch_rp(const DecodeArgs &a, int splits, bool fused, hipStream_t s) {
-  constexpr bool MPV = KVC_ROWS_MFMA_PV && DT == KVC_F32 && RP == 8 && LPR == 16;
+  // P.V of 8 fp32 rows on the matrix cores (the vector-ALU form measured equal)
+  constexpr bool MPV = DT == KVC_F32 && RP == 8 && LPR == 16;
   const dim3 grid((unsigned)(a.n_layers * a.Hkv), (unsigned)splits, (unsigned)a.nb);
   const bool paged = a.pg.block_table != nullptr;
   if (a.hist_dev) {
