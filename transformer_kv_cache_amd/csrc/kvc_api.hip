@@ -538,6 +538,10 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
           e = kvc::launch_combine(a, cache->dtype, cache->D, (hipStream_t)stream);
       }
     } else {
+      // Several rows per KV head: split pass, then the combine pass (an
+      // in-launch merge measured no faster here: these grids exceed one
+      // resident round, so each split's wait for its state stores queues the
+      // next workgroups).
       const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
       if ((phases & kSplit) && splits > 0)
         e = g.kernel == DecodeKernel::kRows

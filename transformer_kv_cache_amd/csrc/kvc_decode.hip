@@ -90,19 +90,6 @@ template <> struct Elem<KVC_BF16> {
   static __device__ __forceinline__ float widen(bits u) { return __uint_as_float((uint32_t)u << 16); }
 };
 
-// Loads of split states written by other workgroups of this launch: they
-// bypass the CU's L1 (which may hold a stale copy of a line shared with
-// another row's states) and are served by the L2 the writers stored to.
-__device__ __forceinline__ float state_load(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void state_load_ml(const float *p, float &m, float &l) {
-  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-  m = __uint_as_float((uint32_t)u);
-  l = __uint_as_float((uint32_t)(u >> 32));
-}
-
 // Key P's score in the log2 domain, scale log2(e) q.k_P, from one wave whose
 // lane j holds elements j, j + 64, ... of q and k_P.
 template <int DT, int EPL>
@@ -115,50 +102,6 @@ __device__ __forceinline__ float key_score(const typename Elem<DT>::bits (&qn)[E
   dot = xor_combine<16>(dot);
   dot = xor_combine<32>(dot);
   return dot * scale_log2;
-}
-
-// Merge of a query row's split states into the running state (M, L, o) of
-// one wave (lane j holds output elements j, j + 64, ...):
-//   o = sum_s 2^(m_s - M') o_s + 2^(M - M') o,  L likewise,  M' = max(M, m_s)
-// over splits 0 .. nsplit-1, in chunks of CH whose loads are all issued
-// before any is used.  The fused kernel's last workgroup and combine_kernel
-// both run exactly this, so their outputs are bit-identical.
-template <int D>
-__device__ __forceinline__ void merge_states(const float *ws_o, const float *ws_ml, int64_t ws_rows,
-                                             int64_t row, int nsplit, int lane, float &M, float &L,
-                                             float (&o)[D / 64]) {
-  constexpr int EPL = D / 64;
-  constexpr int CH = 16;
-  for (int s0 = 0; s0 < nsplit; s0 += CH) {
-    float mv[CH], lv[CH], ov[CH][EPL];
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
-      const size_t ws = (size_t)sp * (size_t)ws_rows + (size_t)row;
-      state_load_ml(ws_ml + ws * 2, mv[t], lv[t]);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) ov[t][j] = state_load(ws_o + ws * D + lane + 64 * j);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float Mc = M;
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      if (s0 + t >= nsplit) mv[t] = kNegInf;
-      Mc = fmaxf(Mc, mv[t]);
-    }
-    const float fr = rescale(M, Mc);
-    L *= fr;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) o[j] *= fr;
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const float f = rescale(mv[t], Mc);
-      L = fmaf(f, lv[t], L);
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) o[j] = fmaf(f, ov[t][j], o[j]);
-    }
-    M = Mc;
-  }
 }
 
 // Cache row index (in rows of D elements) of position P of this (layer,
@@ -394,24 +337,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     bool misplaced = false;
     if (nsplit > 1) {
       // Count this split once the L2 holds its state; the last to arrive
-      // merges.  The 64-bit count also sums each writer's XCD id x and x^2:
-      // with n writers, sum x = n y and sum x^2 = n y^2 hold for the merging
-      // workgroup's id y only if every x equals y (their variance about y is
-      // zero), i.e. only if every state went through this L2.
-      uint32_t xcc;
-      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-      xcc &= 0xFu;
-      const uint64_t mark = 1ull | ((uint64_t)xcc << 16) | ((uint64_t)(xcc * xcc) << 36);
+      // merges (and checks that every state went through its L2).
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      uint64_t prev = 0;
-      if (lane == 0)
-        prev = __hip_atomic_fetch_add(a.counters + row, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      prev = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(prev >> 32)) << 32) |
-             __builtin_amdgcn_readfirstlane((uint32_t)prev);
-      const uint64_t n = prev & 0xFFFFu;
-      if (n != (uint64_t)(nsplit - 1)) return;
+      uint32_t last = 0, mis = 0;
+      if (lane == 0) {
+        bool m = false;
+        last = arrive_last(a.counters + row, nsplit, m);
+        mis = m;
+      }
+      if (!__builtin_amdgcn_readfirstlane(last)) return;
       asm volatile("" ::: "memory");
-      misplaced = ((prev >> 16) & 0xFFFFFu) != n * xcc || (prev >> 36) != n * xcc * xcc;
+      misplaced = __builtin_amdgcn_readfirstlane(mis) != 0;
     } else if (nsplit == 1) {
       // the merge reads back this workgroup's own state: wait until the L2
       // holds it, or the read may return the previous call's
@@ -438,8 +374,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         reinterpret_cast<bits *>(a.v_cache)[slot + lane + 64 * j] = vn[j];
       }
     }
-    if (nsplit > 1 && lane == 0)
-      __hip_atomic_store(a.counters + row, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (nsplit > 1 && lane == 0) reset_counter(a.counters + row);
   }
 }
 

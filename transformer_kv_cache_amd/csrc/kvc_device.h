@@ -55,4 +55,88 @@ __device__ __forceinline__ float xor_combine(float x) {
   return MAX ? fmaxf(y0, y1) : y0 + y1;
 }
 
+
+// ---- split-state merge shared by the split kernels and the combine pass ----
+
+// Loads of split states written by other workgroups of this launch: they
+// bypass the CU's L1 (which may hold a stale copy of a line shared with
+// another row's states) and are served by the L2 the writers stored to.
+__device__ __forceinline__ float state_load(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void state_load_ml(const float *p, float &m, float &l) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  m = __uint_as_float((uint32_t)u);
+  l = __uint_as_float((uint32_t)(u >> 32));
+}
+
+// Merge of a query row's split states into the running state (M, L, o) of
+// one wave (lane j holds output elements j, j + 64, ...):
+//   o = sum_s 2^(m_s - M') o_s + 2^(M - M') o,  L likewise,  M' = max(M, m_s)
+// over splits 0 .. nsplit-1, in chunks of CH whose loads are all issued
+// before any is used.  The fused kernel's last workgroup and combine_kernel
+// both run exactly this, so their outputs are bit-identical.
+template <int D>
+__device__ __forceinline__ void merge_states(const float *ws_o, const float *ws_ml, int64_t ws_rows,
+                                             int64_t row, int nsplit, int lane, float &M, float &L,
+                                             float (&o)[D / 64]) {
+  constexpr int EPL = D / 64;
+  constexpr int CH = 16;
+  for (int s0 = 0; s0 < nsplit; s0 += CH) {
+    float mv[CH], lv[CH], ov[CH][EPL];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
+      const size_t ws = (size_t)sp * (size_t)ws_rows + (size_t)row;
+      state_load_ml(ws_ml + ws * 2, mv[t], lv[t]);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ov[t][j] = state_load(ws_o + ws * D + lane + 64 * j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float Mc = M;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      if (s0 + t >= nsplit) mv[t] = kNegInf;
+      Mc = fmaxf(Mc, mv[t]);
+    }
+    const float fr = rescale(M, Mc);
+    L *= fr;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) o[j] *= fr;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const float f = rescale(mv[t], Mc);
+      L = fmaf(f, lv[t], L);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) o[j] = fmaf(f, ov[t][j], o[j]);
+    }
+    M = Mc;
+  }
+}
+
+// Count a split workgroup's state (already stored) on its unit's 64-bit
+// arrival counter and tell whether it arrived last.  The caller has waited
+// until the L2 acknowledged the state stores (s_waitcnt vmcnt(0)) in every
+// wave that stored; one lane calls this.  The count also sums each
+// writer's XCD id x and x^2: with n earlier writers, sum x = n y and sum
+// x^2 = n y^2 hold for this workgroup's id y only if every x equals y
+// (their variance about y is zero), i.e. only if every state went through
+// this XCD's L2 -- `misplaced` reports otherwise.
+__device__ __forceinline__ bool arrive_last(uint64_t *counter, int nsplit, bool &misplaced) {
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  xcc &= 0xFu;
+  const uint64_t mark = 1ull | ((uint64_t)xcc << 16) | ((uint64_t)(xcc * xcc) << 36);
+  const uint64_t prev = __hip_atomic_fetch_add(counter, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t n = prev & 0xFFFFu;
+  misplaced = ((prev >> 16) & 0xFFFFFu) != n * xcc || (prev >> 36) != n * xcc * xcc;
+  return n == (uint64_t)(nsplit - 1);
+}
+
+// The merging workgroup leaves the counter zero for the next call.
+__device__ __forceinline__ void reset_counter(uint64_t *counter) {
+  __hip_atomic_store(counter, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace kvc
