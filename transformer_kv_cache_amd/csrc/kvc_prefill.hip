@@ -32,8 +32,8 @@
 // D) and the gfx950 transpose load (ds_read_b64_tr_b16) hands each lane one
 // d of four keys, two loads giving exactly that order -- no transposition
 // work in the staging.
-//   bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV product,
-//         fp32 accumulation.
+//   bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV product
+//         (and for the row sum), fp32 accumulation.
 //   fp32: v_mfma_f32_32x32x2_f32, everything in fp32 (no reduced precision).
 // Tiles above the diagonal are never loaded; a wave skips key tiles that lie
 // entirely above its own 32 rows.  Grid order puts the longest (last) query
@@ -388,10 +388,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], sc, -m_new));
         acc_s[kb][i] = p;
-        psum += p;
+        if constexpr (DT != KVC_BF16) psum += p;  // bf16: summed below, as rounded
       }
     }
-    l_run += psum;
 
     // O^T += V^T . P^T
 #pragma unroll
@@ -400,9 +399,18 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           u32x4 pw;
+          // The row sum adds the same bf16-rounded p that the PV product
+          // uses, two per v_dot2 against (1, 1): half the adds, and the
+          // normalised weights sum to one.  (The packed word goes through a
+          // scalar first: a bit_cast of the vector element itself made the
+          // compiler feed element 0 to every dot2.)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pw[j] = pack_bf16x2(acc_s[kb][8 * t + 2 * j], acc_s[kb][8 * t + 2 * j + 1]);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t pk = pack_bf16x2(acc_s[kb][8 * t + 2 * j], acc_s[kb][8 * t + 2 * j + 1]);
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                   __builtin_bit_cast(bf16x2, 0x3f803f80u), psum, false);
+            pw[j] = pk;
+          }
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             // keys 32 kb + 16 t + {0-3, 8-11} (low half-wave) or {4-7, 12-15}
@@ -429,6 +437,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
         }
       }
     }
+    l_run += psum;
   };
 
   // Every wave computes the first n_all tiles; the at most two after them
