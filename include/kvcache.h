@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 9
+#define KVC_ABI_VERSION 10
 
 typedef enum {
   KVC_OK = 0,
@@ -479,6 +479,25 @@ kvc_status kvc_gemm_f32(const float *a, int32_t a_heads, int32_t M, int32_t K,
 kvc_status kvc_layernorm_f32(const float *x, int32_t M, int32_t K,
                              const float *g, const float *b, float eps,
                              float *y, void *stream);
+
+/* Input layer of the GPT-2 block ([KV-2] openai-hub.com/news/2435, "实验到底测了
+ * 什么": GPT-2 Small, learned token and position embeddings): row i of y is
+ * the embedding of token ids[i] plus that of its position p0 + i,
+ *
+ *   y[i][k] = wte[ids[i]][k] + wpe[p0 + i][k],   i < N, k < d,
+ *
+ * with p0 = pos[0] when pos (a device int32) is given -- a length that
+ * advances on the device, as kvc_lengths_add keeps it -- else pos0.  All
+ * device pointers: wte [V, d] and wpe [T, d] fp32 row-major, ids int64 [N],
+ * y [N, d]; d a multiple of 4, wte / wpe / y 16-byte aligned, y overlapping
+ * neither table.  The ids and a device position are read by the kernel, so
+ * they are not checked here: a row whose id lies outside [0, V) or whose
+ * position lies outside [0, T) is written as NaN.  Errors: KVC_E_NULL,
+ * KVC_E_SHAPE (sizes, alignment, overlap, pos0 + N > T without pos),
+ * KVC_E_HIP.  N = 0 is a no-op. */
+kvc_status kvc_embed_f32(const float *wte, int32_t V, const float *wpe, int32_t T,
+                         int32_t d, const int64_t *ids, int32_t N, int32_t pos0,
+                         const int32_t *pos, float *y, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvc_last_error(void);

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 9
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 10
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -474,6 +474,33 @@ def test_linear_layer_norm_limits(lib):
     assert ln(K=4100) == E_SHAPE
     assert ln(eps=-1.0) == E_SHAPE
     assert ln(g=None) == E_NULL
+
+
+def test_embed_error_paths(lib):
+    """kvc_embed_f32 refuses bad sizes, positions, pointers and overlaps
+    before any launch (its valid calls run in the GPU tests)."""
+    h = Host()
+    wte, wpe, ids, y = h.ptr(8 * 64 * 4), h.ptr(16 * 64 * 4), h.ptr(64), h.ptr(4 * 64 * 4)
+
+    def call(**kw):
+        a = dict(wte=wte, V=8, wpe=wpe, T=16, d=64, ids=ids, N=4, pos0=0, pos=None, y=y)
+        a.update(kw)
+        return lib.kvc_embed_f32(a["wte"], a["V"], a["wpe"], a["T"], a["d"], a["ids"], a["N"], a["pos0"],
+                                 a["pos"], a["y"], None)
+
+    assert call(N=0) == OK                          # nothing to do
+    assert call(d=6) == E_SHAPE                     # not a multiple of 4
+    assert call(V=0) == E_SHAPE
+    assert call(N=-1) == E_SHAPE
+    assert call(pos0=13) == E_SHAPE                 # positions 13 .. 16 past T = 16
+    assert "outside" in err(lib)
+    assert call(pos0=-1) == E_SHAPE
+    assert call(wte=None) == E_NULL
+    assert call(ids=None) == E_NULL
+    assert call(pos=h.ptr(), ids=None) == E_NULL    # a device position does not excuse the ids
+    assert call(y=h.ptr(offset=4)) == E_SHAPE       # misaligned
+    assert call(y=wte) == E_SHAPE                   # output over a table
+    assert "overlaps" in err(lib)
 
 
 def test_device_length_step_error_paths(lib):

@@ -156,3 +156,28 @@ def test_layernorm(M, K):
     got = y.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-5), float(np.max(np.abs(got - ref)))
     assert np.array_equal(xd.cpu().numpy(), y.cpu().numpy())
+
+
+@pytest.mark.parametrize("d", [768, 12])
+def test_embed(d):
+    """kvc_embed_f32: row i = wte[ids[i]] + wpe[p0 + i], bit for bit the fp32
+    sum numpy forms; p0 from the host or from a device int32; ids or
+    positions out of range give NaN rows."""
+    from transformer_kv_cache_amd import kvcache as Kc
+    rng = np.random.default_rng(d)
+    V, T = 50, 20
+    wte = rng.standard_normal((V, d)).astype(np.float32)
+    wpe = rng.standard_normal((T, d)).astype(np.float32)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tw, tp = dv(wte), dv(wpe)
+    print(f"[embed] d={d}", flush=True)
+    ids = np.array([3, 0, 49, 7], np.int64)
+    y = Kc.embed(tw, tp, dv(ids), pos0=5).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), (wte[ids] + wpe[5:9]).view(np.uint32))
+    y = Kc.embed(tw, tp, dv(ids), pos=torch.tensor([9], dtype=torch.int32, device="cuda")).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), (wte[ids] + wpe[9:13]).view(np.uint32))
+    bad = np.array([50, -1, 2], np.int64)
+    y = Kc.embed(tw, tp, dv(bad), pos0=0).cpu().numpy()
+    assert np.isnan(y[:2]).all() and np.array_equal(y[2], wte[2] + wpe[2])
+    y = Kc.embed(tw, tp, dv(ids), pos=torch.tensor([18], dtype=torch.int32, device="cuda")).cpu().numpy()
+    assert np.array_equal(y[:2], wte[ids[:2]] + wpe[18:20]) and np.isnan(y[2:]).all()

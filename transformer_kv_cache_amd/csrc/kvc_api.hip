@@ -876,6 +876,42 @@ kvc_status kvc_layernorm_f32(const float *x, int32_t M, int32_t K, const float *
   return ok();
 }
 
+kvc_status kvc_embed_f32(const float *wte, int32_t V, const float *wpe, int32_t T, int32_t d,
+                         const int64_t *ids, int32_t N, int32_t pos0, const int32_t *pos, float *y,
+                         void *stream) {
+  static const char *fn = "kvc_embed_f32";
+  if (V < 1 || T < 1 || d < 4 || d % 4 != 0 || N < 0 || N > 65535)
+    return fail(KVC_E_SHAPE, "%s: V = %d, T = %d, d = %d, N = %d (need V, T >= 1, d a positive multiple "
+                "of 4, 0 <= N <= 65535)", fn, V, T, d, N);
+  if ((int64_t)V * d >= ((int64_t)1 << 40) || (int64_t)T * d >= ((int64_t)1 << 40))
+    return fail(KVC_E_SHAPE, "%s: tables too large", fn);
+  if (!pos && (pos0 < 0 || (int64_t)pos0 + N > T))
+    return fail(KVC_E_SHAPE, "%s: positions %d .. %lld outside [0, %d)", fn, pos0, (long long)pos0 + N - 1,
+                T);
+  if (N == 0) return ok();
+  if (!wte || !wpe || !ids || !y) return fail(KVC_E_NULL, "%s: wte, wpe, ids or y is NULL", fn);
+  if (!aligned16(wte) || !aligned16(wpe) || !aligned16(y))
+    return fail(KVC_E_SHAPE, "%s: wte, wpe and y must be 16-byte aligned", fn);
+  const char *yb = (const char *)y, *ye = yb + (size_t)N * d * sizeof(float);
+  const char *tb = (const char *)wte, *te = tb + (size_t)V * d * sizeof(float);
+  const char *pb = (const char *)wpe, *pe = pb + (size_t)T * d * sizeof(float);
+  if ((yb < te && tb < ye) || (yb < pe && pb < ye)) return fail(KVC_E_SHAPE, "%s: y overlaps a table", fn);
+  kvc::EmbedArgs e{};
+  e.wte = wte;
+  e.wpe = wpe;
+  e.ids = ids;
+  e.pos = pos;
+  e.y = y;
+  e.V = V;
+  e.T = T;
+  e.d = d;
+  e.N = N;
+  e.pos0 = pos0;
+  hipError_t err = kvc::launch_embed(e, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_status(err, fn);
+  return ok();
+}
+
 kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache, int32_t layer0,
                                          int32_t n_layers, const void *q, const void *k,
                                          const void *v, int32_t Hq, int32_t B,

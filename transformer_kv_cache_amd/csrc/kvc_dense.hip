@@ -287,6 +287,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(LinearArgs a) {
   }
 }
 
+// Input embedding: one workgroup per 1024 features of one token row; ids
+// and positions out of range give NaN rows (nothing host-side can see them).
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs e) {
+  const int i = blockIdx.y;
+  const int d4 = e.d / 4;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= d4) return;
+  const int64_t id = e.ids[i];
+  const int64_t p = (int64_t)(e.pos ? e.pos[0] : e.pos0) + i;
+  f32x4 v;
+  if (id < 0 || id >= e.V || p < 0 || p >= e.T) {
+    const float nan = __builtin_nanf("");
+    v = f32x4{nan, nan, nan, nan};
+  } else {
+    v = reinterpret_cast<const f32x4 *>(e.wte)[id * d4 + q] + reinterpret_cast<const f32x4 *>(e.wpe)[p * d4 + q];
+  }
+  reinterpret_cast<f32x4 *>(e.y)[(size_t)i * d4 + q] = v;
+}
+
 template <int RPW, int NP>
 void launch_gemv(const LinearArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)((a.N + 4 * RPW - 1) / (4 * RPW)));
@@ -325,6 +344,12 @@ hipError_t launch_linear(const LinearArgs &a, hipStream_t s) {
   } else {
     launch_rows<kMaxLinearRows>(a, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const EmbedArgs &e, hipStream_t s) {
+  const dim3 grid((unsigned)((e.d / 4 + 255) / 256), (unsigned)e.N);
+  hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, s, e);
   return hipGetLastError();
 }
 

@@ -276,11 +276,21 @@ struct LayerNormArgs {
   float eps;
 };
 
+// Token + position embedding (kvc_embed_f32).
+struct EmbedArgs {
+  const float *wte, *wpe;
+  const int64_t *ids;
+  const int32_t *pos;  // device start position, or null (then pos0)
+  float *y;
+  int32_t V, T, d, N, pos0;
+};
+
 // Host launchers (one translation unit each).  They assume validated
 // arguments and return the launch status.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 hipError_t launch_layernorm(const LayerNormArgs &p, hipStream_t s);
+hipError_t launch_embed(const EmbedArgs &e, hipStream_t s);
 hipError_t launch_lengths_add(int32_t *hist, int B, int n, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool merge, hipStream_t s);

@@ -19,6 +19,7 @@ embedding reused as the output projection; q/k/v are the three d-wide
 thirds of the QKV product with head h owning columns [h D, (h+1) D).
 
 Where each step runs:
+  * the input embedding (token + position): ``kvc_embed_f32``;
   * attention and every cache access: the library's HIP kernels;
   * the dense layers of a decode step (at most 4 new tokens): the library's
     fused ``kvc_linear_f32`` (layer norm + matrix-vector product + bias +
@@ -83,7 +84,7 @@ class GPT2:
         if P + N > self.T:
             raise ValueError(f"context {P + N} exceeds {self.T} positions")
         d, H, D, p = self.d, self.H, self.D, self.p
-        h = self.wte[ids] + self.wpe[P:P + N]
+        h = K.embed(self.wte, self.wpe, ids, pos0=P)
         if N <= self.DECODE_ROWS:
             return self._forward_decode(h, cache, P, last_only)
         a = torch.empty_like(h)
@@ -147,7 +148,7 @@ class GPT2:
         device) at the device position ``hd`` (int32 [1]); every shape and
         argument is fixed, so the step can be captured once and replayed."""
         d, H, D, p, pt = self.d, self.H, self.D, self.p, self.pt
-        h = self.wte[tok] + self.wpe[hd.long()]
+        h = K.embed(self.wte, self.wpe, tok, pos=hd)
         for l in range(self.L):
             qkv = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
             q, k, v = (qkv[:, j * d:(j + 1) * d].view(1, 1, H, 1, D) for j in range(3))

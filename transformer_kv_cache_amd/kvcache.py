@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 9  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 10  # KVC_ABI_VERSION of the header these signatures follow
 MAX_LINEAR_ROWS = 8  # rows kvc_linear_f32 takes (kMaxLinearRows)
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
@@ -137,6 +137,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_gemm_f32.restype = i32
         lib.kvc_layernorm_f32.argtypes = [vp, i32, i32, vp, vp, f32, vp, vp]
         lib.kvc_layernorm_f32.restype = i32
+        lib.kvc_embed_f32.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, vp]
+        lib.kvc_embed_f32.restype = i32
         if path is None:
             _lib = lib
     return lib
@@ -777,4 +779,31 @@ def layer_norm(x, g, b, eps: float = 1e-5, out=None, stream=None):
         raise ValueError(f"out must have shape {(M, K)}")
     _check(library().kvc_layernorm_f32(x.data_ptr(), M, K, g.data_ptr(), b.data_ptr(), float(eps),
                                        out.data_ptr(), _stream(x.device, stream)))
+    return out
+
+
+def embed(wte, wpe, ids, pos0: int = 0, pos=None, out=None, stream=None):
+    """Token + position embedding: row i is wte[ids[i]] + wpe[p0 + i], p0 =
+    ``pos[0]`` (a device int32 tensor) if given, else ``pos0``.  wte [V, d],
+    wpe [T, d] fp32; ids int64 [N] on the device.  Rows with an id or a
+    position out of range come back NaN."""
+    _f32_matrix("wte", wte)
+    _f32_matrix("wpe", wpe)
+    if wte.dim() != 2 or wpe.dim() != 2 or wte.shape[1] != wpe.shape[1]:
+        raise ValueError("wte must be [V, d] and wpe [T, d]")
+    if (not isinstance(ids, torch.Tensor) or ids.dtype != torch.int64 or ids.device != wte.device
+            or ids.dim() != 1 or not ids.is_contiguous()):
+        raise ValueError(f"ids must be a contiguous int64 vector on {wte.device}")
+    if pos is not None and (not isinstance(pos, torch.Tensor) or pos.dtype != torch.int32
+                            or pos.device != wte.device or pos.numel() < 1):
+        raise ValueError(f"pos must be an int32 tensor on {wte.device}")
+    (V, d), T, N = wte.shape, wpe.shape[0], ids.shape[0]
+    if out is None:
+        out = torch.empty((N, d), dtype=torch.float32, device=wte.device)
+    _f32_matrix("out", out)
+    if tuple(out.shape) != (N, d):
+        raise ValueError(f"out must have shape {(N, d)}")
+    _check(library().kvc_embed_f32(wte.data_ptr(), V, wpe.data_ptr(), T, d, ids.data_ptr(), N, int(pos0),
+                                   None if pos is None else pos.data_ptr(), out.data_ptr(),
+                                   _stream(wte.device, stream)))
     return out
