@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 10
+#define KVC_ABI_VERSION 11
 
 typedef enum {
   KVC_OK = 0,
@@ -425,21 +425,27 @@ kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache,
  *           else x[m];  act = 0: identity, 1: GELU, tanh form
  *           0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
  *
- * All fp32, device pointers: x [M, K] row-major; wt [N, K], the weight
+ * All fp32, device pointers: x [M, K] row-major, or head-major [H, M, K/H]
+ * with a_heads = H > 0 (the attention output as the decode call writes it;
+ * K/H a multiple of 4; not with the layer norm); wt [N, K], the weight
  * transposed (output feature n's K input weights contiguous, packed once per
  * model, as kvc_gemm_f32 takes it); bias [N] or NULL; ln_g / ln_b [K] (both
- * or neither); res [M, N] or NULL; y [M, N].  1 <= M <= 8, M * K <= 12288,
- * K a multiple of 4; x, wt, res and y 16-byte aligned.  y may be the same
- * buffer as res (in-place residual update) but must not overlap x.  The
- * caller owns every buffer; nothing is allocated.
+ * or neither); res [M, N] or NULL; y [M, N], or with y_qkv_heads = H > 0 the
+ * attention layout [3, H, M, N/(3H)] (q, k, v of the decode call; N/(3H) a
+ * multiple of 4; no residual).  1 <= M <= 8, M * K <= 12288, K a multiple
+ * of 4; x, wt, res and y 16-byte aligned.  y may be the same buffer as res
+ * (in-place residual update) but must not overlap x.  The caller owns every
+ * buffer; nothing is allocated.
  * Errors: KVC_E_NULL (x, wt or y missing, or only one of ln_g / ln_b),
- * KVC_E_SHAPE (sizes, alignment, act, ln_eps, overlaps), KVC_E_UNSUPPORTED
- * (more rows or inputs than that: prompt-sized inputs go to kvc_gemm_f32),
- * KVC_E_HIP (launch failure). */
-kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *wt,
-                          int32_t N, const float *bias, const float *ln_g,
-                          const float *ln_b, float ln_eps, int32_t act,
-                          const float *res, float *y, void *stream);
+ * KVC_E_SHAPE (sizes, layouts, alignment, act, ln_eps, overlaps),
+ * KVC_E_UNSUPPORTED (more rows or inputs than that -- prompt-sized inputs go
+ * to kvc_gemm_f32 -- or a layout with the norm / residual), KVC_E_HIP
+ * (launch failure). */
+kvc_status kvc_linear_f32(const float *x, int32_t a_heads, int32_t M, int32_t K,
+                          const float *wt, int32_t N, const float *bias,
+                          const float *ln_g, const float *ln_b, float ln_eps,
+                          int32_t act, const float *res, float *y,
+                          int32_t y_qkv_heads, void *stream);
 
 /* ---- dense layers of a prompt ---------------------------------------------
  *

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 10
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 11
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -424,10 +424,11 @@ def test_linear_error_paths(lib):
     g, b = h.ptr(), h.ptr()
 
     def call(**kw):
-        a = dict(x=x, M=1, K=8, w=w, N=8, bias=None, g=None, b=None, eps=1e-5, act=0, res=None, y=y)
+        a = dict(x=x, ah=0, M=1, K=8, w=w, N=8, bias=None, g=None, b=None, eps=1e-5, act=0, res=None,
+                 y=y, qh=0)
         a.update(kw)
-        return lib.kvc_linear_f32(a["x"], a["M"], a["K"], a["w"], a["N"], a["bias"], a["g"], a["b"],
-                                  a["eps"], a["act"], a["res"], a["y"], None)
+        return lib.kvc_linear_f32(a["x"], a["ah"], a["M"], a["K"], a["w"], a["N"], a["bias"], a["g"],
+                                  a["b"], a["eps"], a["act"], a["res"], a["y"], a["qh"], None)
 
     assert call(x=None) == E_NULL
     assert call(w=None) == E_NULL
@@ -445,12 +446,18 @@ def test_linear_error_paths(lib):
     assert call(res=h.ptr(offset=8)) == E_SHAPE
     assert call(y=x) == E_SHAPE                    # output over the input
     assert "overlaps" in err(lib)
+    assert call(ah=3) == E_SHAPE                   # K = 8 does not split in 3
+    assert call(ah=4) == E_SHAPE                   # parts of 2, not a multiple of 4
+    assert call(ah=2, g=x, b=x) == E_UNSUPPORTED   # the norm needs row-major input
+    assert call(qh=1, N=24, res=y) == E_UNSUPPORTED
+    assert call(qh=2, N=12) == E_SHAPE             # 2 per head
 
 
 def test_linear_layer_norm_limits(lib):
     h = Host()
     x, w, y, g, b = h.ptr(65536), h.ptr(), h.ptr(), h.ptr(65536), h.ptr(65536)
-    call = lambda M, K, gg=g, bb=b: lib.kvc_linear_f32(x, M, K, w, 8, None, gg, bb, 1e-5, 0, None, y, None)
+    call = lambda M, K, gg=g, bb=b: lib.kvc_linear_f32(x, 0, M, K, w, 8, None, gg, bb, 1e-5, 0, None, y, 0,
+                                                       None)
     assert call(1, 12292) == E_UNSUPPORTED         # more than 12288 inputs with the norm too
     assert call(5, 3072) == E_UNSUPPORTED          # 15360 inputs
     assert call(1, 8, gg=h.ptr(offset=2)) == E_SHAPE   # gain not 4-byte aligned

@@ -65,6 +65,45 @@ def test_fused_epilogues(ln, act, res, M):
     run_case(M, 768, 3072 if act else 768, ln=ln, act=act, res=res, seed=31 + M)
 
 
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_attention_layouts(M):
+    """kvc_linear_f32 writing q, k, v as [3, H, M, D] (with the layer norm)
+    and reading the attention output head-major [H, M, D] (with the
+    residual), against the row-major reference converted on the host."""
+    from transformer_kv_cache_amd import kvcache as Kc
+    H, D = 12, 64
+    K = N = H * D
+    rng = np.random.default_rng(100 + M)
+    x = (rng.standard_normal((M, K)) * 2 + 0.5).astype(np.float32)
+    w = (0.05 * rng.standard_normal((K, 3 * N))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(3 * N)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    sh = (0.1 * rng.standard_normal(K)).astype(np.float32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xh = G.layer_norm(x.astype(np.float64), g, sh)
+    ref = xh @ w.astype(np.float64) + b
+    bound = 4 * K * 2.0 ** -24 * (np.abs(xh) @ np.abs(w.astype(np.float64))) + 1e-5 * np.abs(ref) + 1e-6
+    print(f"[linear layouts] M={M}", flush=True)
+    y = Kc.linear(d(x), d(w.T), bias=d(b), ln=(d(g), d(sh)), qkv_heads=H)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (3, H, M, D)
+    got = y.cpu().numpy().astype(np.float64).transpose(2, 0, 1, 3).reshape(M, 3 * N)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    # head-major input with an in-place residual
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    wo = (0.05 * rng.standard_normal((K, N))).astype(np.float32)
+    bo = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    r = rng.standard_normal((M, N)).astype(np.float32)
+    ref = a.astype(np.float64) @ wo.astype(np.float64) + bo + r
+    bound = 4 * K * 2.0 ** -24 * (np.abs(a.astype(np.float64)) @ np.abs(wo.astype(np.float64))) \
+        + 1e-5 * np.abs(ref) + 1e-6
+    rt = d(r)
+    Kc.linear(d(a.reshape(M, H, D).transpose(1, 0, 2)), d(wo.T), bias=d(bo), residual=rt, out=rt, a_heads=H)
+    torch.cuda.synchronize()
+    got = rt.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_inplace_residual(M):
     """y written over res (h += x W + b, the residual update of a block)."""

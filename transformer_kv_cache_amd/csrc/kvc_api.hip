@@ -757,9 +757,10 @@ kvc_status kvc_paged_decode_step(const kvc_paged_cache *cache, int32_t layer0, i
                      hist_len, scale, o, workspace, workspace_bytes, stream);
 }
 
-kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *wt, int32_t N,
-                          const float *bias, const float *ln_g, const float *ln_b, float ln_eps,
-                          int32_t act, const float *res, float *y, void *stream) {
+kvc_status kvc_linear_f32(const float *x, int32_t a_heads, int32_t M, int32_t K, const float *wt,
+                          int32_t N, const float *bias, const float *ln_g, const float *ln_b,
+                          float ln_eps, int32_t act, const float *res, float *y, int32_t y_qkv_heads,
+                          void *stream) {
   static const char *fn = "kvc_linear_f32";
   if (!x || !wt || !y) return fail(KVC_E_NULL, "%s: x, wt or y is NULL", fn);
   if ((ln_g == nullptr) != (ln_b == nullptr))
@@ -775,6 +776,17 @@ kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *wt,
   if (act != 0 && act != 1) return fail(KVC_E_SHAPE, "%s: act = %d (0 or 1)", fn, act);
   if (ln_g && !(std::isfinite(ln_eps) && ln_eps >= 0.f))
     return fail(KVC_E_SHAPE, "%s: ln_eps must be finite and >= 0", fn);
+  if (a_heads < 0 || (a_heads > 0 && (K % a_heads != 0 || (K / a_heads) % 4 != 0)))
+    return fail(KVC_E_SHAPE, "%s: a_heads = %d must split K = %d into parts of a multiple of 4", fn,
+                a_heads, K);
+  if (a_heads > 0 && ln_g)
+    return fail(KVC_E_UNSUPPORTED, "%s: the layer norm needs the row-major input", fn);
+  if (y_qkv_heads < 0 ||
+      (y_qkv_heads > 0 && (N % (3 * y_qkv_heads) != 0 || (N / (3 * y_qkv_heads)) % 4 != 0)))
+    return fail(KVC_E_SHAPE, "%s: y_qkv_heads = %d must split N = %d into 3 x heads parts of a "
+                "multiple of 4", fn, y_qkv_heads, N);
+  if (y_qkv_heads > 0 && res)
+    return fail(KVC_E_UNSUPPORTED, "%s: a residual needs the row-major output", fn);
   if (!aligned16(x) || !aligned16(wt) || !aligned16(y) || (res && !aligned16(res)) ||
       (ln_g && (((uintptr_t)ln_g & 3u) || ((uintptr_t)ln_b & 3u))))
     return fail(KVC_E_SHAPE, "%s: x, wt, res and y must be 16-byte aligned", fn);
@@ -798,6 +810,8 @@ kvc_status kvc_linear_f32(const float *x, int32_t M, int32_t K, const float *wt,
   a.N = N;
   a.act = act;
   a.ln_eps = ln_eps;
+  a.a_heads = M > 1 ? a_heads : 0;          // one row: every layout is row-major
+  a.y_qkv_heads = M > 1 ? y_qkv_heads : 0;
   hipError_t e = kvc::launch_linear(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   return ok();

@@ -14,6 +14,9 @@
 // Layout: the weight transposed, wt [N][K] (output feature n's K input
 // weights contiguous, packed once per model, the layout kvc_gemm_f32 takes
 // too); x / y / res row-major [M][K or N], M <= 8 rows, K a multiple of 4.
+// As in kvc_gemm_f32, x may come head-major [H][M][K/H] (the attention
+// output) and y may go out in the attention layout [3][H][M][N/(3H)] (q, k,
+// v of the decode call); with one row both are the row-major layout.
 //
 // One input row (the usual decode step, K <= 3072): gemv_kernel, below --
 // each wave holds all of x across its lanes, so it needs no LDS and no
@@ -100,7 +103,16 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   }
   const f32x4 *x4 = reinterpret_cast<const f32x4 *>(a.x);
   f32x4 *xs4 = reinterpret_cast<f32x4 *>(xs);
-  for (int i = tid; i < M * k4; i += 256) xs4[i] = x4[i];
+  if (a.a_heads > 0) {
+    // head-major x: piece q of row m sits in head 4 q / dh, row m of it
+    const int dh4 = k4 / a.a_heads;
+    for (int i = tid; i < M * k4; i += 256) {
+      const int m = i / k4, q = i - m * k4, hh = q / dh4;
+      xs4[i] = x4[((size_t)hh * M + m) * dh4 + (q - hh * dh4)];
+    }
+  } else {
+    for (int i = tid; i < M * k4; i += 256) xs4[i] = x4[i];
+  }
   __syncthreads();
 
   // 1. Layer norm of each x row in LDS: the mean, then the biased variance
@@ -184,7 +196,12 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
         if (lane == r * MR + m && n < N) {
           float y = v + b_add[r];
           if (a.act == 1) y = gelu_tanh(y);
-          a.y[(size_t)m * N + n] = y + r_add[r][m];
+          size_t yi = (size_t)m * N + n;
+          if (a.y_qkv_heads > 0) {  // [3][H][M][dh]: row (which, head) = n / dh
+            const int dh = N / (3 * a.y_qkv_heads), j = n / dh;
+            yi = ((size_t)j * M + m) * dh + (n - j * dh);
+          }
+          a.y[yi] = y + r_add[r][m];
         }
       }
     }

@@ -251,6 +251,8 @@ struct LinearArgs {
   int32_t M, K, N;
   int32_t act;         // 0: none, 1: GELU (tanh form)
   float ln_eps;
+  int32_t a_heads;     // > 0: x is head-major [H][M][K/H]
+  int32_t y_qkv_heads; // > 0: y is [3][H][M][N/(3H)]
 };
 
 // Dense layer of a prompt on the matrix cores (kvc_gemm_f32):

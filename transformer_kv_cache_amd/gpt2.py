@@ -119,22 +119,19 @@ class GPT2:
         empty cache), output projection + residual, LN2 + FC + GELU,
         projection + residual, and LN_f + output projection."""
         N = h.shape[0]
-        d, H, D, p, pt = self.d, self.H, self.D, self.p, self.pt
+        H, D, p, pt = self.H, self.D, self.p, self.pt
         for l in range(self.L):
-            qkv = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
-            if N == 1:
-                # one row: q, k, v are already [H, 1, D] slices of the product
-                q, k, v = (qkv[:, j * d:(j + 1) * d].view(1, 1, H, 1, D) for j in range(3))
-            else:
-                t = qkv.view(N, 3, H, D).permute(1, 2, 0, 3).contiguous()     # [3, H, N, D]
-                q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
+            # q, k, v written straight in the attention layout [3, H, N, D]
+            t = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]),
+                         qkv_heads=H)
+            q, k, v = (t[j].view(1, 1, H, N, D) for j in range(3))
             if P == 0:
                 o = K.attn_prefill(cache, q, k, v, scale=self.scale, layer0=l)
             else:
                 o = K.decode_step(cache, q, k, v, [P], scale=self.scale, layer0=l,
                                   workspace=self._workspace(cache, N))
-            o = o.view(1, d) if N == 1 else o.view(H, N, D).permute(1, 0, 2).reshape(N, d).contiguous()
-            K.linear(o, pt["w_o"][l], p["b_o"][l], residual=h, out=h)
+            # the output projection reads the attention output head-major
+            K.linear(o.view(H, N, D), pt["w_o"][l], p["b_o"][l], residual=h, out=h, a_heads=H)
             f = K.linear(h, pt["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
                          act="gelu")
             K.linear(f, pt["w_pr"][l], p["b_pr"][l], residual=h, out=h)
@@ -147,14 +144,15 @@ class GPT2:
         """One cached decode step for the token ids ``tok`` (int64 [1] on the
         device) at the device position ``hd`` (int32 [1]); every shape and
         argument is fixed, so the step can be captured once and replayed."""
-        d, H, D, p, pt = self.d, self.H, self.D, self.p, self.pt
+        H, D, p, pt = self.H, self.D, self.p, self.pt
         h = K.embed(self.wte, self.wpe, tok, pos=hd)
         for l in range(self.L):
-            qkv = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]))
-            q, k, v = (qkv[:, j * d:(j + 1) * d].view(1, 1, H, 1, D) for j in range(3))
+            t = K.linear(h, pt["w_qkv"][l], p["b_qkv"][l], ln=(p["ln1_g"][l], p["ln1_b"][l]),
+                         qkv_heads=H)
+            q, k, v = (t[j].view(1, 1, H, 1, D) for j in range(3))
             o = K.decode_step_dl(cache, q, k, v, hd, self.T - 1, scale=self.scale, layer0=l,
                                  workspace=self._workspace(cache, 1))
-            K.linear(o.view(1, d), pt["w_o"][l], p["b_o"][l], residual=h, out=h)
+            K.linear(o.view(H, 1, D), pt["w_o"][l], p["b_o"][l], residual=h, out=h, a_heads=H)
             f = K.linear(h, pt["w_fc"][l], p["b_fc"][l], ln=(p["ln2_g"][l], p["ln2_b"][l]),
                          act="gelu")
             K.linear(f, pt["w_pr"][l], p["b_pr"][l], residual=h, out=h)

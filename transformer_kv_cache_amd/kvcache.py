@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 10  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 11  # KVC_ABI_VERSION of the header these signatures follow
 MAX_LINEAR_ROWS = 8  # rows kvc_linear_f32 takes (kMaxLinearRows)
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
@@ -131,7 +131,7 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_paged_decode_step_dl.restype = i32
         lib.kvc_lengths_add.argtypes = [vp, i32, i32, vp]
         lib.kvc_lengths_add.restype = i32
-        lib.kvc_linear_f32.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, f32, i32, vp, vp, vp]
+        lib.kvc_linear_f32.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp, f32, i32, vp, vp, i32, vp]
         lib.kvc_linear_f32.restype = i32
         lib.kvc_gemm_f32.argtypes = [vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]
         lib.kvc_gemm_f32.restype = i32
@@ -681,19 +681,28 @@ def paged_attn_prefill_varlen(cache: PagedKVCache, q, k, v, cu_seqlens, hist_len
 
 
 def linear(x, wt, bias=None, ln=None, act=None, residual=None, out=None, ln_eps=1e-5,
-           stream=None):
+           a_heads: int = 0, qkv_heads: int = 0, stream=None):
     """y = act(LN(x) wt^T + bias) + residual for the few rows of a decode step
-    (fp32; x [M, K] with M <= 8, wt [N, K]: the weight transposed).  ``ln``
-    is (gain, shift) or None; ``act`` is None or "gelu" (tanh form); ``out``
-    may be ``residual``."""
+    (fp32; x [M, K] with M <= 8, or [H, M, K/H] head-major with ``a_heads`` =
+    H; wt [N, K]: the weight transposed).  ``ln`` is (gain, shift) or None;
+    ``act`` is None or "gelu" (tanh form); with ``qkv_heads`` = H the result
+    is laid out [3, H, M, N/(3H)] (q, k, v of the decode call); ``out`` may
+    be ``residual``."""
     for name, t in (("x", x), ("wt", wt)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
-                or not t.is_contiguous() or t.dim() != 2:
-            raise ValueError(f"{name} must be a contiguous 2-D fp32 CUDA tensor")
-    M, K = x.shape
-    N, K2 = wt.shape
-    if K2 != K:
-        raise ValueError(f"x has {K} features, wt has {K2} columns")
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor")
+    if wt.dim() != 2:
+        raise ValueError("wt must be [N, K]")
+    N, K = wt.shape
+    if a_heads:
+        if x.dim() != 3 or x.shape[0] != a_heads or x.shape[0] * x.shape[2] != K:
+            raise ValueError(f"x must be [{a_heads}, M, {K // max(a_heads, 1)}]")
+        M = x.shape[1]
+    else:
+        if x.dim() != 2 or x.shape[1] != K:
+            raise ValueError(f"x must be [M, {K}]")
+        M = x.shape[0]
 
     def vec(name, t, n):
         if t is None:
@@ -705,16 +714,17 @@ def linear(x, wt, bias=None, ln=None, act=None, residual=None, out=None, ln_eps=
     bias = vec("bias", bias, N)
     g, b = (None, None) if ln is None else (vec("ln gain", ln[0], K), vec("ln shift", ln[1], K))
     residual = vec("residual", residual, M * N)
+    shape = (3, qkv_heads, M, N // (3 * qkv_heads)) if qkv_heads else (M, N)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
     vec("out", out, M * N)
     codes = {None: 0, "gelu": 1}
     if act not in codes:
         raise ValueError(f"act must be None or 'gelu', got {act!r}")
     ptr = lambda t: None if t is None else t.data_ptr()
-    _check(library().kvc_linear_f32(x.data_ptr(), M, K, wt.data_ptr(), N, ptr(bias), ptr(g), ptr(b),
-                                    float(ln_eps), codes[act], ptr(residual), out.data_ptr(),
-                                    _stream(x.device, stream)))
+    _check(library().kvc_linear_f32(x.data_ptr(), a_heads, M, K, wt.data_ptr(), N, ptr(bias), ptr(g),
+                                    ptr(b), float(ln_eps), codes[act], ptr(residual), out.data_ptr(),
+                                    qkv_heads, _stream(x.device, stream)))
     return out
 
 
