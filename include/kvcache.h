@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 11
+#define KVC_ABI_VERSION 12
 
 typedef enum {
   KVC_OK = 0,
@@ -469,14 +469,28 @@ kvc_status kvc_linear_f32(const float *x, int32_t a_heads, int32_t M, int32_t K,
  *        layout [3, H, M, N/(3H)] (q, k, v for kvc_attn_prefill /
  *        kvc_decode_step without a permute); N/(3H) a multiple of 4, and no
  *        res then.
+ *   workspace : optional device scratch of at least
+ *        kvc_gemm_workspace_bytes(M, K, N) bytes, 256-byte aligned,
+ *        zero-filled once before its first use (every call leaves its
+ *        counters zero again); calls sharing one must not overlap.  With it,
+ *        a product whose 64 x 64 output tiles are too few to fill the chip
+ *        splits K over several workgroups per tile, the last of which sums
+ *        the partial tiles in a fixed order (the result does not depend on
+ *        timing).  NULL (or a size of 0 from the query): no split.
  *   K a positive multiple of 64, N >= 1, M >= 0 (0: no-op); a, wt, res, y
  *   16-byte aligned, y not overlapping a.  Errors: KVC_E_NULL, KVC_E_SHAPE
  *   (sizes, layouts, alignment, overlap), KVC_E_UNSUPPORTED (too large for
- *   one launch, a residual with the attention layout), KVC_E_HIP. */
+ *   one launch, a residual with the attention layout), KVC_E_WORKSPACE (a
+ *   workspace smaller than the query's answer), KVC_E_HIP. */
 kvc_status kvc_gemm_f32(const float *a, int32_t a_heads, int32_t M, int32_t K,
                         const float *wt, int32_t N, const float *bias,
                         int32_t act, const float *res, float *y,
-                        int32_t y_qkv_heads, void *stream);
+                        int32_t y_qkv_heads, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kvc_gemm_f32 uses for an M x K x N product on the current
+ * device (0: it would not split K; also 0 for invalid sizes). */
+size_t kvc_gemm_workspace_bytes(int32_t M, int32_t K, int32_t N);
 
 /* layernorm_f32: y[m] = (x[m] - mean) / sqrt(var + eps) * g + b over the K
  * features of each row (biased variance), the GPT-2 block's pre-norm.

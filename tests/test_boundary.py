@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 11
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 12
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -463,9 +463,9 @@ def test_linear_layer_norm_limits(lib):
     assert call(1, 8, gg=h.ptr(offset=2)) == E_SHAPE   # gain not 4-byte aligned
     # the gemm's limits
     gemm = lambda **kw: lib.kvc_gemm_f32(*[{**dict(a=x, ah=0, M=4, K=64, wt=w, N=8, bias=None, act=0,
-                                                  res=None, y=y, qh=0, s=None), **kw}[k]
+                                                  res=None, y=y, qh=0, ws=None, wsb=0, s=None), **kw}[k]
                                            for k in ("a", "ah", "M", "K", "wt", "N", "bias", "act",
-                                                     "res", "y", "qh", "s")])
+                                                     "res", "y", "qh", "ws", "wsb", "s")])
     assert gemm(M=0) == OK
     assert gemm(K=96) == E_SHAPE                   # not a multiple of 64
     assert gemm(N=0) == E_SHAPE
@@ -474,6 +474,9 @@ def test_linear_layer_norm_limits(lib):
     assert gemm(qh=1, N=12, res=y) == E_UNSUPPORTED
     assert gemm(wt=None) == E_NULL
     assert gemm(y=x) == E_SHAPE                    # output over the input
+    # the split-K workspace query: 0 for sizes the call would refuse
+    assert lib.kvc_gemm_workspace_bytes(0, 768, 768) == 0
+    assert lib.kvc_gemm_workspace_bytes(4, 96, 8) == 0
     ln = lambda **kw: lib.kvc_layernorm_f32(*[{**dict(x=x, M=2, K=64, g=g, b=b, eps=1e-5, y=y, s=None),
                                                **kw}[k] for k in ("x", "M", "K", "g", "b", "eps", "y", "s")])
     assert ln(M=0) == OK

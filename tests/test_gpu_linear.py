@@ -163,6 +163,52 @@ def test_gemm_epilogues(act, res, bias):
     run_gemm(200, 768, 3072 if act else 768, act=act, res=res, seed=11 + act + 2 * res, bias=bias)
 
 
+@pytest.mark.parametrize("M,K,N,act,res,qkv", [(512, 3072, 768, False, True, 0), (128, 3072, 768, False, False, 0),
+                                               (128, 768, 2304, False, False, 12), (1, 768, 4, True, False, 0),
+                                               (200, 768, 768, True, True, 0), (65, 640, 100, False, True, 0)])
+def test_gemm_split_k(M, K, N, act, res, qkv):
+    """Products with few output tiles split K over several workgroups per
+    tile (the last sums the partials): against the float64 product, bitwise
+    repeatable over calls, with the workspace's counters back at zero, and
+    the same within the bound as the unsplit product."""
+    from transformer_kv_cache_amd import kvcache as Kc
+    need = int(Kc.library().kvc_gemm_workspace_bytes(M, K, N))
+    rng = np.random.default_rng(M + K + N)
+    a = (rng.standard_normal((M, K)) * 1.5).astype(np.float32)
+    w = (0.05 * rng.standard_normal((K, N))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    r = rng.standard_normal((M, N)).astype(np.float32)
+    ref = a.astype(np.float64) @ w.astype(np.float64) + b
+    if act:
+        ref = G.gelu(ref)
+    if res:
+        ref = ref + r
+    bound = 4 * K * 2.0 ** -24 * (np.abs(a.astype(np.float64)) @ np.abs(w.astype(np.float64))) \
+        + 1e-5 * np.abs(ref) + 1e-6
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    ws = Kc._aligned_workspace(max(need, 256), "cuda")
+    print(f"[gemm split] M={M} K={K} N={N} workspace={need}", flush=True)
+    outs = []
+    for rep in range(2):
+        y = Kc.gemm(d(a), d(w.T), bias=d(b), act="gelu" if act else None, residual=d(r) if res else None,
+                    qkv_heads=qkv, workspace=ws)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        if qkv:
+            got = got.transpose(2, 0, 1, 3).reshape(M, N)
+        outs.append(got)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.all(np.abs(outs[0].astype(np.float64) - ref) <= bound)
+    assert not ws[:2048].any().item(), "arrival counters left nonzero"
+    y1 = Kc.gemm(d(a), d(w.T), bias=d(b), act="gelu" if act else None, residual=d(r) if res else None,
+                 qkv_heads=qkv, workspace=None).cpu().numpy()
+    if qkv:
+        y1 = y1.transpose(2, 0, 1, 3).reshape(M, N)
+    assert np.all(np.abs(y1.astype(np.float64) - ref) <= bound)
+    if M <= 128:
+        assert need > 0  # these shapes do split on this GPU
+
+
 def test_gemm_inplace_residual():
     """y written over res (h += a W + b)."""
     run_gemm(300, 3072, 768, act=False, res=True, seed=13, inplace=True)

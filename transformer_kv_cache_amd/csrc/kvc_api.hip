@@ -817,9 +817,15 @@ kvc_status kvc_linear_f32(const float *x, int32_t a_heads, int32_t M, int32_t K,
   return ok();
 }
 
+size_t kvc_gemm_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+  if (M < 1 || K < 64 || N < 1 || K % 64 != 0) return 0;
+  const int splits = merge_in_launch_supported() ? kvc::gemm_splits(M, K, N) : 1;
+  return kvc::gemm_workspace_bytes(M, K, N, splits);
+}
+
 kvc_status kvc_gemm_f32(const float *a, int32_t a_heads, int32_t M, int32_t K, const float *wt,
                         int32_t N, const float *bias, int32_t act, const float *res, float *y,
-                        int32_t y_qkv_heads, void *stream) {
+                        int32_t y_qkv_heads, void *workspace, size_t workspace_bytes, void *stream) {
   static const char *fn = "kvc_gemm_f32";
   if (M < 0 || K < 64 || N < 1 || K % 64 != 0)
     return fail(KVC_E_SHAPE, "%s: M = %d, K = %d, N = %d (need M >= 0, K a positive multiple of 64, "
@@ -861,6 +867,23 @@ kvc_status kvc_gemm_f32(const float *a, int32_t a_heads, int32_t M, int32_t K, c
   g.act = act;
   g.a_heads = a_heads;
   g.y_qkv_heads = y_qkv_heads;
+  g.splits = 1;
+  g.tiles_m = (M + 63) / 64;
+  g.tiles_n = (N + 63) / 64;
+  if (workspace) {
+    // split K when the output tiles alone leave the chip idle
+    const int splits = merge_in_launch_supported() ? kvc::gemm_splits(M, K, N) : 1;
+    const size_t need = kvc::gemm_workspace_bytes(M, K, N, splits);
+    if (workspace_bytes < need)
+      return fail(KVC_E_WORKSPACE, "%s: workspace of %zu bytes, need %zu (kvc_gemm_workspace_bytes)", fn,
+                  workspace_bytes, need);
+    if ((uintptr_t)workspace & 255u) return fail(KVC_E_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+    if (splits > 1) {
+      g.splits = splits;
+      g.ctr = (uint64_t *)workspace;
+      g.part = (float *)((char *)workspace + kvc::kGemmCounterBytes);
+    }
+  }
   hipError_t e = kvc::launch_gemm(g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   return ok();

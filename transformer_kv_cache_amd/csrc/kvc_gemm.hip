@@ -33,6 +33,7 @@
 // N are clamped on load and skipped on store.
 //
 // Roofline: MFMA (fp32 matrix peak 157.3 TFLOP/s), 2 M N K flops per call.
+#include "kvc_device.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -75,9 +76,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * GM, n0 = blockIdx.x * GN;
   const int M = g.M, N = g.N, K = g.K;
   const int nt = K / GK;
+  // Output tile and K range.  Without a split: the 2-D grid's tile, all of
+  // K.  With one: a 1-D grid in which workgroup i runs on XCD i % 8 and the
+  // S splits of a tile share that XCD (their partials meet in its L2):
+  // i = 8 (S u + s) + x for tile 8 u + x, split s.
+  const int S = g.splits;
+  int tile = 0, split = 0, m0, n0;
+  if (S > 1) {
+    const int i = blockIdx.x, x = i & 7, j = i >> 3;
+    split = j % S;
+    tile = (j / S) * 8 + x;
+    if (tile >= g.tiles_m * g.tiles_n) return;  // padding to a multiple of 8 tiles
+    m0 = (tile / g.tiles_n) * GM;
+    n0 = (tile % g.tiles_n) * GN;
+  } else {
+    m0 = blockIdx.y * GM;
+    n0 = blockIdx.x * GN;
+  }
+  const int tb = (int)((long long)split * nt / S), te = (int)((long long)(split + 1) * nt / S);
 
   // This thread's share of a tile: features k0 + lc .. +3 of rows lr + 16 i
   // (i < 4) of a and of wt, one 16-byte vector each.  Row pointers are
@@ -142,7 +160,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     // the last tile the staging fills an unused buffer and the loads repeat
     // the last tile
     stage(r_next, buf ^ 1);
-    load(t + 3 < nt ? t + 3 : nt - 1, r_next);
+    load(t + 3 < te ? t + 3 : te - 1, r_next);
 #pragma unroll
     for (int s = 0; s < 32; ++s)
       acc[s % CHAINS] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[s >> 2][s & 3], xw[s >> 2][s & 3],
@@ -158,19 +176,51 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
     __syncthreads();
   };
-  // prologue: tile 0 staged, tiles 1 and 2 in flight
-  load(0, 0);
+  // prologue: the first tile staged, the next two in flight
+  load(tb, 0);
   stage(0, 0);
-  if (1 < nt) load(1, 1);
-  if (2 < nt) load(2, 0);
+  if (tb + 1 < te) load(tb + 1, 1);
+  if (tb + 2 < te) load(tb + 2, 0);
   __syncthreads();
-  for (int t = 0; t < nt; t += 2) {
+  for (int t = tb; t < te; t += 2) {
     iteration(t, 0, 1);
-    if (t + 1 >= nt) break;
+    if (t + 1 >= te) break;
     iteration(t + 1, 1, 0);
   }
 #pragma unroll
   for (int c = 1; c < CHAINS; ++c) acc[0] += acc[c];
+
+  bool misplaced = false;
+  if (S > 1) {
+    // This split's partial tile, lane-contiguous per accumulator register.
+    const size_t tiles = (size_t)g.tiles_m * g.tiles_n;
+    float *pp = g.part + ((size_t)split * tiles + tile) * (GM * GN) + wave * 1024 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pp[64 * r] = acc[0][r];
+    // every wave's stores acknowledged by the L2 before the arrival
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __shared__ int arrival;
+    __syncthreads();
+    if (tid == 0) {
+      bool mis = false;
+      const bool last = arrive_last(g.ctr + tile, S, mis);
+      arrival = last ? (mis ? 2 : 1) : 0;
+    }
+    __syncthreads();
+    const int arr = arrival;
+    if (arr == 0) return;  // not the last split of this tile
+    misplaced = arr == 2;
+    // Sum the partials in split order (fixed, whichever split came last),
+    // read through the L2 the writers stored to.
+    f32x16 sum = f32x16{};
+    for (int sp = 0; sp < S; ++sp) {
+      const float *q = g.part + ((size_t)sp * tiles + tile) * (GM * GN) + wave * 1024 + lane;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum[r] += state_load(q + 64 * r);
+    }
+    acc[0] = sum;
+    if (tid == 0) reset_counter(g.ctr + tile);
+  }
 
   // Epilogue: accumulator r holds row 8 (r / 4) + 4 half + r % 4 of the
   // wave's quarter, column col.
@@ -184,7 +234,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       float v = acc[0][r] + b;
       if (g.act == 1) v = gelu_tanh(v);
       if (g.res) v += g.res[(size_t)m * N + n];
-      g.y[y_index(g, m, n)] = v;
+      // splits from more than one XCD (never expected): NaN, not a wrong sum
+      g.y[y_index(g, m, n)] = misplaced ? __builtin_nanf("") : v;
     }
   }
 }
@@ -243,9 +294,49 @@ __global__ __launch_bounds__(256) void layernorm_kernel(LayerNormArgs p) {
 
 }  // namespace
 
+// A K split when the output tiles leave most CUs idle (at most 128 tiles):
+// the split count S <= 8 (the last workgroup reads every partial back), at
+// least two K tiles per split, that minimises the K tiles the busiest CU
+// runs, ceil(T S / 256) ceil(nt / S), plus one tile's worth for the
+// reduction when S > 1 (ties: fewer splits).  Measured (fp32, M = 128):
+// 3072 -> 768 70 -> 24 us, 768 -> 2304 25 -> 19 us, 768 -> 3072 25 -> 21 us.
+// With more tiles the product is bound by the operand traffic of 64 x 64
+// tiles, which a split does not reduce (M = 1000, 192 tiles: 3072 -> 768 71
+// -> 69 us, 768 -> 768 25.5 -> 33 us at S = 4), so none is taken.
+int gemm_splits(int M, int K, int N) {
+  const long long T = (long long)((M + GM - 1) / GM) * ((N + GN - 1) / GN);
+  const int nt = K / GK;
+  if (T > 128 || nt < 4) return 1;
+  int best = 1;
+  long long best_cost = nt;
+  for (int sp = 2; sp <= 8 && sp <= nt / 2; ++sp) {
+    const long long cost = (T * sp + 255) / 256 * ((nt + sp - 1) / sp) + 1;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+// Workspace: a fixed block of counters (a split happens only below 256
+// tiles), so that calls of different shapes can share one workspace without
+// one call's partials landing on another's counters; then the partials.
+size_t gemm_workspace_bytes(int M, int K, int N, int splits) {
+  (void)K;
+  if (splits <= 1) return 0;
+  const size_t T = (size_t)((M + GM - 1) / GM) * ((N + GN - 1) / GN);
+  return kGemmCounterBytes + (size_t)splits * T * GM * GN * sizeof(float);
+}
+
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
-  const dim3 grid((unsigned)((g.N + GN - 1) / GN), (unsigned)((g.M + GM - 1) / GM));
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, g);
+  if (g.splits > 1) {
+    const unsigned tiles8 = (unsigned)((g.tiles_m * g.tiles_n + 7) / 8 * 8);
+    hipLaunchKernelGGL(gemm_kernel, dim3(tiles8 * (unsigned)g.splits), dim3(256), 0, s, g);
+  } else {
+    const dim3 grid((unsigned)((g.N + GN - 1) / GN), (unsigned)((g.M + GM - 1) / GM));
+    hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 

@@ -267,7 +267,23 @@ struct GemmArgs {
   int32_t act;          // 0: none, 1: GELU (tanh form)
   int32_t a_heads;      // 0: row-major a
   int32_t y_qkv_heads;  // 0: row-major y
+  // Split of K over `splits` workgroups per output tile (1: none).  Each
+  // writes its partial tile to part[split][tile][64 x 64]; the last one to
+  // arrive on the tile's counter (ctr[tile], zero before the call and left
+  // zero) sums them in split order and applies the epilogue.
+  int32_t splits;
+  int32_t tiles_m, tiles_n;
+  float *part;
+  uint64_t *ctr;
 };
+
+// K split of a kvc_gemm_f32 call (1 when the output tiles alone fill the
+// chip) and the workspace it needs (0 without a split): kGemmCounterBytes of
+// arrival counters (one per tile; splits only happen below 256 tiles), then
+// the partial tiles.
+constexpr size_t kGemmCounterBytes = 256 * sizeof(uint64_t);
+int gemm_splits(int M, int K, int N);
+size_t gemm_workspace_bytes(int M, int K, int N, int splits);
 
 // Row-wise layer norm (kvc_layernorm_f32): y = (x - mean) / sqrt(var + eps)
 // * g + b over the K features of each of M rows.

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 11  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 12  # KVC_ABI_VERSION of the header these signatures follow
 MAX_LINEAR_ROWS = 8  # rows kvc_linear_f32 takes (kMaxLinearRows)
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
@@ -133,8 +133,10 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_lengths_add.restype = i32
         lib.kvc_linear_f32.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp, f32, i32, vp, vp, i32, vp]
         lib.kvc_linear_f32.restype = i32
-        lib.kvc_gemm_f32.argtypes = [vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]
+        lib.kvc_gemm_f32.argtypes = [vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp, ctypes.c_size_t, vp]
         lib.kvc_gemm_f32.restype = i32
+        lib.kvc_gemm_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.kvc_gemm_workspace_bytes.restype = ctypes.c_size_t
         lib.kvc_layernorm_f32.argtypes = [vp, i32, i32, vp, vp, f32, vp, vp]
         lib.kvc_layernorm_f32.restype = i32
         lib.kvc_embed_f32.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, vp]
@@ -735,13 +737,48 @@ def _f32_matrix(name, t):
     return t
 
 
+_gemm_ws = {}
+_gemm_ws_retired = []
+
+
+def gemm_workspace(M: int, K: int, N: int, device, stream=None):
+    """The zero-filled split-K workspace kvc_gemm_f32 uses for this product:
+    one per device, grown as needed (a retired buffer is kept alive, since
+    queued work or a captured graph may still use it) and shared by every
+    product that does not bring its own -- each call leaves its counters
+    zero, so calls that follow one another may share it; products on
+    different streams that can overlap must each pass their own.  None when
+    the product does not split.  Not grown during graph capture: run the
+    largest product once before capturing, or pass a workspace."""
+    need = int(library().kvc_gemm_workspace_bytes(M, K, N))
+    if need == 0:
+        return None
+    device = torch.device(device)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    ws = _gemm_ws.get(device)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("gemm: run the product once before capture, or pass a workspace")
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        with torch.cuda.stream(s):
+            ws = _aligned_workspace(max(need, 0 if ws is None else ws.numel()), device)
+        if device in _gemm_ws:
+            _gemm_ws_retired.append(_gemm_ws[device])
+        _gemm_ws[device] = ws
+    return ws
+
+
 def gemm(a, wt, bias=None, act=None, residual=None, out=None, a_heads: int = 0,
-         qkv_heads: int = 0, stream=None):
+         qkv_heads: int = 0, workspace="auto", stream=None):
     """y = act(a wt^T + bias) + residual on the matrix cores (fp32), for
     prompt-sized inputs.  a is [M, K], or [H, M, K/H] head-major with
     ``a_heads`` = H; wt is the weight transposed, [N, K].  With ``qkv_heads``
     = H the result is laid out [3, H, M, N/(3H)] (q, k, v for the attention
-    calls).  ``out`` may be ``residual``."""
+    calls).  ``out`` may be ``residual``.  ``workspace``: "auto" (the
+    device's shared split-K workspace, see gemm_workspace), None (no split)
+    or a zero-filled uint8 tensor of at least kvc_gemm_workspace_bytes(M, K,
+    N) bytes."""
     _f32_matrix("a", a)
     _f32_matrix("wt", wt)
     if wt.dim() != 2:
@@ -768,9 +805,14 @@ def gemm(a, wt, bias=None, act=None, residual=None, out=None, a_heads: int = 0,
     if act not in codes:
         raise ValueError(f"act must be None or 'gelu', got {act!r}")
     ptr = lambda t: None if t is None else t.data_ptr()
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        workspace = gemm_workspace(M, K, N, a.device, stream) if M > 0 else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().kvc_gemm_f32(a.data_ptr(), a_heads, M, K, wt.data_ptr(), N, ptr(bias),
                                   codes[act], ptr(residual), out.data_ptr(), qkv_heads,
-                                  _stream(a.device, stream)))
+                                  ptr(workspace), ws_bytes, _stream(a.device, stream)))
     return out
 
 
