@@ -32,6 +32,16 @@
 // with the MFMAs, with one barrier per tile.  Rows past M and columns past
 // N are clamped on load and skipped on store.
 //
+// Split K.  A product with few output tiles (a short prompt: M = 128 gives
+// 24-96 tiles for 256 CUs) leaves most CUs idle while each workgroup walks
+// all of K.  Given a workspace, such a product runs S workgroups per tile,
+// each over a contiguous 1/S of the K tiles; each stores its partial tile,
+// waits until the L2 has it and counts itself on the tile's arrival counter
+// (the same counter as the decode step's in-launch merge, XCD check
+// included); the last to arrive sums the S partials in split order -- the
+// same sum whichever split came last -- applies the epilogue and clears the
+// counter.  The 1-D grid puts every split of a tile on one XCD.
+//
 // Roofline: MFMA (fp32 matrix peak 157.3 TFLOP/s), 2 M N K flops per call.
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -319,9 +329,10 @@ int gemm_splits(int M, int K, int N) {
   return best;
 }
 
-// Workspace: a fixed block of counters (a split happens only below 256
-// tiles), so that calls of different shapes can share one workspace without
-// one call's partials landing on another's counters; then the partials.
+// Workspace: a fixed block of 256 counters (a split happens only at 128
+// tiles or fewer), so that calls of different shapes can share one workspace
+// without one call's partials landing on another's counters; then the
+// partials.
 size_t gemm_workspace_bytes(int M, int K, int N, int splits) {
   (void)K;
   if (splits <= 1) return 0;
