@@ -2,6 +2,7 @@
 // argument validation, launch geometry and the kernel launches.  Every check
 // runs before the first enqueue, so a rejected call leaves device memory
 // untouched and never touches the HIP runtime.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -151,14 +152,17 @@ VectorPlan plan_vector(int units, int max_keys, int rows_per_load, bool merge_su
 // in-launch merge needs every split of a row on one XCD, which the
 // round-robin dispatch gives when the count divides 8.
 bool merge_in_launch_supported() {
-  static int cache[64];  // 0 unknown, 1 supported, 2 not
+  static std::atomic<int> cache[64];  // 0 unknown, 1 supported, 2 not (calls may come from any thread)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
-  if (dev < 64 && cache[dev]) return cache[dev] == 1;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c) return c == 1;
+  }
   int n = 0;
   const bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess &&
                   n >= 1 && n <= 8 && (8 % n) == 0;
-  if (dev < 64) cache[dev] = ok ? 1 : 2;
+  if (dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok;
 }
 
