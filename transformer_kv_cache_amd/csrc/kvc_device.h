@@ -58,25 +58,32 @@ __device__ __forceinline__ float xor_combine(float x) {
 
 // ---- split-state merge shared by the split kernels and the combine pass ----
 
-// Loads of split states written by other workgroups of this launch: they
-// bypass the CU's L1 (which may hold a stale copy of a line shared with
-// another row's states) and are served by the L2 the writers stored to.
+// Reads of split states written by other workgroups of the same launch.
+// A workgroup-scope load is coherent only within the workgroup, so the CU's
+// L1 may serve it from a copy of the line taken earlier.  Partial outputs
+// are whole lines of one (split, row), read once by the row's one merging
+// workgroup after their writers finished, so no earlier copy can exist; the
+// (max, sum) pairs of 16 rows share a line, so those are read by an atomic
+// (an add of 0), which the L2 the writers stored to performs.
 __device__ __forceinline__ float state_load(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void state_load_ml(const float *p, float &m, float &l) {
-  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-  m = __uint_as_float((uint32_t)u);
-  l = __uint_as_float((uint32_t)(u >> 32));
+__device__ __forceinline__ uint64_t state_fetch_ml(const float *p) {
+  // The zero is hidden from the compiler, which would otherwise turn the
+  // no-op atomic into a plain load.
+  uint64_t zero = 0;
+  asm volatile("" : "+v"(zero));
+  return __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), zero, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merge of a query row's split states into the running state (M, L, o) of
 // one wave (lane j holds output elements j, j + 64, ...):
 //   o = sum_s 2^(m_s - M') o_s + 2^(M - M') o,  L likewise,  M' = max(M, m_s)
 // over splits 0 .. nsplit-1, in chunks of CH whose loads are all issued
-// before any is used.  The fused kernel's last workgroup and combine_kernel
-// both run exactly this, so their outputs are bit-identical.
+// before any is used (lane t < CH fetches split s0 + t's pair, which every
+// lane then takes from it).  The fused kernel's last workgroup and
+// combine_kernel both run exactly this, so their outputs are bit-identical.
 template <int D>
 __device__ __forceinline__ void merge_states(const float *ws_o, const float *ws_ml, int64_t ws_rows,
                                              int64_t row, int nsplit, int lane, float &M, float &L,
@@ -85,15 +92,23 @@ __device__ __forceinline__ void merge_states(const float *ws_o, const float *ws_
   constexpr int CH = 16;
   for (int s0 = 0; s0 < nsplit; s0 += CH) {
     float mv[CH], lv[CH], ov[CH][EPL];
+    uint64_t ml = 0;
+    if (lane < CH && s0 + lane < nsplit)
+      ml = state_fetch_ml(ws_ml + ((size_t)(s0 + lane) * (size_t)ws_rows + (size_t)row) * 2);
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
       const int sp = (s0 + t < nsplit) ? s0 + t : nsplit - 1;
       const size_t ws = (size_t)sp * (size_t)ws_rows + (size_t)row;
-      state_load_ml(ws_ml + ws * 2, mv[t], lv[t]);
 #pragma unroll
       for (int j = 0; j < EPL; ++j) ov[t][j] = state_load(ws_o + ws * D + lane + 64 * j);
     }
     __builtin_amdgcn_sched_barrier(0);
+    const uint32_t ml_lo = (uint32_t)ml, ml_hi = (uint32_t)(ml >> 32);
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      mv[t] = __uint_as_float(__builtin_amdgcn_readlane(ml_lo, t));
+      lv[t] = __uint_as_float(__builtin_amdgcn_readlane(ml_hi, t));
+    }
     float Mc = M;
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
