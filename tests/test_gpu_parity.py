@@ -352,6 +352,33 @@ def test_repeated_calls_reuse_workspace_bitwise(n_layers):
     assert np.max(np.abs(outs[0] - run_oracle(w)[0][0][:n_layers])) <= TOL["f32"]
 
 
+def test_in_launch_merge_many_inputs_bitwise():
+    """The one-launch merge, run back to back on 48 different query sets (so
+    that many merging workgroups read split states other workgroups of the
+    same launch have just stored), gives bit for bit the two-launch form's
+    output every time; the first is also checked against the oracle."""
+    from transformer_kv_cache_amd import kvcache as K
+    w = synth.decode_12layer(1000, seed=41)
+    q0, k, v = w.steps[0]
+    cache = K.KVCache(12, 1, 12, 1024, 64, torch.float32, k=to_dev(w.k_cache), v=to_dev(w.v_cache))
+    K.append(cache, to_dev(k), to_dev(v), w.hist)
+    ws_one = K.new_decode_workspace(cache, 12, 12, 1)
+    ws_two = K.new_decode_workspace(cache, 12, 12, 1)
+    rng = np.random.default_rng(41)
+    qs = [q0] + [rng.standard_normal(q0.shape).astype(np.float32) for _ in range(47)]
+    one, two = [], []
+    for q in qs:
+        qd = to_dev(q)
+        one.append(K.attn_decode(cache, qd, w.hist, workspace=ws_one))
+        o = K.decode_split(cache, qd, w.hist, workspace=ws_two)
+        K.decode_combine(cache, qd, w.hist, out=o, workspace=ws_two)
+        two.append(o)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(one, two)):
+        assert np.array_equal(bits(to_host(a)), bits(to_host(b))), f"query set {i}"
+    assert np.max(np.abs(to_host(one[0]) - run_oracle(w)[0][0])) <= TOL["f32"]
+
+
 def test_capacity_error_leaves_cache_untouched():
     from transformer_kv_cache_amd import kvcache as K
     w = synth.decode_12layer(1023, seed=1)
