@@ -12,10 +12,6 @@
 
 #include "kvc_internal.h"
 
-namespace kvc {
-int prefill_query_tile();
-}
-
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -166,6 +162,30 @@ bool merge_in_launch_supported() {
   return ok;
 }
 
+// Compute units of the current device (read once per device; 0 if the
+// runtime does not say, which makes every prefill take key split 1).
+int device_cus() {
+  static std::atomic<int> cache[64];  // 0 unknown, else CUs + 1
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c) return c - 1;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+  if (dev < 64) cache[dev].store(n + 1, std::memory_order_relaxed);
+  return n;
+}
+
+// Key split of a prefill call: from its grid at key split 1 (the first batch
+// slice's), see kvc::prefill_key_split.
+int prefill_ks(const kvc_cache *cache, int32_t n_layers, int32_t Hq, int max_len) {
+  const long long nb = cache->B < kvc::kMaxBatchPerLaunch ? cache->B : kvc::kMaxBatchPerLaunch;
+  const long long wg1 = (long long)n_layers * Hq * ((max_len + 127) / 128) * nb;
+  return kvc::prefill_key_split(cache->dtype, cache->D, wg1, device_cus());
+}
+
 // Shared by kvc_append and kvc_paged_append (pg.block_table set: `cache` is
 // the logical view of the pools, Tmax = max_blocks * block_size).
 kvc_status append_impl(const char *fn, const kvc_cache *cache, const kvc::PagedGeom &pg,
@@ -291,7 +311,9 @@ kvc_status varlen_impl(const char *fn, const kvc_cache *cache, const kvc::PagedG
     return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
   int max_len = 0;
   for (int b = 0; b < cache->B; ++b) max_len = lens[b] > max_len ? lens[b] : max_len;
-  const int64_t tiles = (max_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+  const int ks = prefill_ks(cache, n_layers, Hq, max_len);
+  const int bm = kvc::prefill_query_tile(ks);
+  const int64_t tiles = (max_len + bm - 1) / bm;
   if (tiles > 65535 || T * Hq >= 4294967296LL)
     return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or tokens for one launch", fn);
 
@@ -317,8 +339,8 @@ kvc_status varlen_impl(const char *fn, const kvc_cache *cache, const kvc::PagedG
       if (lens[b] > slice_len) slice_len = lens[b];
       if (hist_len[b] > 0 && lens[b] > 0) history = true;
     }
-    a.q_tiles = (slice_len + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, history, (hipStream_t)stream);
+    a.q_tiles = (slice_len + bm - 1) / bm;
+    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, history, ks, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
@@ -646,7 +668,9 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_la
   if (!q || !k || !v || !o) return fail(KVC_E_NULL, "%s: q, k, v or o is NULL", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(KVC_E_SHAPE, "%s: q / k / v / o must be 16-byte aligned", fn);
-  const int64_t tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
+  const int ks = prefill_ks(cache, n_layers, Hq, S);
+  const int bm = kvc::prefill_query_tile(ks);
+  const int64_t tiles = (S + bm - 1) / bm;
   if (tiles > 65535 || (int64_t)cache->B * Hq * S >= 4294967296LL)
     return fail(KVC_E_UNSUPPORTED, "%s: too many query tiles or rows for one launch", fn);
 
@@ -667,8 +691,8 @@ kvc_status kvc_attn_prefill(const kvc_cache *cache, int32_t layer0, int32_t n_la
       a.q_row0[i] = (uint32_t)((int64_t)(b0 + i) * Hq * S);
       a.kv_row0[i] = (uint32_t)((int64_t)(b0 + i) * cache->Hkv * S);
     }
-    a.q_tiles = (S + kvc::prefill_query_tile() - 1) / kvc::prefill_query_tile();
-    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, false, (hipStream_t)stream);
+    a.q_tiles = (S + bm - 1) / bm;
+    hipError_t e = kvc::launch_prefill(a, cache->dtype, cache->D, false, ks, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();

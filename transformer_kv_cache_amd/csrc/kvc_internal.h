@@ -317,7 +317,12 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
 hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, int ks, hipStream_t s);
+// Key split (1 or 2) of a prefill call whose grid at key split 1 has
+// `workgroups` workgroups, on `cus` compute units; query rows per workgroup
+// at key split ks.
+int prefill_key_split(int dtype, int D, long long workgroups, int cus);
+int prefill_query_tile(int ks);
 
 // Geometry shared by kvc_decode_workspace_bytes and the decode launchers.
 // One query row per KV head runs on the vector kernel; a few rows with

@@ -35,6 +35,12 @@
 //   bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV product
 //         (and for the row sum), fp32 accumulation.
 //   fp32: v_mfma_f32_32x32x2_f32, everything in fp32 (no reduced precision).
+// Key split (fp32 at D = 64 on small grids): the workgroup owns 64 new tokens
+// instead, two row groups of 32, and the two waves of a row group take the
+// two 32-key halves of every tile, each with its own online-softmax state;
+// at the end one hands its (max, sum, output) to the other through LDS,
+// which rescales both to the larger max and adds them.  That halves the
+// matrix work on a workgroup's longest chain for the same tile staging.
 // Tiles above the diagonal are never loaded; a wave skips key tiles that lie
 // entirely above its own 32 rows.  Grid order puts the longest (last) query
 // tiles of every sequence first, and with a (layer, head) count that is a
@@ -53,7 +59,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128;  // query rows per workgroup (32 per wave)
 constexpr int BN = 64;   // keys per tile
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -84,8 +89,12 @@ template <int D> struct Smem<KVC_F32, D> {
   alignas(16) float v[BN * kVStride];
 };
 
-template <int DT, int D, bool HIST, bool PAGED>
+template <int DT, int D, int KS, bool HIST, bool PAGED>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
+  static_assert(KS == 1 || KS == 2, "key split");
+  constexpr int RG = 4 / KS;                   // query row groups of 32 rows
+  constexpr int BM = 32 * RG;                  // query rows per workgroup
+  constexpr int KBW = BN / 32 / KS;            // 32-key blocks per wave and tile
   constexpr int EB = Dtype<DT>::kBytes;
   constexpr int EV = Dtype<DT>::kPer16B;
   constexpr int RB = D * EB;                   // bytes per row
@@ -93,13 +102,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   constexpr int TILE_VECS = BN * LPR;          // 16-byte vectors per K (or V) tile
   constexpr int VPT = TILE_VECS / 256;         // per thread
   constexpr int DB = D / 32;                   // 32-wide d blocks of O^T
-  constexpr int KB = BN / 32;                  // 32-key blocks of S^T
   static_assert(TILE_VECS % 256 == 0, "tile load split");
   __shared__ Smem<DT, D> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  const int rg = wave % RG;        // query row group
+  const int kh = wave / RG;        // key block of every tile: keys kb0 .. kb0 + 32 KBW - 1
+  const int kb0 = 32 * KBW * kh;
   const int h = lane >> 5;     // half-wave
   const int col = lane & 31;   // MFMA column / row within a 32 block
   // Transpose-load address of this lane (bf16 V operand): in its 16-lane
@@ -148,8 +159,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   const int hkv = hq / group;
   const bool writer = (hq % group) == 0;
   const int q0 = qt * BM;
-  const int qrow = q0 + wave * 32 + col;            // this lane's new token
-  const int wave_last = P + q0 + wave * 32 + 31;    // last position the wave's rows see
+  const int qrow = q0 + rg * 32 + col;              // this lane's new token
+  const int wave_last = P + q0 + rg * 32 + 31;      // last position the wave's rows see
   const int q_end = (q0 + BM < S) ? q0 + BM : S;
   const int kv_end = P + q_end;                     // positions this tile needs
 
@@ -189,9 +200,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   float l_run = 0.f;
 
   const int n_kt = (kv_end + BN - 1) / BN;
-  // Tiles every wave needs: their first key is at most the first row's
-  // position.  At most two more follow, which some waves skip.
-  const int n_all_raw = (P + q0 + 31) / BN + 1;
+  // Tiles every wave needs: the first key of every wave's block is at most
+  // the position of the first row.  At most two more follow, which some
+  // waves skip.
+  const int first_last = P + q0 + 31 - 32 * KBW * (KS - 1);
+  const int n_all_raw = first_last >= 0 ? first_last / BN + 1 : 0;
   const int n_all = n_all_raw < n_kt ? n_all_raw : n_kt;
 
   // Tile staging.  Each thread moves VPT 16-byte vectors of K and of V per
@@ -310,20 +323,20 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
 
   auto compute = [&](int kt) {
     const int key0 = kt * BN;
-    // S^T blocks: acc_s[kb][i] = score of key key0 + 32 kb + 8 (i/4) + 4 h + i%4
-    // for query qrow.
-    // The KB accumulator chains are interleaved so that consecutive MFMAs are
+    // S^T blocks: acc_s[kb][i] = score of key key0 + kb0 + 32 kb + 8 (i/4) +
+    // 4 h + i%4 for query qrow.
+    // The KBW accumulator chains are interleaved so that consecutive MFMAs are
     // independent.
-    f32x16 acc_s[KB];
+    f32x16 acc_s[KBW];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) acc_s[kb] = f32x16{};
+    for (int kb = 0; kb < KBW; ++kb) acc_s[kb] = f32x16{};
     if constexpr (DT == KVC_BF16) {
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
           const u32x4 kf = *reinterpret_cast<const u32x4 *>(
-              &sm.k[(32 * kb + col) * Smem<DT, D>::kKStride + 16 * ds + 8 * h]);
+              &sm.k[(kb0 + 32 * kb + col) * Smem<DT, D>::kKStride + 16 * ds + 8 * h]);
           acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qv[ds]), acc_s[kb], 0, 0, 0);
         }
@@ -333,9 +346,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
       for (int j = 0; j < D / 8; ++j) {
         const f32x4 qf = __builtin_bit_cast(f32x4, qv[j]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
           const f32x4 kf = *reinterpret_cast<const f32x4 *>(
-              &sm.k[(32 * kb + col) * Smem<DT, D>::kKStride + 8 * j + 4 * h]);
+              &sm.k[(kb0 + 32 * kb + col) * Smem<DT, D>::kKStride + 8 * j + 4 * h]);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[r], qf[r], acc_s[kb], 0, 0, 0);
@@ -347,10 +360,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     // first row or past kv_end (a wave-uniform branch).  Key key0 + 32 kb +
     // 8 (i/4) + 4 h + i%4 is visible iff it is <= P + qrow and < kv_end,
     // i.e. iff the compile-time offset 32 kb + 8 (i/4) + i%4 is <= lim.
-    if ((key0 + BN - 1 > P + q0 + wave * 32) || (key0 + BN > kv_end)) {
-      const int lim = (P + qrow < kv_end - 1 ? P + qrow : kv_end - 1) - key0 - 4 * h;
+    if ((key0 + kb0 + 32 * KBW - 1 > P + q0 + rg * 32) || (key0 + kb0 + 32 * KBW > kv_end)) {
+      const int lim = (P + qrow < kv_end - 1 ? P + qrow : kv_end - 1) - key0 - kb0 - 4 * h;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KBW; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) acc_s[kb][i] = kNegInf;
@@ -363,7 +376,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     const float sc = a.scale_log2;
     float mt = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc_s[kb][i]);
     }
@@ -374,8 +387,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     // any constant leaves the softmax unchanged.
     const bool grow = mt > m_run + 8.f;  // also true on the first tile
     const float m_new = grow ? mt : m_run;
+    // Under the key split a query can have seen no visible key yet in its
+    // wave's half (its max still -inf); subtracting 0 instead keeps its
+    // weights 0 rather than 2^(-inf + inf).  Without the split the first tile
+    // holds key 0, which every query sees.
+    const float m_sub = (KS == 2 && m_new == kNegInf) ? 0.f : m_new;
     if (__any(grow)) {
-      const float alpha = fast_exp2(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_sub);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
@@ -383,10 +401,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], sc, -m_new));
+        const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], sc, -m_sub));
         acc_s[kb][i] = p;
         if constexpr (DT != KVC_BF16) psum += p;  // bf16: summed below, as rounded
       }
@@ -394,7 +412,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
 
     // O^T += V^T . P^T
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
       if constexpr (DT == KVC_BF16) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -415,7 +433,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
           for (int db = 0; db < DB; ++db) {
             // keys 32 kb + 16 t + {0-3, 8-11} (low half-wave) or {4-7, 12-15}
             // (high), the order of pw; this lane's d = 32 db + col
-            const uint16_t *vb = &sm.v[(32 * kb + 16 * t) * Smem<DT, D>::kVStride + 32 * db + v_tr_off];
+            const uint16_t *vb = &sm.v[(kb0 + 32 * kb + 16 * t) * Smem<DT, D>::kVStride + 32 * db + v_tr_off];
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4i16 *)vb);
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -428,7 +446,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
       } else {
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-          const int vrow = 32 * kb + 8 * (s >> 2) + 4 * h + (s & 3);
+          const int vrow = kb0 + 32 * kb + 8 * (s >> 2) + 4 * h + (s & 3);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const float vf = sm.v[vrow * Smem<DT, D>::kVStride + 32 * db + col];
@@ -451,11 +469,41 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   }
   if (n_all < n_kt) {
     stage(n_all);
-    if (n_all * BN <= wave_last) compute(n_all);
+    if (n_all * BN + kb0 <= wave_last) compute(n_all);
   }
   if (n_all + 1 < n_kt) {
     stage(n_all + 1);
-    if ((n_all + 1) * BN <= wave_last) compute(n_all + 1);
+    if ((n_all + 1) * BN + kb0 <= wave_last) compute(n_all + 1);
+  }
+
+  if constexpr (KS == 2) {
+    // The two waves of a row group hold online-softmax states over disjoint
+    // keys, each relative to its own running max: wave kh = 1 hands its
+    // state over through LDS (register j of every lane, lanes contiguous)
+    // and wave kh = 0 rescales both to the larger max and adds them.
+    constexpr int NO = DB * 16;
+    float *st = reinterpret_cast<float *>(&sm) + rg * (NO + 2) * 64;
+    static_assert(RG * (NO + 2) * 64 * 4 <= (int)sizeof(Smem<DT, D>), "state hand-over fits");
+    __syncthreads();  // every wave is done with the last tile's K / V
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[(16 * db + i) * 64 + lane] = acc_o[db][i];
+      st[NO * 64 + lane] = m_run;
+      st[(NO + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = st[NO * 64 + lane], l1 = st[(NO + 1) * 64 + lane];
+      const float m = fmaxf(m_run, m1);
+      const float f0 = fast_exp2(m_run - m), f1 = fast_exp2(m1 - m);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[db][i] = acc_o[db][i] * f0 + st[(16 * db + i) * 64 + lane] * f1;
+      l_run = l_run * f0 + l1 * f1;
+    }
   }
 
   // Normalise and write O.  The wave's 32 x D outputs go through its own
@@ -470,8 +518,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
   static_assert(4 * 32 * ORB <= (int)sizeof(Smem<DT, D>), "output staging fits");
   constexpr int R16 = D * EB / 16;  // 16-byte pieces per row
   const float inv = 1.f / l_tot;
-  char *ow = reinterpret_cast<char *>(&sm) + wave * 32 * ORB;
-  __syncthreads();  // every wave is done with the last tile's K / V
+  char *ow = reinterpret_cast<char *>(&sm) + rg * 32 * ORB;
+  __syncthreads();  // every wave is done with the last tile's K / V (and the hand-over)
+  if (kh != 0) return;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -491,55 +540,73 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a) {
     const int idx = lane + 64 * it;
     const int r = idx / R16, ch = idx % R16;
     const u32x4 val = *reinterpret_cast<const u32x4 *>(ow + r * ORB + ch * 16);
-    const int tok = q0 + wave * 32 + r;
+    const int tok = q0 + rg * 32 + r;
     if (tok < S)
       __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(a.o + q_off + (size_t)tok * q_stride + ch * 16));
   }
 }
 
 // Register budgets: at D = 64, three workgroups per CU for bf16 and two for
-// fp32; D = 128 keeps one, since capping it would spill.  HIST: some
-// sequence has cached positions before its new tokens; PAGED: the cache is
-// a paged pool.
-template <int DT, bool HIST, bool PAGED>
+// fp32; D = 128 keeps one, since capping it would spill.  KS: key split (2
+// only for fp32 at D = 64, see prefill_key_split).  HIST: some sequence has
+// cached positions before its new tokens; PAGED: the cache is a paged pool.
+template <int DT, int KS, bool HIST, bool PAGED>
 __global__ __launch_bounds__(256, DT == KVC_BF16 ? 3 : 2) void prefill_kernel_d64(PrefillArgs a) {
-  prefill_tile<DT, 64, HIST, PAGED>(a);
+  prefill_tile<DT, 64, KS, HIST, PAGED>(a);
 }
 template <int DT, bool HIST, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_kernel_d128(PrefillArgs a) {
-  prefill_tile<DT, 128, HIST, PAGED>(a);
+  prefill_tile<DT, 128, 1, HIST, PAGED>(a);
 }
 
 template <int DT, bool HIST, bool PAGED>
-void launch_dt(const PrefillArgs &a, int D, hipStream_t s) {
+void launch_dt(const PrefillArgs &a, int D, int ks, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_layers * a.Hq), (unsigned)a.q_tiles, (unsigned)a.nb);
-  if (D == 64)
-    hipLaunchKernelGGL((prefill_kernel_d64<DT, HIST, PAGED>), grid, dim3(256), 0, s, a);
-  else
+  if (D == 128)
     hipLaunchKernelGGL((prefill_kernel_d128<DT, HIST, PAGED>), grid, dim3(256), 0, s, a);
+  else if constexpr (DT == KVC_F32)
+    if (ks == 2)
+      hipLaunchKernelGGL((prefill_kernel_d64<DT, 2, HIST, PAGED>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel_d64<DT, 1, HIST, PAGED>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel_d64<DT, 1, HIST, PAGED>), grid, dim3(256), 0, s, a);
 }
 
 template <int DT>
-void launch_flags(const PrefillArgs &a, int D, bool history, hipStream_t s) {
+void launch_flags(const PrefillArgs &a, int D, bool history, int ks, hipStream_t s) {
   const bool paged = a.pg.block_table != nullptr;
   if (paged) {
-    if (history) launch_dt<DT, true, true>(a, D, s);
-    else launch_dt<DT, false, true>(a, D, s);
+    if (history) launch_dt<DT, true, true>(a, D, ks, s);
+    else launch_dt<DT, false, true>(a, D, ks, s);
   } else {
-    if (history) launch_dt<DT, true, false>(a, D, s);
-    else launch_dt<DT, false, false>(a, D, s);
+    if (history) launch_dt<DT, true, false>(a, D, ks, s);
+    else launch_dt<DT, false, false>(a, D, ks, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, hipStream_t s) {
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, int ks, hipStream_t s) {
   if (a.q_tiles <= 0 || a.nb <= 0) return hipSuccess;
-  if (dtype == KVC_F32) launch_flags<KVC_F32>(a, D, history, s);
-  else launch_flags<KVC_BF16>(a, D, history, s);
+  if (ks != 1 && !(ks == 2 && dtype == KVC_F32 && D == 64)) return hipErrorInvalidValue;
+  if (dtype == KVC_F32) launch_flags<KVC_F32>(a, D, history, ks, s);
+  else launch_flags<KVC_BF16>(a, D, history, ks, s);
   return hipGetLastError();
 }
 
-int prefill_query_tile() { return BM; }
+// Key split for a call whose one-split grid has `workgroups` workgroups on a
+// device of `cus` compute units.  fp32 at D = 64 is bound by the matrix
+// cores, so two waves per row group, each taking half of every key tile,
+// halve a workgroup's longest chain; that pays while the grid is small
+// (fewer than two workgroups per CU: short prompts, single layers), and
+// costs the doubled tile staging on larger grids.  Measured (12 layers,
+// H=12, cold): fp32 S=256 35.5 -> 25.3 us; S=1024 200 -> 204 us (kept at 1);
+// bf16 S=256 10.2 -> 10.8 us (kept at 1).
+int prefill_key_split(int dtype, int D, long long workgroups, int cus) {
+  return (dtype == KVC_F32 && D == 64 && workgroups < 2LL * cus) ? 2 : 1;
+}
+
+int prefill_query_tile(int ks) { return 32 * 4 / ks; }
 
 }  // namespace kvc
