@@ -594,6 +594,14 @@ def main():
             r = {k: round(v, 3) for k, v in r.items()}
             r["lengths"] = (wb.hist + 1).tolist()
             extras[name] = r
+        # One GPU's share of the GQA workload under 8-way tensor parallelism
+        # over the KV heads (1 KV head, 4 query heads, same lengths): what
+        # each of eight GPUs would run, with no exchange on this path.
+        log("batched_decode_bf16_gqa_tp8_shard")
+        r = bench_decode(torch, K, synth.batched_decode(seed=3, gqa=True, tp=8), args.steps,
+                         args.warmup, 4)
+        r.pop("_out0")
+        extras["batched_decode_bf16_gqa_tp8_shard"] = {k: round(v, 3) for k, v in r.items()}
         paged = {}
         for bs in (16, 64):
             log(f"paged decode 12-layer fp32 T=1024, block size {bs}")

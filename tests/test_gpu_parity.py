@@ -221,6 +221,14 @@ def test_fused_batched_decode(gqa):
     check(synth.batched_decode(seed=6, gqa=gqa), fused=True)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_batched_decode_tp8_shard(fused):
+    """One GPU's share of the GQA workload under 8-way tensor parallelism
+    (one KV head, four query heads per layer), the shape the benchmark
+    times for it."""
+    check(synth.batched_decode(seed=3, gqa=True, tp=8), fused=fused)
+
+
 @pytest.mark.parametrize("N", [1, 3, 8, 9, 17])
 @pytest.mark.parametrize("G", [1, 4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

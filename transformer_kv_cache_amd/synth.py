@@ -183,13 +183,20 @@ def causal_prefill(S, dtype, seed=0, L=12) -> Workload:
                          Hq=12, Hkv=12, D=64, Tmax=1024, prefill_len=S)
 
 
-def batched_decode(seed=0, gqa=False, B=8, L=12) -> Workload:
+def batched_decode(seed=0, gqa=False, B=8, L=12, tp=1) -> Workload:
     """bf16 cache, B sequences whose visible-key counts are U[1, 1024],
-    Tmax=1024; MHA (H=12, D=64) or GQA (32 query heads, 8 KV heads, D=128)."""
+    Tmax=1024; MHA (H=12, D=64) or GQA (32 query heads, 8 KV heads, D=128).
+    ``tp`` > 1 (GQA only) gives one GPU's share under tp-way tensor
+    parallelism over the KV heads: 32/tp query and 8/tp KV heads, the same
+    lengths (they are drawn first)."""
     if gqa:
-        return make_workload("batched_decode_gqa", seed=seed, dtype="bf16", L=L, B=B,
-                             Hq=32, Hkv=8, D=128, Tmax=1024, draw_lengths=(1, 1024),
-                             step_lens=(1,))
+        if tp < 1 or 8 % tp:
+            raise ValueError("tp must divide the 8 KV heads")
+        return make_workload("batched_decode_gqa" + (f"_tp{tp}" if tp > 1 else ""), seed=seed,
+                             dtype="bf16", L=L, B=B, Hq=32 // tp, Hkv=8 // tp, D=128, Tmax=1024,
+                             draw_lengths=(1, 1024), step_lens=(1,))
+    if tp != 1:
+        raise ValueError("tp applies to the GQA workload")
     return make_workload("batched_decode_mha", seed=seed, dtype="bf16", L=L, B=B,
                          Hq=12, Hkv=12, D=64, Tmax=1024, draw_lengths=(1, 1024),
                          step_lens=(1,))
