@@ -56,3 +56,21 @@ def test_paged_from_contiguous_round_trip():
             assert np.array_equal(vp[:, table[b, t // 16], :, t % 16], w.v_cache[:, b, :, t])
     spare = np.setdiff1d(np.arange(kp.shape[1]), table)
     assert synth.is_canary(kp[:, spare]).all() and synth.is_canary(vp[:, spare]).all()
+
+
+def test_tensor_parallel_shard_keeps_the_lengths():
+    """One GPU's share of the GQA workload under tp-way tensor parallelism:
+    8/tp KV heads and 32/tp query heads, the same drawn lengths; tp must
+    divide the KV heads and only applies to the GQA workload."""
+    import pytest
+    full = synth.batched_decode(seed=3, gqa=True, L=2)
+    for tp in (2, 8):
+        s = synth.batched_decode(seed=3, gqa=True, L=2, tp=tp)
+        assert (s.Hq, s.Hkv, s.D) == (32 // tp, 8 // tp, 128)
+        assert np.array_equal(s.hist, full.hist)
+        assert s.k_cache.shape == (2, 8, 8 // tp, 1024, 128)
+    for bad in (0, 3, 16):
+        with pytest.raises(ValueError):
+            synth.batched_decode(seed=3, gqa=True, L=2, tp=bad)
+    with pytest.raises(ValueError):
+        synth.batched_decode(seed=3, gqa=False, L=2, tp=2)
