@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
 # A plain streaming read of the step's 75.5 MB (2,304 workgroups, each 32 KB
 # of 16-byte loads issued at once, cold, back-to-back launches) measured on
-# the box at 12.37 us: the most this step's bytes can move at, as a fraction
+# an MI355X at 12.37 us: the most this step's bytes can move at, as a fraction
 # of HBM_PEAK_GBS.
 PLAIN_READ_FRAC = 0.763
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix-core peaks
