@@ -597,9 +597,10 @@ def main():
         # One GPU's share of the GQA workload under 8-way tensor parallelism
         # over the KV heads (1 KV head, 4 query heads, same lengths): what
         # each of eight GPUs would run, with no exchange on this path.
+        # (an eighth of the bytes: 24 replicas keep the rotation past 512 MB)
         log("batched_decode_bf16_gqa_tp8_shard")
         r = bench_decode(torch, K, synth.batched_decode(seed=3, gqa=True, tp=8), args.steps,
-                         args.warmup, 4)
+                         args.warmup, 24)
         r.pop("_out0")
         extras["batched_decode_bf16_gqa_tp8_shard"] = {k: round(v, 3) for k, v in r.items()}
         paged = {}
