@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 12
+#define KVC_ABI_VERSION 13
 
 typedef enum {
   KVC_OK = 0,
@@ -518,6 +518,21 @@ kvc_status kvc_layernorm_f32(const float *x, int32_t M, int32_t K,
 kvc_status kvc_embed_f32(const float *wte, int32_t V, const float *wpe, int32_t T,
                          int32_t d, const int64_t *ids, int32_t N, int32_t pos0,
                          const int32_t *pos, float *y, void *stream);
+
+/* Greedy choice of the next token ([KV-2] openai-hub.com/news/2435, "实验到底测
+ * 了什么": greedy decoding, batch 1): index[0] = the first i in [0, n) at
+ * which x[i] is largest, a NaN counting as larger than every number (so the
+ * first NaN wins).  With seq given, the same launch then advances the device
+ * counter *seq_pos by one and, if its new value p lies in [0, seq_capacity),
+ * stores the index at seq[p]: the token history of a graph-captured
+ * generation loop, which then needs no other kernel per token.  All device
+ * pointers: x fp32 [n], 16-byte aligned; index int64 [1]; seq int64
+ * [seq_capacity] and seq_pos int64 [1], both given or both NULL.  Errors:
+ * KVC_E_NULL (x, index, or one of seq / seq_pos without the other),
+ * KVC_E_SHAPE (n < 1 or n >= 2^31, x misaligned, seq_capacity < 1 with seq),
+ * KVC_E_HIP. */
+kvc_status kvc_argmax_f32(const float *x, int64_t n, int64_t *index, int64_t *seq,
+                          int64_t *seq_pos, int64_t seq_capacity, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvc_last_error(void);

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
             "kvc_decode_workspace_bytes", "kvc_last_error", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvc_abi_version() == K.ABI_VERSION == 12
+    assert lib.kvc_abi_version() == K.ABI_VERSION == 13
 
 
 def test_cache_bytes_against_the_page_table(lib):
@@ -511,6 +511,29 @@ def test_embed_error_paths(lib):
     assert call(y=h.ptr(offset=4)) == E_SHAPE       # misaligned
     assert call(y=wte) == E_SHAPE                   # output over a table
     assert "overlaps" in err(lib)
+
+
+def test_argmax_error_paths(lib):
+    """kvc_argmax_f32 refuses bad sizes and pointers before any launch (its
+    valid calls run in the GPU tests)."""
+    h = Host()
+    x, idx, seq, pos = h.ptr(64 * 4), h.ptr(8), h.ptr(8 * 8), h.ptr(8)
+
+    def call(**kw):
+        a = dict(x=x, n=64, index=idx, seq=None, seq_pos=None, cap=0)
+        a.update(kw)
+        return lib.kvc_argmax_f32(a["x"], a["n"], a["index"], a["seq"], a["seq_pos"], a["cap"], None)
+
+    assert call(n=0) == E_SHAPE
+    assert call(n=-5) == E_SHAPE
+    assert call(n=1 << 31) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(index=None) == E_NULL
+    assert call(seq=seq) == E_NULL                  # history without its counter
+    assert call(seq_pos=pos) == E_NULL              # counter without a history
+    assert "both" in err(lib)
+    assert call(seq=seq, seq_pos=pos, cap=0) == E_SHAPE
+    assert call(x=h.ptr(offset=4)) == E_SHAPE       # misaligned
 
 
 def test_device_length_step_error_paths(lib):

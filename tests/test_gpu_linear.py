@@ -266,3 +266,39 @@ def test_embed(d):
     assert np.isnan(y[:2]).all() and np.array_equal(y[2], wte[2] + wpe[2])
     y = Kc.embed(tw, tp, dv(ids), pos=torch.tensor([18], dtype=torch.int32, device="cuda")).cpu().numpy()
     assert np.array_equal(y[:2], wte[ids[:2]] + wpe[18:20]) and np.isnan(y[2:]).all()
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 4096, 8193, 50257, 300001])
+def test_argmax(n):
+    """kvc_argmax_f32 equals numpy's argmax (the first maximum; a NaN wins,
+    the first NaN): random rows, planted ties at both ends, an all -inf row,
+    NaN at the start, middle and end; and the token-history bookkeeping,
+    which stops writing past the capacity but still counts."""
+    from transformer_kv_cache_amd import kvcache as Kc
+    rng = np.random.default_rng(n)
+    print(f"[argmax] n={n}", flush=True)
+    cases = [rng.standard_normal(n).astype(np.float32)]
+    t = rng.standard_normal(n).astype(np.float32)
+    t[n // 3] = t[-1] = t[n // 2] = 9.0           # ties: the first of them
+    cases.append(t)
+    cases.append(np.full(n, -np.inf, np.float32))
+    for where in (0, n // 2, n - 1):
+        t = rng.standard_normal(n).astype(np.float32)
+        t[where] = np.nan
+        t[(where + n // 4) % n] = np.inf
+        cases.append(t)
+    t = rng.integers(-3, 3, n).astype(np.float32)  # many equal maxima
+    cases.append(t)
+    for c in cases:
+        x = torch.from_numpy(c).cuda()
+        got = int(Kc.argmax(x).item())
+        assert got == int(np.argmax(c)), (got, int(np.argmax(c)))
+    # history: three calls into a two-slot history starting before slot 0
+    x = torch.from_numpy(cases[0]).cuda()
+    seq = torch.full((2,), -7, dtype=torch.int64, device="cuda")
+    pos = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    out = torch.empty(1, dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        Kc.argmax(x, out=out, seq=seq, seq_pos=pos)
+    want = int(np.argmax(cases[0]))
+    assert seq.tolist() == [want, want] and pos.item() == 2 and out.item() == want

@@ -977,6 +977,28 @@ kvc_status kvc_embed_f32(const float *wte, int32_t V, const float *wpe, int32_t 
   return ok();
 }
 
+kvc_status kvc_argmax_f32(const float *x, int64_t n, int64_t *index, int64_t *seq, int64_t *seq_pos,
+                          int64_t seq_capacity, void *stream) {
+  static const char *fn = "kvc_argmax_f32";
+  if (n < 1 || n >= ((int64_t)1 << 31))
+    return fail(KVC_E_SHAPE, "%s: n = %lld (need 1 <= n < 2^31)", fn, (long long)n);
+  if (!x || !index) return fail(KVC_E_NULL, "%s: x or index is NULL", fn);
+  if (!seq != !seq_pos) return fail(KVC_E_NULL, "%s: seq and seq_pos must both be given or both NULL", fn);
+  if (seq && seq_capacity < 1)
+    return fail(KVC_E_SHAPE, "%s: seq_capacity = %lld (need >= 1)", fn, (long long)seq_capacity);
+  if (!aligned16(x)) return fail(KVC_E_SHAPE, "%s: x must be 16-byte aligned", fn);
+  kvc::ArgmaxArgs a{};
+  a.x = x;
+  a.index = index;
+  a.seq = seq;
+  a.seq_pos = seq_pos;
+  a.cap = seq ? seq_capacity : 0;
+  a.n = (int32_t)n;
+  hipError_t err = kvc::launch_argmax(a, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_status(err, fn);
+  return ok();
+}
+
 kvc_status kvc_paged_attn_prefill_varlen(const kvc_paged_cache *cache, int32_t layer0,
                                          int32_t n_layers, const void *q, const void *k,
                                          const void *v, int32_t Hq, int32_t B,

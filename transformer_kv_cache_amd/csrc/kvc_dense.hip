@@ -323,6 +323,84 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs e) {
   reinterpret_cast<f32x4 *>(e.y)[(size_t)i * d4 + q] = v;
 }
 
+// Greedy token choice: one workgroup of 1024 lanes scans x in 16-byte pieces
+// (eight in flight per lane), keeping the first maximum it meets; lanes, then
+// waves, keep the better of two (value, index) pairs -- a NaN beats every
+// number, equal values go to the smaller index -- so the result is the first
+// maximum whatever the scan order.  A 50257-wide row is 200 KB: one
+// workgroup streams it in a few microseconds, with no second pass.
+__device__ __forceinline__ bool argmax_better(float v1, int i1, float v2, int i2) {
+  const bool n1 = v1 != v1, n2 = v2 != v2;
+  if (n1 != n2) return n1;
+  if (!n1 && v1 != v2) return v1 > v2;
+  return i1 < i2;
+}
+
+__global__ __launch_bounds__(1024) void argmax_kernel(ArgmaxArgs a) {
+  const int tid = threadIdx.x;
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  const int n4 = a.n / 4;
+  const f32x4 *x4 = reinterpret_cast<const f32x4 *>(a.x);
+  constexpr int U = 8;
+  for (int q0 = tid; q0 < n4; q0 += 1024 * U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + 1024 * u;
+      v[u] = x4[q < n4 ? q : n4 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + 1024 * u;
+      if (q < n4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (argmax_better(v[u][e], 4 * q + e, bv, bi)) {
+            bv = v[u][e];
+            bi = 4 * q + e;
+          }
+      }
+    }
+  }
+  for (int i = 4 * n4 + tid; i < a.n; i += 1024) {
+    const float v = a.x[i];
+    if (argmax_better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (argmax_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = bv;
+    si[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 16; ++w)
+      if (argmax_better(sv[w], si[w], bv, bi)) {
+        bv = sv[w];
+        bi = si[w];
+      }
+    a.index[0] = bi;
+    if (a.seq) {
+      const int64_t p = a.seq_pos[0] + 1;
+      a.seq_pos[0] = p;
+      if (p >= 0 && p < a.cap) a.seq[p] = bi;
+    }
+  }
+}
+
 template <int RPW, int NP>
 void launch_gemv(const LinearArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)((a.N + 4 * RPW - 1) / (4 * RPW)));
@@ -361,6 +439,11 @@ hipError_t launch_linear(const LinearArgs &a, hipStream_t s) {
   } else {
     launch_rows<kMaxLinearRows>(a, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

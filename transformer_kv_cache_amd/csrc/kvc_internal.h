@@ -303,12 +303,22 @@ struct EmbedArgs {
   int32_t V, T, d, N, pos0;
 };
 
+// Greedy token choice (kvc_argmax_f32).
+struct ArgmaxArgs {
+  const float *x;
+  int64_t *index;
+  int64_t *seq, *seq_pos;  // token history and its device counter, or null
+  int64_t cap;
+  int32_t n;
+};
+
 // Host launchers (one translation unit each).  They assume validated
 // arguments and return the launch status.
 hipError_t launch_linear(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 hipError_t launch_layernorm(const LayerNormArgs &p, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs &e, hipStream_t s);
+hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t s);
 hipError_t launch_lengths_add(int32_t *hist, int B, int n, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool merge, hipStream_t s);

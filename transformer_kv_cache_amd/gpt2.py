@@ -170,17 +170,16 @@ class GPT2:
         ids = torch.tensor([int(x) for x in prompt], device=self.device)
         z = self.forward(ids, cache, 0, last_only=True)
         toks = torch.empty(n_new, dtype=torch.int64, device=self.device)
-        tok = torch.argmax(z[0]).view(1)
-        toks[0] = tok[0]
+        tok = torch.empty(1, dtype=torch.int64, device=self.device)
+        # step counts the tokens chosen so far, minus one: each argmax
+        # advances it and files its token at toks[step]
+        step = torch.full((1,), -1, dtype=torch.int64, device=self.device)
+        K.argmax(z[0], out=tok, seq=toks, seq_pos=step)
         hd = torch.tensor([len(prompt)], dtype=torch.int32, device=self.device)
-        step = torch.zeros(1, dtype=torch.int64, device=self.device)
-        one = torch.ones(1, dtype=torch.int64, device=self.device)
 
         def body():
             zz = self._decode_token_dl(tok, hd, cache)
-            tok.copy_(torch.argmax(zz[0]).view(1))
-            step.add_(one)
-            toks.index_copy_(0, step, tok)
+            K.argmax(zz[0], out=tok, seq=toks, seq_pos=step)
             K.lengths_add(hd, 1)
 
         if n_new == 1:

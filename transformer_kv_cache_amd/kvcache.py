@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvcache.so")
 
 KVC_F32, KVC_BF16 = 0, 1
-ABI_VERSION = 12  # KVC_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 13  # KVC_ABI_VERSION of the header these signatures follow
 MAX_LINEAR_ROWS = 8  # rows kvc_linear_f32 takes (kMaxLinearRows)
 _DTYPE_CODE = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_CAPACITY",
@@ -141,6 +141,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
         lib.kvc_layernorm_f32.restype = i32
         lib.kvc_embed_f32.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, vp]
         lib.kvc_embed_f32.restype = i32
+        lib.kvc_argmax_f32.argtypes = [vp, i64, vp, vp, vp, i64, vp]
+        lib.kvc_argmax_f32.restype = i32
         if path is None:
             _lib = lib
     return lib
@@ -858,4 +860,27 @@ def embed(wte, wpe, ids, pos0: int = 0, pos=None, out=None, stream=None):
     _check(library().kvc_embed_f32(wte.data_ptr(), V, wpe.data_ptr(), T, d, ids.data_ptr(), N, int(pos0),
                                    None if pos is None else pos.data_ptr(), out.data_ptr(),
                                    _stream(wte.device, stream)))
+    return out
+
+
+def argmax(x, out=None, seq=None, seq_pos=None, stream=None):
+    """Index of the first maximum of the fp32 vector ``x`` (a NaN counts as
+    the largest value) into ``out`` (int64 [1] on the device).  With ``seq``
+    (int64 [capacity]) and ``seq_pos`` (int64 [1]) the same launch also does
+    ``seq_pos += 1; seq[seq_pos] = index`` (skipped past the capacity)."""
+    if (not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.dim() != 1
+            or not x.is_contiguous() or x.device.type != "cuda"):
+        raise ValueError("x must be a contiguous fp32 vector on the GPU")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=x.device)
+    for name, t in (("out", out), ("seq", seq), ("seq_pos", seq_pos)):
+        if t is not None and (not isinstance(t, torch.Tensor) or t.dtype != torch.int64
+                              or t.device != x.device or t.numel() < 1 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int64 tensor on {x.device}")
+    if (seq is None) != (seq_pos is None):
+        raise ValueError("seq and seq_pos go together")
+    _check(library().kvc_argmax_f32(x.data_ptr(), x.numel(), out.data_ptr(),
+                                    None if seq is None else seq.data_ptr(),
+                                    None if seq_pos is None else seq_pos.data_ptr(),
+                                    0 if seq is None else seq.numel(), _stream(x.device, stream)))
     return out
