@@ -1,0 +1,100 @@
+"""A wider seeded random sweep through the C ABI against the CPU oracle, in
+chunks: decode (contiguous and paged caches, block sizes 1 to 128, the fused
+step and append + attention, GQA groups up to 16 and chunks up to 17 new
+rows, so every split kernel is reached, with histories from empty to full)
+and packed variable-length prefill (ragged and empty prompts on cached
+prefixes, GQA, D = 64 and 128).  Outputs within the dtype tolerance, cache
+bytes bit-exact; each failure names its case."""
+import json
+
+import numpy as np
+import pytest
+
+from transformer_kv_cache_amd import synth
+from gpu_common import assert_matches, run_gpu, run_oracle, run_paged, run_paged_oracle
+import test_gpu_varlen as TV
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 40
+
+
+def _decode_case(rng, i):
+    dtype = ("f32", "bf16")[rng.integers(0, 2)]
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    N = int(rng.choice([1, 1, 1, 2, 3, 4, 7, 8, 9, 16, 17]))
+    Hkv = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 5))
+    L = int(rng.integers(1, 4))
+    Tmax = int(rng.integers(N + 1, 1400))
+    hist = rng.integers(0, Tmax - N + 1, size=B)
+    if rng.random() < 0.3:
+        hist[rng.integers(0, B)] = Tmax - N
+    if rng.random() < 0.2:
+        hist[rng.integers(0, B)] = 0
+    paged = bool(rng.random() < 0.35)
+    bs = int(rng.choice([1, 2, 8, 16, 32, 128]))
+    return dict(i=i, dtype=dtype, D=D, G=G, N=N, Hkv=Hkv, B=B, L=L, Tmax=Tmax,
+                hist=[int(h) for h in hist], paged=paged, bs=bs, fused=bool(rng.integers(0, 2)))
+
+
+def _decode_cases(n=240, seed=91000):
+    rng = np.random.default_rng(seed)
+    return [_decode_case(rng, i) for i in range(n)]
+
+
+def _varlen_cases(n=80, seed=92000):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = ("f32", "bf16")[rng.integers(0, 2)]
+        D = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.integers(1, 4))
+        B = int(rng.integers(1, 6))
+        L = int(rng.integers(1, 3))
+        Tmax = int(rng.integers(8, 900))
+        lens = rng.integers(0, min(300, Tmax) + 1, size=B)
+        hist = [int(rng.integers(0, Tmax - ln + 1)) for ln in lens]
+        out.append(dict(i=i, dtype=dtype, D=D, G=G, Hkv=Hkv, B=B, L=L, Tmax=Tmax,
+                        lens=[int(x) for x in lens], hist=hist))
+    return out
+
+
+DECODE = _decode_cases()
+VARLEN = _varlen_cases()
+
+
+def _run_decode(c):
+    if not c["paged"]:
+        w = synth.make_workload(f"rs{c['i']}", seed=91000 + c["i"], dtype=c["dtype"], L=c["L"],
+                                B=c["B"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+                                Tmax=c["Tmax"], hist=c["hist"], step_lens=(c["N"],))
+        assert_matches(w, run_gpu(w, c["fused"]), run_oracle(w))
+        return
+    bs = c["bs"]
+    mb = (c["Tmax"] + bs - 1) // bs
+    w = synth.make_paged_workload(f"rs{c['i']}", seed=91000 + c["i"], dtype=c["dtype"], L=c["L"],
+                                  B=c["B"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+                                  block_size=bs, max_blocks=mb,
+                                  hist=[min(h, mb * bs - c["N"]) for h in c["hist"]],
+                                  step_lens=(c["N"],))
+    assert_matches(w, run_paged(w, c["fused"]), run_paged_oracle(w))
+
+
+@pytest.mark.parametrize("chunk", range(len(DECODE) // CHUNK))
+def test_random_decode(chunk):
+    for c in DECODE[chunk * CHUNK:(chunk + 1) * CHUNK]:
+        print(f"[random decode] {json.dumps(c)}", flush=True)
+        _run_decode(c)
+
+
+@pytest.mark.parametrize("chunk", range(len(VARLEN) // CHUNK))
+def test_random_varlen_prefill(chunk):
+    for c in VARLEN[chunk * CHUNK:(chunk + 1) * CHUNK]:
+        print(f"[random varlen] {json.dumps(c)}", flush=True)
+        w = synth.make_varlen_workload(f"rv{c['i']}", seed=92000 + c["i"], dtype=c["dtype"],
+                                       L=c["L"], B=c["B"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"],
+                                       D=c["D"], Tmax=c["Tmax"], hist=c["hist"], lens=c["lens"])
+        TV.check(w)
