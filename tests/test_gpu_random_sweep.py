@@ -1,9 +1,9 @@
 """A wider seeded random sweep through the C ABI against the CPU oracle, in
 chunks: decode (contiguous and paged caches, block sizes 1 to 128, the fused
 step and append + attention, GQA groups up to 16 and chunks up to 17 new
-rows, so every split kernel is reached, with histories from empty to full)
-and packed variable-length prefill (ragged and empty prompts on cached
-prefixes, GQA, D = 64 and 128).  Outputs within the dtype tolerance, cache
+rows, so every split kernel is reached, with histories from empty to full),
+packed variable-length prefill (ragged and empty prompts on cached
+prefixes, GQA, D = 64 and 128) and padded prefill followed by a decode step.  Outputs within the dtype tolerance, cache
 bytes bit-exact; each failure names its case."""
 import json
 
@@ -62,8 +62,22 @@ def _varlen_cases(n=80, seed=92000):
     return out
 
 
+def _prefill_cases(n=40, seed=93000):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Tmax = int(rng.integers(2, 1100))
+        S = int(rng.integers(1, min(Tmax, 700) + 1))
+        out.append(dict(i=i, dtype=("f32", "bf16")[rng.integers(0, 2)], D=int(rng.choice([64, 128])),
+                        G=int(rng.choice([1, 2, 4])), Hkv=int(rng.integers(1, 4)),
+                        B=int(rng.integers(1, 4)), L=int(rng.integers(1, 4)), Tmax=Tmax, S=S,
+                        N=int(rng.choice([0, 1, 3]))))
+    return out
+
+
 DECODE = _decode_cases()
 VARLEN = _varlen_cases()
+PREFILL = _prefill_cases()
 
 
 def _run_decode(c):
@@ -98,3 +112,16 @@ def test_random_varlen_prefill(chunk):
                                        L=c["L"], B=c["B"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"],
                                        D=c["D"], Tmax=c["Tmax"], hist=c["hist"], lens=c["lens"])
         TV.check(w)
+
+
+@pytest.mark.parametrize("chunk", range(len(PREFILL) // CHUNK))
+def test_random_prefill_then_decode(chunk):
+    """Padded causal prefill of S tokens (the key split applies to the
+    small fp32 grids among them), then, room permitting, a decode step."""
+    for c in PREFILL[chunk * CHUNK:(chunk + 1) * CHUNK]:
+        print(f"[random prefill] {json.dumps(c)}", flush=True)
+        steps = (c["N"],) if c["N"] and c["S"] + c["N"] <= c["Tmax"] else ()
+        w = synth.make_workload(f"rp{c['i']}", seed=93000 + c["i"], dtype=c["dtype"], L=c["L"],
+                                B=c["B"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+                                Tmax=c["Tmax"], prefill_len=c["S"], step_lens=steps)
+        assert_matches(w, run_gpu(w), run_oracle(w))
