@@ -3,8 +3,8 @@
 One step = the whole decode hot path for GPT-2 Small at context 1024: the new
 token's K/V rows written into all 12 layers' caches and the attention of the
 new query rows against the 1024 cached keys, issued as one kvc_decode_step:
-one kernel, the split-K pass over the cached keys whose last split workgroup
-of each row merges the row's splits with the new key and appends its row.
+one kernel of one workgroup per query row (144 rows), each streaming its
+row's 1023 cached keys, merging them with the new key and appending its row.
 Inputs: fp32, B=1, 12 layers x 12 heads, D=64, history P=1023, N(0,1) from a
 fixed seed.
 
@@ -44,7 +44,7 @@ HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
 PLAIN_READ_FRAC = 0.763
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix-core peaks
 METRIC = "decode attention µs/step + achieved HBM GB/s at T=1024; prefill TFLOP/s"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")  # split kernel
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.txt")
 DECODE_SOURCES = [os.path.join(ROOT, "transformer_kv_cache_amd", "csrc", f)
                   for f in ("kvc_decode.hip", "kvc_device.h", "kvc_internal.h", "kvc_api.hip")]
 
@@ -219,7 +219,8 @@ def bench_decode(torch, K, w, steps, warmup, rotate, per_layer=False, eager=Fals
     res["append_us"] = GraphTimer(torch, append_only, rotate).time(steps)
     # the fused step reads the new rows from k_new/v_new and writes them once
     res["step_bytes"] = decode_bytes(w, N) + new_rows_bytes(w, N)
-    # split pass alone (kvc_decode_split: the same kernel without the merge).
+    # split pass alone (kvc_decode_split: the split kernel without a merge; the
+    # one-call step of one query row per KV head may run the row kernel instead).
     # One query row per KV head: K/V of the cached keys [0, P) and q read;
     # the merge adds key P from k_new/v_new and appends it.  Several rows per
     # KV head (multi-row kernels): K/V of all keys (new rows from
@@ -661,9 +662,9 @@ def main():
         "config": {"workload": "GPT-2 Small KV-cache decode step, 12 layers, fp32, B=1, H=12, "
                                "D=64, Tmax=1024, history 1023 + 1 new token (T=1024)",
                    "layers": 12, "batch": 1, "heads": 12, "head_dim": 64, "context": 1024,
-                   "step": "kvc_decode_step: one kernel -- split-K pass over the cached keys, "
-                           "the last split workgroup of each row merges the row's splits with "
-                           "the new key and appends its row",
+                   "step": "kvc_decode_step: one kernel -- one workgroup per query row streams "
+                           "the row's cached keys, merges them with the new key and appends "
+                           "its row",
                    "rotating_cache_replicas": args.rotate},
         "decode_us_per_step": round(step_us, 3),
         "decode_us_per_step_min": round(head["step_us_min"], 3),
@@ -674,9 +675,9 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_kernel<f32,D64,KPL8,merge> (the whole step in one launch: "
-                               "split-K over keys [0,1023), the last split of each row merges "
-                               "and adds key 1023, appending its row)",
+                     "kernel": "decode_row_kernel<f32,D64,KPL8,128 lanes> (the whole step in one "
+                               "launch of 144 workgroups: each streams keys [0,1023) of its "
+                               "row, adds key 1023 and appends its row)",
                      "launch_us": round(step_us, 3),
                      "algorithmic_bytes": step_bytes,
                      "split_pass_only_us": round(head["split_us"], 3),

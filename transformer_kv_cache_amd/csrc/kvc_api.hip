@@ -178,6 +178,17 @@ int device_cus() {
   return n;
 }
 
+// Single-row calls whose rows alone about fill the chip (from one workgroup
+// per two CUs to two per CU) run one workgroup per row (decode_row_kernel):
+// no split states, arrival counters or merge through the L2.  Measured on
+// the 12-layer fp32 step at T=1024 (144 rows on 256 CUs): see the kernel's
+// notes.  Fewer rows leave most CUs idle (a one-layer call has 12), more
+// queue behind one another, and the split grid serves both.
+bool row_kernel_fits(int units) {
+  const long long cus = device_cus();
+  return cus > 0 && 2LL * units >= cus && units <= 2LL * cus;
+}
+
 // Key split of a prefill call: from its grid at key split 1 (the first batch
 // slice's), see kvc::prefill_key_split.
 int prefill_ks(const kvc_cache *cache, int32_t n_layers, int32_t Hq, int max_len) {
@@ -555,7 +566,12 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
       // merge alone gives the output (v_P)
       a.grid_splits = splits > 0 ? splits : 1;
       a.grid_splits_div = kvc::magic_for(a.grid_splits);
-      if (phases == kBoth && plan.merge_in_launch) {
+      // (a paged cache needs blocks that hold a whole row-group load)
+      const bool row_kernel = phases == kBoth && row_kernel_fits(a.units) &&
+                              (!pg.block_table || (1 << pg.bs_log2) >= kvc::decode_row_min_block(cache->dtype, cache->D));
+      if (row_kernel) {
+        e = kvc::launch_decode_row(a, cache->dtype, cache->D, (hipStream_t)stream);
+      } else if (phases == kBoth && plan.merge_in_launch) {
         e = kvc::launch_decode(a, cache->dtype, cache->D, kpl, true, (hipStream_t)stream);
       } else {
         if ((phases & kSplit) && splits > 0)

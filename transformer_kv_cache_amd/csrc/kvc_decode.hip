@@ -73,7 +73,7 @@ __device__ __forceinline__ float row_allreduce(float x) {
 }
 
 template <int NRG>
-constexpr int kLog2Nrg = NRG == 8 ? 3 : NRG == 16 ? 4 : NRG == 32 ? 5 : 6;
+constexpr int kLog2Nrg = NRG == 4 ? 2 : NRG == 8 ? 3 : NRG == 16 ? 4 : NRG == 32 ? 5 : NRG == 64 ? 6 : 7;
 
 // K/V rows are read exactly once per call: non-temporal loads keep them from
 // displacing reusable lines in the caches.
@@ -394,6 +394,240 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// One workgroup per query row, for calls whose rows alone fill the chip
+// (about one per CU).  The workgroup streams the whole key range [0, P) of
+// its (layer, sequence, KV head) in chunks of CH = NRG * KPL keys, with the
+// next chunk's K and V loads in flight while the current chunk is reduced
+// (two register buffers; chunks past the end are clamped to key P - 1 and
+// reduce to nothing, so no load sits behind a branch).  Rows are laid out
+// as in decode_kernel's split: a key row is LPR lanes wide, one 16-byte
+// vector per lane, so a wave's load reads 1 KB of consecutive rows (two
+// vectors per lane, each load then reading half rows at the row stride,
+// measured slower despite a third less vector work).  Each row group carries its online-softmax
+// state across the chunks (rescaled by 2^(m_old - m_new) when its running
+// max grows); at the end the states merge across the wave with cross-lane
+// exchanges and across the waves through LDS, then with key P's state as in
+// the split form.  Nothing goes through the workspace: the merge is an LDS
+// round trip instead of a state store, its acknowledgement, an arrival
+// atomic and the merging workgroup's loads through the L2.  Streaming from
+// one workgroup per row leaves the CUs beyond the row count idle, which the
+// host plan weighs against that merge.
+//   PAGED: blocks of at least NRG positions, looked up with one scalar load
+// per chunk load (the host sends smaller blocks to the split kernel, whose
+// per-lane lookups would make every chunk wait for the one before it).
+template <int DT, int D, int KPL, int NT, bool PAGED, bool DEVLEN>
+__global__ __launch_bounds__(NT) void decode_row_kernel(DecodeArgs a) {
+  constexpr int EV = Dtype<DT>::kPer16B;
+  constexpr int LPR = D * Dtype<DT>::kBytes / 16;  // lanes per row
+  constexpr int NW = NT / 64;                      // waves
+  constexpr int NRG = NT / LPR;                    // rows per load
+  constexpr int CH = NRG * KPL;                    // keys per chunk
+  constexpr int EPL = D / 64;
+  typedef typename Elem<DT>::bits bits;
+  static_assert(LPR * EV == D && LPR >= 8, "row layout");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = tid / LPR;
+  const int c = tid % LPR;
+  const int u = blockIdx.x;
+  const int units = a.units, n_layers = a.n_layers, Hkv = a.Hkv, B = a.B, Tmax = a.Tmax;
+  const int layer0 = a.layer0, b0 = a.b0;
+  const uint32_t hkv_div = a.hkv_div, nl_div = a.nl_div;
+  const char *k_cache = a.k_cache, *v_cache = a.v_cache, *qp = a.q;
+  const float scale_log2 = a.scale_log2;
+  asm volatile("" ::"s"(units), "s"(n_layers), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(b0),
+               "s"(hkv_div), "s"(nl_div), "s"(k_cache), "s"(v_cache), "s"(qp), "s"(scale_log2));
+  if (u >= units) return;
+  const int t = div_magic(u, Hkv, hkv_div);
+  const int hkv = u - t * Hkv;
+  const int bb = div_magic(t, n_layers, nl_div);
+  const int l = t - bb * n_layers;
+  const int P = seq_hist<DEVLEN>(a, bb);
+  const int b = b0 + bb;
+  const uint32_t head = (uint32_t)(((layer0 + l) * B + b) * Hkv + hkv);
+  const size_t crow0 = (size_t)head * (uint32_t)Tmax;
+  const uint32_t row = (uint32_t)((l * B + b) * Hkv + hkv);
+  const int nch = (P + CH - 1) / CH;
+  const char *kc = k_cache + crow0 * (LPR * 16);
+  const char *vc = v_cache + crow0 * (LPR * 16);
+
+  // Chunk ch's K loads, then its V loads (positions past P - 1 clamped to it).
+  auto load_chunk = [&](int ch, u32x4 (&kw)[KPL], u32x4 (&vw)[KPL]) {
+    const int key0 = ch * CH;
+    if constexpr (PAGED) {
+      size_t prow[KPL];
+      paged_rows_grouped<KPL, NRG>(a.pg, b, key0, P - 1, rg, layer0 + l, hkv, Hkv, prow);
+      const u32x4 *kb = reinterpret_cast<const u32x4 *>(k_cache);
+      const u32x4 *vb = reinterpret_cast<const u32x4 *>(v_cache);
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) kw[kk] = stream_load(kb + prow[kk] * LPR + c);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) vw[kk] = stream_load(vb + prow[kk] * LPR + c);
+    } else {
+      uint32_t off[KPL];
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int pos = key0 + kk * NRG + rg;
+        off[kk] = (uint32_t)((pos < P - 1 ? pos : P - 1) * LPR + c) * 16u;
+        kw[kk] = stream_load(reinterpret_cast<const u32x4 *>(kc + off[kk]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) vw[kk] = stream_load(reinterpret_cast<const u32x4 *>(vc + off[kk]));
+    }
+  };
+
+  // Key P's rows (lane j holds elements j + 64 e): q, and k_P / v_P from the
+  // new rows (fused step) or from cache slot P.
+  const size_t slot = slot_row<PAGED>(a, b, P, layer0 + l, hkv) * D;
+  bits qn[EPL], kn[EPL], vn[EPL];
+  {
+    const bits *qb = reinterpret_cast<const bits *>(qp) + (size_t)row * D;
+    const bits *kb = a.k_new ? reinterpret_cast<const bits *>(a.k_new) + (size_t)row * D
+                             : reinterpret_cast<const bits *>(k_cache) + slot;
+    const bits *vb = a.v_new ? reinterpret_cast<const bits *>(a.v_new) + (size_t)row * D
+                             : reinterpret_cast<const bits *>(v_cache) + slot;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      qn[j] = qb[lane + 64 * j];
+      kn[j] = kb[lane + 64 * j];
+      vn[j] = vb[lane + 64 * j];
+    }
+  }
+
+  float m = kNegInf, lsum = 0.f, acc[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+  if (nch > 0) {
+    const u32x4 qw = reinterpret_cast<const u32x4 *>(qp)[(size_t)row * LPR + c];
+    u32x4 kA[KPL], vA[KPL], kB[KPL], vB[KPL];
+    load_chunk(0, kA, vA);
+    // q pre-scaled: scores come out in the log2 domain
+    float qf[EV];
+    unpack16<DT>(qw, qf);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) qf[e] *= scale_log2;
+    // Fold chunk ch into the row group's state.
+    auto reduce_chunk = [&](int ch, const u32x4 (&kw)[KPL], const u32x4 (&vw)[KPL]) {
+      const int last = P - 1 - ch * CH;  // offset of the last visible key
+      float s[KPL];
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        float kf[EV];
+        unpack16<DT>(kw[kk], kf);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) dot = fmaf(qf[e], kf[e], dot);
+        dot = row_allreduce<LPR>(dot);
+        s[kk] = (rg <= last - kk * NRG) ? dot : kNegInf;
+      }
+      float mn = m;
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) mn = fmaxf(mn, s[kk]);
+      const float f = rescale(m, mn);
+      lsum *= f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] *= f;
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        const float p = (mn == kNegInf) ? 0.f : fast_exp2(s[kk] - mn);
+        lsum += p;
+        float vf[EV];
+        unpack16<DT>(vw[kk], vf);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+      }
+      m = mn;
+    };
+    // Two chunks per trip with no branch inside: a chunk past the end (odd
+    // nch) reduces to a no-op (every score masked), and the last trip's
+    // prefetch reads key P - 1 again.
+    for (int ch = 0; ch < nch; ch += 2) {
+      load_chunk(ch + 1, kB, vB);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce_chunk(ch, kA, vA);
+      load_chunk(ch + 2, kA, vA);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce_chunk(ch + 1, kB, vB);
+    }
+  }
+
+  // Merge the row groups of each wave (lanes with the same c) ...
+  {
+    float M = m;
+    if constexpr (LPR <= 8) M = xor_combine<8, true>(M);
+    if constexpr (LPR <= 16) M = xor_combine<16, true>(M);
+    M = xor_combine<32, true>(M);
+    const float f = rescale(m, M);
+    lsum *= f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] *= f;
+    if constexpr (LPR <= 8) {
+      lsum = xor_combine<8>(lsum);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<8>(acc[e]);
+    }
+    if constexpr (LPR <= 16) {
+      lsum = xor_combine<16>(lsum);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = xor_combine<16>(acc[e]);
+    }
+    lsum = xor_combine<32>(lsum);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = xor_combine<32>(acc[e]);
+    m = M;
+  }
+  // ... and the waves through LDS into wave 0 (lane j: elements j + 64 e).
+  __shared__ float sh_o[NW][D];
+  __shared__ float sh_m[NW];
+  __shared__ float sh_l[NW];
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EV; ++e) sh_o[wave][c * EV + e] = acc[e];
+    if (c == 0) {
+      sh_m[wave] = m;
+      sh_l[wave] = lsum;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float Mw = sh_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, sh_m[w]);
+  float Lw = 0.f, ow[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) ow[j] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float f = rescale(sh_m[w], Mw);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) ow[j] = fmaf(f, sh_o[w][lane + 64 * j], ow[j]);
+    Lw = fmaf(f, sh_l[w], Lw);
+  }
+  // Key P's state (M, 1, v_P) merged with the keys before it.
+  float M = key_score<DT, EPL>(qn, kn, scale_log2);
+  const float Mc = fmaxf(M, Mw);
+  const float fp = rescale(M, Mc), fw = rescale(Mw, Mc);
+  const float L = fmaf(fw, Lw, fp);
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const float val = fmaf(fw, ow[j], fp * Elem<DT>::widen(vn[j])) * inv;
+    store_elems<DT>(a.o, (size_t)row * D + lane + 64 * j, &val, 1);
+  }
+  if (a.k_new) {
+    // the append of the new row (no workgroup of this launch reads slot P)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      reinterpret_cast<bits *>(a.k_cache)[slot + lane + 64 * j] = kn[j];
+      reinterpret_cast<bits *>(a.v_cache)[slot + lane + 64 * j] = vn[j];
+    }
+  }
+}
+
 // Merge of the split-K states of query rows as a second launch.  One wave
 // per row, lane j holding elements j, j + 64, ... of it.  Grid: x = blocks
 // of 4 rows over the Hq * N rows of one (layer, sequence), y = layer, z =
@@ -503,6 +737,34 @@ hipError_t launch_dt(const DecodeArgs &a, int kpl, unsigned grid, hipStream_t s)
   }
 }
 
+// Two waves per row, 8 keys per lane group and chunk (measured on the
+// 12-layer fp32 step at T=1024: 14.3 us against 14.8 with four waves, 19.4
+// with one, 17.3 with eight; 4 or 16 keys per lane group slower).
+constexpr int kRowThreads = 128;
+constexpr int kRowKpl = 8;
+
+template <int DT, int D>
+constexpr int row_nrg() {
+  return kRowThreads / (D * Dtype<DT>::kBytes / 16);
+}
+
+template <int DT, int D, bool PAGED>
+hipError_t launch_row_pg(const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)a.units);
+  if (a.hist_dev)
+    hipLaunchKernelGGL((decode_row_kernel<DT, D, kRowKpl, kRowThreads, PAGED, true>), grid, dim3(kRowThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_row_kernel<DT, D, kRowKpl, kRowThreads, PAGED, false>), grid, dim3(kRowThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_row_dt(const DecodeArgs &a, hipStream_t s) {
+  if (!a.pg.block_table) return launch_row_pg<DT, D, false>(a, s);
+  if (a.pg.bs_log2 < kLog2Nrg<row_nrg<DT, D>()>) return hipErrorInvalidValue;
+  return launch_row_pg<DT, D, true>(a, s);
+}
+
 }  // namespace
 
 int decode_rows_per_load(int dtype, int D) {
@@ -547,6 +809,17 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool me
                             : launch_dt<KVC_BF16, 64, false>(a, kpl, grid, s);
   return merge ? launch_dt<KVC_BF16, 128, true>(a, kpl, grid, s)
                : launch_dt<KVC_BF16, 128, false>(a, kpl, grid, s);
+}
+
+hipError_t launch_decode_row(const DecodeArgs &a, int dtype, int D, hipStream_t s) {
+  if (a.rows != 1 || a.N != 1 || a.group != 1 || a.units < 1) return hipErrorInvalidValue;
+  if (dtype == KVC_F32) return D == 64 ? launch_row_dt<KVC_F32, 64>(a, s) : launch_row_dt<KVC_F32, 128>(a, s);
+  return D == 64 ? launch_row_dt<KVC_BF16, 64>(a, s) : launch_row_dt<KVC_BF16, 128>(a, s);
+}
+
+int decode_row_min_block(int dtype, int D) {
+  if (dtype == KVC_F32) return D == 64 ? row_nrg<KVC_F32, 64>() : row_nrg<KVC_F32, 128>();
+  return D == 64 ? row_nrg<KVC_BF16, 64>() : row_nrg<KVC_BF16, 128>();
 }
 
 }  // namespace kvc
