@@ -238,9 +238,10 @@ kvc_status kvc_lengths_add(int32_t *hist_len_dev, int32_t B, int32_t n,
  * with both given the phases of kvc_decode_step.  Call kvc_decode_combine
  * with the same arguments as kvc_decode_split, on the same stream, before
  * anything else uses the workspace; together they compute the one-call
- * form's result.  Calls with one query row per KV head whose rows about fill
- * the GPU (from half a row per compute unit to two) run the one-call form as
- * one workgroup per row, which sums the same terms in another order, so
+ * form's result.  Calls whose (layer, sequence, KV head) units about fill
+ * the GPU (from half a unit per compute unit to two) and that have at most
+ * 8 query rows per KV head run the one-call form as one workgroup per unit
+ * over its whole key range, which sums the same terms in another order, so
  * there the two forms agree to fp32 rounding rather than bit for bit.
  *
  * kvc_decode_split runs the split-K pass: each (layer, sequence, KV head,

@@ -585,6 +585,15 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
       // resident round, so each split's wait for its state stores queues the
       // next workgroups).
       const int splits = (max_keys + g.split_keys - 1) / g.split_keys;
+      // One workgroup per (layer, sequence, KV head) over the whole key range
+      // when those alone about fill the chip, as for one row per KV head.
+      const int heads = n_layers * a.nb * cache->Hkv;
+      if (phases == kBoth && g.kernel == DecodeKernel::kRows && row_kernel_fits(heads) &&
+          (!pg.block_table || (1 << pg.bs_log2) >= kvc::decode_rows_min_block(cache->dtype, cache->D))) {
+        e = kvc::launch_decode_rows_loop(a, cache->dtype, cache->D, fused, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e, fn);
+        continue;
+      }
       if ((phases & kSplit) && splits > 0)
         e = g.kernel == DecodeKernel::kRows
                 ? kvc::launch_decode_rows(a, cache->dtype, cache->D, splits, fused, (hipStream_t)stream)

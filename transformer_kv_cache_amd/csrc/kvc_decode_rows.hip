@@ -399,6 +399,300 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
   }
 }
 
+// The same rows, one workgroup per (layer, sequence, KV head) streaming the
+// whole key range [0, P + N), for calls whose KV heads alone about fill the
+// chip (the 12-layer chunked step has 144).  Chunks of NRG * KPL keys are
+// laid out as one split above and go two register buffers deep (the next
+// chunk's loads in flight while the current one is reduced, two chunks per
+// loop trip with no branch inside: a chunk past the end is clamped to the
+// last key and masked).  Per query row the wave keeps a running max and sum
+// (wave-uniform after the cross-lane reductions) and each lane its partial
+// outputs; when a row's max grows, its partial outputs are rescaled by
+// 2^(m_old - m_new) -- on the matrix-core path a lane's accumulators all
+// belong to its own row f(c), on the vector path lane c holds rows j ^ f(c)
+// and gathers their factors over the key row with the reverse butterfly.
+// The sums over the wave's key rows and the merge of the waves run once,
+// after the last chunk, and the output is written directly: no split
+// states, no combine pass.
+template <int DT, int LPR, int RP, int KPL, int NT, bool MPV, bool FUSED, bool PAGED, bool DEVLEN>
+__global__ __launch_bounds__(NT) void decode_rows_loop_kernel(DecodeArgs a) {
+  constexpr int EV = Dtype<DT>::kPer16B;
+  constexpr int D = LPR * EV;
+  constexpr int F = first_step<LPR>();
+  constexpr int NW = NT / 64;
+  constexpr int NRG = NT / LPR;
+  constexpr int CH = NRG * KPL;
+  constexpr int NV = RP * EV;
+  static_assert(LPR == 8 || LPR == 16, "key row width");
+  static_assert(RP >= 2 && RP <= 16 && (RP & (RP - 1)) == 0, "rows");
+  static_assert(!MPV || (DT == KVC_F32 && RP == 8 && LPR == 16), "matrix-core P.V: fp32, 8 rows");
+
+  __shared__ float sh_o[NW][RP * D];
+  __shared__ float sh_m[NW][RP], sh_l[NW][RP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane & (LPR - 1);
+  const int kg = lane / LPR;
+  const int rg = tid / LPR;
+
+  const int lh = blockIdx.x;
+  const int bb = blockIdx.z;
+  const int P = seq_hist<DEVLEN>(a, bb);
+  const int Hkv = a.Hkv, B = a.B, Tmax = a.Tmax, layer0 = a.layer0, N = a.N, rows = a.rows;
+  const int Hq = a.Hq;
+  const uint32_t hkv_div = a.hkv_div;
+  const float scale_log2 = a.scale_log2;
+  asm volatile("" ::"s"(P), "s"(Hkv), "s"(B), "s"(Tmax), "s"(layer0), "s"(N), "s"(rows), "s"(Hq),
+               "s"(hkv_div), "s"(scale_log2));
+  const int nkeys = P + N;
+  const int nch = (nkeys + CH - 1) / CH;
+  const int l = div_magic(lh, Hkv, hkv_div);
+  const int hkv = lh - l * Hkv;
+  const int b = a.b0 + bb;
+
+  const size_t crow0 = (((size_t)(layer0 + l) * B + b) * Hkv + hkv) * (size_t)Tmax;
+  const char *kc = a.k_cache + crow0 * (LPR * 16);
+  const char *vc = a.v_cache + crow0 * (LPR * 16);
+  const size_t nrow0 = (((size_t)l * B + b) * Hkv + hkv) * (size_t)N;
+  const long long qrow0 = (((long long)l * B + b) * Hq + (long long)hkv * a.group) * N;
+
+  const int f = row_perm<RP, LPR>(c);
+  const int lim = f < rows ? P + f % N : -1;
+
+  u32x4 qw[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j) {
+    const int rr = j ^ f;
+    qw[j] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + (rr < rows ? rr : rows - 1)) * LPR + c];
+  }
+
+  // Chunk ch's K loads, then its V loads; keys past the last clamped to it,
+  // keys [P, P + N) from the new rows in the fused step.
+  auto load_chunk = [&](int ch, u32x4 (&kw)[KPL], u32x4 (&vw)[KPL]) {
+    const int key0 = ch * CH;
+    size_t prow[KPL];
+    if constexpr (PAGED) paged_rows_grouped<KPL, NRG>(a.pg, b, key0, nkeys - 1, rg, layer0 + l, hkv, Hkv, prow);
+    const u32x4 *vp[KPL];
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      const int key = key0 + kk * NRG + rg;
+      const int kidx = key < nkeys ? key : nkeys - 1;
+      const u32x4 *kp;
+      if (FUSED && kidx >= P) {
+        kp = reinterpret_cast<const u32x4 *>(a.k_new) + (nrow0 + (kidx - P)) * LPR + c;
+        vp[kk] = reinterpret_cast<const u32x4 *>(a.v_new) + (nrow0 + (kidx - P)) * LPR + c;
+      } else if constexpr (PAGED) {
+        kp = reinterpret_cast<const u32x4 *>(a.k_cache) + prow[kk] * LPR + c;
+        vp[kk] = reinterpret_cast<const u32x4 *>(a.v_cache) + prow[kk] * LPR + c;
+      } else {
+        const uint32_t off = (uint32_t)(kidx * LPR + c) * 16u;
+        kp = reinterpret_cast<const u32x4 *>(kc + off);
+        vp[kk] = reinterpret_cast<const u32x4 *>(vc + off);
+      }
+      kw[kk] = stream_load(kp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) vw[kk] = stream_load(vp[kk]);
+  };
+
+  float qf[RP][EV];
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 acc4[4];
+  float acc[MPV ? 1 : NV];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < (MPV ? 1 : NV); ++i) acc[i] = 0.f;
+
+  auto reduce_chunk = [&](int ch, const u32x4 (&kw)[KPL], const u32x4 (&vw)[KPL]) {
+    const int key0 = ch * CH;
+    float s[KPL];
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      float kf[EV];
+      unpack16<DT>(kw[kk], kf);
+      float part[RP];
+#pragma unroll
+      for (int j = 0; j < RP; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) d = fmaf(qf[j][e], kf[e], d);
+        part[j] = d;
+      }
+      const float dot = reduce_rows<RP, F>(part);
+      s[kk] = (key0 + kk * NRG + rg <= lim) ? dot : kNegInf;
+    }
+    float mc = s[0];
+#pragma unroll
+    for (int kk = 1; kk < KPL; ++kk) mc = fmaxf(mc, s[kk]);
+    if constexpr (LPR == 8) mc = xor_combine<8, true>(mc);
+    mc = xor_combine<16, true>(mc);
+    mc = xor_combine<32, true>(mc);
+    const float mn = fmaxf(m_run, mc);
+    const float fac = rescale(m_run, mn);
+    float lc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KPL; ++kk) {
+      s[kk] = (mn == kNegInf) ? 0.f : fast_exp2(s[kk] - mn);
+      lc += s[kk];
+    }
+    if constexpr (LPR == 8) lc = xor_combine<8>(lc);
+    lc = xor_combine<16>(lc);
+    lc = xor_combine<32>(lc);
+    l_run = fmaf(l_run, fac, lc);
+    m_run = mn;
+    if constexpr (MPV) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc4[t] *= fac;
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        float vf[EV];
+        unpack16<DT>(vw[kk], vf);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc4[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[t], s[kk], acc4[t], 0, 0, 0);
+      }
+    } else {
+      float fr[RP];
+      fr[0] = fac;
+      gather_rows<RP, F, F + log2_of<RP>() - 1>(fr);
+#pragma unroll
+      for (int j = 0; j < RP; ++j)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[j * EV + e] *= fr[j];
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        float u[RP];
+        u[0] = s[kk];
+        gather_rows<RP, F, F + log2_of<RP>() - 1>(u);
+        float vf[EV];
+        unpack16<DT>(vw[kk], vf);
+#pragma unroll
+        for (int j = 0; j < RP; ++j)
+#pragma unroll
+          for (int e = 0; e < EV; ++e) acc[j * EV + e] = fmaf(u[j], vf[e], acc[j * EV + e]);
+      }
+    }
+  };
+
+  {
+    u32x4 kA[KPL], vA[KPL], kB[KPL], vB[KPL];
+    load_chunk(0, kA, vA);
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+      unpack16<DT>(qw[j], qf[j]);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) qf[j][e] *= scale_log2;
+    }
+    for (int ch = 0; ch < nch; ch += 2) {
+      load_chunk(ch + 1, kB, vB);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce_chunk(ch, kA, vA);
+      load_chunk(ch + 2, kA, vA);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce_chunk(ch + 1, kB, vB);
+    }
+  }
+
+  // Fused step: the new rows to their cache slots, after the loop so that no
+  // store sits in it (no workgroup reads those slots during the call).
+  if constexpr (FUSED) {
+    if (tid < N * LPR) {  // N * LPR <= 8 * 16 <= NT
+      const int i = tid / LPR, cc = tid % LPR;
+      const u32x4 kv = reinterpret_cast<const u32x4 *>(a.k_new)[(nrow0 + i) * LPR + cc];
+      const u32x4 vv = reinterpret_cast<const u32x4 *>(a.v_new)[(nrow0 + i) * LPR + cc];
+      const size_t dst = PAGED ? paged_row(a.pg, b, P + i, layer0 + l, hkv, Hkv) : crow0 + P + i;
+      reinterpret_cast<u32x4 *>(a.k_cache)[dst * LPR + cc] = kv;
+      reinterpret_cast<u32x4 *>(a.v_cache)[dst * LPR + cc] = vv;
+    }
+  }
+  // Sums over the wave's key rows into this wave's LDS slice, as in the
+  // split kernel, then the merge of the waves and the output.
+  if constexpr (MPV) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<f32x4 *>(&sh_o[wave][f * D + 16 * kg + 4 * r]) =
+          f32x4{acc4[0][r], acc4[1][r], acc4[2][r], acc4[3][r]};
+  } else {
+    if constexpr (LPR == 8) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = xor_combine<8>(acc[i]);
+    }
+    float half[NV / 2];
+#pragma unroll
+    for (int i = 0; i < NV / 2; ++i) half[i] = swap_add<32>(acc[i], acc[i + NV / 2]);
+    const int q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i) {
+      const int idx = q * (NV / 4) + i;
+      const int j = idx / EV, e = idx % EV;
+      const float v = swap_add<16>(half[i], half[i + NV / 4]);
+      if (LPR == 16 || (kg & 1) == 0) sh_o[wave][(j ^ f) * D + c * EV + e] = v;
+    }
+  }
+  if (kg == 0) {
+    sh_m[wave][f] = m_run;
+    sh_l[wave][f] = l_run;
+  }
+  __syncthreads();
+  for (int t = tid; t < rows * (D / 4); t += NT) {
+    const int r = t / (D / 4);
+    const int d = (t % (D / 4)) * 4;
+    float M = sh_m[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sh_m[w][r]);
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float fw = rescale(sh_m[w][r], M);
+      o += fw * *reinterpret_cast<const f32x4 *>(&sh_o[w][r * D + d]);
+      L = fmaf(fw, sh_l[w][r], L);
+    }
+    const float inv = 1.f / L;
+    const float val[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    store_elems<DT>(a.o, (size_t)(qrow0 + r) * D + d, val, 4);
+  }
+}
+
+constexpr int kRowsLoopThreads = 256;
+
+template <int DT, int LPR, int RP>
+hipError_t launch_loop_rp(const DecodeArgs &a, bool fused, hipStream_t s) {
+  constexpr bool MPV = DT == KVC_F32 && RP == 8 && LPR == 16;
+  constexpr int KPL = 8;
+  constexpr int NT = kRowsLoopThreads;
+  const dim3 grid((unsigned)(a.n_layers * a.Hkv), 1u, (unsigned)a.nb);
+  const bool paged = a.pg.block_table != nullptr;
+  if (paged && (1 << a.pg.bs_log2) < NT / LPR) return hipErrorInvalidValue;
+  if (a.hist_dev) {
+    if (!fused) return hipErrorInvalidValue;  // device lengths: the fused step only
+    if (paged)
+      hipLaunchKernelGGL((decode_rows_loop_kernel<DT, LPR, RP, KPL, NT, MPV, true, true, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_rows_loop_kernel<DT, LPR, RP, KPL, NT, MPV, true, false, true>), grid, dim3(NT), 0, s, a);
+  } else if (fused && paged)
+    hipLaunchKernelGGL((decode_rows_loop_kernel<DT, LPR, RP, KPL, NT, MPV, true, true, false>), grid, dim3(NT), 0, s, a);
+  else if (fused)
+    hipLaunchKernelGGL((decode_rows_loop_kernel<DT, LPR, RP, KPL, NT, MPV, true, false, false>), grid, dim3(NT), 0, s, a);
+  else if (paged)
+    hipLaunchKernelGGL((decode_rows_loop_kernel<DT, LPR, RP, KPL, NT, MPV, false, true, false>), grid, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_rows_loop_kernel<DT, LPR, RP, KPL, NT, MPV, false, false, false>), grid, dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int LPR>
+hipError_t launch_loop_dt(const DecodeArgs &a, bool fused, hipStream_t s) {
+  if (a.rows <= 2) return launch_loop_rp<DT, LPR, 2>(a, fused, s);
+  if (a.rows <= 4) return launch_loop_rp<DT, LPR, 4>(a, fused, s);
+  if constexpr (DT == KVC_BF16 || LPR == 16) return launch_loop_rp<DT, LPR, 8>(a, fused, s);
+  return hipErrorInvalidValue;
+}
+
 // Keys each lane group loads per split (a split covers 256 / LPR times as
 // many): 8 measured best for the chunked fp32 and the bf16 GQA decode
 // workloads (2, 4, 6, 12 and 16 were slower or equal).
@@ -454,6 +748,17 @@ hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits,
   if (dtype == KVC_F32) return launch_dt<KVC_F32, 16>(a, splits, fused, s);
   return D == 128 ? launch_dt<KVC_BF16, 16>(a, splits, fused, s)
                   : launch_dt<KVC_BF16, 8>(a, splits, fused, s);
+}
+
+hipError_t launch_decode_rows_loop(const DecodeArgs &a, int dtype, int D, bool fused, hipStream_t s) {
+  if (!decode_rows_fits(dtype, D, a.rows) || a.row_tiles != 1) return hipErrorInvalidValue;
+  if (dtype == KVC_F32) return launch_loop_dt<KVC_F32, 16>(a, fused, s);
+  return D == 128 ? launch_loop_dt<KVC_BF16, 16>(a, fused, s) : launch_loop_dt<KVC_BF16, 8>(a, fused, s);
+}
+
+int decode_rows_min_block(int dtype, int D) {
+  const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;
+  return kRowsLoopThreads / lpr;
 }
 
 }  // namespace kvc
