@@ -184,9 +184,11 @@ int device_cus() {
 // the 12-layer fp32 step at T=1024 (144 rows on 256 CUs): see the kernel's
 // notes.  Fewer rows leave most CUs idle (a one-layer call has 12), more
 // queue behind one another, and the split grid serves both.
+constexpr long long kRowKernelMaxPerCu = 2;
+
 bool row_kernel_fits(int units) {
   const long long cus = device_cus();
-  return cus > 0 && 2LL * units >= cus && units <= 2LL * cus;
+  return cus > 0 && 2LL * units >= cus && units <= kRowKernelMaxPerCu * cus;
 }
 
 // Key split of a prefill call: from its grid at key split 1 (the first batch
@@ -566,9 +568,9 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
       // merge alone gives the output (v_P)
       a.grid_splits = splits > 0 ? splits : 1;
       a.grid_splits_div = kvc::magic_for(a.grid_splits);
-      // (a paged cache needs blocks that hold a whole row-group load)
+      // (a paged cache: block tables it can stage in LDS)
       const bool row_kernel = phases == kBoth && row_kernel_fits(a.units) &&
-                              (!pg.block_table || (1 << pg.bs_log2) >= kvc::decode_row_min_block(cache->dtype, cache->D));
+                              (!pg.block_table || pg.max_blocks <= kvc::decode_row_max_blocks());
       if (row_kernel) {
         e = kvc::launch_decode_row(a, cache->dtype, cache->D, (hipStream_t)stream);
       } else if (phases == kBoth && plan.merge_in_launch) {

@@ -73,7 +73,7 @@ __device__ __forceinline__ float row_allreduce(float x) {
 }
 
 template <int NRG>
-constexpr int kLog2Nrg = NRG == 4 ? 2 : NRG == 8 ? 3 : NRG == 16 ? 4 : NRG == 32 ? 5 : NRG == 64 ? 6 : 7;
+constexpr int kLog2Nrg = NRG == 8 ? 3 : NRG == 16 ? 4 : NRG == 32 ? 5 : 6;
 
 // K/V rows are read exactly once per call: non-temporal loads keep them from
 // displacing reusable lines in the caches.
@@ -394,6 +394,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// Block ids of one sequence the paged row kernel stages in LDS (8 KB).
+constexpr int kRowMaxBlocks = 2048;
+
 // One workgroup per query row, for calls whose rows alone fill the chip
 // (about one per CU).  The workgroup streams the whole key range [0, P) of
 // its (layer, sequence, KV head) in chunks of CH = NRG * KPL keys, with the
@@ -412,9 +415,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 // atomic and the merging workgroup's loads through the L2.  Streaming from
 // one workgroup per row leaves the CUs beyond the row count idle, which the
 // host plan weighs against that merge.
-//   PAGED: blocks of at least NRG positions, looked up with one scalar load
-// per chunk load (the host sends smaller blocks to the split kernel, whose
-// per-lane lookups would make every chunk wait for the one before it).
+//   PAGED: the row's block ids are staged in LDS once (at most kRowMaxBlocks
+// of them; the host sends longer tables to the split kernel), so a chunk's
+// loads wait only for LDS reads, not for block-table loads from memory.
 template <int DT, int D, int KPL, int NT, bool PAGED, bool DEVLEN>
 __global__ __launch_bounds__(NT) void decode_row_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;
@@ -453,12 +456,31 @@ __global__ __launch_bounds__(NT) void decode_row_kernel(DecodeArgs a) {
   const char *kc = k_cache + crow0 * (LPR * 16);
   const char *vc = v_cache + crow0 * (LPR * 16);
 
+  __shared__ int32_t sh_blk[PAGED ? kRowMaxBlocks : 1];
+  if constexpr (PAGED) {
+    const int bsl = a.pg.bs_log2;
+    const int nblk = (P + (1 << bsl) - 1) >> bsl;
+    const int32_t *tbl = a.pg.block_table + (size_t)b * a.pg.max_blocks;
+    for (int i = tid; i < nblk; i += NT) {
+      const int blk = tbl[i];
+      sh_blk[i] = blk < 0 ? 0 : (blk >= a.pg.num_blocks ? a.pg.num_blocks - 1 : blk);
+    }
+    __syncthreads();
+  }
+
   // Chunk ch's K loads, then its V loads (positions past P - 1 clamped to it).
   auto load_chunk = [&](int ch, u32x4 (&kw)[KPL], u32x4 (&vw)[KPL]) {
     const int key0 = ch * CH;
     if constexpr (PAGED) {
+      const int bsl = a.pg.bs_log2;
       size_t prow[KPL];
-      paged_rows_grouped<KPL, NRG>(a.pg, b, key0, P - 1, rg, layer0 + l, hkv, Hkv, prow);
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int pos0 = key0 + kk * NRG + rg;
+        const int pos = pos0 < P - 1 ? pos0 : P - 1;
+        prow[kk] = ((((size_t)(layer0 + l) * a.pg.num_blocks + sh_blk[pos >> bsl]) * Hkv + hkv) << bsl) +
+                   (size_t)(pos & ((1 << bsl) - 1));
+      }
       const u32x4 *kb = reinterpret_cast<const u32x4 *>(k_cache);
       const u32x4 *vb = reinterpret_cast<const u32x4 *>(v_cache);
 #pragma unroll
@@ -743,11 +765,6 @@ hipError_t launch_dt(const DecodeArgs &a, int kpl, unsigned grid, hipStream_t s)
 constexpr int kRowThreads = 128;
 constexpr int kRowKpl = 8;
 
-template <int DT, int D>
-constexpr int row_nrg() {
-  return kRowThreads / (D * Dtype<DT>::kBytes / 16);
-}
-
 template <int DT, int D, bool PAGED>
 hipError_t launch_row_pg(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)a.units);
@@ -761,7 +778,7 @@ hipError_t launch_row_pg(const DecodeArgs &a, hipStream_t s) {
 template <int DT, int D>
 hipError_t launch_row_dt(const DecodeArgs &a, hipStream_t s) {
   if (!a.pg.block_table) return launch_row_pg<DT, D, false>(a, s);
-  if (a.pg.bs_log2 < kLog2Nrg<row_nrg<DT, D>()>) return hipErrorInvalidValue;
+  if (a.pg.max_blocks > kRowMaxBlocks) return hipErrorInvalidValue;
   return launch_row_pg<DT, D, true>(a, s);
 }
 
@@ -817,9 +834,6 @@ hipError_t launch_decode_row(const DecodeArgs &a, int dtype, int D, hipStream_t 
   return D == 64 ? launch_row_dt<KVC_BF16, 64>(a, s) : launch_row_dt<KVC_BF16, 128>(a, s);
 }
 
-int decode_row_min_block(int dtype, int D) {
-  if (dtype == KVC_F32) return D == 64 ? row_nrg<KVC_F32, 64>() : row_nrg<KVC_F32, 128>();
-  return D == 64 ? row_nrg<KVC_BF16, 64>() : row_nrg<KVC_BF16, 128>();
-}
+int decode_row_max_blocks() { return kRowMaxBlocks; }
 
 }  // namespace kvc

@@ -325,8 +325,8 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int D, int kpl, bool me
 // One workgroup per query row (G = N = 1, grid = a.units): the whole key
 // range and the merge with key P in one workgroup, no workspace state.
 hipError_t launch_decode_row(const DecodeArgs &a, int dtype, int D, hipStream_t s);
-// Smallest paged block size (positions) launch_decode_row takes.
-int decode_row_min_block(int dtype, int D);
+// Longest block table (blocks per sequence) launch_decode_row takes.
+int decode_row_max_blocks();
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
 hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits,
