@@ -61,10 +61,13 @@ def test_paged_block_sizes(bs):
     check(w, True)
 
 
+@pytest.mark.parametrize("block_size", [1, 16, 256])
 @pytest.mark.parametrize("fused", [False, True])
-def test_paged_chunked(fused):
-    """N = 8 new rows per call: the matrix-core kernel through the table."""
-    check(synth.paged_decode_12layer(1000, block_size=16, seed=44, N=8), fused)
+def test_paged_chunked(fused, block_size):
+    """N = 8 new rows per call, 12 layers (144 KV heads: one workgroup per
+    head over the whole key range, block ids staged in LDS) through the
+    table, at block sizes from one position to more than a chunk."""
+    check(synth.paged_decode_12layer(1000, block_size=block_size, seed=44, N=8), fused)
 
 
 @pytest.mark.parametrize("gqa", [False, True])

@@ -591,7 +591,7 @@ kvc_status decode_impl(const char *fn, int phases, const kvc_cache *cache,
       // when those alone about fill the chip, as for one row per KV head.
       const int heads = n_layers * a.nb * cache->Hkv;
       if (phases == kBoth && g.kernel == DecodeKernel::kRows && row_kernel_fits(heads) &&
-          (!pg.block_table || (1 << pg.bs_log2) >= kvc::decode_rows_min_block(cache->dtype, cache->D))) {
+          (!pg.block_table || pg.max_blocks <= kvc::decode_rows_loop_max_blocks())) {
         e = kvc::launch_decode_rows_loop(a, cache->dtype, cache->D, fused, (hipStream_t)stream);
         if (e != hipSuccess) return hip_status(e, fn);
         continue;

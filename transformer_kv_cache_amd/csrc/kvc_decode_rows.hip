@@ -414,6 +414,9 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(DecodeArgs a) {
 // The sums over the wave's key rows and the merge of the waves run once,
 // after the last chunk, and the output is written directly: no split
 // states, no combine pass.
+// Block ids of one sequence the paged loop kernel stages in LDS (8 KB).
+constexpr int kRowsLoopMaxBlocks = 2048;
+
 template <int DT, int LPR, int RP, int KPL, int NT, bool MPV, bool FUSED, bool PAGED, bool DEVLEN>
 __global__ __launch_bounds__(NT) void decode_rows_loop_kernel(DecodeArgs a) {
   constexpr int EV = Dtype<DT>::kPer16B;
@@ -468,12 +471,35 @@ __global__ __launch_bounds__(NT) void decode_rows_loop_kernel(DecodeArgs a) {
     qw[j] = reinterpret_cast<const u32x4 *>(a.q)[(qrow0 + (rr < rows ? rr : rows - 1)) * LPR + c];
   }
 
+  // A paged cache's block ids of this sequence, staged in LDS once (the host
+  // sends tables longer than kRowsLoopMaxBlocks to the split kernel).
+  __shared__ int32_t sh_blk[PAGED ? kRowsLoopMaxBlocks : 1];
+  if constexpr (PAGED) {
+    const int bsl = a.pg.bs_log2;
+    const int nblk = (nkeys + (1 << bsl) - 1) >> bsl;
+    const int32_t *tbl = a.pg.block_table + (size_t)b * a.pg.max_blocks;
+    for (int i = tid; i < nblk; i += NT) {
+      const int blk = tbl[i];
+      sh_blk[i] = blk < 0 ? 0 : (blk >= a.pg.num_blocks ? a.pg.num_blocks - 1 : blk);
+    }
+    __syncthreads();
+  }
+
   // Chunk ch's K loads, then its V loads; keys past the last clamped to it,
   // keys [P, P + N) from the new rows in the fused step.
   auto load_chunk = [&](int ch, u32x4 (&kw)[KPL], u32x4 (&vw)[KPL]) {
     const int key0 = ch * CH;
     size_t prow[KPL];
-    if constexpr (PAGED) paged_rows_grouped<KPL, NRG>(a.pg, b, key0, nkeys - 1, rg, layer0 + l, hkv, Hkv, prow);
+    if constexpr (PAGED) {
+      const int bsl = a.pg.bs_log2;
+#pragma unroll
+      for (int kk = 0; kk < KPL; ++kk) {
+        const int pos0 = key0 + kk * NRG + rg;
+        const int pos = pos0 < nkeys - 1 ? pos0 : nkeys - 1;
+        prow[kk] = ((((size_t)(layer0 + l) * a.pg.num_blocks + sh_blk[pos >> bsl]) * Hkv + hkv) << bsl) +
+                   (size_t)(pos & ((1 << bsl) - 1));
+      }
+    }
     const u32x4 *vp[KPL];
 #pragma unroll
     for (int kk = 0; kk < KPL; ++kk) {
@@ -667,7 +693,7 @@ hipError_t launch_loop_rp(const DecodeArgs &a, bool fused, hipStream_t s) {
   constexpr int NT = kRowsLoopThreads;
   const dim3 grid((unsigned)(a.n_layers * a.Hkv), 1u, (unsigned)a.nb);
   const bool paged = a.pg.block_table != nullptr;
-  if (paged && (1 << a.pg.bs_log2) < NT / LPR) return hipErrorInvalidValue;
+  if (paged && a.pg.max_blocks > kRowsLoopMaxBlocks) return hipErrorInvalidValue;
   if (a.hist_dev) {
     if (!fused) return hipErrorInvalidValue;  // device lengths: the fused step only
     if (paged)
@@ -756,9 +782,6 @@ hipError_t launch_decode_rows_loop(const DecodeArgs &a, int dtype, int D, bool f
   return D == 128 ? launch_loop_dt<KVC_BF16, 16>(a, fused, s) : launch_loop_dt<KVC_BF16, 8>(a, fused, s);
 }
 
-int decode_rows_min_block(int dtype, int D) {
-  const int lpr = D * (dtype == KVC_BF16 ? 2 : 4) / 16;
-  return kRowsLoopThreads / lpr;
-}
+int decode_rows_loop_max_blocks() { return kRowsLoopMaxBlocks; }
 
 }  // namespace kvc

@@ -333,9 +333,10 @@ hipError_t launch_decode_rows(const DecodeArgs &a, int dtype, int D, int splits,
                               bool fused_append, hipStream_t s);
 // decode_rows_kernel's rows with one workgroup per (layer, sequence, KV
 // head) over the whole key range, writing o directly (grid x = n_layers *
-// Hkv, z = nb); paged caches need blocks of decode_rows_min_block positions.
+// Hkv, z = nb); paged caches with at most decode_rows_loop_max_blocks
+// blocks per sequence.
 hipError_t launch_decode_rows_loop(const DecodeArgs &a, int dtype, int D, bool fused, hipStream_t s);
-int decode_rows_min_block(int dtype, int D);
+int decode_rows_loop_max_blocks();
 hipError_t launch_combine(const DecodeArgs &a, int dtype, int D, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int D, bool history, int ks, hipStream_t s);
 // Key split (1 or 2) of a prefill call whose grid at key split 1 has
