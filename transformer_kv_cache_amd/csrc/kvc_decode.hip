@@ -1,6 +1,8 @@
-// kvc_decode.hip -- split-K ("flash-decode") attention of one new query row
-// per KV head against the KV cache, with the merge of the splits done inside
-// the same launch.
+// kvc_decode.hip -- attention of one new query row per KV head against the
+// KV cache: split-K ("flash-decode") with the merge of the splits done inside
+// the same launch, and, for calls whose rows alone about fill the GPU, one
+// workgroup per row streaming its whole key range (decode_row_kernel, below
+// the split kernel).
 //
 // What it computes ([KV-4] jennyma11.github.io/infra/ch07-01.html, "Decode
 // 阶段", listing 1-2; [KV-2] openai-hub.com/news/2435, "一个很容易漏掉的错误"):

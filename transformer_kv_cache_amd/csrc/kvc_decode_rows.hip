@@ -42,6 +42,8 @@
 // Merge.  The four waves through LDS, then as in the other split kernels:
 // the output directly for a single split, else (max, sum, partial output)
 // per row into the workspace for the combine.
+//   decode_rows_loop_kernel (below) runs the same rows with one workgroup per
+// KV head over the whole key range, for calls whose heads about fill the GPU.
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
