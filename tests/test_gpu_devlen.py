@@ -107,25 +107,39 @@ def test_lengths_past_the_bound_are_clamped():
     assert np.array_equal(bits(outs[0]), bits(outs[1]))
 
 
-@pytest.mark.parametrize("gqa", [False, True])
-def test_paged_graph_captured_decode_loop(gqa):
+PAGED_LOOP_CASES = {
+    # small calls: the split kernels
+    "f32_small": dict(dtype="f32", L=2, B=3, Hq=4, Hkv=4, D=64, max_blocks=16,
+                      hist=[0, 17, 250], step_lens=(1,) * 5),
+    "gqa_bf16_small": dict(dtype="bf16", L=2, B=3, Hq=8, Hkv=2, D=128, max_blocks=16,
+                           hist=[0, 17, 250], step_lens=(1,) * 5),
+    # 144 KV heads: one workgroup per query row / per KV head over the whole
+    # key range, block ids staged in LDS, lengths from the device
+    "f32_12layer": dict(dtype="f32", L=12, B=1, Hq=12, Hkv=12, D=64, max_blocks=64,
+                        hist=[700], step_lens=(1,) * 3),
+    "f32_12layer_chunked": dict(dtype="f32", L=12, B=1, Hq=12, Hkv=12, D=64, max_blocks=64,
+                                hist=[600], step_lens=(8,) * 2),
+}
+
+
+@pytest.mark.parametrize("case", list(PAGED_LOOP_CASES))
+def test_paged_graph_captured_decode_loop(case):
     """The same loop on a paged cache (shuffled blocks of 16): every replay
     matches the oracle's paged append + attention, and the pools end
     byte-identical."""
     from transformer_kv_cache_amd import kvcache as K
-    w = synth.make_paged_workload("devlen_paged", seed=70 + gqa, dtype="bf16" if gqa else "f32",
-                                  L=2, B=3, Hq=8 if gqa else 4, Hkv=2 if gqa else 4,
-                                  D=128 if gqa else 64, block_size=16, max_blocks=16,
-                                  hist=[0, 17, 250], step_lens=(1,) * 5)
+    w = synth.make_paged_workload("devlen_paged", seed=70 + len(case), block_size=16,
+                                  **PAGED_LOOP_CASES[case])
     dt = torch_dtype(w.dtype)
     cache = K.PagedKVCache(w.L, w.num_blocks, w.Hkv, w.block_size, w.D, dt, k=to_dev(w.k_pool),
                            v=to_dev(w.v_pool))
     bt = torch.from_numpy(w.block_table).cuda()
     q, k, v = (to_dev(a) for a in w.steps[0])
+    N = q.shape[3]
     out = torch.empty_like(q)
     hd = torch.from_numpy(w.hist.astype(np.int32)).cuda()
-    ws = K.new_paged_decode_workspace(cache, w.L, w.B, w.Hq, 1, w.max_blocks)
-    hist_max = w.max_blocks * w.block_size - 1
+    ws = K.new_paged_decode_workspace(cache, w.L, w.B, w.Hq, N, w.max_blocks)
+    hist_max = w.max_blocks * w.block_size - N
     K.paged_decode_step_dl(cache, q, k, v, hd, hist_max, bt, scale=w.scale, out=out, workspace=ws)
     torch.cuda.synchronize()
     cache.k.copy_(to_dev(w.k_pool))
@@ -137,12 +151,12 @@ def test_paged_graph_captured_decode_loop(gqa):
         with torch.cuda.graph(g, stream=s):
             K.paged_decode_step_dl(cache, q, k, v, hd, hist_max, bt, scale=w.scale, out=out,
                                    workspace=ws)
-            K.lengths_add(hd, 1)
+            K.lengths_add(hd, N)
     torch.cuda.current_stream().wait_stream(s)
     kp, vp = w.k_pool.copy(), w.v_pool.copy()
     hist = w.hist.copy()
     for n, (qs, ks, vs) in enumerate(w.steps):
-        print(f"[devlen] paged loop gqa={gqa} step {n} hist={hist.tolist()}", flush=True)
+        print(f"[devlen] paged loop {case} step {n} hist={hist.tolist()}", flush=True)
         q.copy_(to_dev(qs)); k.copy_(to_dev(ks)); v.copy_(to_dev(vs))
         g.replay()
         torch.cuda.synchronize()
@@ -150,6 +164,6 @@ def test_paged_graph_captured_decode_loop(gqa):
         ref = oracle.paged_attention(qs, kp, vp, hist, w.block_table, w.scale)
         got = synth.to_float(to_host(out))
         assert float(np.max(np.abs(got - ref))) <= TOL[w.dtype], n
-        hist = hist + 1
+        hist = hist + N
     assert np.array_equal(bits(to_host(cache.k)), bits(kp))
     assert np.array_equal(bits(to_host(cache.v)), bits(vp))
