@@ -90,6 +90,37 @@ ROW_KERNEL_CASES = [
 ]
 
 
+# Two to eight query rows per KV head with 128 to 512 KV heads per call run
+# one workgroup per KV head over the whole key range in chunks of 4 keys per
+# lane group (64 keys for fp32 D=64 and bf16 D=128, 128 for bf16 D=64): keys
+# P + N around the chunk boundaries, an empty history, GQA groups and a
+# chunk that is also a GQA group.
+ROWS_LOOP_CASES = [
+    # (dtype, D, L, Hq, Hkv, N, hist)
+    ("f32", 64, 12, 12, 12, 8, [0]),
+    ("f32", 64, 12, 12, 12, 8, [55]),
+    ("f32", 64, 12, 12, 12, 8, [56]),
+    ("f32", 64, 12, 12, 12, 8, [57]),
+    ("f32", 64, 12, 12, 12, 8, [120]),
+    ("f32", 64, 12, 12, 12, 3, [61, 200]),
+    ("bf16", 128, 12, 48, 12, 1, [63]),
+    ("bf16", 128, 12, 48, 12, 1, [64]),
+    ("bf16", 128, 12, 48, 12, 1, [1000]),
+    ("bf16", 128, 12, 24, 12, 3, [5, 300]),
+    ("bf16", 64, 12, 48, 12, 1, [127]),
+    ("bf16", 64, 12, 48, 12, 1, [128]),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", range(len(ROWS_LOOP_CASES)))
+def test_rows_loop_kernel_shapes(case, fused):
+    dtype, D, L, Hq, Hkv, N, hist = ROWS_LOOP_CASES[case]
+    w = synth.make_workload(f"rows_loop_{case}", seed=150 + case, dtype=dtype, L=L, B=len(hist),
+                            Hq=Hq, Hkv=Hkv, D=D, Tmax=1024, hist=hist, step_lens=(N,))
+    check(w, fused=fused)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("case", range(len(ROW_KERNEL_CASES)))
 def test_row_kernel_shapes(case, fused):
